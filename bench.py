@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Benchmark of the QSA decode step on one MI355X.
+
+Workload (default): 12 QSA layers with independent seeded caches at 255,181
+tokens of context (the 256k input size of the source post), 4 x 128 f16
+indexer keys, 16 q / 2 KV heads x 256 f16 K/V, indexer top-k 2048 tokens.  One
+benchmark step = one decode step of every layer in turn (12 layer-steps; the
+12 pooled caches, 784 MB together, do not fit the 256 MB Infinity Cache, so
+every step streams from HBM).  Every layer-step runs the whole path: append +
+incremental pool, score of every cached block, top-k, gather + attention.
+
+Prints ONE JSON line.  `value` is QSA-layer decode steps per second.
+`roofline` is for the dominant kernel (the block-score stream), timed with HIP
+events around its launches on the stream it runs on.  `cpu_baseline` times
+the CPU oracle on a bounded sample of the same workload (rank 0, N = 1 only).
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "QSA-layer decode steps/s at 256k ctx + achieved HBM GB/s (% of peak)"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def layer_step_bytes(w, n):
+    """Algorithmic HBM bytes of one layer-step at n tokens (current one included)."""
+    nb = n // 4
+    idx_row = w.idx_heads * w.idx_dim * (2 if w.idx_f16 else 4)
+    kv_row = w.kv_heads * w.head_dim * 2
+    n_sel = 4 * min(w.k_blocks, nb) + n % 4
+    pooled = idx_row * nb                         # score stream
+    gathered = 2 * kv_row * n_sel                 # K and V rows of the chosen cells
+    append = idx_row + 2 * kv_row                 # new raw key, K and V rows
+    pool = 4 * idx_row + idx_row if n % 4 == 0 else 0   # a completed block: 4 rows in, 1 out
+    queries = 4 * (w.idx_heads * w.idx_dim + w.idx_heads + 2 * w.q_heads * w.head_dim)
+    return pooled + gathered + append + pool + queries
+
+
+def score_kernel_bytes(w, nb):
+    idx_row = w.idx_heads * w.idx_dim * (2 if w.idx_f16 else 4)
+    return idx_row * nb + 4 * (w.idx_heads * w.idx_dim + w.idx_heads) + 4 * nb
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_record(w, nb):
+    """HBM bytes per score launch from committed rocprofv3 counter runs, if the
+    kernel source has not changed since they were taken."""
+    p = os.path.join(ROOT, "profiles", "score_kernel_traffic.json")
+    src = os.path.join(ROOT, "sparse_attention_decode_cache_amd", "csrc", "k_score.hip")
+    try:
+        rec = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if rec.get("k_score_sha256_16") != source_hash(src) or rec.get("workload") != w.name:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, n_steps):
+    """The CPU oracle on one layer of the same workload, `n_steps` decode steps."""
+    import numpy as np
+    import oracle
+    from qsagen import workloads as W
+    t0 = time.time()
+    cap = w.n0 + n_steps
+    dt = np.float16 if w.idx_f16 else np.float32
+    raw = np.zeros((cap,) + w.idx_row, dt)
+    K = np.zeros((cap,) + w.kv_row, np.float16)
+    V = np.zeros_like(K)
+    rows = np.arange(w.n0)
+    raw[:w.n0] = W.host_raw_rows(w, rows, 0)
+    K[:w.n0], V[:w.n0] = W.host_kv_rows(w, rows, 0)
+    L = oracle.OracleLayer(raw, K, V, W.host_gamma(w, 0), w.rms_eps, w.rope_theta, w.n0, w.k_blocks)
+    L.rebuild()
+    log(f"cpu baseline: oracle cache built in {time.time() - t0:.1f}s")
+    steps = []
+    for s in range(n_steps):
+        pos = w.n0 + s
+        rr = W.host_raw_rows(w, [pos], 0)[0]
+        kr, vr = (x[0] for x in W.host_kv_rows(w, [pos], 0))
+        qi, wt, q = W.host_step_inputs(w, 0, s)
+        t = time.perf_counter()
+        L.step(rr, kr, vr, qi, wt, q)
+        steps.append(time.perf_counter() - t)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(len(steps) / sum(steps), 3), "unit": "QSA-layer decode steps/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"{n_steps} decode steps of layer 0 of {w.name} (n0={w.n0}), fp64 C oracle "
+                      f"with OpenMP over blocks; cache build excluded; median step "
+                      f"{1e3 * statistics.median(steps):.1f} ms"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="qsa-256k-12layers")
+    ap.add_argument("--cpu-steps", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=8, help="score-kernel timing passes")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus must be 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_attention_decode_cache_amd as qsa
+    from qsagen import workloads as W
+
+    w0 = W.WORKLOADS[args.workload]
+    total = args.warmup + args.steps
+    import dataclasses
+    w = dataclasses.replace(w0, steps=total)
+    cap = w.capacity()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    desc = qsa.make_desc(w.idx_heads, w.idx_dim, qsa.QSA_F16 if w.idx_f16 else qsa.QSA_F32,
+                         w.q_heads, w.kv_heads, w.head_dim, w.top_k_tokens, w.rms_eps, w.rope_theta)
+    t0 = time.time()
+    layers = []
+    for li in range(w.layers):
+        buf = qsa.LayerBuffers(desc, cap)
+        W.dev_fill_layer_(w, buf, li, w.n0)
+        gamma = W.dev_gamma(w, li)
+        qsa.qsa_cache_update(desc, buf.cache, gamma, 0, w.n0 // 4)
+        inp = W.dev_step_inputs(w, li, 0, total)
+        layers.append({"buf": buf, "gamma": gamma, "inp": inp,
+                       "state": qsa.qsa_seq_state(w.n0, w.n0 // 4),
+                       "out": torch.empty((w.q_heads, w.head_dim), dtype=torch.float32, device=dev)})
+    ws = qsa.workspace(desc, cap)
+    torch.cuda.synchronize()
+    log(f"{w.name}: {w.layers} layers, capacity {cap}, set up in {time.time() - t0:.1f}s")
+
+    def layer_step(L, s):
+        inp = L["inp"]
+        qsa.qsa_decode_step(desc, L["buf"].cache, L["state"], inp.raw[s], inp.k[s], inp.v[s],
+                            L["gamma"], inp.q_idx[s], inp.w[s], inp.q[s], L["out"], None, None, ws,
+                            stream)
+
+    for s in range(args.warmup):
+        for L in layers:
+            layer_step(L, s)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    nbytes = 0
+    torch.cuda.synchronize()
+    events[0].record(stream)
+    for i in range(args.steps):
+        s = args.warmup + i
+        for L in layers:
+            n = L["state"].n_tokens + 1
+            nbytes += layer_step_bytes(w, n)
+            layer_step(L, s)
+        events[i + 1].record(stream)
+    torch.cuda.synchronize()
+    step_ms = [events[i].elapsed_time(events[i + 1]) for i in range(args.steps)]
+    total_ms = events[0].elapsed_time(events[-1])
+    layer_steps = args.steps * w.layers
+    value = layer_steps / (total_ms / 1e3)
+    step_gbs = nbytes / (total_ms / 1e3) / 1e9
+    log(f"timed {args.steps} steps: {total_ms:.3f} ms, {value:.0f} layer-steps/s, {step_gbs:.0f} GB/s")
+
+    # Dominant kernel: the block-score stream.  Same kernel and grid as inside the
+    # decode step, launched through qsa_index_score and bracketed by HIP events on
+    # the same stream, over the same 12 caches (round-robin, so HBM-resident).
+    nb = layers[0]["state"].n_tokens // 4
+    q_idx = layers[0]["inp"].q_idx[0]
+    wt = layers[0]["inp"].w[0]
+    scores = torch.empty(nb, dtype=torch.float32, device=dev)
+    durs = []
+    for rep in range(args.kernel_reps):
+        for L in layers:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            qsa.qsa_index_score(desc, L["buf"].cache, nb, q_idx, wt, scores, stream)
+            e1.record(stream)
+            durs.append((e0, e1))
+    torch.cuda.synchronize()
+    kms = [a.elapsed_time(b) for a, b in durs[len(layers):]]   # drop the first pass
+    k_avg_s = statistics.mean(kms) / 1e3
+    kbytes = score_kernel_bytes(w, nb)
+    achieved = kbytes / k_avg_s / 1e9
+    traffic = traffic_record(w, nb)
+    log(f"score kernel: {1e6 * k_avg_s:.2f} us avg over {len(kms)} launches, {achieved:.0f} GB/s")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "QSA-layer decode steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.layers, "context_tokens": w0.n0,
+                   "layer_steps_per_step": w.layers, "idx": f"{w.idx_heads}x{w.idx_dim} "
+                   f"{'f16' if w.idx_f16 else 'f32'}", "attn": f"{w.q_heads}/{w.kv_heads}x{w.head_dim} f16",
+                   "top_k_tokens": w.top_k_tokens, "storage": "f16", "accumulate": "f32"},
+        "layer_step_us": {"median": round(1e3 * statistics.median(step_ms) / w.layers, 3),
+                          "p10": round(1e3 * sorted(step_ms)[len(step_ms) // 10] / w.layers, 3),
+                          "p90": round(1e3 * sorted(step_ms)[(9 * len(step_ms)) // 10] / w.layers, 3)},
+        "step_hbm": {"achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(step_gbs / HBM_PEAK_GBS, 4),
+                     "bytes_per_layer_step": round(nbytes / layer_steps)},
+        "roofline": {"bound": "hbm", "kernel": "k_score (block-score stream)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "bytes_per_launch": kbytes,
+                     "avg_launch_us": round(1e6 * k_avg_s, 3)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline ...")
+        result["cpu_baseline"] = cpu_baseline(w0, args.cpu_steps)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

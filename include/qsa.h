@@ -1,0 +1,193 @@
+/*
+ * qsa.h -- C ABI of the QSA (Qwen Sparse Attention) decode-step library for
+ * AMD Instinct MI355X (gfx950).  Implemented in hand-written HIP kernels in
+ * libqsa.so.
+ *
+ * Method source: post 10 by "ariera" on qiita.com, "第10回 EVO-X2（Ryzen AI Max+
+ * 395 / 128GB）+ Qwen3.8-Flash-Next用のllama.cpp改造で長コンテキストのTGを高速化した話".
+ * Sections cited by heading:
+ *   "QSA indexer"                              -- pool / RMS norm / RoPE / score / top-k
+ *   "incremental pooled-key cache（COMMON-004）" -- cache of completed-block summaries
+ *   "selected QSA K/V gather（COMMON-005）"     -- attend over gathered K/V rows only
+ *   "block-domain top-k（COMMON-006）実装は見送り" -- top-k on blocks, then tail cells
+ *   "なぜFlash Attentionがcontext長に比例していたのか" -- at most 2048 + 4 - 1 cells
+ *
+ * One decode step of one layer, for the token at position n-1 (n tokens,
+ * current one included), micro-block m = 4:
+ *   N_b  = floor(n / 4) completed blocks, tail = n mod 4 cells;
+ *   1. summary row b (b < N_b) = RoPE_{p=4b}( RMSNorm_gamma( mean of raw
+ *      indexer-key rows 4b..4b+3 ) ), per indexer head, rounded once to the
+ *      raw-key dtype; rows are cached and only [valid, N_b) are recomputed;
+ *   2. s[b] = sum_h w[h] * <q_idx[h], summary[b][h]>  for b < N_b;
+ *   3. the K_b = min(top_k_tokens / 4, N_b) blocks ranked first by
+ *      (s descending, b ascending), returned as ascending ids;
+ *   4. cells = {4b .. 4b+3 : b chosen} + {4 N_b .. n-1}  (4 K_b + tail <= 2051
+ *      for top_k_tokens = 2048); for each query head h, with KV head
+ *      g = floor(h * Hkv / Hq): out[h] = softmax_c(scale * <q[h], K[c][g]>) . V[c][g].
+ *
+ * Conventions
+ *   - Every buffer is caller-owned.  Pointers marked DEVICE must point to
+ *     device memory of the current HIP device, 16-byte aligned; HOST pointers
+ *     are host memory.  The library never allocates, frees or synchronises.
+ *   - Every call only enqueues work on `stream` and returns; results are
+ *     valid when the stream reaches that point.  The host never reads device
+ *     memory, so no call blocks.
+ *   - Argument checks run before any launch.  On a failed check nothing is
+ *     enqueued, no state is changed, and the status is QSA_ERR_ARG,
+ *     QSA_ERR_UNSUPPORTED (shape outside the supported set) or
+ *     QSA_ERR_WORKSPACE.  A launch failure returns QSA_ERR_HIP.
+ *     qsa_last_error() gives a thread-local description of the last failure.
+ *   - Supported shapes: block = 4; idx_heads in {1, 4}; idx_dim in {64, 128};
+ *     idx row (idx_heads * idx_dim * sizeof(dtype)) <= 1024 bytes;
+ *     head_dim in {64, 128, 256}; q_heads = G * kv_heads with G in {1,2,4,8};
+ *     top_k_tokens a positive
+ *     multiple of 4; capacity a positive multiple of 4, <= 2^26 tokens.
+ *   - A workspace (DEVICE, 256-byte aligned, >= qsa_workspace_bytes) holds
+ *     scratch only.  Calls that share a workspace must be stream-ordered.
+ *     Its contents need no initialisation and are meaningless between calls.
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QSA_OK = 0,
+    QSA_ERR_ARG = -1,          /* null pointer, bad range, n > capacity, ... */
+    QSA_ERR_UNSUPPORTED = -2,  /* shape outside the supported set above */
+    QSA_ERR_WORKSPACE = -3,    /* workspace missing, misaligned or too small */
+    QSA_ERR_HIP = -4           /* a kernel launch failed */
+} qsa_status;
+
+typedef enum { QSA_F32 = 0, QSA_F16 = 1 } qsa_dtype;
+
+/* Per-layer constants (HOST struct, read during the call only). */
+typedef struct {
+    int32_t block;         /* micro-block size m; must be 4 */
+    int32_t idx_heads;     /* H_i: indexer heads */
+    int32_t idx_dim;       /* D_i: indexer head dim (even) */
+    int32_t idx_dtype;     /* qsa_dtype of raw indexer keys AND of summaries */
+    float rms_eps;         /* added to the mean square inside the root */
+    float rope_theta;      /* RoPE base; frequency of pair j is theta^(-2j/D_i) */
+    int32_t q_heads;       /* Hq */
+    int32_t kv_heads;      /* Hkv */
+    int32_t head_dim;      /* Dh */
+    int32_t top_k_tokens;  /* indexer top-k in tokens; K = top_k_tokens / 4 blocks */
+    float attn_scale;      /* logit scale; 0 means 1/sqrt(head_dim) */
+} qsa_layer_desc;
+
+/* One sequence x one layer cache (HOST struct of DEVICE pointers). */
+typedef struct {
+    void *idx_k;           /* DEVICE [capacity][H_i][D_i] idx_dtype; row t = position t */
+    void *summary;         /* DEVICE [capacity/4][H_i][D_i] idx_dtype; row b = block b */
+    uint16_t *k;           /* DEVICE [capacity][Hkv][Dh] binary16 bits; row t = position t */
+    uint16_t *v;           /* DEVICE [capacity][Hkv][Dh] binary16 bits */
+    int32_t capacity;      /* tokens */
+} qsa_layer_cache;
+
+/* Host-side sequence state: tokens in the cache and the summary watermark
+ * (rows [0, n_valid_blocks) are trusted). */
+typedef struct {
+    int32_t n_tokens;
+    int32_t n_valid_blocks;
+} qsa_seq_state;
+
+/* Scratch bytes needed by qsa_decode_step / qsa_gather_attend /
+ * qsa_topk_blocks for any token count up to `capacity`.  Returns 0 for an
+ * invalid or unsupported descriptor. */
+size_t qsa_workspace_bytes(const qsa_layer_desc *desc, int32_t capacity);
+
+/* State load or distrust from position `pos` [post 10, COMMON-004 section:
+ * the cache is invalidated and rebuilt when next needed]:
+ * n_valid_blocks = min(n_valid_blocks, floor(pos / 4)); tokens are kept.
+ * HOST only; no device work.  Negative pos is treated as 0. */
+void qsa_state_invalidate(qsa_seq_state *st, int32_t pos);
+
+/* Sequence edit at `pos`: n_tokens = min(n_tokens, pos), then
+ * qsa_state_invalidate(st, pos).  HOST only. */
+void qsa_state_truncate(qsa_seq_state *st, int32_t pos);
+
+/* Stage 1 [post 10, "QSA indexer", "incremental pooled-key cache
+ * （COMMON-004）"]: (re)compute summary rows [blk_begin, blk_end) from raw
+ * indexer-key rows 4*blk_begin .. 4*blk_end-1 already in cache->idx_k.
+ * gamma: DEVICE fp32 [D_i].  Rows are independent; recomputing a range is
+ * idempotent and bitwise deterministic.  Mean, norm and rotation are
+ * evaluated in double (the RoPE angle at positions near 2^18 needs it) and
+ * rounded once to the storage dtype.
+ * Errors: ARG if 0 <= blk_begin <= blk_end <= capacity/4 fails or a needed
+ * pointer is null.  An empty range enqueues nothing. */
+qsa_status qsa_cache_update(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
+                            const float *gamma, int32_t blk_begin, int32_t blk_end,
+                            hipStream_t stream);
+
+/* Stage 2 [post 10, "QSA indexer"]: scores[b] = sum_h w[h] * sum_i
+ * q_idx[h][i] * summary[b][h][i] for b < n_blocks, in fp32 (w folded into
+ * q_idx once per call).  q_idx: DEVICE fp32 [H_i][D_i]; w: DEVICE fp32
+ * [H_i]; scores: DEVICE fp32 [n_blocks].  n_blocks = 0 enqueues nothing.
+ * Errors: ARG if n_blocks < 0 or n_blocks > capacity/4 or a pointer is null. */
+qsa_status qsa_index_score(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
+                           int32_t n_blocks, const float *q_idx, const float *w,
+                           float *scores, hipStream_t stream);
+
+/* Stage 3 [post 10, "QSA indexer"; "block-domain top-k（COMMON-006）実装は
+ * 見送り"]: writes the min(k_blocks, n_blocks) ids ranked first by (score
+ * descending, id ascending) to sel (DEVICE int32), in ascending id order.
+ * -0.0 and +0.0 are equal; scores must be finite.  The result does not depend
+ * on scheduling or atomic order.  scores: DEVICE fp32 [n_blocks].
+ * Workspace >= qsa_workspace_bytes of any descriptor whose capacity >=
+ * 4 * n_blocks.
+ * Errors: ARG if n_blocks < 0, k_blocks < 1 or a pointer is null;
+ * WORKSPACE if ws is null, misaligned or smaller than needed. */
+qsa_status qsa_topk_blocks(const float *scores, int32_t n_blocks, int32_t k_blocks,
+                           int32_t *sel, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Stage 4 [post 10, "selected QSA K/V gather（COMMON-005）"]: attention of
+ * the current query over the cells {4*sel[i] + j : i < n_sel_blocks, j < 4}
+ * followed by the tail cells 4*floor(n_tokens/4) .. n_tokens-1, reading only
+ * those K/V rows.  sel: DEVICE int32 [n_sel_blocks], ascending, each id <
+ * floor(n_tokens/4); may be NULL only when n_sel_blocks == floor(n_tokens/4)
+ * (every block kept).  q: DEVICE fp32 [Hq][Dh]; out: DEVICE fp32 [Hq][Dh].
+ * Split-context flash-decode: partial softmax states go to the workspace and
+ * are merged in a fixed order, so results are bitwise repeatable.
+ * Errors: ARG if n_tokens < 1, n_tokens > capacity, n_sel_blocks outside
+ * [0, min(top_k_tokens/4, floor(n_tokens/4))] or a pointer is null;
+ * WORKSPACE as above. */
+qsa_status qsa_gather_attend(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
+                             int32_t n_tokens, const int32_t *sel, int32_t n_sel_blocks,
+                             const float *q, float *out, void *ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+/* The fused decode step (stages 1-4 on one stream, no host synchronisation)
+ * [post 10, all sections above].  Appends the new token at pos =
+ * st->n_tokens: copies idx_k_row (DEVICE [H_i][D_i] idx_dtype), k_row and
+ * v_row (DEVICE [Hkv][Dh] binary16) into the cache at row pos; n = pos + 1;
+ * rebuilds summary rows [st->n_valid_blocks, n/4); scores, selects and
+ * attends as above.  gamma, q_idx, w, q, out as in the stage calls.
+ * sel_out (DEVICE int32 [min(K, n/4)]) and scores_out (DEVICE fp32 [n/4])
+ * are optional (NULL to skip).  On success st becomes {n, n/4}; on any
+ * error st is unchanged.
+ * Errors: ARG if st->n_tokens < 0, pos >= capacity or a pointer is null;
+ * UNSUPPORTED / WORKSPACE as above. */
+qsa_status qsa_decode_step(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
+                           qsa_seq_state *st, const void *idx_k_row, const uint16_t *k_row,
+                           const uint16_t *v_row, const float *gamma, const float *q_idx,
+                           const float *w, const float *q, float *out, int32_t *sel_out,
+                           float *scores_out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Static text for a status code. */
+const char *qsa_status_string(qsa_status s);
+
+/* Thread-local detail of the last non-OK status returned on this thread
+ * ("" if none). */
+const char *qsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QSA_H */

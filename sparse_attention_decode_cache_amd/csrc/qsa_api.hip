@@ -1,0 +1,415 @@
+// qsa_api.hip -- the C ABI declared in include/qsa.h: argument checks,
+// workspace carve-up and the launch sequence of each entry point.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "qsa_internal.h"
+
+using namespace qsa;
+
+namespace {
+
+thread_local char tl_err[512] = "";
+
+qsa_status fail(qsa_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(tl_err, sizeof(tl_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+qsa_status ok()
+{
+    tl_err[0] = '\0';
+    return QSA_OK;
+}
+
+qsa_status hip_fail(hipError_t e, const char *where)
+{
+    return fail(QSA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int elem_bytes(int32_t dtype) { return dtype == QSA_F16 ? 2 : 4; }
+
+qsa_status check_desc(const qsa_layer_desc *d)
+{
+    if (!d)
+        return fail(QSA_ERR_ARG, "desc is NULL");
+    if (d->block != 4)
+        return fail(QSA_ERR_UNSUPPORTED, "block must be 4 (got %d)", d->block);
+    if (d->idx_dtype != QSA_F16 && d->idx_dtype != QSA_F32)
+        return fail(QSA_ERR_UNSUPPORTED, "idx_dtype %d", d->idx_dtype);
+    if (d->idx_heads != 1 && d->idx_heads != 4)
+        return fail(QSA_ERR_UNSUPPORTED, "idx_heads must be 1 or 4 (got %d)", d->idx_heads);
+    if (d->idx_dim != 64 && d->idx_dim != 128)
+        return fail(QSA_ERR_UNSUPPORTED, "idx_dim must be 64 or 128 (got %d)", d->idx_dim);
+    if (d->idx_heads * d->idx_dim * elem_bytes(d->idx_dtype) > 1024)
+        return fail(QSA_ERR_UNSUPPORTED, "indexer row larger than 1024 bytes");
+    if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 256)
+        return fail(QSA_ERR_UNSUPPORTED, "head_dim must be 64, 128 or 256 (got %d)", d->head_dim);
+    if (d->kv_heads < 1 || d->q_heads < 1 || d->q_heads % d->kv_heads != 0)
+        return fail(QSA_ERR_UNSUPPORTED, "q_heads %d not a multiple of kv_heads %d", d->q_heads,
+                    d->kv_heads);
+    const int G = d->q_heads / d->kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(QSA_ERR_UNSUPPORTED, "q_heads / kv_heads must be 1, 2, 4 or 8 (got %d)", G);
+    if (d->top_k_tokens < 4 || d->top_k_tokens % 4 != 0)
+        return fail(QSA_ERR_UNSUPPORTED, "top_k_tokens must be a positive multiple of 4 (got %d)",
+                    d->top_k_tokens);
+    if (!(d->rms_eps >= 0.0f) || !(d->rope_theta > 0.0f) || !(d->attn_scale >= 0.0f) ||
+        !isfinite(d->rope_theta) || !isfinite(d->attn_scale))
+        return fail(QSA_ERR_ARG, "rms_eps / rope_theta / attn_scale out of range");
+    return QSA_OK;
+}
+
+qsa_status check_cache(const qsa_layer_cache *c, bool need_idx, bool need_sum, bool need_kv)
+{
+    if (!c)
+        return fail(QSA_ERR_ARG, "cache is NULL");
+    if (c->capacity < 4 || c->capacity % 4 != 0 || c->capacity > (1 << 26))
+        return fail(QSA_ERR_ARG, "capacity must be a positive multiple of 4, <= 2^26 (got %d)",
+                    c->capacity);
+    if ((need_idx && (!c->idx_k || !aligned(c->idx_k, 16))) ||
+        (need_sum && (!c->summary || !aligned(c->summary, 16))) ||
+        (need_kv && (!c->k || !c->v || !aligned(c->k, 16) || !aligned(c->v, 16))))
+        return fail(QSA_ERR_ARG, "cache pointer NULL or not 16-byte aligned");
+    return QSA_OK;
+}
+
+float attn_scale(const qsa_layer_desc *d)
+{
+    return d->attn_scale > 0.0f ? d->attn_scale : 1.0f / sqrtf((float)d->head_dim);
+}
+
+int64_t decode_part_floats(const qsa_layer_desc *d)
+{
+    const int G = d->q_heads / d->kv_heads;
+    const int64_t max_cells = (int64_t)d->top_k_tokens + 3;
+    return (int64_t)d->kv_heads * n_splits(max_cells) * part_stride(G, d->head_dim);
+}
+
+WsLayout decode_layout(const qsa_layer_desc *d, int32_t capacity)
+{
+    return ws_layout(capacity / 4, d->top_k_tokens / 4, decode_part_floats(d));
+}
+
+qsa_status check_ws(void *ws, size_t ws_bytes, size_t need)
+{
+    if (!ws || !aligned(ws, 256))
+        return fail(QSA_ERR_WORKSPACE, "workspace NULL or not 256-byte aligned");
+    if (ws_bytes < need)
+        return fail(QSA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+    return QSA_OK;
+}
+
+// Stage 4 launch shared by qsa_gather_attend and qsa_decode_step.
+qsa_status do_attend(const qsa_layer_desc *d, const qsa_layer_cache *c, int32_t n_tokens,
+                     const int32_t *sel, int32_t n_sel_blocks, const float *q, float *out,
+                     float *part, hipStream_t stream)
+{
+    AttendArgs a{};
+    a.k = c->k;
+    a.v = c->v;
+    a.sel = sel;
+    a.q = q;
+    a.part = part;
+    a.out = out;
+    a.n_sel_blocks = n_sel_blocks;
+    a.nb = n_tokens / 4;
+    a.n_cells = 4 * n_sel_blocks + n_tokens % 4;
+    if (!sel)
+        a.n_cells = n_tokens;      // every block kept: cells are 0..n-1
+    a.n_split = (int32_t)n_splits(a.n_cells);
+    a.kv_heads = d->kv_heads;
+    a.scale = attn_scale(d);
+    hipError_t e = launch_attend(a, d->head_dim, d->q_heads / d->kv_heads, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "attend");
+    return QSA_OK;
+}
+
+// Stage 3 launch over keys + histogram already in the workspace.
+qsa_status do_select(char *ws, const WsLayout &L, int32_t nb, int32_t k, int32_t *sel,
+                     hipStream_t stream)
+{
+    SelectArgs s{};
+    s.keys = (const uint32_t *)(ws + L.keys);
+    s.hist = (const uint32_t *)(ws + L.hist);
+    s.ctrl = (uint32_t *)(ws + L.ctrl);
+    s.bitmap = (uint64_t *)(ws + L.bitmap);
+    s.cand = (uint64_t *)(ws + L.cand);
+    s.sel = sel;
+    s.nb = nb;
+    s.k = k;
+    hipError_t e = launch_select(s, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "select");
+    return QSA_OK;
+}
+
+int32_t ctrl_hist_words(const WsLayout &L) { return (int32_t)((L.hist - L.ctrl) / 4 + kHistBins); }
+
+}  // namespace
+
+extern "C" {
+
+size_t qsa_workspace_bytes(const qsa_layer_desc *desc, int32_t capacity)
+{
+    if (check_desc(desc) != QSA_OK || capacity < 4 || capacity % 4 != 0 || capacity > (1 << 26))
+        return 0;
+    return decode_layout(desc, capacity).total;
+}
+
+void qsa_state_invalidate(qsa_seq_state *st, int32_t pos)
+{
+    if (!st)
+        return;
+    if (pos < 0)
+        pos = 0;
+    const int32_t b = pos / 4;
+    if (st->n_valid_blocks > b)
+        st->n_valid_blocks = b;
+}
+
+void qsa_state_truncate(qsa_seq_state *st, int32_t pos)
+{
+    if (!st)
+        return;
+    if (pos < 0)
+        pos = 0;
+    if (st->n_tokens > pos)
+        st->n_tokens = pos;
+    qsa_state_invalidate(st, pos);
+}
+
+qsa_status qsa_cache_update(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
+                            const float *gamma, int32_t blk_begin, int32_t blk_end,
+                            hipStream_t stream)
+{
+    qsa_status s;
+    if ((s = check_desc(desc)) != QSA_OK || (s = check_cache(cache, true, true, false)) != QSA_OK)
+        return s;
+    if (!gamma)
+        return fail(QSA_ERR_ARG, "gamma is NULL");
+    if (blk_begin < 0 || blk_end < blk_begin || blk_end > cache->capacity / 4)
+        return fail(QSA_ERR_ARG, "block range [%d, %d) outside [0, %d]", blk_begin, blk_end,
+                    cache->capacity / 4);
+    if (blk_end == blk_begin)
+        return ok();
+    UpdateArgs a{};
+    a.idx_k = cache->idx_k;
+    a.summary = cache->summary;
+    a.gamma = gamma;
+    a.b0 = blk_begin;
+    a.nblk = blk_end - blk_begin;
+    a.H = desc->idx_heads;
+    a.D = desc->idx_dim;
+    a.eps = (double)desc->rms_eps;
+    a.theta = (double)desc->rope_theta;
+    hipError_t e = launch_update(a, desc->idx_dtype == QSA_F16, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "cache_update");
+    return ok();
+}
+
+qsa_status qsa_index_score(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
+                           int32_t n_blocks, const float *q_idx, const float *w, float *scores,
+                           hipStream_t stream)
+{
+    qsa_status s;
+    if ((s = check_desc(desc)) != QSA_OK || (s = check_cache(cache, false, true, false)) != QSA_OK)
+        return s;
+    if (n_blocks < 0 || n_blocks > cache->capacity / 4)
+        return fail(QSA_ERR_ARG, "n_blocks %d outside [0, %d]", n_blocks, cache->capacity / 4);
+    if (!q_idx || !w || !scores)
+        return fail(QSA_ERR_ARG, "q_idx / w / scores is NULL");
+    if (n_blocks == 0)
+        return ok();
+    ScoreArgs a{};
+    a.summary = cache->summary;
+    a.q = q_idx;
+    a.w = w;
+    a.scores = scores;
+    a.nb = n_blocks;
+    a.D = desc->idx_dim;
+    const int rowb = desc->idx_heads * desc->idx_dim * elem_bytes(desc->idx_dtype);
+    hipError_t e = launch_score(a, desc->idx_dtype == QSA_F16, rowb, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "index_score");
+    return ok();
+}
+
+qsa_status qsa_topk_blocks(const float *scores, int32_t n_blocks, int32_t k_blocks, int32_t *sel,
+                           void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (n_blocks < 0 || n_blocks > (1 << 24) || k_blocks < 1)
+        return fail(QSA_ERR_ARG, "n_blocks %d / k_blocks %d out of range", n_blocks, k_blocks);
+    if ((n_blocks > 0 && !scores) || !sel)
+        return fail(QSA_ERR_ARG, "scores / sel is NULL");
+    if (n_blocks == 0)
+        return ok();
+    if (n_blocks <= k_blocks) {
+        hipError_t e = launch_iota(sel, n_blocks, stream);
+        return e == hipSuccess ? ok() : hip_fail(e, "topk_blocks");
+    }
+    const WsLayout L = ws_layout(n_blocks, 0, 0);
+    qsa_status st = check_ws(ws, ws_bytes, L.total);
+    if (st != QSA_OK)
+        return st;
+    char *w = (char *)ws;
+    hipError_t e = launch_fill_zero((uint32_t *)(w + L.ctrl), ctrl_hist_words(L), stream);
+    if (e == hipSuccess)
+        e = launch_keys_hist(scores, n_blocks, (uint32_t *)(w + L.keys), (uint32_t *)(w + L.hist),
+                             stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "topk_blocks");
+    st = do_select(w, L, n_blocks, k_blocks, sel, stream);
+    return st == QSA_OK ? ok() : st;
+}
+
+qsa_status qsa_gather_attend(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
+                             int32_t n_tokens, const int32_t *sel, int32_t n_sel_blocks,
+                             const float *q, float *out, void *ws, size_t ws_bytes,
+                             hipStream_t stream)
+{
+    qsa_status s;
+    if ((s = check_desc(desc)) != QSA_OK || (s = check_cache(cache, false, false, true)) != QSA_OK)
+        return s;
+    const int32_t nb = n_tokens / 4;
+    const int32_t K = desc->top_k_tokens / 4;
+    if (n_tokens < 1 || n_tokens > cache->capacity)
+        return fail(QSA_ERR_ARG, "n_tokens %d outside [1, %d]", n_tokens, cache->capacity);
+    if (n_sel_blocks < 0 || n_sel_blocks > nb || n_sel_blocks > K)
+        return fail(QSA_ERR_ARG, "n_sel_blocks %d outside [0, min(%d, %d)]", n_sel_blocks, K, nb);
+    if (!sel && n_sel_blocks != nb)
+        return fail(QSA_ERR_ARG, "sel may be NULL only when every block is kept");
+    if (!q || !out)
+        return fail(QSA_ERR_ARG, "q / out is NULL");
+    const WsLayout L = decode_layout(desc, cache->capacity);
+    if ((s = check_ws(ws, ws_bytes, L.total)) != QSA_OK)
+        return s;
+    s = do_attend(desc, cache, n_tokens, sel, n_sel_blocks, q, out,
+                  (float *)((char *)ws + L.part), stream);
+    return s == QSA_OK ? ok() : s;
+}
+
+qsa_status qsa_decode_step(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
+                           qsa_seq_state *st, const void *idx_k_row, const uint16_t *k_row,
+                           const uint16_t *v_row, const float *gamma, const float *q_idx,
+                           const float *w, const float *q, float *out, int32_t *sel_out,
+                           float *scores_out, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    qsa_status s;
+    if ((s = check_desc(desc)) != QSA_OK || (s = check_cache(cache, true, true, true)) != QSA_OK)
+        return s;
+    if (!st)
+        return fail(QSA_ERR_ARG, "state is NULL");
+    if (!idx_k_row || !k_row || !v_row || !gamma || !q_idx || !w || !q || !out)
+        return fail(QSA_ERR_ARG, "an input or output pointer is NULL");
+    if (!aligned(idx_k_row, 4) || !aligned(k_row, 4) || !aligned(v_row, 4) ||
+        !aligned(q, 16))
+        return fail(QSA_ERR_ARG, "row pointers must be 4-byte aligned and q 16-byte aligned");
+    const int32_t pos = st->n_tokens;
+    if (pos < 0 || pos >= cache->capacity)
+        return fail(QSA_ERR_ARG, "position %d outside [0, %d)", pos, cache->capacity);
+    if (st->n_valid_blocks < 0)
+        return fail(QSA_ERR_ARG, "n_valid_blocks %d < 0", st->n_valid_blocks);
+    const WsLayout L = decode_layout(desc, cache->capacity);
+    if ((s = check_ws(ws, ws_bytes, L.total)) != QSA_OK)
+        return s;
+
+    const int32_t n = pos + 1;
+    const int32_t nb = n / 4;
+    const int32_t K = desc->top_k_tokens / 4;
+    const int32_t b0 = st->n_valid_blocks < nb ? st->n_valid_blocks : nb;
+    const bool need_select = nb > K;
+    const int ebytes = elem_bytes(desc->idx_dtype);
+    const int rowb = desc->idx_heads * desc->idx_dim * ebytes;
+    char *wsp = (char *)ws;
+
+    // 1. append + pool [b0, nb) (+ clear the top-k control words and histogram)
+    UpdateArgs u{};
+    u.idx_k = cache->idx_k;
+    u.summary = cache->summary;
+    u.k = cache->k;
+    u.v = cache->v;
+    u.new_idx_row = idx_k_row;
+    u.new_k_row = k_row;
+    u.new_v_row = v_row;
+    u.gamma = gamma;
+    u.clear_ptr = need_select ? (uint32_t *)(wsp + L.ctrl) : nullptr;
+    u.clear_words = need_select ? ctrl_hist_words(L) : 0;
+    u.idx_row_words = rowb / 4;
+    u.kv_row_words = desc->kv_heads * desc->head_dim / 2;
+    u.pos = pos;
+    u.b0 = b0;
+    u.nblk = nb - b0;
+    u.H = desc->idx_heads;
+    u.D = desc->idx_dim;
+    u.eps = (double)desc->rms_eps;
+    u.theta = (double)desc->rope_theta;
+    hipError_t e = launch_update(u, desc->idx_dtype == QSA_F16, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "decode_step/update");
+
+    // 2. score every completed block (+ keys and histogram for the top-k)
+    if (nb > 0 && (need_select || scores_out)) {
+        ScoreArgs a{};
+        a.summary = cache->summary;
+        a.q = q_idx;
+        a.w = w;
+        a.scores = scores_out;
+        a.keys = need_select ? (uint32_t *)(wsp + L.keys) : nullptr;
+        a.hist = need_select ? (uint32_t *)(wsp + L.hist) : nullptr;
+        a.nb = nb;
+        a.D = desc->idx_dim;
+        e = launch_score(a, desc->idx_dtype == QSA_F16, rowb, stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "decode_step/score");
+    }
+
+    // 3. top-k (every block is kept when nb <= K)
+    const int32_t *sel = nullptr;
+    int32_t n_sel = nb;
+    if (need_select) {
+        int32_t *dst = sel_out ? sel_out : (int32_t *)(wsp + L.sel);
+        if ((s = do_select(wsp, L, nb, K, dst, stream)) != QSA_OK)
+            return s;
+        sel = dst;
+        n_sel = K;
+    } else if (sel_out && nb > 0) {
+        e = launch_iota(sel_out, nb, stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "decode_step/iota");
+    }
+
+    // 4. gather + attend
+    if ((s = do_attend(desc, cache, n, sel, n_sel, q, out, (float *)(wsp + L.part), stream)) !=
+        QSA_OK)
+        return s;
+
+    st->n_tokens = n;
+    st->n_valid_blocks = nb;
+    return ok();
+}
+
+const char *qsa_status_string(qsa_status s)
+{
+    switch (s) {
+    case QSA_OK: return "ok";
+    case QSA_ERR_ARG: return "invalid argument";
+    case QSA_ERR_UNSUPPORTED: return "unsupported shape";
+    case QSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case QSA_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+const char *qsa_last_error(void) { return tl_err; }
+
+}  // extern "C"

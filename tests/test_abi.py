@@ -1,0 +1,111 @@
+"""The C ABI on the CPU: every symbol declared in include/*.h is exported,
+argument errors are reported before anything is launched, and the host-only
+state calls behave as documented.  No call here reaches a kernel launch."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        for m in re.finditer(r"\b(qsa_[a-z_0-9]+)\s*\(", text):
+            names.add(m.group(1))
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    import sparse_attention_decode_cache_amd as qsa
+    L = qsa.lib()
+    declared = _declared()
+    assert declared == set(qsa.EXPORTS), declared ^ set(qsa.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def _objs():
+    import sparse_attention_decode_cache_amd as qsa
+    d = qsa.make_desc(4, 128, qsa.QSA_F16, 16, 2, 256, 2048)
+    c = qsa.qsa_layer_cache(0x1000, 0x2000, 0x3000, 0x4000, 4096)
+    return qsa, d, c
+
+
+def test_workspace_bytes():
+    qsa, d, _ = _objs()
+    n = qsa.qsa_workspace_bytes(d, 255248)
+    assert n > 255248 // 4 * 12 and n % 256 == 0
+    assert qsa.qsa_workspace_bytes(d, 4095) == 0          # capacity not a multiple of 4
+    bad = qsa.make_desc(4, 128, qsa.QSA_F32, 16, 2, 256, 2048)   # 2 KB indexer rows
+    assert qsa.qsa_workspace_bytes(bad, 4096) == 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("block", 8, -2), ("idx_heads", 2, -2), ("idx_dim", 96, -2), ("head_dim", 512, -2),
+    ("q_heads", 12, -2), ("q_heads", 32, -2), ("top_k_tokens", 2046, -2), ("top_k_tokens", 0, -2),
+    ("idx_dtype", 7, -2), ("rope_theta", 0.0, -1)])
+def test_descriptor_errors(field, value, status):
+    qsa, d, c = _objs()
+    setattr(d, field, value)
+    st = qsa.qsa_seq_state(10, 0)
+    rc = qsa.lib().qsa_decode_step(ctypes.byref(d), ctypes.byref(c), ctypes.byref(st), *[ctypes.c_void_p(16)] * 8,
+                                   None, None, None, 0, None)
+    assert rc == status
+    assert (st.n_tokens, st.n_valid_blocks) == (10, 0)     # state untouched on error
+    assert qsa.lib().qsa_last_error()
+
+
+def test_argument_errors_before_launch():
+    qsa, d, c = _objs()
+    L = qsa.lib()
+    P = ctypes.c_void_p
+    D, C = ctypes.byref(d), ctypes.byref(c)
+    # null / bad ranges
+    assert L.qsa_cache_update(D, C, None, 0, 4, None) == -1
+    assert L.qsa_cache_update(D, C, P(16), 3, 2, None) == -1
+    assert L.qsa_cache_update(D, C, P(16), 0, 1025, None) == -1
+    assert L.qsa_index_score(D, C, 1025, P(16), P(16), P(16), None) == -1
+    assert L.qsa_index_score(D, C, 10, None, P(16), P(16), None) == -1
+    assert L.qsa_topk_blocks(P(16), -1, 5, P(16), None, 0, None) == -1
+    assert L.qsa_topk_blocks(P(16), 100, 0, P(16), None, 0, None) == -1
+    assert L.qsa_topk_blocks(P(16), 100, 5, P(16), None, 0, None) == -3          # no workspace
+    assert L.qsa_topk_blocks(P(16), 100, 5, P(16), P(256), 16, None) == -3        # too small
+    assert L.qsa_topk_blocks(P(16), 100, 5, P(16), P(255 + 256), 1 << 20, None) == -3   # misaligned
+    assert L.qsa_gather_attend(D, C, 0, P(16), 0, P(16), P(16), P(256), 1 << 30, None) == -1
+    assert L.qsa_gather_attend(D, C, 4097, P(16), 0, P(16), P(16), P(256), 1 << 30, None) == -1
+    assert L.qsa_gather_attend(D, C, 4096, P(16), 513, P(16), P(16), P(256), 1 << 30, None) == -1
+    assert L.qsa_gather_attend(D, C, 4096, None, 5, P(16), P(16), P(256), 1 << 30, None) == -1
+    assert L.qsa_gather_attend(D, C, 4096, P(16), 5, P(16), P(16), P(256), 64, None) == -3
+    # decode step: position at capacity, null rows, small workspace
+    st = qsa.qsa_seq_state(4096, 1024)
+    args = [P(16)] * 8
+    assert L.qsa_decode_step(D, C, ctypes.byref(st), *args, None, None, P(256), 1 << 30, None) == -1
+    st = qsa.qsa_seq_state(100, 25)
+    assert L.qsa_decode_step(D, C, ctypes.byref(st), None, *args[1:], None, None, P(256), 1 << 30, None) == -1
+    assert L.qsa_decode_step(D, C, ctypes.byref(st), *args, None, None, P(256), 100, None) == -3
+    assert (st.n_tokens, st.n_valid_blocks) == (100, 25)
+    c2 = qsa.qsa_layer_cache(0x1000, 0x2000, 0x3000, 0x4000, 4094)               # capacity % 4
+    assert L.qsa_decode_step(D, ctypes.byref(c2), ctypes.byref(st), *args, None, None, P(256), 1 << 30, None) == -1
+    assert L.qsa_status_string(-3) == b"workspace missing or too small"
+
+
+def test_state_invalidate_and_truncate():
+    import sparse_attention_decode_cache_amd as qsa
+    st = qsa.qsa_seq_state(1000, 250)
+    qsa.qsa_state_invalidate(st, 999)
+    assert (st.n_tokens, st.n_valid_blocks) == (1000, 249)
+    qsa.qsa_state_invalidate(st, 2000)
+    assert (st.n_tokens, st.n_valid_blocks) == (1000, 249)
+    qsa.qsa_state_invalidate(st, 13)
+    assert (st.n_tokens, st.n_valid_blocks) == (1000, 3)
+    st = qsa.qsa_seq_state(1000, 250)
+    qsa.qsa_state_truncate(st, 601)
+    assert (st.n_tokens, st.n_valid_blocks) == (601, 150)
+    qsa.qsa_state_truncate(st, -5)
+    assert (st.n_tokens, st.n_valid_blocks) == (0, 0)
