@@ -41,7 +41,8 @@
  *     idx row (idx_heads * idx_dim * sizeof(dtype)) <= 1024 bytes;
  *     head_dim in {64, 128, 256}; q_heads = G * kv_heads with G in {1,2,4,8};
  *     top_k_tokens a positive
- *     multiple of 4; capacity a positive multiple of 4, <= 2^26 tokens.
+ *     multiple of 4, at most 16380; capacity a positive multiple of 4, at
+ *     most 2^21 tokens (n_blocks of qsa_topk_blocks at most 2^19).
  *   - A workspace (DEVICE, 256-byte aligned, >= qsa_workspace_bytes) holds
  *     scratch only.  Calls that share a workspace must be stream-ordered.
  *     Its contents need no initialisation and are meaningless between calls.

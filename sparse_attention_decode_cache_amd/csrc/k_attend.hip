@@ -7,13 +7,15 @@
 //
 // Split-context flash decode.  Cells are enumerated e = 0..n_cells-1 (chosen
 // blocks ascending, 4 cells each, then the tail).  Workgroup (split, g) takes
-// cells [64*split, 64*split + 64) of KV head g for all G query heads of that
+// C = 16 (Dh >= 128) or 32 (Dh = 64) consecutive cells of KV head g -- about
+// 258 workgroups for 2051 cells and 2 KV heads, so the whole chip loads in
+// parallel -- for all G query heads of that
 // group (GQA: each K/V row is read once for G heads).  Per wave, one lane
 // covers 8 dims of a cell (Dh/8 lanes per cell), so a wave-wide 16-byte load
 // brings whole rows.  All K and V loads of a lane are issued up front.
 //   QK:  per-lane partial dots for G heads, transposing butterfly over the
 //        Dh/8 lanes of the cell -> logits in LDS;
-//   softmax over the split's 64 cells, per head (one wave reduction);
+//   softmax over the split's cells, per head (one wave reduction);
 //   PV:  per-lane accumulation, butterfly across the cells of a wave, LDS sum
 //        across the 4 waves -> partial (m, l, acc) in the workspace.
 // A second kernel merges the partials of a head in split order (fixed order:
@@ -74,7 +76,7 @@ __global__ __launch_bounds__(256) void k_attend(AttendArgs a)
 {
     constexpr int LPC = DH / 8;                 // lanes per cell
     constexpr int CPL = kWave / LPC;            // cells per wave-wide load
-    constexpr int CPW = kCellsPerSplit;         // cells per workgroup
+    constexpr int CPW = cells_per_split(DH);    // cells per workgroup
     constexpr int CPWW = CPW / 4;               // cells per wave
     constexpr int IT = CPWW / CPL;              // loads per lane (each of K and V)
     static_assert(IT >= 1 && G <= LPC && G * 8 >= CPL, "unsupported attention shape");
@@ -83,6 +85,8 @@ __global__ __launch_bounds__(256) void k_attend(AttendArgs a)
     __shared__ float s_m[G], s_l[G];
     __shared__ float s_red[4][G][DH];
 
+    __shared__ int32_t s_blk[CPW / 4];
+
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = t >> 6;
@@ -90,36 +94,39 @@ __global__ __launch_bounds__(256) void k_attend(AttendArgs a)
     const int chunk = lane % LPC;               // dims [8*chunk, 8*chunk + 8)
     const int split = blockIdx.x;
     const int g = blockIdx.y;
+    const int e0 = split * CPW;
 
-    // Issue every K and V load of this lane first.
+    // The split's chosen block ids, staged once so that the K/V addresses
+    // below need no dependent global load.
+    if (a.sel && t < CPW / 4) {
+        const int i = e0 / 4 + t;
+        s_blk[t] = i < a.n_sel_blocks ? a.sel[i] : -1;
+    }
+    __syncthreads();
+
+    // Every K and V load of this lane, issued back to back.  Cells outside
+    // the list (or with an id outside [0, nb)) read row 0 and are masked.
     uint4 kr[IT], vr[IT];
     bool ok[IT];
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
         const int lc = wave * CPWW + it * CPL + sub;
-        const int e = split * CPW + lc;
-        ok[it] = e < a.n_cells;
-        int64_t cell = 0;
-        if (ok[it]) {
-            if (!a.sel) {
-                cell = e;
-            } else if (e < 4 * a.n_sel_blocks) {
-                const int32_t b = a.sel[e >> 2];
-                // An id outside [0, nb) is never dereferenced: the cell is skipped.
-                ok[it] = (uint32_t)b < (uint32_t)a.nb;
+        const int e = e0 + lc;
+        bool v = e < a.n_cells;
+        int64_t cell = e;
+        if (a.sel) {
+            if (e < 4 * a.n_sel_blocks) {
+                const int32_t b = s_blk[lc >> 2];
+                v = v && (uint32_t)b < (uint32_t)a.nb;
                 cell = 4 * (int64_t)b + (e & 3);
             } else {
                 cell = 4 * (int64_t)a.nb + (e - 4 * a.n_sel_blocks);
             }
         }
-        const size_t off = ((size_t)cell * a.kv_heads + g) * DH + (size_t)chunk * 8;
-        if (ok[it]) {
-            kr[it] = *(const uint4 *)(a.k + off);
-            vr[it] = *(const uint4 *)(a.v + off);
-        } else {
-            kr[it] = make_uint4(0u, 0u, 0u, 0u);
-            vr[it] = make_uint4(0u, 0u, 0u, 0u);
-        }
+        ok[it] = v;
+        const size_t off = ((size_t)(v ? cell : 0) * a.kv_heads + g) * DH + (size_t)chunk * 8;
+        kr[it] = *(const uint4 *)(a.k + off);
+        vr[it] = *(const uint4 *)(a.v + off);
     }
 
     float qr[G][8];
@@ -160,12 +167,14 @@ __global__ __launch_bounds__(256) void k_attend(AttendArgs a)
     __syncthreads();
 
     // ---- softmax over the split's cells, one head per wave at a time
+    static_assert(CPW <= kWave, "one cell per lane in the softmax");
     for (int h = wave; h < G; h += 4) {
-        const float x = s_lg[lane][h];           // CPW == 64: one cell per lane
-        const float m = wave_max(x);             // finite: cell 0 of a split always exists
+        const float x = lane < CPW ? s_lg[lane][h] : -INFINITY;
+        const float m = wave_max(x);             // -inf only if no cell of the split is valid
         const float p = x == -INFINITY ? 0.0f : expf(x - m);
         const float l = wave_sum(p);
-        s_lg[lane][h] = p;
+        if (lane < CPW)
+            s_lg[lane][h] = p;
         if (lane == 0) {
             s_m[h] = m;
             s_l[h] = l;
@@ -217,25 +226,85 @@ __global__ __launch_bounds__(256) void k_attend(AttendArgs a)
     }
 }
 
-// out[h][d] = sum_s e^(m_s - M) acc_s[h][d] / sum_s e^(m_s - M) l_s, in split order.
-template <int DH, int G>
-__global__ __launch_bounds__(DH) void k_merge(AttendArgs a)
+// out[h][d] = sum_s e^(m_s - M) acc_s[h][d] / sum_s e^(m_s - M) l_s.
+// Workgroup (h, 64-dim slice): the split weights go to LDS once, then 4 groups
+// of 64 threads each stream every 4th split's partials for their dim (many
+// independent loads in flight) and are summed in a fixed order, so the result
+// is bitwise repeatable.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeDims = 64;
+constexpr int kMaxSplits = 1024;
+
+__device__ inline float block_reduce(float v, float *s_tmp, bool is_max)
 {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float y = __shfl_xor(v, o);
+        v = is_max ? fmaxf(v, y) : v + y;
+    }
+    if ((t & 63) == 0)
+        s_tmp[t >> 6] = v;
+    __syncthreads();
+    float r = s_tmp[0];
+    for (int i = 1; i < kMergeThreads / 64; ++i)
+        r = is_max ? fmaxf(r, s_tmp[i]) : r + s_tmp[i];
+    __syncthreads();
+    return r;
+}
+
+template <int DH, int G>
+__global__ __launch_bounds__(kMergeThreads) void k_merge(AttendArgs a)
+{
+    __shared__ float s_f[kMaxSplits];
+    __shared__ float s_tmp[kMergeThreads / 64];
+    __shared__ float s_acc[kMergeThreads / kMergeDims][kMergeDims];
     const int h = blockIdx.x;
     const int g = h / G, hh = h % G;
-    const int d = threadIdx.x;
+    const int t = threadIdx.x;
+    const int ns = a.n_split;
     const size_t ps = (size_t)part_stride(G, DH);
-    const float *base = a.part + (size_t)g * a.n_split * ps;
-    float M = -INFINITY;
-    for (int s = 0; s < a.n_split; ++s)
-        M = fmaxf(M, base[s * ps + hh]);
-    float L = 0.0f, acc = 0.0f;
-    for (int s = 0; s < a.n_split; ++s) {
-        const float f = expf(base[s * ps + hh] - M);
-        L = fmaf(f, base[s * ps + G + hh], L);
-        acc = fmaf(f, base[s * ps + 2 * G + hh * DH + d], acc);
+    const float *base = a.part + (size_t)g * ns * ps;
+
+    float mx = -INFINITY;
+    for (int s = t; s < ns; s += kMergeThreads) {
+        s_f[s] = base[s * ps + hh];
+        mx = fmaxf(mx, s_f[s]);
     }
-    a.out[(size_t)h * DH + d] = acc / L;
+    const float M = block_reduce(mx, s_tmp, true);
+    float lsum = 0.0f;
+    for (int s = t; s < ns; s += kMergeThreads) {
+        const float f = s_f[s] == -INFINITY ? 0.0f : expf(s_f[s] - M);
+        s_f[s] = f;
+        lsum += f * base[s * ps + G + hh];
+    }
+    const float L = block_reduce(lsum, s_tmp, false);   // also orders the s_f writes
+
+    constexpr int NG = kMergeThreads / kMergeDims;       // split groups
+    const int grp = t / kMergeDims;
+    const int d = blockIdx.y * kMergeDims + t % kMergeDims;
+    const float *p = base + 2 * G + hh * DH + d;
+    float acc = 0.0f;
+    int s = grp;
+    for (; s + 7 * NG < ns; s += 8 * NG) {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            x[i] = p[(size_t)(s + i * NG) * ps];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            acc = fmaf(s_f[s + i * NG], x[i], acc);
+    }
+    for (; s < ns; s += NG)
+        acc = fmaf(s_f[s], p[(size_t)s * ps], acc);
+    s_acc[grp][t % kMergeDims] = acc;
+    __syncthreads();
+    if (grp == 0) {
+        float tot = s_acc[0][t];
+        for (int i = 1; i < NG; ++i)
+            tot += s_acc[i][t];
+        a.out[(size_t)h * DH + d] = tot / L;
+    }
 }
 
 template <int DH, int G>
@@ -245,7 +314,10 @@ hipError_t go(const AttendArgs &a, hipStream_t s)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((k_merge<DH, G>), dim3(a.kv_heads * G), dim3(DH), 0, s, a);
+    if (a.n_split > kMaxSplits)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_merge<DH, G>), dim3(a.kv_heads * G, DH / kMergeDims), dim3(kMergeThreads),
+                       0, s, a);
     return hipGetLastError();
 }
 

@@ -9,9 +9,16 @@
 // reused in this step), and the per-row partial dot products are reduced with
 // a transposing butterfly -- log2(LPR) exchange rounds for T rows instead of
 // log2(LPR) rounds per row.  w[h] is folded into q_idx once per lane.
-// Optional outputs: fp32 scores, order-preserving 32-bit keys and a histogram
-// of the keys' top 12 bits (the first radix digit of the top-k).
-#include "qsa_internal.h"
+//
+// Outputs (all optional, plain stores, no atomics): fp32 scores; the
+// order-preserving 32-bit key of every score; and, for the top-k, each tile's
+// T = R/8 largest composite keys (key << 32 | ~block), sorted descending.
+//
+// Fused stage 1: in a decode step at most one summary row is new.  Workgroup 0
+// (dispatched first) appends the token's rows, pools that block, then scores
+// the LAST tile -- the one holding the new row -- so the pooling latency hides
+// under the stream of the other workgroups.
+#include "qsa_pool.h"
 
 namespace qsa {
 namespace {
@@ -51,25 +58,62 @@ __device__ inline uint32_t score_key(float s)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Tile list: the T largest of the R composites in s_c (0 = no row), written
+// descending to lists[tile*T ...]; counts[tile] = min(T, rows in the tile).
+// Ranks are exact because composites are unique.  Whole workgroup calls.
+template <int R, int T>
+__device__ inline void write_tile_list(const uint64_t *s_c, uint64_t *lists, uint32_t *counts,
+                                       int tile, int valid_rows)
+{
+    for (int i = threadIdx.x; i < R; i += blockDim.x) {
+        const uint64_t c = s_c[i];
+        if (c == 0)
+            continue;
+        int rank = 0;
+#pragma unroll 8
+        for (int u = 0; u < R; ++u)
+            rank += s_c[u] > c ? 1 : 0;
+        if (rank < T)
+            lists[(size_t)tile * T + rank] = c;
+    }
+    if (threadIdx.x == 0)
+        counts[tile] = (uint32_t)(valid_rows < T ? valid_rows : T);
+}
+
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <int LPR>
+struct ScoreShape {
+    static constexpr int RPL = kWave / LPR;           // rows per wave-wide load
+    static constexpr int T = LPR < 16 ? LPR : 16;     // loads in flight per lane
+    static constexpr int RPW = T * RPL;               // rows per wave tile
+    static constexpr int R = 4 * RPW;                 // rows per workgroup tile
+};
 
 template <bool F16, int LPR>
 __global__ __launch_bounds__(256) void k_score(ScoreArgs a)
 {
+    using S = ScoreShape<LPR>;
     constexpr int EPL = F16 ? 8 : 4;           // elements per 16-byte chunk
-    constexpr int RPL = kWave / LPR;           // rows per wave-wide load
-    constexpr int T = LPR < 16 ? LPR : 16;     // loads in flight per lane
-    constexpr int RPW = T * RPL;               // rows per wave tile
+    constexpr int RPL = S::RPL, T = S::T, RPW = S::RPW, R = S::R;
     constexpr int ROWB = LPR * 16;             // row bytes
+    __shared__ uint64_t s_c[R];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int chunk = lane % LPR;
     const int sub = lane / LPR;
-    const int64_t base = ((int64_t)blockIdx.x * 4 + wave) * RPW;
-    if (base >= a.nb)
-        return;
+    const int tile = blockIdx.x == 0 ? (int)gridDim.x - 1 : (int)blockIdx.x - 1;
+    if (blockIdx.x == 0 && a.fuse) {
+        if (a.upd.new_idx_row)
+            append_rows(a.upd, threadIdx.x, 256);
+        if (a.upd.nblk > 0)
+            pool_row<F16>(a.upd, a.upd.b0, threadIdx.x);
+        __threadfence();   // the pooled row is read back below by this workgroup
+        __syncthreads();
+    }
+    const int64_t base = ((int64_t)tile * 4 + wave) * RPW;
 
     float qw[EPL];
 #pragma unroll
@@ -113,44 +157,70 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a)
     Butterfly<LPR / 2, T>::run(v, lane, toff);
 
     constexpr int OWN = LPR / T;               // lanes sharing one final sum
-    if (lane % OWN != 0)
-        return;
+    const int local = wave * RPW + toff * RPL + sub;
     const int64_t r = base + (int64_t)toff * RPL + sub;
-    if (r >= a.nb)
-        return;
-    const float s = v[0];
-    if (a.scores)
-        a.scores[r] = s;
-    if (a.keys || a.hist) {
-        const uint32_t key = score_key(s);
-        if (a.keys)
-            a.keys[r] = key;
-        if (a.hist)
-            atomicAdd(&a.hist[key >> (32 - kHistBits)], 1u);
+    if (lane % OWN == 0) {
+        uint64_t c = 0;
+        if (r < a.nb) {
+            const float s = v[0];
+            if (a.scores)
+                a.scores[r] = s;
+            if (a.keys) {
+                const uint32_t key = score_key(s);
+                a.keys[r] = key;
+                c = comp_key(key, (uint32_t)r);
+            }
+        }
+        s_c[local] = c;
+    }
+    if (a.lists) {
+        __syncthreads();
+        const int64_t valid = a.nb - (int64_t)tile * R;
+        write_tile_list<R, R / kListDiv>(s_c, a.lists, a.counts, tile,
+                                         (int)(valid < R ? valid : R));
     }
 }
 
-__global__ __launch_bounds__(256) void k_keys_hist(const float *scores, int32_t nb, uint32_t *keys,
-                                                   uint32_t *hist)
+// Keys and tile lists from given fp32 scores (stand-alone top-k), R = 256.
+__global__ __launch_bounds__(kKeysTile) void k_keys(const float *scores, int32_t nb, uint32_t *keys,
+                                                    uint64_t *lists, uint32_t *counts)
 {
-    for (int i = blockIdx.x * 256 + threadIdx.x; i < nb; i += gridDim.x * 256) {
+    __shared__ uint64_t s_c[kKeysTile];
+    const int i = blockIdx.x * kKeysTile + threadIdx.x;
+    uint64_t c = 0;
+    if (i < nb) {
         const uint32_t key = score_key(scores[i]);
         keys[i] = key;
-        atomicAdd(&hist[key >> (32 - kHistBits)], 1u);
+        c = comp_key(key, (uint32_t)i);
     }
+    s_c[threadIdx.x] = c;
+    __syncthreads();
+    const int valid = nb - (int)blockIdx.x * kKeysTile;
+    write_tile_list<kKeysTile, kKeysTile / kListDiv>(s_c, lists, counts, blockIdx.x,
+                                                     valid < kKeysTile ? valid : kKeysTile);
 }
 
 template <bool F16, int LPR>
 hipError_t go(const ScoreArgs &a, hipStream_t s)
 {
-    constexpr int T = LPR < 16 ? LPR : 16;
-    constexpr int rows_per_wg = 4 * T * (kWave / LPR);
-    const int grid = (int)((a.nb + rows_per_wg - 1) / rows_per_wg);
+    const int grid = (int)((a.nb + ScoreShape<LPR>::R - 1) / ScoreShape<LPR>::R);
     hipLaunchKernelGGL((k_score<F16, LPR>), dim3(grid), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
+
+int score_tile_rows(bool f16, int row_bytes)
+{
+    (void)f16;
+    switch (row_bytes / 16) {
+    case 8: return ScoreShape<8>::R;
+    case 16: return ScoreShape<16>::R;
+    case 32: return ScoreShape<32>::R;
+    case 64: return ScoreShape<64>::R;
+    }
+    return 0;
+}
 
 hipError_t launch_score(const ScoreArgs &a, bool f16, int row_bytes, hipStream_t s)
 {
@@ -174,14 +244,13 @@ hipError_t launch_score(const ScoreArgs &a, bool f16, int row_bytes, hipStream_t
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_keys_hist(const float *scores, int32_t nb, uint32_t *keys, uint32_t *hist,
-                            hipStream_t s)
+hipError_t launch_keys(const float *scores, int32_t nb, uint32_t *keys, uint64_t *lists,
+                       uint32_t *counts, hipStream_t s)
 {
     if (nb <= 0)
         return hipSuccess;
-    int grid = (nb + 255) / 256;
-    grid = grid > 2048 ? 2048 : grid;
-    hipLaunchKernelGGL(k_keys_hist, dim3(grid), dim3(256), 0, s, scores, nb, keys, hist);
+    const int grid = (nb + kKeysTile - 1) / kKeysTile;
+    hipLaunchKernelGGL(k_keys, dim3(grid), dim3(kKeysTile), 0, s, scores, nb, keys, lists, counts);
     return hipGetLastError();
 }
 

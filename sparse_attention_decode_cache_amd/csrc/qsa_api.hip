@@ -58,8 +58,9 @@ qsa_status check_desc(const qsa_layer_desc *d)
     const int G = d->q_heads / d->kv_heads;
     if (G != 1 && G != 2 && G != 4 && G != 8)
         return fail(QSA_ERR_UNSUPPORTED, "q_heads / kv_heads must be 1, 2, 4 or 8 (got %d)", G);
-    if (d->top_k_tokens < 4 || d->top_k_tokens % 4 != 0)
-        return fail(QSA_ERR_UNSUPPORTED, "top_k_tokens must be a positive multiple of 4 (got %d)",
+    if (d->top_k_tokens < 4 || d->top_k_tokens % 4 != 0 || d->top_k_tokens > 16380)
+        return fail(QSA_ERR_UNSUPPORTED,
+                    "top_k_tokens must be a positive multiple of 4, at most 16380 (got %d)",
                     d->top_k_tokens);
     if (!(d->rms_eps >= 0.0f) || !(d->rope_theta > 0.0f) || !(d->attn_scale >= 0.0f) ||
         !isfinite(d->rope_theta) || !isfinite(d->attn_scale))
@@ -71,8 +72,8 @@ qsa_status check_cache(const qsa_layer_cache *c, bool need_idx, bool need_sum, b
 {
     if (!c)
         return fail(QSA_ERR_ARG, "cache is NULL");
-    if (c->capacity < 4 || c->capacity % 4 != 0 || c->capacity > (1 << 26))
-        return fail(QSA_ERR_ARG, "capacity must be a positive multiple of 4, <= 2^26 (got %d)",
+    if (c->capacity < 4 || c->capacity % 4 != 0 || c->capacity > (1 << 21))
+        return fail(QSA_ERR_ARG, "capacity must be a positive multiple of 4, <= 2^21 (got %d)",
                     c->capacity);
     if ((need_idx && (!c->idx_k || !aligned(c->idx_k, 16))) ||
         (need_sum && (!c->summary || !aligned(c->summary, 16))) ||
@@ -90,7 +91,7 @@ int64_t decode_part_floats(const qsa_layer_desc *d)
 {
     const int G = d->q_heads / d->kv_heads;
     const int64_t max_cells = (int64_t)d->top_k_tokens + 3;
-    return (int64_t)d->kv_heads * n_splits(max_cells) * part_stride(G, d->head_dim);
+    return (int64_t)d->kv_heads * n_splits(max_cells, d->head_dim) * part_stride(G, d->head_dim);
 }
 
 WsLayout decode_layout(const qsa_layer_desc *d, int32_t capacity)
@@ -124,7 +125,7 @@ qsa_status do_attend(const qsa_layer_desc *d, const qsa_layer_cache *c, int32_t 
     a.n_cells = 4 * n_sel_blocks + n_tokens % 4;
     if (!sel)
         a.n_cells = n_tokens;      // every block kept: cells are 0..n-1
-    a.n_split = (int32_t)n_splits(a.n_cells);
+    a.n_split = (int32_t)n_splits(a.n_cells, d->head_dim);
     a.kv_heads = d->kv_heads;
     a.scale = attn_scale(d);
     hipError_t e = launch_attend(a, d->head_dim, d->q_heads / d->kv_heads, stream);
@@ -133,26 +134,24 @@ qsa_status do_attend(const qsa_layer_desc *d, const qsa_layer_cache *c, int32_t 
     return QSA_OK;
 }
 
-// Stage 3 launch over keys + histogram already in the workspace.
-qsa_status do_select(char *ws, const WsLayout &L, int32_t nb, int32_t k, int32_t *sel,
-                     hipStream_t stream)
+// Stage 3 launch over the keys and tile lists already in the workspace.
+qsa_status do_select(char *ws, const WsLayout &L, int32_t nb, int32_t k, int32_t tile_rows,
+                     int32_t *sel, hipStream_t stream)
 {
     SelectArgs s{};
     s.keys = (const uint32_t *)(ws + L.keys);
-    s.hist = (const uint32_t *)(ws + L.hist);
-    s.ctrl = (uint32_t *)(ws + L.ctrl);
-    s.bitmap = (uint64_t *)(ws + L.bitmap);
-    s.cand = (uint64_t *)(ws + L.cand);
+    s.lists = (const uint64_t *)(ws + L.lists);
+    s.counts = (const uint32_t *)(ws + L.counts);
     s.sel = sel;
     s.nb = nb;
     s.k = k;
+    s.ntiles = (nb + tile_rows - 1) / tile_rows;
+    s.T = tile_rows / kListDiv;
     hipError_t e = launch_select(s, stream);
     if (e != hipSuccess)
         return hip_fail(e, "select");
     return QSA_OK;
 }
-
-int32_t ctrl_hist_words(const WsLayout &L) { return (int32_t)((L.hist - L.ctrl) / 4 + kHistBins); }
 
 }  // namespace
 
@@ -160,7 +159,7 @@ extern "C" {
 
 size_t qsa_workspace_bytes(const qsa_layer_desc *desc, int32_t capacity)
 {
-    if (check_desc(desc) != QSA_OK || capacity < 4 || capacity % 4 != 0 || capacity > (1 << 26))
+    if (check_desc(desc) != QSA_OK || capacity < 4 || capacity % 4 != 0 || capacity > (1 << 21))
         return 0;
     return decode_layout(desc, capacity).total;
 }
@@ -247,7 +246,7 @@ qsa_status qsa_index_score(const qsa_layer_desc *desc, const qsa_layer_cache *ca
 qsa_status qsa_topk_blocks(const float *scores, int32_t n_blocks, int32_t k_blocks, int32_t *sel,
                            void *ws, size_t ws_bytes, hipStream_t stream)
 {
-    if (n_blocks < 0 || n_blocks > (1 << 24) || k_blocks < 1)
+    if (n_blocks < 0 || n_blocks > (1 << 19) || k_blocks < 1)
         return fail(QSA_ERR_ARG, "n_blocks %d / k_blocks %d out of range", n_blocks, k_blocks);
     if ((n_blocks > 0 && !scores) || !sel)
         return fail(QSA_ERR_ARG, "scores / sel is NULL");
@@ -262,13 +261,11 @@ qsa_status qsa_topk_blocks(const float *scores, int32_t n_blocks, int32_t k_bloc
     if (st != QSA_OK)
         return st;
     char *w = (char *)ws;
-    hipError_t e = launch_fill_zero((uint32_t *)(w + L.ctrl), ctrl_hist_words(L), stream);
-    if (e == hipSuccess)
-        e = launch_keys_hist(scores, n_blocks, (uint32_t *)(w + L.keys), (uint32_t *)(w + L.hist),
-                             stream);
+    hipError_t e = launch_keys(scores, n_blocks, (uint32_t *)(w + L.keys),
+                               (uint64_t *)(w + L.lists), (uint32_t *)(w + L.counts), stream);
     if (e != hipSuccess)
         return hip_fail(e, "topk_blocks");
-    st = do_select(w, L, n_blocks, k_blocks, sel, stream);
+    st = do_select(w, L, n_blocks, k_blocks, kKeysTile, sel, stream);
     return st == QSA_OK ? ok() : st;
 }
 
@@ -332,7 +329,8 @@ qsa_status qsa_decode_step(const qsa_layer_desc *desc, const qsa_layer_cache *ca
     const int rowb = desc->idx_heads * desc->idx_dim * ebytes;
     char *wsp = (char *)ws;
 
-    // 1. append + pool [b0, nb) (+ clear the top-k control words and histogram)
+    // 1. append + pool [b0, nb).  One new row (the usual decode step) is pooled
+    //    by the score kernel's first workgroup; anything else runs on its own.
     UpdateArgs u{};
     u.idx_k = cache->idx_k;
     u.summary = cache->summary;
@@ -342,8 +340,6 @@ qsa_status qsa_decode_step(const qsa_layer_desc *desc, const qsa_layer_cache *ca
     u.new_k_row = k_row;
     u.new_v_row = v_row;
     u.gamma = gamma;
-    u.clear_ptr = need_select ? (uint32_t *)(wsp + L.ctrl) : nullptr;
-    u.clear_words = need_select ? ctrl_hist_words(L) : 0;
     u.idx_row_words = rowb / 4;
     u.kv_row_words = desc->kv_heads * desc->head_dim / 2;
     u.pos = pos;
@@ -353,21 +349,29 @@ qsa_status qsa_decode_step(const qsa_layer_desc *desc, const qsa_layer_cache *ca
     u.D = desc->idx_dim;
     u.eps = (double)desc->rms_eps;
     u.theta = (double)desc->rope_theta;
-    hipError_t e = launch_update(u, desc->idx_dtype == QSA_F16, stream);
-    if (e != hipSuccess)
-        return hip_fail(e, "decode_step/update");
+    const bool score = nb > 0 && (need_select || scores_out);
+    const bool fuse = score && u.nblk <= 1;
+    hipError_t e;
+    if (!fuse) {
+        e = launch_update(u, desc->idx_dtype == QSA_F16, stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "decode_step/update");
+    }
 
-    // 2. score every completed block (+ keys and histogram for the top-k)
-    if (nb > 0 && (need_select || scores_out)) {
+    // 2. score every completed block (keys for the top-k)
+    if (score) {
         ScoreArgs a{};
         a.summary = cache->summary;
         a.q = q_idx;
         a.w = w;
         a.scores = scores_out;
         a.keys = need_select ? (uint32_t *)(wsp + L.keys) : nullptr;
-        a.hist = need_select ? (uint32_t *)(wsp + L.hist) : nullptr;
+        a.lists = need_select ? (uint64_t *)(wsp + L.lists) : nullptr;
+        a.counts = need_select ? (uint32_t *)(wsp + L.counts) : nullptr;
         a.nb = nb;
         a.D = desc->idx_dim;
+        a.fuse = fuse ? 1 : 0;
+        a.upd = u;
         e = launch_score(a, desc->idx_dtype == QSA_F16, rowb, stream);
         if (e != hipSuccess)
             return hip_fail(e, "decode_step/score");
@@ -378,7 +382,8 @@ qsa_status qsa_decode_step(const qsa_layer_desc *desc, const qsa_layer_cache *ca
     int32_t n_sel = nb;
     if (need_select) {
         int32_t *dst = sel_out ? sel_out : (int32_t *)(wsp + L.sel);
-        if ((s = do_select(wsp, L, nb, K, dst, stream)) != QSA_OK)
+        if ((s = do_select(wsp, L, nb, K, score_tile_rows(desc->idx_dtype == QSA_F16, rowb), dst,
+                           stream)) != QSA_OK)
             return s;
         sel = dst;
         n_sel = K;

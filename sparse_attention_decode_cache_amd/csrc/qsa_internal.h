@@ -10,16 +10,11 @@
 namespace qsa {
 
 constexpr int kWave = 64;           // CDNA wavefront width
-constexpr int kHistBits = 12;       // first radix digit of the top-k key
-constexpr int kHistBins = 1 << kHistBits;
-constexpr int kCellsPerSplit = 64;  // cells handled by one attention workgroup
+constexpr int kListDiv = 8;         // per-tile top-k lists keep R / 8 entries
 
-// Control words at the start of the workspace.
-enum Ctrl : int { kCtrlSelectDone = 0, kCtrlCandCount = 1, kCtrlWords = 64 };
-
-// Workspace carve-up.  ctrl and hist are contiguous so one fill clears both.
+// Workspace carve-up.
 struct WsLayout {
-    size_t ctrl, hist, bitmap, keys, cand, sel, part, total;
+    size_t keys, lists, counts, sel, part, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -33,11 +28,9 @@ inline WsLayout ws_layout(int64_t max_blocks, int64_t sel_entries, int64_t part_
         off = align256(off + bytes);
         return o;
     };
-    L.ctrl = take(sizeof(uint32_t) * kCtrlWords);
-    L.hist = take(sizeof(uint32_t) * kHistBins);
-    L.bitmap = take(sizeof(uint64_t) * (size_t)((max_blocks + 63) / 64));
     L.keys = take(sizeof(uint32_t) * (size_t)max_blocks);
-    L.cand = take(sizeof(uint64_t) * (size_t)max_blocks);
+    L.lists = take(sizeof(uint64_t) * (size_t)((max_blocks + kListDiv - 1) / kListDiv + 64));
+    L.counts = take(sizeof(uint32_t) * (size_t)(max_blocks / 16 + 64));
     L.sel = take(sizeof(int32_t) * (size_t)sel_entries);
     L.part = take(sizeof(float) * (size_t)part_floats);
     L.total = off;
@@ -47,7 +40,15 @@ inline WsLayout ws_layout(int64_t max_blocks, int64_t sel_entries, int64_t part_
 // Floats of one attention partial: m[G], l[G], acc[G][Dh].
 __host__ __device__ inline int64_t part_stride(int G, int Dh) { return 2 * (int64_t)G + (int64_t)G * Dh; }
 
-inline int64_t n_splits(int64_t n_cells) { return (n_cells + kCellsPerSplit - 1) / kCellsPerSplit; }
+// Cells handled by one attention workgroup: 16 for Dh >= 128 (enough
+// workgroups to cover the chip at 2051 cells), 32 for Dh = 64 (a wave-wide
+// load covers 8 cells there).
+__host__ __device__ constexpr int cells_per_split(int Dh) { return Dh >= 128 ? 16 : 32; }
+
+inline int64_t n_splits(int64_t n_cells, int Dh)
+{
+    return (n_cells + cells_per_split(Dh) - 1) / cells_per_split(Dh);
+}
 
 // ------------------------------------------------------------- launchers
 struct UpdateArgs {
@@ -76,28 +77,42 @@ struct ScoreArgs {
     const float *w;
     float *scores;              // optional fp32 scores
     uint32_t *keys;             // optional order-preserving keys
-    uint32_t *hist;             // optional histogram of the key's top 12 bits
+    uint64_t *lists;            // optional per-tile top-T composites (with keys)
+    uint32_t *counts;           // entries of each tile's list
     int32_t nb;
     int32_t D;
+    int32_t fuse;               // workgroup 0 first runs `upd` (append, pool <= 1 row)
+    UpdateArgs upd;
 };
 hipError_t launch_score(const ScoreArgs &a, bool f16, int row_bytes, hipStream_t s);
+// Rows per score workgroup (tile) for a given indexer row size.
+int score_tile_rows(bool f16, int row_bytes);
 
-hipError_t launch_keys_hist(const float *scores, int32_t nb, uint32_t *keys, uint32_t *hist,
-                            hipStream_t s);
+// Keys and per-tile lists (R = 256) from given fp32 scores.
+constexpr int kKeysTile = 256;
+hipError_t launch_keys(const float *scores, int32_t nb, uint32_t *keys, uint64_t *lists,
+                       uint32_t *counts, hipStream_t s);
 hipError_t launch_fill_zero(uint32_t *p, int32_t words, hipStream_t s);
 hipError_t launch_iota(int32_t *p, int32_t n, hipStream_t s);
 
+// Per-tile candidate lists: a tile of R consecutive blocks keeps its T = R/8
+// largest composite keys, sorted descending.  R depends on the producer.
 struct SelectArgs {
-    const uint32_t *keys;
-    const uint32_t *hist;
-    uint32_t *ctrl;
-    uint64_t *bitmap;
-    uint64_t *cand;
+    const uint32_t *keys;       // [nb] order-preserving score keys
+    const uint64_t *lists;      // [ntiles * T] composites, descending per tile
+    const uint32_t *counts;     // [ntiles] valid entries per list
     int32_t *sel;
     int32_t nb;
     int32_t k;
+    int32_t ntiles;
+    int32_t T;
 };
 hipError_t launch_select(const SelectArgs &a, hipStream_t s);
+
+__host__ __device__ inline uint64_t comp_key(uint32_t key, uint32_t id)
+{
+    return ((uint64_t)key << 32) | (uint64_t)(~id);
+}
 
 struct AttendArgs {
     const uint16_t *k;
