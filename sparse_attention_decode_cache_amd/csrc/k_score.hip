@@ -19,6 +19,7 @@
 // the LAST tile -- the one holding the new row -- so the pooling latency hides
 // under the stream of the other workgroups.
 #include "qsa_pool.h"
+#include "qsa_wave.h"
 
 namespace qsa {
 namespace {
@@ -59,25 +60,32 @@ __device__ inline uint32_t score_key(float s)
 }
 
 // Tile list: the T largest of the R composites in s_c (0 = no row), written
-// descending to lists[tile*T ...]; counts[tile] = min(T, rows in the tile).
-// Ranks are exact because composites are unique.  Whole workgroup calls.
+// descending to lists[tile*T ...]; slots past the tile's rows get 0.  Ranks
+// are exact because composites are unique and nonzero.  All 256 threads
+// work: P = 256/R consecutive threads share an entry, each counting the
+// larger composites in 1/P of the tile, summed with DPP quad moves.  Whole
+// workgroup calls (uniform control flow: DPP reads neighbouring lanes).
 template <int R, int T>
-__device__ inline void write_tile_list(const uint64_t *s_c, uint64_t *lists, uint32_t *counts,
-                                       int tile, int valid_rows)
+__device__ inline void write_tile_list(const uint64_t *s_c, uint64_t *lists, int tile, int valid_rows)
 {
-    for (int i = threadIdx.x; i < R; i += blockDim.x) {
-        const uint64_t c = s_c[i];
-        if (c == 0)
-            continue;
-        int rank = 0;
+    static_assert(R == 64 || R == 128 || R == 256, "tile rows");
+    constexpr int P = 256 / R;
+    constexpr int SPAN = R / P;
+    const int i = threadIdx.x / P, part = threadIdx.x % P;
+    const uint64_t c = s_c[i];
+    uint32_t rank = 0;
 #pragma unroll 8
-        for (int u = 0; u < R; ++u)
-            rank += s_c[u] > c ? 1 : 0;
-        if (rank < T)
-            lists[(size_t)tile * T + rank] = c;
-    }
-    if (threadIdx.x == 0)
-        counts[tile] = (uint32_t)(valid_rows < T ? valid_rows : T);
+    for (int u = 0; u < SPAN; ++u)
+        rank += s_c[part * SPAN + u] > c ? 1u : 0u;
+    if constexpr (P >= 2)
+        rank += wave::dpp<wave::kQuadXor1>(rank);
+    if constexpr (P == 4)
+        rank += wave::dpp<wave::kQuadXor2>(rank);
+    if (part == 0 && c != 0 && rank < (uint32_t)T)
+        lists[(size_t)tile * T + rank] = c;
+    // the nonzero composites take ranks [0, valid_rows): the rest are empty
+    if ((int)threadIdx.x >= valid_rows && threadIdx.x < (unsigned)T)
+        lists[(size_t)tile * T + threadIdx.x] = 0;
 }
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -176,14 +184,13 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a)
     if (a.lists) {
         __syncthreads();
         const int64_t valid = a.nb - (int64_t)tile * R;
-        write_tile_list<R, R / kListDiv>(s_c, a.lists, a.counts, tile,
-                                         (int)(valid < R ? valid : R));
+        write_tile_list<R, R / kListDiv>(s_c, a.lists, tile, (int)(valid < R ? valid : R));
     }
 }
 
 // Keys and tile lists from given fp32 scores (stand-alone top-k), R = 256.
 __global__ __launch_bounds__(kKeysTile) void k_keys(const float *scores, int32_t nb, uint32_t *keys,
-                                                    uint64_t *lists, uint32_t *counts)
+                                                    uint64_t *lists)
 {
     __shared__ uint64_t s_c[kKeysTile];
     const int i = blockIdx.x * kKeysTile + threadIdx.x;
@@ -196,7 +203,7 @@ __global__ __launch_bounds__(kKeysTile) void k_keys(const float *scores, int32_t
     s_c[threadIdx.x] = c;
     __syncthreads();
     const int valid = nb - (int)blockIdx.x * kKeysTile;
-    write_tile_list<kKeysTile, kKeysTile / kListDiv>(s_c, lists, counts, blockIdx.x,
+    write_tile_list<kKeysTile, kKeysTile / kListDiv>(s_c, lists, blockIdx.x,
                                                      valid < kKeysTile ? valid : kKeysTile);
 }
 
@@ -245,12 +252,12 @@ hipError_t launch_score(const ScoreArgs &a, bool f16, int row_bytes, hipStream_t
 }
 
 hipError_t launch_keys(const float *scores, int32_t nb, uint32_t *keys, uint64_t *lists,
-                       uint32_t *counts, hipStream_t s)
+                       hipStream_t s)
 {
     if (nb <= 0)
         return hipSuccess;
     const int grid = (nb + kKeysTile - 1) / kKeysTile;
-    hipLaunchKernelGGL(k_keys, dim3(grid), dim3(kKeysTile), 0, s, scores, nb, keys, lists, counts);
+    hipLaunchKernelGGL(k_keys, dim3(grid), dim3(kKeysTile), 0, s, scores, nb, keys, lists);
     return hipGetLastError();
 }
 

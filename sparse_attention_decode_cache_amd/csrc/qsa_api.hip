@@ -141,7 +141,6 @@ qsa_status do_select(char *ws, const WsLayout &L, int32_t nb, int32_t k, int32_t
     SelectArgs s{};
     s.keys = (const uint32_t *)(ws + L.keys);
     s.lists = (const uint64_t *)(ws + L.lists);
-    s.counts = (const uint32_t *)(ws + L.counts);
     s.sel = sel;
     s.nb = nb;
     s.k = k;
@@ -262,7 +261,7 @@ qsa_status qsa_topk_blocks(const float *scores, int32_t n_blocks, int32_t k_bloc
         return st;
     char *w = (char *)ws;
     hipError_t e = launch_keys(scores, n_blocks, (uint32_t *)(w + L.keys),
-                               (uint64_t *)(w + L.lists), (uint32_t *)(w + L.counts), stream);
+                               (uint64_t *)(w + L.lists), stream);
     if (e != hipSuccess)
         return hip_fail(e, "topk_blocks");
     st = do_select(w, L, n_blocks, k_blocks, kKeysTile, sel, stream);
@@ -367,7 +366,6 @@ qsa_status qsa_decode_step(const qsa_layer_desc *desc, const qsa_layer_cache *ca
         a.scores = scores_out;
         a.keys = need_select ? (uint32_t *)(wsp + L.keys) : nullptr;
         a.lists = need_select ? (uint64_t *)(wsp + L.lists) : nullptr;
-        a.counts = need_select ? (uint32_t *)(wsp + L.counts) : nullptr;
         a.nb = nb;
         a.D = desc->idx_dim;
         a.fuse = fuse ? 1 : 0;

@@ -14,7 +14,7 @@ constexpr int kListDiv = 8;         // per-tile top-k lists keep R / 8 entries
 
 // Workspace carve-up.
 struct WsLayout {
-    size_t keys, lists, counts, sel, part, total;
+    size_t keys, lists, sel, part, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -30,7 +30,6 @@ inline WsLayout ws_layout(int64_t max_blocks, int64_t sel_entries, int64_t part_
     };
     L.keys = take(sizeof(uint32_t) * (size_t)max_blocks);
     L.lists = take(sizeof(uint64_t) * (size_t)((max_blocks + kListDiv - 1) / kListDiv + 64));
-    L.counts = take(sizeof(uint32_t) * (size_t)(max_blocks / 16 + 64));
     L.sel = take(sizeof(int32_t) * (size_t)sel_entries);
     L.part = take(sizeof(float) * (size_t)part_floats);
     L.total = off;
@@ -78,7 +77,6 @@ struct ScoreArgs {
     float *scores;              // optional fp32 scores
     uint32_t *keys;             // optional order-preserving keys
     uint64_t *lists;            // optional per-tile top-T composites (with keys)
-    uint32_t *counts;           // entries of each tile's list
     int32_t nb;
     int32_t D;
     int32_t fuse;               // workgroup 0 first runs `upd` (append, pool <= 1 row)
@@ -91,16 +89,16 @@ int score_tile_rows(bool f16, int row_bytes);
 // Keys and per-tile lists (R = 256) from given fp32 scores.
 constexpr int kKeysTile = 256;
 hipError_t launch_keys(const float *scores, int32_t nb, uint32_t *keys, uint64_t *lists,
-                       uint32_t *counts, hipStream_t s);
+                       hipStream_t s);
 hipError_t launch_fill_zero(uint32_t *p, int32_t words, hipStream_t s);
 hipError_t launch_iota(int32_t *p, int32_t n, hipStream_t s);
 
 // Per-tile candidate lists: a tile of R consecutive blocks keeps its T = R/8
-// largest composite keys, sorted descending.  R depends on the producer.
+// largest composite keys, sorted descending, zero-filled past the tile's
+// blocks (a composite is never 0).  R depends on the producer.
 struct SelectArgs {
     const uint32_t *keys;       // [nb] order-preserving score keys
     const uint64_t *lists;      // [ntiles * T] composites, descending per tile
-    const uint32_t *counts;     // [ntiles] valid entries per list
     int32_t *sel;
     int32_t nb;
     int32_t k;

@@ -102,6 +102,30 @@ __device__ inline float reduce_max_f(float v)
                  fmaxf(__uint_as_float(readlane(x, 32)), __uint_as_float(readlane(x, 48))));
 }
 
+__device__ inline float reduce_min_f(float v)
+{
+    uint32_t x = __float_as_uint(v);
+    x = row_reduce(x, [](uint32_t a, uint32_t b) {
+        return __float_as_uint(fminf(__uint_as_float(a), __uint_as_float(b)));
+    });
+    return fminf(fminf(__uint_as_float(readlane(x, 0)), __uint_as_float(readlane(x, 16))),
+                 fminf(__uint_as_float(readlane(x, 32)), __uint_as_float(readlane(x, 48))));
+}
+
+__device__ inline uint32_t reduce_min_u32(uint32_t x)
+{
+    auto mn = [](uint32_t a, uint32_t b) { return a < b ? a : b; };
+    x = row_reduce(x, mn);
+    return mn(mn(readlane(x, 0), readlane(x, 16)), mn(readlane(x, 32), readlane(x, 48)));
+}
+
+__device__ inline uint32_t reduce_max_u32(uint32_t x)
+{
+    auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+    x = row_reduce(x, mx);
+    return mx(mx(readlane(x, 0), readlane(x, 16)), mx(readlane(x, 32), readlane(x, 48)));
+}
+
 __device__ inline uint64_t readlane64(uint64_t x, int lane)
 {
     return ((uint64_t)readlane((uint32_t)(x >> 32), lane) << 32) | readlane((uint32_t)x, lane);
