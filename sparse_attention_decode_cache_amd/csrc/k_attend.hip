@@ -2,333 +2,381 @@
 //
 // [post 10, "selected QSA K/V gather（COMMON-005）"]: only the K/V rows of the
 // chosen cells (4 per chosen block, plus the tail of the unfinished block) are
-// read, and ordinary softmax attention runs over them.  Here the gather is not
+// read, and ordinary softmax attention runs over them.  The gather is not
 // materialised: the attention workgroups load the selected rows directly.
 //
 // Split-context flash decode.  Cells are enumerated e = 0..n_cells-1 (chosen
 // blocks ascending, 4 cells each, then the tail).  Workgroup (split, g) takes
-// C = 16 (Dh >= 128) or 32 (Dh = 64) consecutive cells of KV head g -- about
-// 258 workgroups for 2051 cells and 2 KV heads, so the whole chip loads in
-// parallel -- for all G query heads of that
-// group (GQA: each K/V row is read once for G heads).  Per wave, one lane
-// covers 8 dims of a cell (Dh/8 lanes per cell), so a wave-wide 16-byte load
-// brings whole rows.  All K and V loads of a lane are issued up front.
-//   QK:  per-lane partial dots for G heads, transposing butterfly over the
-//        Dh/8 lanes of the cell -> logits in LDS;
-//   softmax over the split's cells, per head (one wave reduction);
-//   PV:  per-lane accumulation, butterfly across the cells of a wave, LDS sum
-//        across the 4 waves -> partial (m, l, acc) in the workspace.
-// A second kernel merges the partials of a head in split order (fixed order:
+// 16 consecutive cells of KV head g for all G query heads of the group (GQA:
+// each K/V row is read once for G heads) -- 258 workgroups for 2051 cells and
+// 2 KV heads, one per CU.  1024 threads; every K and V load is issued at once:
+//   wave 0 (QK): the 16 x G logits on the matrix cores, K rows fed straight
+//              from memory as the A operand, q (split into two f16 halves)
+//              as B;
+//   softmax:   one 16-lane DPP row per head (16 cells);
+//   waves 8-15 (PV): a lane owns (8-dim chunk, head, cell group) and keeps
+//              the V chunks of its cells in registers (coalesced: a wave-wide
+//              load covers whole rows); partial sums of the cell groups meet
+//              in LDS and are summed in a fixed order.
+// The split's partial (m, l, acc) goes to the workspace; a second kernel
+// merges the partials of a head (one global latency round, fixed order:
 // bitwise repeatable).
 #include "qsa_internal.h"
+#include "qsa_select.h"
+#include "qsa_wave.h"
 
 namespace qsa {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 
-template <int O, int CNT>
-struct Butterfly {
-    // Before: v[0..CNT) partial sums of CNT different outputs.  Exchanges over
-    // lane offsets O, O/2, ..., STOP (exclusive) halve the live set each round.
-    template <int STOP>
-    static __device__ inline void run(float *v, int lane, int &toff)
-    {
-        if constexpr (O <= STOP) {
-            return;
-        } else if constexpr (CNT > 1) {
-            constexpr int H = CNT / 2;
-            const bool up = (lane & O) != 0;
-#pragma unroll
-            for (int k = 0; k < H; ++k) {
-                const float send = up ? v[k] : v[k + H];
-                const float keep = up ? v[k + H] : v[k];
-                v[k] = keep + __shfl_xor(send, O);
-            }
-            if (up)
-                toff += H;
-            Butterfly<O / 2, H>::template run<STOP>(v, lane, toff);
-        } else {
-            v[0] += __shfl_xor(v[0], O);
-            Butterfly<O / 2, 1>::template run<STOP>(v, lane, toff);
-        }
-    }
-};
+constexpr int kAT = 1024;                   // threads of an attention workgroup
+constexpr int kCells = kCellsPerSplit;      // cells per workgroup (16: one MFMA tile)
+constexpr int kPV0 = kAT / 2;               // PV lanes [512, 1024)
+static_assert(kCells == 16, "one 16x16 MFMA tile of cells, one 16-lane row per softmax");
 
-__device__ inline float wave_max(float x)
-{
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        x = fmaxf(x, __shfl_xor(x, o));
-    return x;
-}
-
-__device__ inline float wave_sum(float x)
-{
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1)
-        x += __shfl_xor(x, o);
-    return x;
-}
+typedef float float4v __attribute__((ext_vector_type(4)));
 
 template <int DH, int G>
-__global__ __launch_bounds__(256) void k_attend(AttendArgs a)
+struct AttShape {
+    static constexpr int KS = DH / 32;                      // MFMA k-steps of a row
+    static constexpr int CH = DH / 8;                       // 16-byte chunks of a row
+    static constexpr int SV0 = (kAT - kPV0) / (CH * G);
+    static constexpr int SV = SV0 < kCells ? SV0 : kCells;  // cell groups of the PV lanes
+    static constexpr int PV_LANES = SV * CH * G;
+    static constexpr int CPG = kCells / SV;                 // cells per PV lane
+    static_assert(G <= 16 && CPG * SV == kCells && PV_LANES <= kAT - kPV0, "shape");
+};
+
+template <int DH, int G>
+struct AttLds {
+    using S = AttShape<DH, G>;
+    float lg[kCells][G + 1];
+    float m[G], l[G];
+    alignas(16) float acc[S::SV][G * DH];
+    int32_t blk[kCells / 4];
+};
+
+// Attention of split `split` of KV head g; L.blk holds the split's 4 block
+// ids (read only for cells inside the chosen blocks) and is visible to all
+// threads.  Whole workgroup calls.
+template <int DH, int G>
+__device__ void attend_split(const AttendArgs &a, AttLds<DH, G> &L, int split, int g)
 {
-    constexpr int LPC = DH / 8;                 // lanes per cell
-    constexpr int CPL = kWave / LPC;            // cells per wave-wide load
-    constexpr int CPW = cells_per_split(DH);    // cells per workgroup
-    constexpr int CPWW = CPW / 4;               // cells per wave
-    constexpr int IT = CPWW / CPL;              // loads per lane (each of K and V)
-    static_assert(IT >= 1 && G <= LPC && G * 8 >= CPL, "unsupported attention shape");
-
-    __shared__ float s_lg[CPW][G];
-    __shared__ float s_m[G], s_l[G];
-    __shared__ float s_red[4][G][DH];
-
-    __shared__ int32_t s_blk[CPW / 4];
-
+    using S = AttShape<DH, G>;
     const int t = threadIdx.x;
-    const int lane = t & 63;
-    const int wave = t >> 6;
-    const int sub = lane / LPC;                 // cell within a wave-wide load
-    const int chunk = lane % LPC;               // dims [8*chunk, 8*chunk + 8)
-    const int split = blockIdx.x;
-    const int g = blockIdx.y;
-    const int e0 = split * CPW;
+    const int lane = t & 63, wave = t >> 6;
+    const int e0 = split * kCells;
 
-    // The split's chosen block ids, staged once so that the K/V addresses
-    // below need no dependent global load.
-    if (a.sel && t < CPW / 4) {
-        const int i = e0 / 4 + t;
-        s_blk[t] = i < a.n_sel_blocks ? a.sel[i] : -1;
-    }
-    __syncthreads();
-
-    // Every K and V load of this lane, issued back to back.  Cells outside
-    // the list (or with an id outside [0, nb)) read row 0 and are masked.
-    uint4 kr[IT], vr[IT];
-    bool ok[IT];
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int lc = wave * CPWW + it * CPL + sub;
+    // Row of local cell lc; invalid cells (past n_cells, or a block id
+    // outside [0, nb)) read row 0 and are masked.
+    auto cell_row = [&](int lc, bool &valid) -> size_t {
         const int e = e0 + lc;
-        bool v = e < a.n_cells;
-        int64_t cell = e;
-        if (a.sel) {
-            if (e < 4 * a.n_sel_blocks) {
-                const int32_t b = s_blk[lc >> 2];
-                v = v && (uint32_t)b < (uint32_t)a.nb;
-                cell = 4 * (int64_t)b + (e & 3);
-            } else {
-                cell = 4 * (int64_t)a.nb + (e - 4 * a.n_sel_blocks);
+        valid = e < a.n_cells;
+        int64_t cell;
+        if (e < 4 * a.n_sel_blocks) {
+            const int32_t b = L.blk[lc >> 2];
+            valid = valid && (uint32_t)b < (uint32_t)a.nb;
+            cell = 4 * (int64_t)b + (lc & 3);
+        } else {
+            cell = 4 * (int64_t)a.nb + (e - 4 * a.n_sel_blocks);
+        }
+        return valid ? (size_t)cell : 0;
+    };
+
+    const int tv = t - kPV0;
+    const int v_chunk = tv % S::CH, v_head = (tv / S::CH) % G, v_grp = tv / (S::CH * G);
+    uint4 vr[S::CPG];
+
+    if (wave == 0) {
+        // ---- logits on the matrix cores: D[cell][head] = K[cell][:] . q[head][:]
+        // 16x16x32 f16 MFMA: lane l feeds A[cell l%16][8(l/16) .. +8] (K row)
+        // and B[8(l/16) .. +8][head l%16] (q, zero past G), and receives
+        // D[4(l/16) + j][l%16].  q = hi + lo in f16, both multiplied: the
+        // products are exact in fp32, so the dot keeps fp32 accuracy.
+        const int mc = lane & 15, kg = lane >> 4;
+        bool valid;
+        const size_t row = cell_row(mc, valid);
+        const uint4 *kp = (const uint4 *)(a.k + (row * a.kv_heads + g) * DH) + kg;
+        uint4 kr[S::KS];
+#pragma unroll
+        for (int i = 0; i < S::KS; ++i)
+            kr[i] = kp[4 * i];
+        const bool hq = mc < G;
+        const float4 *qp = (const float4 *)(a.q + ((size_t)g * G + (hq ? mc : 0)) * DH) + 2 * kg;
+        float4v d = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int i = 0; i < S::KS; ++i) {
+            const float4 x = qp[8 * i], y = qp[8 * i + 1];
+            const float qf[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+            half8 hi, lo, kh;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float q = hq ? qf[j] : 0.0f;
+                hi[j] = (_Float16)q;
+                lo[j] = (_Float16)(q - (float)hi[j]);
+            }
+            __builtin_memcpy(&kh, &kr[i], 16);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, hi, d, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, lo, d, 0, 0, 0);
+        }
+        if (hq) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int lc = 4 * kg + j;
+                bool v;
+                (void)cell_row(lc, v);
+                L.lg[lc][mc] = v ? a.scale * d[j] : -INFINITY;
             }
         }
-        ok[it] = v;
-        const size_t off = ((size_t)(v ? cell : 0) * a.kv_heads + g) * DH + (size_t)chunk * 8;
-        kr[it] = *(const uint4 *)(a.k + off);
-        vr[it] = *(const uint4 *)(a.v + off);
-    }
-
-    float qr[G][8];
+    } else if (tv >= 0 && tv < S::PV_LANES) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const float4 *qp = (const float4 *)(a.q + (size_t)(g * G + h) * DH + chunk * 8);
-        const float4 x = qp[0], y = qp[1];
-        qr[h][0] = x.x; qr[h][1] = x.y; qr[h][2] = x.z; qr[h][3] = x.w;
-        qr[h][4] = y.x; qr[h][5] = y.y; qr[h][6] = y.z; qr[h][7] = y.w;
-    }
-
-    // ---- logits
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        half8 kh;
-        __builtin_memcpy(&kh, &kr[it], 16);
-        float kf[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            kf[j] = (float)kh[j];
-        float p[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float acc = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                acc = fmaf(qr[h][j], kf[j], acc);
-            p[h] = acc;
-        }
-        int hoff = 0;
-        Butterfly<LPC / 2, G>::template run<0>(p, lane, hoff);
-        constexpr int OWN = LPC / G;
-        if (chunk % OWN == 0) {
-            const int lc = wave * CPWW + it * CPL + sub;
-            s_lg[lc][hoff] = ok[it] ? a.scale * p[0] : -INFINITY;
+        for (int i = 0; i < S::CPG; ++i) {
+            bool valid;
+            const size_t row = cell_row(v_grp + S::SV * i, valid);
+            vr[i] = *(const uint4 *)(a.v + (row * a.kv_heads + g) * DH + v_chunk * 8);
         }
     }
     __syncthreads();
 
-    // ---- softmax over the split's cells, one head per wave at a time
-    static_assert(CPW <= kWave, "one cell per lane in the softmax");
-    for (int h = wave; h < G; h += 4) {
-        const float x = lane < CPW ? s_lg[lane][h] : -INFINITY;
-        const float m = wave_max(x);             // -inf only if no cell of the split is valid
+    // ---- softmax over the 16 cells, head = wave, cells = lanes 0-15 (row 0)
+    if (wave < G) {
+        const float x = L.lg[lane & 15][wave];
+        const float m = wave::row_max_f(x);          // -inf only if no cell is valid
         const float p = x == -INFINITY ? 0.0f : expf(x - m);
-        const float l = wave_sum(p);
-        if (lane < CPW)
-            s_lg[lane][h] = p;
+        const float l = wave::row_sum_f(p);
+        if (lane < kCells)
+            L.lg[lane][wave] = p;
         if (lane == 0) {
-            s_m[h] = m;
-            s_l[h] = l;
+            L.m[wave] = m;
+            L.l[wave] = l;
         }
     }
     __syncthreads();
 
-    // ---- P . V
-    float acc[G * 8];
-#pragma unroll
-    for (int i = 0; i < G * 8; ++i)
-        acc[i] = 0.0f;
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-        const int lc = wave * CPWW + it * CPL + sub;
-        half8 vh;
-        __builtin_memcpy(&vh, &vr[it], 16);
-        float vf[8];
+    // ---- P . V over this lane's cells
+    if (tv >= 0 && tv < S::PV_LANES) {
+        float acc[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            vf[j] = (float)vh[j];
+            acc[j] = 0.0f;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float p = s_lg[lc][h];
+        for (int i = 0; i < S::CPG; ++i) {
+            const float p = L.lg[v_grp + S::SV * i][v_head];
+            half8 vh;
+            __builtin_memcpy(&vh, &vr[i], 16);
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                acc[h * 8 + j] = fmaf(p, vf[j], acc[h * 8 + j]);
+                acc[j] = fmaf(p, (float)vh[j], acc[j]);
         }
-    }
-    // Sum over the CPL cells of a wave-wide load: lanes differing in bits >= log2(LPC).
-    int ioff = 0;
-    Butterfly<32, G * 8>::template run<LPC / 2>(acc, lane, ioff);
-    constexpr int LIVE = (G * 8) / CPL;
-#pragma unroll
-    for (int i = 0; i < LIVE; ++i) {
-        const int flat = ioff + i;
-        s_red[wave][flat >> 3][chunk * 8 + (flat & 7)] = acc[i];
+        float4 *dst = (float4 *)&L.acc[v_grp][v_head * DH + v_chunk * 8];
+        dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
     }
     __syncthreads();
 
     float *part = a.part + ((size_t)g * a.n_split + split) * (size_t)part_stride(G, DH);
-    for (int i = t; i < G * DH; i += 256) {
-        const int h = i / DH, d = i % DH;
-        part[2 * G + i] = s_red[0][h][d] + s_red[1][h][d] + s_red[2][h][d] + s_red[3][h][d];
+    for (int i = t; i < G * DH; i += kAT) {
+        float s = L.acc[0][i];
+#pragma unroll
+        for (int grp = 1; grp < S::SV; ++grp)
+            s += L.acc[grp][i];
+        part[2 * G + i] = s;
     }
     if (t < G) {
-        part[t] = s_m[t];
-        part[G + t] = s_l[t];
+        part[t] = L.m[t];
+        part[G + t] = L.l[t];
     }
+}
+
+template <int DH, int G>
+__global__ __launch_bounds__(kAT) void k_attend(AttendArgs a)
+{
+    __shared__ AttLds<DH, G> L;
+    const int split = blockIdx.x;
+    // the split's block ids (identity when every block is kept)
+    if (threadIdx.x < kCells / 4) {
+        const int i = split * (kCells / 4) + threadIdx.x;
+        L.blk[threadIdx.x] = !a.sel ? i : (i < a.n_sel_blocks ? a.sel[i] : -1);
+    }
+    __syncthreads();
+    attend_split<DH, G>(a, L, split, blockIdx.y);
+}
+
+// Stages 3 and 4 in one kernel: every attention workgroup runs the top-k
+// routine itself (the same deterministic result everywhere, each on its own
+// CU in parallel) and keeps the ids of its own 4 slots; workgroup (0, 0) also
+// writes the whole list when the caller asked for it.  No select launch and
+// no round trip of the id list through memory.
+struct FusedArgs {
+    AttendArgs att;
+    SelectArgs sel;             // sel.sel: optional output of all k ids
+};
+
+template <int DH, int G>
+__global__ __launch_bounds__(kAT) void k_select_attend(FusedArgs f)
+{
+    static_assert(kAT == sel::kT, "one workgroup size for both stages");
+    __shared__ AttLds<DH, G> L;
+    extern __shared__ uint4 sel_lds[];
+    const int split = blockIdx.x;
+    if (threadIdx.x < kCells / 4)
+        L.blk[threadIdx.x] = -1;
+    __syncthreads();
+    const uint32_t s0 = (uint32_t)split * (kCells / 4);
+    int32_t *all = (blockIdx.x == 0 && blockIdx.y == 0) ? f.sel.sel : nullptr;
+    int32_t *blk = L.blk;
+    sel::run(f.sel, reinterpret_cast<char *>(sel_lds), [=](uint32_t slot, uint32_t id) {
+        if (slot - s0 < (uint32_t)(kCells / 4))
+            blk[slot - s0] = (int32_t)id;
+        if (all)
+            all[slot] = (int32_t)id;
+    });
+    __syncthreads();
+    attend_split<DH, G>(f.att, L, split, blockIdx.y);
 }
 
 // out[h][d] = sum_s e^(m_s - M) acc_s[h][d] / sum_s e^(m_s - M) l_s.
-// Workgroup (h, 64-dim slice): the split weights go to LDS once, then 4 groups
-// of 64 threads each stream every 4th split's partials for their dim (many
-// independent loads in flight) and are summed in a fixed order, so the result
-// is bitwise repeatable.
-constexpr int kMergeThreads = 256;
-constexpr int kMergeDims = 64;
-constexpr int kMaxSplits = 1024;
-
-__device__ inline float block_reduce(float v, float *s_tmp, bool is_max)
-{
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        const float y = __shfl_xor(v, o);
-        v = is_max ? fmaxf(v, y) : v + y;
-    }
-    if ((t & 63) == 0)
-        s_tmp[t >> 6] = v;
-    __syncthreads();
-    float r = s_tmp[0];
-    for (int i = 1; i < kMergeThreads / 64; ++i)
-        r = is_max ? fmaxf(r, s_tmp[i]) : r + s_tmp[i];
-    __syncthreads();
-    return r;
-}
+// Workgroup (h, 64-dim slice), 16 waves, one global latency round: thread s
+// loads m_s while wave w loads (l_s, acc_s[d]) of splits w, w+16, ...; M by
+// a block max; thread s turns m_s into the weight e^(m_s - M) in LDS; each
+// wave sums its splits, and wave 0 sums the 16 wave results in order:
+// a fixed order, bitwise repeatable.
+constexpr int kMT = 1024;
+constexpr int kMW = kMT / kWave;
+constexpr int kMRound = 8;                  // splits per wave per load round
+constexpr int kMaxSplits = kMT;
 
 template <int DH, int G>
-__global__ __launch_bounds__(kMergeThreads) void k_merge(AttendArgs a)
+__global__ __launch_bounds__(kMT) void k_merge(AttendArgs a)
 {
-    __shared__ float s_f[kMaxSplits];
-    __shared__ float s_tmp[kMergeThreads / 64];
-    __shared__ float s_acc[kMergeThreads / kMergeDims][kMergeDims];
+    __shared__ float s_w[kMaxSplits];
+    __shared__ float s_red[kMW];
+    __shared__ float s_l[kMW], s_acc[kMW][kWave];
     const int h = blockIdx.x;
     const int g = h / G, hh = h % G;
-    const int t = threadIdx.x;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int ns = a.n_split;
     const size_t ps = (size_t)part_stride(G, DH);
     const float *base = a.part + (size_t)g * ns * ps;
+    const int d = blockIdx.y * kWave + lane;
 
-    float mx = -INFINITY;
-    for (int s = t; s < ns; s += kMergeThreads) {
-        s_f[s] = base[s * ps + hh];
-        mx = fmaxf(mx, s_f[s]);
-    }
-    const float M = block_reduce(mx, s_tmp, true);
-    float lsum = 0.0f;
-    for (int s = t; s < ns; s += kMergeThreads) {
-        const float f = s_f[s] == -INFINITY ? 0.0f : expf(s_f[s] - M);
-        s_f[s] = f;
-        lsum += f * base[s * ps + G + hh];
-    }
-    const float L = block_reduce(lsum, s_tmp, false);   // also orders the s_f writes
-
-    constexpr int NG = kMergeThreads / kMergeDims;       // split groups
-    const int grp = t / kMergeDims;
-    const int d = blockIdx.y * kMergeDims + t % kMergeDims;
-    const float *p = base + 2 * G + hh * DH + d;
-    float acc = 0.0f;
-    int s = grp;
-    for (; s + 7 * NG < ns; s += 8 * NG) {
-        float x[8];
+    // first round of (l, acc) loads, issued before anything waits
+    float l[kMRound], x[kMRound];
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            x[i] = p[(size_t)(s + i * NG) * ps];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            acc = fmaf(s_f[s + i * NG], x[i], acc);
+    for (int i = 0; i < kMRound; ++i) {
+        const int s = wave + i * kMW;
+        const float *p = base + (size_t)(s < ns ? s : 0) * ps;
+        l[i] = p[G + hh];
+        x[i] = p[2 * G + hh * DH + d];
     }
-    for (; s < ns; s += NG)
-        acc = fmaf(s_f[s], p[(size_t)s * ps], acc);
-    s_acc[grp][t % kMergeDims] = acc;
+    const float ms = t < ns ? base[(size_t)t * ps + hh] : -INFINITY;
+    const float wm = wave::reduce_max_f(ms);
+    if (lane == 0)
+        s_red[wave] = wm;
     __syncthreads();
-    if (grp == 0) {
-        float tot = s_acc[0][t];
-        for (int i = 1; i < NG; ++i)
-            tot += s_acc[i][t];
-        a.out[(size_t)h * DH + d] = tot / L;
+    float M = s_red[0];
+#pragma unroll
+    for (int w = 1; w < kMW; ++w)
+        M = fmaxf(M, s_red[w]);
+    if (t < ns)
+        s_w[t] = ms == -INFINITY ? 0.0f : expf(ms - M);
+    __syncthreads();
+
+    float acc = 0.0f, lsum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kMRound; ++i) {
+        const int s = wave + i * kMW;
+        if (s < ns) {
+            acc = fmaf(s_w[s], x[i], acc);
+            lsum = fmaf(s_w[s], l[i], lsum);
+        }
+    }
+    for (int s0 = wave + kMRound * kMW; s0 < ns; s0 += kMRound * kMW) {
+#pragma unroll
+        for (int i = 0; i < kMRound; ++i) {
+            const int s = s0 + i * kMW;
+            const float *p = base + (size_t)(s < ns ? s : 0) * ps;
+            l[i] = p[G + hh];
+            x[i] = p[2 * G + hh * DH + d];
+        }
+#pragma unroll
+        for (int i = 0; i < kMRound; ++i) {
+            const int s = s0 + i * kMW;
+            if (s < ns) {
+                acc = fmaf(s_w[s], x[i], acc);
+                lsum = fmaf(s_w[s], l[i], lsum);
+            }
+        }
+    }
+    if (lane == 0)
+        s_l[wave] = lsum;
+    s_acc[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+        float A = s_acc[0][lane], L = s_l[0];
+#pragma unroll
+        for (int w = 1; w < kMW; ++w) {
+            A += s_acc[w][lane];
+            L += s_l[w];
+        }
+        a.out[(size_t)h * DH + d] = A / L;
     }
 }
 
 template <int DH, int G>
-hipError_t go(const AttendArgs &a, hipStream_t s)
+hipError_t merge(const AttendArgs &a, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_attend<DH, G>), dim3(a.n_split, a.kv_heads), dim3(256), 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    if (a.n_split > kMaxSplits)
-        return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_merge<DH, G>), dim3(a.kv_heads * G, DH / kMergeDims), dim3(kMergeThreads),
-                       0, s, a);
+    hipLaunchKernelGGL((k_merge<DH, G>), dim3(a.kv_heads * G, DH / kWave), dim3(kMT), 0, s, a);
     return hipGetLastError();
 }
 
+template <int DH, int G>
+hipError_t go(const AttendArgs &a, const SelectArgs *sa, hipStream_t s)
+{
+    if (a.n_split > kMaxSplits)
+        return hipErrorInvalidValue;
+    if (!sa) {
+        hipLaunchKernelGGL((k_attend<DH, G>), dim3(a.n_split, a.kv_heads), dim3(kAT), 0, s, a);
+    } else {
+        const size_t lds = sel::lds_bytes(sa->nb);
+        if (lds + sizeof(AttLds<DH, G>) > sel::kMaxLds)
+            return hipErrorInvalidValue;
+        if (lds > 32 * 1024) {
+            static hipError_t attr = hipFuncSetAttribute(
+                (const void *)k_select_attend<DH, G>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                (int)(sel::kMaxLds - sizeof(AttLds<DH, G>)));
+            if (attr != hipSuccess)
+                return attr;
+        }
+        FusedArgs f{a, *sa};
+        hipLaunchKernelGGL((k_select_attend<DH, G>), dim3(a.n_split, a.kv_heads), dim3(kAT), lds, s,
+                           f);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    return merge<DH, G>(a, s);
+}
+
 template <int DH>
-hipError_t go_g(const AttendArgs &a, int G, hipStream_t s)
+hipError_t go_g(const AttendArgs &a, const SelectArgs *sa, int G, hipStream_t s)
 {
     switch (G) {
-    case 1: return go<DH, 1>(a, s);
-    case 2: return go<DH, 2>(a, s);
-    case 4: return go<DH, 4>(a, s);
-    case 8: return go<DH, 8>(a, s);
+    case 1: return go<DH, 1>(a, sa, s);
+    case 2: return go<DH, 2>(a, sa, s);
+    case 4: return go<DH, 4>(a, sa, s);
+    case 8: return go<DH, 8>(a, sa, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t dispatch(const AttendArgs &a, const SelectArgs *sa, int Dh, int G, hipStream_t s)
+{
+    switch (Dh) {
+    case 64: return go_g<64>(a, sa, G, s);
+    case 128: return go_g<128>(a, sa, G, s);
+    case 256: return go_g<256>(a, sa, G, s);
     }
     return hipErrorInvalidValue;
 }
@@ -337,12 +385,15 @@ hipError_t go_g(const AttendArgs &a, int G, hipStream_t s)
 
 hipError_t launch_attend(const AttendArgs &a, int Dh, int G, hipStream_t s)
 {
-    switch (Dh) {
-    case 64: return go_g<64>(a, G, s);
-    case 128: return go_g<128>(a, G, s);
-    case 256: return go_g<256>(a, G, s);
-    }
-    return hipErrorInvalidValue;
+    return dispatch(a, nullptr, Dh, G, s);
+}
+
+hipError_t launch_select_attend(const AttendArgs &a, const SelectArgs &sa, int Dh, int G,
+                                hipStream_t s)
+{
+    if (sa.T != 8 && sa.T != 16 && sa.T != 32)
+        return hipErrorInvalidValue;
+    return dispatch(a, &sa, Dh, G, s);
 }
 
 }  // namespace qsa

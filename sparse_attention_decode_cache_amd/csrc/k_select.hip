@@ -1,445 +1,17 @@
-// k_select.hip -- stage 3: deterministic block-domain top-k.
-//
-// Rank blocks by (score desc, id asc), keep the first k, return them in
-// ascending id order [post 10, "QSA indexer"; "block-domain top-k（COMMON-006）
-// 実装は見送り"].  Each block has the 64-bit composite key
-//     (order-preserving score key << 32) | ~id,
-// unique, nonzero and ordered exactly like (score desc, id asc), so the top k
-// are the composites >= kappa, the k-th largest: no ties are left to break
-// and the chosen set is a function of the scores alone.
-//
-// Input from the score pass: every block's key, and each tile's T largest
-// composites sorted descending, zero-filled (a tile = R = 8T consecutive
-// blocks).  Their union U has about N/8 entries.  One workgroup of 1024
-// threads (4 waves per SIMD, so LDS latency overlaps); thread t holds the
-// 16-byte chunks t + 1024q of U in registers (coalesced loads, 8 entries).
-// Per entry the work is a few branch-free VALU operations; fast path:
-//   1. min / max of the listed keys (finite scores required);
-//   2. a 1024-bin histogram LINEAR in the score over [min, max] -- a monotone
-//      map of the composite, so whole bins are ordered -- and the bin d
-//      holding the k-th largest of U; on scores spread like sums of products
-//      it holds a handful of entries;
-//   3. the entries of bin d are ranked by counting: kappa = the k-th of U;
-//   4. exactness: a tile can hide a block >= kappa only if its list is full
-//      (last slot nonzero) and that last entry is >= kappa.  If none is, the
-//      entries >= kappa ARE the top k of all N blocks;
-//   5. they are marked in an LDS bitmap of the ids; a prefix sum of the word
-//      popcounts gives each winner its output slot directly.
-// Anything the fast path cannot decide exactly -- fewer than k listed
-// entries, non-finite or all-equal scores, a crowded bin, a tile that may
-// hide winners, N > 65,536 -- takes the general path: radix refinement over
-// every key, marked in the same bitmap.
-#include "qsa_internal.h"
-#include "qsa_wave.h"
+// k_select.hip -- stage 3 as its own kernel: one workgroup runs the top-k
+// routine of qsa_select.h and writes the chosen block ids, ascending.
+#include "qsa_select.h"
 
 namespace qsa {
 namespace {
 
-constexpr int kT = 1024;                       // threads
-constexpr int kWaves = kT / kWave;
-constexpr int kChunks = 4;                     // 16-byte list chunks held per thread
-constexpr int kEntries = 2 * kChunks;          // list entries held per thread
-constexpr int kFastWords = 2048;               // bitmap words of the fast path (ids < 65,536)
-constexpr int kBins = kT;                      // linear bins of the fast path: one per thread
-constexpr int kCap = 256;                      // entries of bin d ranked by counting
-constexpr size_t kSelectMaxLds = 144 * 1024;   // of the 160 KB LDS of a gfx950 CU
-
-struct Smem {
-    uint32_t hist[kBins + kWave];              // + one dummy bin per lane
-    uint64_t cand[kCap];
-    alignas(16) uint32_t scan0[kWaves];
-    alignas(16) uint32_t scan1[kWaves];
-    alignas(16) uint32_t rmin[kWaves];
-    alignas(16) uint32_t rmax[kWaves];
-    uint64_t kappa;
-    uint32_t d, above, in_d, ncand;
-    // general path
-    uint32_t wsum[kWaves], woff[kWaves];
-    uint64_t wmin[kWaves], wmax[kWaves];
-    uint64_t bmin, bmax;
-    uint32_t wtot, bin, gabove;
-};
-
-__device__ inline uint64_t max64(uint64_t a, uint64_t b) { return a > b ? a : b; }
-__device__ inline uint64_t min64(uint64_t a, uint64_t b) { return a < b ? a : b; }
-
-// The score an order-preserving key was made from (-0 was folded into +0).
-__device__ inline float key_score(uint32_t key)
+__global__ __launch_bounds__(sel::kT) void k_select(SelectArgs a)
 {
-    return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
-}
-
-// Keys of finite scores: strictly between the keys of -inf and +inf.
-constexpr uint32_t kKeyFiniteLo = 0x00800000u;
-constexpr uint32_t kKeyFiniteHi = 0xFF7FFFFFu;
-
-// Exclusive prefix sum over the threads in thread order, one barrier: DPP
-// scan inside each wave; every thread adds up the wave totals in `slot`
-// (kWaves words, used by this call only).
-__device__ inline uint32_t scan_excl(uint32_t v, uint32_t *slot, uint32_t &total)
-{
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const uint32_t x = wave::incl_scan_add(v);
-    if (lane == 63)
-        slot[w] = x;
-    __syncthreads();
-    uint32_t off = 0, tot = 0;
-#pragma unroll
-    for (int i = 0; i < kWaves; i += 4) {
-        const uint4 s = reinterpret_cast<const uint4 *>(slot)[i / 4];
-        tot += s.x + s.y + s.z + s.w;
-        off += (i < w ? s.x : 0u) + (i + 1 < w ? s.y : 0u) + (i + 2 < w ? s.z : 0u) +
-               (i + 3 < w ? s.w : 0u);
-    }
-    total = tot;
-    return off + x - v;
-}
-
-// ------------------------------------------------------------ general path
-
-// Block-wide exclusive prefix sum (wave 0 scans the wave totals).
-__device__ inline uint32_t block_excl_scan(uint32_t v, Smem &sm, uint32_t *total)
-{
-    const int t = threadIdx.x, w = t >> 6;
-    const uint32_t x = wave::incl_scan_add(v);
-    if ((t & 63) == 63)
-        sm.wsum[w] = x;
-    __syncthreads();
-    if (w == 0) {
-        const uint32_t s = t < kT / 64 ? sm.wsum[t] : 0u;
-        const uint32_t inc = wave::incl_scan_add(s);
-        if (t < kT / 64)
-            sm.woff[t] = inc - s;
-        if (t == kT / 64 - 1)
-            sm.wtot = inc;
-    }
-    __syncthreads();
-    if (total)
-        *total = sm.wtot;
-    return sm.woff[w] + x - v;
-}
-
-__device__ inline void block_minmax(Smem &sm, uint64_t lo, uint64_t hi, uint64_t &mn, uint64_t &mx)
-{
-    lo = wave::reduce_min_u64(lo);
-    hi = wave::reduce_max_u64(hi);
-    const int t = threadIdx.x, w = t >> 6;
-    if ((t & 63) == 0) {
-        sm.wmin[w] = lo;
-        sm.wmax[w] = hi;
-    }
-    __syncthreads();
-    if (w == 0) {
-        const uint64_t a = wave::reduce_min_u64(t < kT / 64 ? sm.wmin[t] : ~0ull);
-        const uint64_t b = wave::reduce_max_u64(t < kT / 64 ? sm.wmax[t] : 0ull);
-        if (t == 0) {
-            sm.bmin = a;
-            sm.bmax = b;
-        }
-    }
-    __syncthreads();
-    mn = sm.bmin;
-    mx = sm.bmax;
-    __syncthreads();
-}
-
-// Thread t owns bins [t*bpt, t*bpt + bpt).  Finds the bin b holding the
-// need-th largest item: above(b) < need <= above(b) + hist[b], above(b) =
-// items in higher bins.  Result in sm.bin / sm.gabove.
-__device__ inline void find_bin(Smem &sm, int nbins, uint32_t need)
-{
-    const int t = threadIdx.x;
-    const int bpt = (nbins + kT - 1) / kT;
-    const int b0 = t * bpt;
-    uint32_t mine = 0;
-    for (int i = 0; i < bpt; ++i)
-        mine += b0 + i < nbins ? sm.hist[b0 + i] : 0u;
-    uint32_t total;
-    const uint32_t below = block_excl_scan(mine, sm, &total);
-    uint32_t acc = total - below - mine;
-    if (acc < need && acc + mine >= need) {
-        for (int i = bpt - 1; i >= 0; --i) {
-            const uint32_t h = b0 + i < nbins ? sm.hist[b0 + i] : 0u;
-            if (acc + h >= need) {
-                sm.bin = (uint32_t)(b0 + i);
-                sm.gabove = acc;
-                break;
-            }
-            acc += h;
-        }
-    }
-    __syncthreads();
-}
-
-// Radix refinement over the composites visited by for_each(f): marks exactly
-// `need` of them -- the largest -- via mark(c).  Digits start below the
-// leading bits shared by the smallest and the largest item.
-template <class ForEach, class Mark>
-__device__ void refine_and_mark(Smem &sm, ForEach for_each, Mark mark, uint32_t need)
-{
-    uint64_t lo = ~0ull, hi = 0, mn, mx;
-    for_each([&](uint64_t c) {
-        lo = min64(lo, c);
-        hi = max64(hi, c);
+    extern __shared__ uint4 sel_lds[];
+    int32_t *out = a.sel;
+    sel::run(a, reinterpret_cast<char *>(sel_lds), [=](uint32_t slot, uint32_t id) {
+        out[slot] = (int32_t)id;
     });
-    block_minmax(sm, lo, hi, mn, mx);
-    if (mn == mx) {
-        for_each([&](uint64_t c) {
-            if (c == mx)
-                mark(c);
-        });
-        __syncthreads();
-        return;
-    }
-    const int common = __clzll((long long)(mn ^ mx));
-    uint64_t pmask = common == 0 ? 0ull : ~0ull << (64 - common);
-    uint64_t prefix = mx & pmask;
-    int width = 64 - common < 10 ? 64 - common : 10;
-    int shift = 64 - common - width;
-    for (;;) {
-        const uint64_t dmask = (1ull << width) - 1;
-        const int nbins = 1 << width;
-        for (int i = threadIdx.x; i < nbins; i += kT)
-            sm.hist[i] = 0u;
-        __syncthreads();
-        for_each([&](uint64_t c) {
-            if ((c & pmask) == prefix)
-                atomicAdd(&sm.hist[(c >> shift) & dmask], 1u);
-        });
-        __syncthreads();
-        find_bin(sm, nbins, need);
-        const uint32_t d = sm.bin, above = sm.gabove, in_d = sm.hist[d];
-        for_each([&](uint64_t c) {
-            if ((c & pmask) == prefix && ((c >> shift) & dmask) > d)
-                mark(c);
-        });
-        need -= above;
-        prefix |= (uint64_t)d << shift;
-        pmask |= dmask << shift;
-        if (in_d == need || shift == 0) {
-            // composites are unique: at shift 0 exactly one is left
-            for_each([&](uint64_t c) {
-                if ((c & pmask) == prefix)
-                    mark(c);
-            });
-            __syncthreads();
-            return;
-        }
-        width = shift < 8 ? shift : 8;
-        shift -= width;
-        __syncthreads();
-    }
-}
-
-// ------------------------------------------------------------------ kernel
-
-__global__ __launch_bounds__(kT) void k_select(SelectArgs a)
-{
-    extern __shared__ uint64_t dyn_lds[];
-    Smem &sm = *reinterpret_cast<Smem *>(dyn_lds);
-    const uint32_t nb = (uint32_t)a.nb;
-    const uint32_t k = (uint32_t)a.k;
-    const uint32_t nwords = (nb + 31) >> 5;
-    uint32_t *bitmap = reinterpret_cast<uint32_t *>(dyn_lds + (sizeof(Smem) + 7) / 8);
-    uint32_t *wpre = bitmap + (nwords > (uint32_t)kFastWords ? nwords : (uint32_t)kFastWords);
-    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-    const uint32_t nchunks = (uint32_t)a.ntiles * (uint32_t)a.T / 2;
-    bool general = nchunks > (uint32_t)(kT * kChunks);
-
-    // clear: histogram, bitmap words 2t and 2t+1, the candidate counter
-    sm.hist[t] = 0u;
-    if (t < kWave)
-        sm.hist[kBins + t] = 0u;
-    uint2 *own = reinterpret_cast<uint2 *>(bitmap) + t;
-    *own = make_uint2(0u, 0u);
-    if (t == 0)
-        sm.ncand = 0u;
-
-    // chunks t + 1024q of U (2 composites each), all loads in flight together
-    uint64_t u[kEntries];
-    {
-        const uint4 *src = reinterpret_cast<const uint4 *>(a.lists);
-#pragma unroll
-        for (int q = 0; q < kChunks; ++q) {
-            const uint32_t c = (uint32_t)t + (uint32_t)(kT * q);
-            const uint4 v = src[c < nchunks ? c : nchunks - 1];
-            const bool in = !general && c < nchunks;
-            u[2 * q] = in ? ((uint64_t)v.y << 32) | v.x : 0ull;
-            u[2 * q + 1] = in ? ((uint64_t)v.w << 32) | v.z : 0ull;
-        }
-    }
-    // 1. key range of the listed entries (an empty slot has key 0: it wraps
-    //    to the top in key - 1 and is the bottom for the maximum)
-    uint32_t kmin1 = 0xFFFFFFFFu, kmax = 0u;
-#pragma unroll
-    for (int e = 0; e < kEntries; ++e) {
-        const uint32_t key = (uint32_t)(u[e] >> 32);
-        kmin1 = min(kmin1, key - 1u);
-        kmax = max(kmax, key);
-    }
-    kmin1 = wave::reduce_min_u32(kmin1);
-    kmax = wave::reduce_max_u32(kmax);
-    if (lane == 0) {
-        sm.rmin[wv] = kmin1;
-        sm.rmax[wv] = kmax;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kWaves; i += 4) {
-        const uint4 a4 = reinterpret_cast<const uint4 *>(sm.rmin)[i / 4];
-        const uint4 b4 = reinterpret_cast<const uint4 *>(sm.rmax)[i / 4];
-        kmin1 = min(min(kmin1, a4.x), min(a4.y, min(a4.z, a4.w)));
-        kmax = max(max(kmax, b4.x), max(b4.y, max(b4.z, b4.w)));
-    }
-    const uint32_t kmin = kmin1 + 1u;
-    const float mn = key_score(kmin), mx = key_score(kmax);
-    const float range = mx - mn;
-    const float scale = (float)kBins / range;
-    general = general || kmin1 == 0xFFFFFFFFu || kmin < kKeyFiniteLo || kmax > kKeyFiniteHi ||
-              !(range > 0.0f) || !(range < __builtin_inff()) || !(scale < __builtin_inff());
-
-    if (!general) {
-        // 2. linear histogram (all keys finite here: key != 0 <=> listed)
-        uint32_t bins[kEntries];
-#pragma unroll
-        for (int e = 0; e < kEntries; ++e) {
-            const uint32_t key = (uint32_t)(u[e] >> 32);
-            const float s = key != 0u ? key_score(key) : mn;       // in [mn, mx]
-            const uint32_t b = (uint32_t)((s - mn) * scale);       // in [0, 1024]
-            bins[e] = b < (uint32_t)kBins - 1 ? b : (uint32_t)kBins - 1;
-            atomicAdd(&sm.hist[key != 0u ? bins[e] : (uint32_t)(kBins + lane)], 1u);
-        }
-        __syncthreads();
-        // the bin holding the k-th largest (thread t <-> bin t)
-        const uint32_t h = sm.hist[t];
-        uint32_t total;
-        const uint32_t below = scan_excl(h, sm.scan0, total);
-        const uint32_t acc = total - below - h;             // entries in higher bins
-        if (acc < k && acc + h >= k) {
-            sm.d = (uint32_t)t;
-            sm.above = acc;
-            sm.in_d = h;
-        }
-        __syncthreads();
-        const uint32_t d = sm.d, need = k - sm.above, m = sm.in_d;
-        general = total < k || m > (uint32_t)kCap;
-
-        if (!general) {
-            // 3. kappa: the need-th largest entry of bin d, ranked by counting
-            bool hit[kEntries];
-            uint32_t nd = 0;
-#pragma unroll
-            for (int e = 0; e < kEntries; ++e) {
-                hit[e] = u[e] != 0ull && bins[e] == d;
-                nd += hit[e] ? 1u : 0u;
-            }
-            if (nd) {
-                uint32_t o = atomicAdd(&sm.ncand, nd);
-#pragma unroll
-                for (int e = 0; e < kEntries; ++e)
-                    if (hit[e])
-                        sm.cand[o++] = u[e];
-            }
-            __syncthreads();
-            if ((uint32_t)t < m) {
-                const uint64_t c = sm.cand[t];
-                uint32_t r = 0;
-#pragma unroll 4
-                for (uint32_t i = 0; i < m; ++i)
-                    r += sm.cand[i] > c ? 1u : 0u;
-                if (r == need - 1)
-                    sm.kappa = c;
-            }
-            __syncthreads();
-            const uint64_t kappa = sm.kappa;
-
-            // 4. winners into the bitmap; exactness check.  The last slot of
-            //    a list is the odd entry of chunks c with (c+1) % (T/2) == 0,
-            //    i.e. of every chunk of threads with (t+1) % (T/2) == 0.
-            bool win[kEntries];
-#pragma unroll
-            for (int e = 0; e < kEntries; ++e)
-                win[e] = u[e] >= kappa;
-            const bool holds_last = (((uint32_t)t + 1) & ((uint32_t)a.T / 2 - 1)) == 0;
-            bool bad = false;
-#pragma unroll
-            for (int q = 0; q < kChunks; ++q)
-                bad = bad || (holds_last && win[2 * q + 1]);
-#pragma unroll
-            for (int e = 0; e < kEntries; ++e)
-                if (win[e]) {
-                    const uint32_t id = ~(uint32_t)u[e];
-                    atomicOr(&bitmap[id >> 5], 1u << (id & 31));
-                }
-            general = __syncthreads_or(bad ? 1 : 0) != 0;
-            if (!general) {
-                // 5. word prefix sums over the bitmap (thread t: words 2t, 2t+1),
-                //    then each winner's slot = prefix of its word + bits below it
-                const uint2 wd = *own;
-                const uint32_t p0 = (uint32_t)__popc(wd.x), p1 = (uint32_t)__popc(wd.y);
-                uint32_t unused;
-                const uint32_t pre = scan_excl(p0 + p1, sm.scan1, unused);
-                reinterpret_cast<uint2 *>(wpre)[t] = make_uint2(pre, pre + p0);
-                __syncthreads();
-                uint32_t slot[kEntries];
-#pragma unroll
-                for (int e = 0; e < kEntries; ++e) {
-                    const uint32_t id = ~(uint32_t)u[e];
-                    const uint32_t w = win[e] ? id >> 5 : 0u;
-                    slot[e] = wpre[w] + (uint32_t)__popc(bitmap[w] & ((1u << (id & 31)) - 1u));
-                }
-#pragma unroll
-                for (int e = 0; e < kEntries; ++e)
-                    if (win[e] && slot[e] < k)
-                        a.sel[slot[e]] = (int32_t)~(uint32_t)u[e];
-                return;
-            }
-        }
-    }
-
-    // ---------------------------------------------------------- general path
-    __syncthreads();
-    for (uint32_t i = t; i < nwords; i += kT)
-        bitmap[i] = 0u;
-    __syncthreads();
-    auto each_key = [&](auto f) {
-        for (uint32_t base = 0; base < nb; base += kT * 8) {
-            uint32_t kk[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const uint32_t e = base + q * kT + t;
-                kk[q] = a.keys[e < nb ? e : nb - 1];
-            }
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const uint32_t e = base + q * kT + t;
-                if (e < nb)
-                    f(comp_key(kk[q], e));
-            }
-        }
-    };
-    refine_and_mark(sm, each_key, [&](uint64_t c) {
-        const uint32_t id = ~(uint32_t)c;
-        atomicOr(&bitmap[id >> 5], 1u << (id & 31));
-    }, k);
-    __syncthreads();
-    const uint32_t per = (nwords + kT - 1) / kT;
-    const uint32_t w0 = t * per;
-    const uint32_t w1 = w0 + per < nwords ? w0 + per : nwords;
-    uint32_t c = 0;
-    for (uint32_t w = w0; w < w1; ++w)
-        c += (uint32_t)__popc(bitmap[w]);
-    uint32_t o = block_excl_scan(c, sm, nullptr);
-    for (uint32_t w = w0; w < w1; ++w) {
-        uint32_t bits = bitmap[w];
-        while (bits) {
-            const int b = __ffs(bits) - 1;
-            bits &= bits - 1;
-            if (o < k)
-                a.sel[o] = (int32_t)(w * 32 + b);
-            ++o;
-        }
-    }
 }
 
 }  // namespace
@@ -448,19 +20,17 @@ hipError_t launch_select(const SelectArgs &a, hipStream_t s)
 {
     if (a.T != 8 && a.T != 16 && a.T != 32)
         return hipErrorInvalidValue;
-    const size_t nwords = (size_t)((a.nb + 31) / 32);
-    const size_t bm = nwords > (size_t)kFastWords ? nwords : (size_t)kFastWords;
-    const size_t lds = (sizeof(Smem) + 7) / 8 * 8 + 4 * bm + 4 * (size_t)kFastWords;
-    if (lds > kSelectMaxLds)
+    const size_t lds = sel::lds_bytes(a.nb);
+    if (lds > sel::kMaxLds)
         return hipErrorInvalidValue;
     if (lds > 64 * 1024) {
         static hipError_t attr = hipFuncSetAttribute((const void *)k_select,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                     (int)kSelectMaxLds);
+                                                     (int)sel::kMaxLds);
         if (attr != hipSuccess)
             return attr;
     }
-    hipLaunchKernelGGL(k_select, dim3(1), dim3(kT), lds, s, a);
+    hipLaunchKernelGGL(k_select, dim3(1), dim3(sel::kT), lds, s, a);
     return hipGetLastError();
 }
 

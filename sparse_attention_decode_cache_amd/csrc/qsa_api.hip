@@ -5,6 +5,7 @@
 #include <stdio.h>
 
 #include "qsa_internal.h"
+#include "qsa_select.h"
 
 using namespace qsa;
 
@@ -91,7 +92,7 @@ int64_t decode_part_floats(const qsa_layer_desc *d)
 {
     const int G = d->q_heads / d->kv_heads;
     const int64_t max_cells = (int64_t)d->top_k_tokens + 3;
-    return (int64_t)d->kv_heads * n_splits(max_cells, d->head_dim) * part_stride(G, d->head_dim);
+    return (int64_t)d->kv_heads * n_splits(max_cells) * part_stride(G, d->head_dim);
 }
 
 WsLayout decode_layout(const qsa_layer_desc *d, int32_t capacity)
@@ -109,9 +110,27 @@ qsa_status check_ws(void *ws, size_t ws_bytes, size_t need)
 }
 
 // Stage 4 launch shared by qsa_gather_attend and qsa_decode_step.
-qsa_status do_attend(const qsa_layer_desc *d, const qsa_layer_cache *c, int32_t n_tokens,
-                     const int32_t *sel, int32_t n_sel_blocks, const float *q, float *out,
-                     float *part, hipStream_t stream)
+// Compute units of the current device (cached per device).
+int64_t device_cus()
+{
+    static thread_local int cached_dev = -1;
+    static thread_local int64_t cached_cus = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return 0;
+    if (dev != cached_dev) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cached_dev = dev;
+        cached_cus = cus;
+    }
+    return cached_cus;
+}
+
+AttendArgs attend_args(const qsa_layer_desc *d, const qsa_layer_cache *c, int32_t n_tokens,
+                       const int32_t *sel, int32_t n_sel_blocks, const float *q, float *out,
+                       float *part)
 {
     AttendArgs a{};
     a.k = c->k;
@@ -123,20 +142,28 @@ qsa_status do_attend(const qsa_layer_desc *d, const qsa_layer_cache *c, int32_t 
     a.n_sel_blocks = n_sel_blocks;
     a.nb = n_tokens / 4;
     a.n_cells = 4 * n_sel_blocks + n_tokens % 4;
-    if (!sel)
+    if (!sel && n_sel_blocks == a.nb)
         a.n_cells = n_tokens;      // every block kept: cells are 0..n-1
-    a.n_split = (int32_t)n_splits(a.n_cells, d->head_dim);
+    a.n_split = (int32_t)n_splits(a.n_cells);
     a.kv_heads = d->kv_heads;
     a.scale = attn_scale(d);
+    return a;
+}
+
+qsa_status do_attend(const qsa_layer_desc *d, const qsa_layer_cache *c, int32_t n_tokens,
+                     const int32_t *sel, int32_t n_sel_blocks, const float *q, float *out,
+                     float *part, hipStream_t stream)
+{
+    const AttendArgs a = attend_args(d, c, n_tokens, sel, n_sel_blocks, q, out, part);
     hipError_t e = launch_attend(a, d->head_dim, d->q_heads / d->kv_heads, stream);
     if (e != hipSuccess)
         return hip_fail(e, "attend");
     return QSA_OK;
 }
 
-// Stage 3 launch over the keys and tile lists already in the workspace.
-qsa_status do_select(char *ws, const WsLayout &L, int32_t nb, int32_t k, int32_t tile_rows,
-                     int32_t *sel, hipStream_t stream)
+// Top-k arguments over the keys and tile lists already in the workspace.
+SelectArgs select_args(char *ws, const WsLayout &L, int32_t nb, int32_t k, int32_t tile_rows,
+                       int32_t *sel)
 {
     SelectArgs s{};
     s.keys = (const uint32_t *)(ws + L.keys);
@@ -146,7 +173,13 @@ qsa_status do_select(char *ws, const WsLayout &L, int32_t nb, int32_t k, int32_t
     s.k = k;
     s.ntiles = (nb + tile_rows - 1) / tile_rows;
     s.T = tile_rows / kListDiv;
-    hipError_t e = launch_select(s, stream);
+    return s;
+}
+
+qsa_status do_select(char *ws, const WsLayout &L, int32_t nb, int32_t k, int32_t tile_rows,
+                     int32_t *sel, hipStream_t stream)
+{
+    hipError_t e = launch_select(select_args(ws, L, nb, k, tile_rows, sel), stream);
     if (e != hipSuccess)
         return hip_fail(e, "select");
     return QSA_OK;
@@ -375,26 +408,40 @@ qsa_status qsa_decode_step(const qsa_layer_desc *desc, const qsa_layer_cache *ca
             return hip_fail(e, "decode_step/score");
     }
 
-    // 3. top-k (every block is kept when nb <= K)
-    const int32_t *sel = nullptr;
-    int32_t n_sel = nb;
+    // 3 + 4. top-k (every block is kept when nb <= K), gather + attend.  When
+    //    the tile lists fit one workgroup and the attention grid fits one
+    //    workgroup per CU, every attention workgroup selects for itself (one
+    //    kernel; a second workgroup on a CU would halve the speed of both);
+    //    otherwise the select kernel runs first.
+    float *part = (float *)(wsp + L.part);
+    const int G = desc->q_heads / desc->kv_heads;
     if (need_select) {
-        int32_t *dst = sel_out ? sel_out : (int32_t *)(wsp + L.sel);
-        if ((s = do_select(wsp, L, nb, K, score_tile_rows(desc->idx_dtype == QSA_F16, rowb), dst,
-                           stream)) != QSA_OK)
+        const int tile_rows = score_tile_rows(desc->idx_dtype == QSA_F16, rowb);
+        SelectArgs sa = select_args(wsp, L, nb, K, tile_rows, sel_out);
+        const AttendArgs aa = attend_args(desc, cache, n, nullptr, K, q, out, part);
+        if (sel::fits_fast(sa.ntiles, sa.T) &&
+            (int64_t)aa.n_split * aa.kv_heads <= device_cus()) {
+            e = launch_select_attend(aa, sa, desc->head_dim, G, stream);
+            if (e != hipSuccess)
+                return hip_fail(e, "decode_step/select_attend");
+        } else {
+            int32_t *dst = sel_out ? sel_out : (int32_t *)(wsp + L.sel);
+            sa.sel = dst;
+            e = launch_select(sa, stream);
+            if (e != hipSuccess)
+                return hip_fail(e, "decode_step/select");
+            if ((s = do_attend(desc, cache, n, dst, K, q, out, part, stream)) != QSA_OK)
+                return s;
+        }
+    } else {
+        if (sel_out && nb > 0) {
+            e = launch_iota(sel_out, nb, stream);
+            if (e != hipSuccess)
+                return hip_fail(e, "decode_step/iota");
+        }
+        if ((s = do_attend(desc, cache, n, nullptr, nb, q, out, part, stream)) != QSA_OK)
             return s;
-        sel = dst;
-        n_sel = K;
-    } else if (sel_out && nb > 0) {
-        e = launch_iota(sel_out, nb, stream);
-        if (e != hipSuccess)
-            return hip_fail(e, "decode_step/iota");
     }
-
-    // 4. gather + attend
-    if ((s = do_attend(desc, cache, n, sel, n_sel, q, out, (float *)(wsp + L.part), stream)) !=
-        QSA_OK)
-        return s;
 
     st->n_tokens = n;
     st->n_valid_blocks = nb;

@@ -39,14 +39,12 @@ inline WsLayout ws_layout(int64_t max_blocks, int64_t sel_entries, int64_t part_
 // Floats of one attention partial: m[G], l[G], acc[G][Dh].
 __host__ __device__ inline int64_t part_stride(int G, int Dh) { return 2 * (int64_t)G + (int64_t)G * Dh; }
 
-// Cells handled by one attention workgroup: 16 for Dh >= 128 (enough
-// workgroups to cover the chip at 2051 cells), 32 for Dh = 64 (a wave-wide
-// load covers 8 cells there).
-__host__ __device__ constexpr int cells_per_split(int Dh) { return Dh >= 128 ? 16 : 32; }
+// Cells handled by one attention workgroup.
+constexpr int kCellsPerSplit = 16;
 
-inline int64_t n_splits(int64_t n_cells, int Dh)
+inline int64_t n_splits(int64_t n_cells)
 {
-    return (n_cells + cells_per_split(Dh) - 1) / cells_per_split(Dh);
+    return (n_cells + kCellsPerSplit - 1) / kCellsPerSplit;
 }
 
 // ------------------------------------------------------------- launchers
@@ -127,5 +125,9 @@ struct AttendArgs {
     float scale;
 };
 hipError_t launch_attend(const AttendArgs &a, int Dh, int G, hipStream_t s);
+// Stages 3 + 4 fused: every attention workgroup selects (a.sel is ignored;
+// the chosen ids come from `sa`, sa.sel optionally receives them all).
+hipError_t launch_select_attend(const AttendArgs &a, const SelectArgs &sa, int Dh, int G,
+                                hipStream_t s);
 
 }  // namespace qsa

@@ -74,6 +74,22 @@ __device__ inline uint64_t row_reduce64(uint64_t x, Op op)
     return x;
 }
 
+// Float reductions inside each 16-lane row (every lane of a row gets its row's
+// result; fixed combination order).
+__device__ inline float row_max_f(float v)
+{
+    return __uint_as_float(row_reduce(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+        return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+    }));
+}
+
+__device__ inline float row_sum_f(float v)
+{
+    return __uint_as_float(row_reduce(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+        return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+    }));
+}
+
 // Whole-wave reductions; the result is wave-uniform.
 __device__ inline uint32_t reduce_add(uint32_t x)
 {
