@@ -131,7 +131,8 @@ qsa_status qsa_cache_update(const qsa_layer_desc *desc, const qsa_layer_cache *c
  * q_idx[h][i] * summary[b][h][i] for b < n_blocks, in fp32 (w folded into
  * q_idx once per call).  q_idx: DEVICE fp32 [H_i][D_i]; w: DEVICE fp32
  * [H_i]; scores: DEVICE fp32 [n_blocks].  n_blocks = 0 enqueues nothing.
- * Errors: ARG if n_blocks < 0 or n_blocks > capacity/4 or a pointer is null. */
+ * Errors: ARG if n_blocks < 0 or n_blocks > capacity/4, a pointer is null or
+ * q_idx is not 16-byte aligned. */
 qsa_status qsa_index_score(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
                            int32_t n_blocks, const float *q_idx, const float *w,
                            float *scores, hipStream_t stream);

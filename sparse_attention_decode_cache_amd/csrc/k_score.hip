@@ -3,30 +3,46 @@
 // s[b] = sum_h w[h] * <q_idx[h], summary[b][h]>   [post 10, "QSA indexer"]
 //
 // This is the only pass whose bytes grow with context (N_b rows of up to 1 KB),
-// so it is written as a pure HBM stream: each lane owns one 16-byte chunk of a
-// row (LPR lanes cover a row, 64/LPR rows per wave-wide load), a wave issues
-// all T loads of its tile before using any (non-temporal: the rows are not
-// reused in this step), and the per-row partial dot products are reduced with
-// a transposing butterfly -- log2(LPR) exchange rounds for T rows instead of
-// log2(LPR) rounds per row.  w[h] is folded into q_idx once per lane.
+// so it is written as a pure HBM stream.  A row is split over L = min(16,
+// LPR) lanes (one DPP row) that each take C = LPR/L of its 16-byte chunks; a
+// wave-wide load covers 64/L consecutive rows, L*16 bytes of each: whole
+// cache lines, 1 KB per instruction.  Every load of the tile is issued before
+// any is used (non-temporal: the rows are not reused in this step).  Each
+// lane ends with the partial dots of V rows; a transposing butterfly inside
+// the 16-lane row (DPP moves only: row mirror, half mirror, quad swaps)
+// finishes V rows in log2(L) rounds.  w[h] is folded into q_idx once per lane.
 //
 // Outputs (all optional, plain stores, no atomics): fp32 scores; the
 // order-preserving 32-bit key of every score; and, for the top-k, each tile's
 // T = R/8 largest composite keys (key << 32 | ~block), sorted descending.
 //
 // Fused stage 1: in a decode step at most one summary row is new.  Workgroup 0
-// (dispatched first) appends the token's rows, pools that block, then scores
-// the LAST tile -- the one holding the new row -- so the pooling latency hides
-// under the stream of the other workgroups.
+// (dispatched first) scores the LAST tile -- the one holding the new row --
+// and, while its loads are in flight, appends the token's rows and pools that
+// block straight into LDS; the lanes that loaded the row's stale chunks take
+// the pooled ones from there.  The pooling latency hides under the stream.
 #include "qsa_pool.h"
 #include "qsa_wave.h"
 
 namespace qsa {
 namespace {
 
-// Transposing butterfly over the lanes of one row group.  Before: v[0..CNT)
-// are partial sums of CNT different rows.  After: v[0] holds the full sum of
-// row index `toff` (lanes that end with equal `toff` hold equal sums).
+// Lane partner of exchange round O inside a 16-lane row: a lane whose bit O
+// differs (mirror moves also flip the lower bits; rounds run from high O to
+// low, so lanes differing only in lower bits still hold the same row set).
+template <int O>
+__device__ inline float partner(float x)
+{
+    constexpr int ctrl = O == 8 ? wave::kRowMirror
+                       : O == 4 ? wave::kRowHalfMirror
+                       : O == 2 ? wave::kQuadXor2 : wave::kQuadXor1;
+    return __uint_as_float(wave::dpp<ctrl>(__float_as_uint(x)));
+}
+
+// Transposing butterfly over the L = 2*O lanes of a row group.  Before:
+// v[0..CNT) are partial sums of CNT different rows.  After: v[0] holds the
+// full sum of row index `toff` (lanes that end with equal `toff` hold equal
+// sums).
 template <int O, int CNT>
 struct Butterfly {
     static __device__ inline void run(float *v, int lane, int &toff)
@@ -40,13 +56,13 @@ struct Butterfly {
             for (int k = 0; k < H; ++k) {
                 const float send = up ? v[k] : v[k + H];
                 const float keep = up ? v[k + H] : v[k];
-                v[k] = keep + __shfl_xor(send, O);
+                v[k] = keep + partner<O>(send);
             }
             if (up)
                 toff += H;
             Butterfly<O / 2, H>::run(v, lane, toff);
         } else {
-            v[0] += __shfl_xor(v[0], O);
+            v[0] += partner<O>(v[0]);
             Butterfly<O / 2, 1>::run(v, lane, toff);
         }
     }
@@ -93,10 +109,14 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 template <int LPR>
 struct ScoreShape {
-    static constexpr int RPL = kWave / LPR;           // rows per wave-wide load
-    static constexpr int T = LPR < 16 ? LPR : 16;     // loads in flight per lane
-    static constexpr int RPW = T * RPL;               // rows per wave tile
-    static constexpr int R = 4 * RPW;                 // rows per workgroup tile
+    static constexpr int L = LPR < 16 ? LPR : 16;      // lanes per row
+    static constexpr int C = LPR / L;                   // chunks per lane per row
+    static constexpr int RI = kWave / L;                // rows per wave-wide load
+    static constexpr int LOADS = LPR >= 16 ? 16 : 8;    // loads per lane
+    static constexpr int V = LOADS / C;                 // row groups per lane
+    static constexpr int RPW = V * RI;                  // rows per wave
+    static constexpr int R = 4 * RPW;                   // rows per workgroup tile
+    static_assert(V >= 1 && V <= L, "one butterfly finishes the rows");
 };
 
 template <bool F16, int LPR>
@@ -104,77 +124,109 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a)
 {
     using S = ScoreShape<LPR>;
     constexpr int EPL = F16 ? 8 : 4;           // elements per 16-byte chunk
-    constexpr int RPL = S::RPL, T = S::T, RPW = S::RPW, R = S::R;
+    constexpr int L = S::L, C = S::C, RI = S::RI, V = S::V, R = S::R;
     constexpr int ROWB = LPR * 16;             // row bytes
     __shared__ uint64_t s_c[R];
+    __shared__ u32x4 s_new[LPR];               // the row pooled by workgroup 0
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int chunk = lane % LPR;
-    const int sub = lane / LPR;
+    const int col = lane % L;                  // lane within its row
+    const int sub = lane / L;                  // row within a wave-wide load
     const int tile = blockIdx.x == 0 ? (int)gridDim.x - 1 : (int)blockIdx.x - 1;
+    const int64_t base = (int64_t)tile * R + (int64_t)wave * S::RPW;
+
+    // q and w for the C chunks this lane reads of every row (a chunk lies
+    // inside one head: D is a multiple of 8), loaded ahead of the row stream
+    float4 qraw[C][EPL / 4];
+    float wraw[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int e0 = (col + L * c) * EPL;
+#pragma unroll
+        for (int k4 = 0; k4 < EPL / 4; ++k4)
+            qraw[c][k4] = ((const float4 *)(a.q + e0))[k4];
+        wraw[c] = a.w[e0 / a.D];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // load i: row group g = i / C, chunk col + L*(i % C) of row base + g*RI + sub
+    const char *rows = (const char *)a.summary;
+    u32x4 buf[S::LOADS];
+#pragma unroll
+    for (int i = 0; i < S::LOADS; ++i) {
+        const int64_t r = base + (int64_t)(i / C) * RI + sub;
+        const u32x4 *src = (const u32x4 *)(rows + (r < a.nb ? r : 0) * ROWB) + col + L * (i % C);
+        buf[i] = __builtin_nontemporal_load(src);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // Fused stage 1 (workgroup 0, whose tile holds the last row): append,
+    // pool the new block into LDS while the loads fly, and hand the pooled
+    // row to the lanes that loaded its stale chunks -- no reload, no fence.
     if (blockIdx.x == 0 && a.fuse) {
         if (a.upd.new_idx_row)
             append_rows(a.upd, threadIdx.x, 256);
         if (a.upd.nblk > 0)
-            pool_row<F16>(a.upd, a.upd.b0, threadIdx.x);
-        __threadfence();   // the pooled row is read back below by this workgroup
+            pool_row<F16>(a.upd, a.upd.b0, threadIdx.x, s_new);
         __syncthreads();
-    }
-    const int64_t base = ((int64_t)tile * 4 + wave) * RPW;
-
-    float qw[EPL];
+        if (a.upd.nblk > 0) {
 #pragma unroll
-    for (int k = 0; k < EPL; ++k) {
-        const int e = chunk * EPL + k;
-        qw[k] = a.q[e] * a.w[e / a.D];
-    }
-
-    const char *rows = (const char *)a.summary;
-    u32x4 buf[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const int64_t r = base + (int64_t)t * RPL + sub;
-        if (r < a.nb)
-            buf[t] = __builtin_nontemporal_load((const u32x4 *)(rows + r * ROWB) + chunk);
-        else
-            buf[t] = u32x4{0u, 0u, 0u, 0u};
-    }
-
-    float v[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        float acc = 0.0f;
-        if constexpr (F16) {
-            half8 h;
-            __builtin_memcpy(&h, &buf[t], 16);
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                acc = fmaf(qw[k], (float)h[k], acc);
-        } else {
-            const float f[4] = {__uint_as_float(buf[t][0]), __uint_as_float(buf[t][1]),
-                                __uint_as_float(buf[t][2]), __uint_as_float(buf[t][3])};
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                acc = fmaf(qw[k], f[k], acc);
+            for (int i = 0; i < S::LOADS; ++i) {
+                const int64_t r = base + (int64_t)(i / C) * RI + sub;
+                if (r == a.upd.b0)
+                    buf[i] = s_new[col + L * (i % C)];
+            }
         }
-        v[t] = acc;
+    }
+
+    float qw[C][EPL];
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int k4 = 0; k4 < EPL / 4; ++k4) {
+            qw[c][4 * k4] = qraw[c][k4].x * wraw[c];
+            qw[c][4 * k4 + 1] = qraw[c][k4].y * wraw[c];
+            qw[c][4 * k4 + 2] = qraw[c][k4].z * wraw[c];
+            qw[c][4 * k4 + 3] = qraw[c][k4].w * wraw[c];
+        }
+
+    float v[V];
+#pragma unroll
+    for (int g = 0; g < V; ++g) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const u32x4 &b = buf[g * C + c];
+            if constexpr (F16) {
+                half8 h;
+                __builtin_memcpy(&h, &b, 16);
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    acc = fmaf(qw[c][k], (float)h[k], acc);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    acc = fmaf(qw[c][k], __uint_as_float(b[k]), acc);
+            }
+        }
+        v[g] = acc;
     }
 
     int toff = 0;
-    Butterfly<LPR / 2, T>::run(v, lane, toff);
+    Butterfly<L / 2, V>::run(v, lane, toff);
 
-    constexpr int OWN = LPR / T;               // lanes sharing one final sum
-    const int local = wave * RPW + toff * RPL + sub;
-    const int64_t r = base + (int64_t)toff * RPL + sub;
-    if (lane % OWN == 0) {
+    constexpr int OWN = L / V;                 // lanes sharing one final sum
+    const int local = wave * S::RPW + toff * RI + sub;
+    const int64_t r = (int64_t)tile * R + local;
+    if (col % OWN == 0) {
         uint64_t c = 0;
         if (r < a.nb) {
-            const float s = v[0];
+            const float sc = v[0];
             if (a.scores)
-                a.scores[r] = s;
+                a.scores[r] = sc;
             if (a.keys) {
-                const uint32_t key = score_key(s);
+                const uint32_t key = score_key(sc);
                 a.keys[r] = key;
                 c = comp_key(key, (uint32_t)r);
             }
@@ -219,9 +271,8 @@ hipError_t go(const ScoreArgs &a, hipStream_t s)
 
 int score_tile_rows(bool f16, int row_bytes)
 {
-    (void)f16;
     switch (row_bytes / 16) {
-    case 8: return ScoreShape<8>::R;
+    case 8: return f16 ? ScoreShape<8>::R : 0;
     case 16: return ScoreShape<16>::R;
     case 32: return ScoreShape<32>::R;
     case 64: return ScoreShape<64>::R;

@@ -259,6 +259,8 @@ qsa_status qsa_index_score(const qsa_layer_desc *desc, const qsa_layer_cache *ca
         return fail(QSA_ERR_ARG, "n_blocks %d outside [0, %d]", n_blocks, cache->capacity / 4);
     if (!q_idx || !w || !scores)
         return fail(QSA_ERR_ARG, "q_idx / w / scores is NULL");
+    if (!aligned(q_idx, 16))
+        return fail(QSA_ERR_ARG, "q_idx must be 16-byte aligned");
     if (n_blocks == 0)
         return ok();
     ScoreArgs a{};
@@ -341,8 +343,9 @@ qsa_status qsa_decode_step(const qsa_layer_desc *desc, const qsa_layer_cache *ca
     if (!idx_k_row || !k_row || !v_row || !gamma || !q_idx || !w || !q || !out)
         return fail(QSA_ERR_ARG, "an input or output pointer is NULL");
     if (!aligned(idx_k_row, 4) || !aligned(k_row, 4) || !aligned(v_row, 4) ||
-        !aligned(q, 16))
-        return fail(QSA_ERR_ARG, "row pointers must be 4-byte aligned and q 16-byte aligned");
+        !aligned(q, 16) || !aligned(q_idx, 16))
+        return fail(QSA_ERR_ARG,
+                    "row pointers must be 4-byte aligned and q, q_idx 16-byte aligned");
     const int32_t pos = st->n_tokens;
     if (pos < 0 || pos >= cache->capacity)
         return fail(QSA_ERR_ARG, "position %d outside [0, %d)", pos, cache->capacity);

@@ -66,9 +66,10 @@ __device__ inline void append_rows(const UpdateArgs &a, int t, int nthreads)
 }
 
 // Pool summary row b with a 256-thread workgroup (thread t).  Every thread of
-// a wave must call it (wave reduction); waves h >= H do nothing.
+// a wave must call it (wave reduction); waves h >= H do nothing.  When
+// lds_row is given, the stored row is also written there (same bits).
 template <bool F16>
-__device__ inline void pool_row(const UpdateArgs &a, int64_t b, int t)
+__device__ inline void pool_row(const UpdateArgs &a, int64_t b, int t, void *lds_row = nullptr)
 {
     const int h = t >> 6;
     const int j = t & 63;
@@ -113,12 +114,21 @@ __device__ inline void pool_row(const UpdateArgs &a, int64_t b, int t)
     const size_t dst = (size_t)b * row;
     if constexpr (F16) {
         uint16_t *sm = (uint16_t *)a.summary;
-        sm[dst + e_lo] = f64_to_f16_rne(o_lo);
-        sm[dst + e_hi] = f64_to_f16_rne(o_hi);
+        const uint16_t v_lo = f64_to_f16_rne(o_lo), v_hi = f64_to_f16_rne(o_hi);
+        sm[dst + e_lo] = v_lo;
+        sm[dst + e_hi] = v_hi;
+        if (lds_row) {
+            ((uint16_t *)lds_row)[e_lo] = v_lo;
+            ((uint16_t *)lds_row)[e_hi] = v_hi;
+        }
     } else {
         float *sm = (float *)a.summary;
         sm[dst + e_lo] = (float)o_lo;
         sm[dst + e_hi] = (float)o_hi;
+        if (lds_row) {
+            ((float *)lds_row)[e_lo] = (float)o_lo;
+            ((float *)lds_row)[e_hi] = (float)o_hi;
+        }
     }
 }
 
