@@ -14,20 +14,23 @@
 // composites sorted descending, zero-filled (a tile = R = 8T consecutive
 // blocks).  Their union U has about N/8 entries.  1024 threads; thread t holds
 // the 16-byte chunks t + 1024q of U in registers (coalesced, 8 entries).
-// Fast path, 5 barriers, a few branch-free VALU operations per entry:
+// Fast path: a few branch-free VALU operations per entry, and the steps that
+// need only one wave's worth of work done by wave 0 while the others wait
+// (a barrier is cheaper than 16 copies of the same work):
 //   1. min / max of the listed keys (finite scores required);
 //   2. a 1024-bin histogram LINEAR in the score over [min, max] -- a monotone
-//      map of the composite, so whole bins are ordered; every wave then scans
-//      the histogram itself and finds the bin d holding the k-th largest
-//      (a handful of entries on scores spread like sums of products);
-//   3. the entries of bin d go to LDS; every wave ranks them by counting:
+//      map of the composite, so whole bins are ordered; wave 0 finds the bin
+//      d holding the k-th largest (a handful of entries on scores spread like
+//      sums of products; empty slots sit in bin 0, never resolved here);
+//   3. the entries of bin d go to LDS; wave 0 ranks them by counting:
 //      kappa = the k-th largest of U;
-//   4. exactness: a tile can hide a block >= kappa only if its list is full
+//   4. the winners (entries >= kappa) are marked in an LDS bitmap of the ids;
+//      exactness: a tile can hide a block >= kappa only if its list is full
 //      (last slot nonzero) and that last entry is >= kappa.  If none is, the
 //      entries >= kappa ARE the top k of all N blocks;
-//   5. they are marked in an LDS bitmap of the ids; word popcount prefix sums
-//      (DPP within a wave, wave offsets by lane permute) give each winner its
-//      output slot, handed to emit(slot, id).
+//   5. thread t owns 64 ids of the bitmap; a popcount prefix sum (DPP in the
+//      wave, wave totals in LDS) gives its first slot, and it hands its ids
+//      to emit(slot, id) in ascending order.
 // Anything the fast path cannot decide exactly -- fewer than k listed
 // entries, non-finite or all-equal scores, a crowded bin, a tile that may
 // hide winners, N > 65,536 -- takes the general path: radix refinement over
@@ -49,12 +52,13 @@ constexpr int kCap = 256;                      // entries of bin d ranked by cou
 constexpr size_t kMaxLds = 144 * 1024;         // of the 160 KB LDS of a gfx950 CU
 
 struct Smem {
-    uint32_t hist[kBins + kWave];              // + one dummy bin per lane
+    uint32_t hist[kBins];
     uint64_t cand[kCap];
     alignas(16) uint32_t rmin[kWaves];
     alignas(16) uint32_t rmax[kWaves];
     alignas(16) uint32_t wtot[kWaves];
-    uint32_t ncand;
+    uint64_t kappa;
+    uint32_t d, need, in_d, ncand, bad;
     // general path
     uint32_t wsum[kWaves], woff[kWaves];
     uint64_t wmin[kWaves], wmax[kWaves];
@@ -62,12 +66,12 @@ struct Smem {
     uint32_t gtot, bin, gabove;
 };
 
-// Dynamic LDS of run(): Smem, the id bitmap, the word prefix sums.
+// Dynamic LDS of run(): Smem and the id bitmap.
 inline size_t lds_bytes(int32_t nb)
 {
     const size_t nwords = (size_t)(nb + 31) / 32;
     const size_t bm = nwords > (size_t)kFastWords ? nwords : (size_t)kFastWords;
-    return (sizeof(Smem) + 15) / 16 * 16 + 4 * bm + 4 * (size_t)kFastWords;
+    return (sizeof(Smem) + 15) / 16 * 16 + 4 * bm;
 }
 
 // True when the fast path can hold the lists of N blocks in T-entry lists.
@@ -229,9 +233,8 @@ __device__ void refine_and_mark(Smem &sm, ForEach for_each, Mark mark, uint32_t 
 
 // Whole workgroup (kT threads) calls; `lds` holds lds_bytes(a.nb) bytes.
 // emit(slot, id) receives each of the k winners exactly once, slot = its rank
-// in ascending id order, from whichever thread found it.  Returns after the
-// last emit of the calling thread; callers synchronise before reading what
-// emit wrote.
+// in ascending id order.  Returns after the last emit of the calling thread;
+// callers synchronise before reading what emit wrote.
 template <class Emit>
 __device__ void run(const SelectArgs &a, char *lds, Emit emit)
 {
@@ -240,19 +243,18 @@ __device__ void run(const SelectArgs &a, char *lds, Emit emit)
     const uint32_t k = (uint32_t)a.k;
     const uint32_t nwords = (nb + 31) >> 5;
     uint32_t *bitmap = reinterpret_cast<uint32_t *>(lds + (sizeof(Smem) + 15) / 16 * 16);
-    uint32_t *wpre = bitmap + (nwords > (uint32_t)kFastWords ? nwords : (uint32_t)kFastWords);
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const uint32_t nchunks = (uint32_t)a.ntiles * (uint32_t)a.T / 2;
     bool general = nchunks > (uint32_t)(kT * kChunks);
 
-    // clear: histogram, bitmap words 2t and 2t+1, the candidate counter
+    // clear: histogram, bitmap words 2t and 2t+1, the counters
     sm.hist[t] = 0u;
-    if (t < kWave)
-        sm.hist[kBins + t] = 0u;
     uint2 *own = reinterpret_cast<uint2 *>(bitmap) + t;
     *own = make_uint2(0u, 0u);
-    if (t == 0)
+    if (t == 0) {
         sm.ncand = 0u;
+        sm.bad = 0u;
+    }
 
     // chunks t + 1024q of U (2 composites each), all loads in flight together
     uint64_t u[kEntries];
@@ -298,90 +300,87 @@ __device__ void run(const SelectArgs &a, char *lds, Emit emit)
               !(range > 0.0f) || !(range < __builtin_inff()) || !(scale < __builtin_inff());
 
     if (!general) {
-        // 2. linear histogram (all keys finite here: key != 0 <=> listed)
+        // 2. linear histogram; an empty slot (NaN score) lands in bin 0, which
+        //    the fast path never resolves (it falls back below)
         uint32_t bins[kEntries];
 #pragma unroll
         for (int e = 0; e < kEntries; ++e) {
-            const uint32_t key = (uint32_t)(u[e] >> 32);
-            const float s = key != 0u ? key_score(key) : mn;       // in [mn, mx]
-            const uint32_t b = (uint32_t)((s - mn) * scale);       // in [0, 1024]
+            const float s = fmaxf(key_score((uint32_t)(u[e] >> 32)), mn);   // in [mn, mx]
+            const uint32_t b = (uint32_t)((s - mn) * scale);                // in [0, 1024]
             bins[e] = b < (uint32_t)kBins - 1 ? b : (uint32_t)kBins - 1;
-            atomicAdd(&sm.hist[key != 0u ? bins[e] : (uint32_t)(kBins + lane)], 1u);
+            atomicAdd(&sm.hist[bins[e]], 1u);
         }
         __syncthreads();                                                // barrier 2
-        // every wave: lane l scans bins [16l, 16l + 16); the lane whose range
-        // holds the k-th largest finds its bin d
-        uint32_t hb[16];
+        if (wv == 0) {
+            // wave 0: lane l scans bins [16l, 16l + 16); the lane whose range
+            // holds the k-th largest finds its bin d
+            uint32_t hb[16];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint4 h4 = reinterpret_cast<const uint4 *>(sm.hist + 16 * lane)[i];
-            hb[4 * i] = h4.x;
-            hb[4 * i + 1] = h4.y;
-            hb[4 * i + 2] = h4.z;
-            hb[4 * i + 3] = h4.w;
-        }
-        uint32_t hs = 0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            hs += hb[i];
-        const uint32_t incl = wave::incl_scan_add(hs);
-        const uint32_t total = wave::readlane(incl, 63);
-        uint32_t acc = total - incl;                        // entries in higher lanes' bins
-        uint32_t d_l = 0, above_l = 0, in_l = 0;
-        const bool finder = acc < k && acc + hs >= k;
-#pragma unroll
-        for (int b = 15; b >= 0; --b) {
-            if (acc < k && acc + hb[b] >= k) {
-                d_l = 16u * lane + b;
-                above_l = acc;
-                in_l = hb[b];
+            for (int i = 0; i < 4; ++i) {
+                const uint4 h4 = reinterpret_cast<const uint4 *>(sm.hist + 16 * lane)[i];
+                hb[4 * i] = h4.x;
+                hb[4 * i + 1] = h4.y;
+                hb[4 * i + 2] = h4.z;
+                hb[4 * i + 3] = h4.w;
             }
-            acc += hb[b];
+            uint32_t hs = 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                hs += hb[i];
+            const uint32_t incl = wave::incl_scan_add(hs);
+            uint32_t acc = wave::readlane(incl, 63) - incl;   // entries in higher lanes' bins
+            if (acc < k && acc + hs >= k) {
+#pragma unroll
+                for (int b = 15; b >= 0; --b) {
+                    if (acc < k && acc + hb[b] >= k) {
+                        sm.d = 16u * lane + b;
+                        sm.need = k - acc;
+                        sm.in_d = hb[b];
+                    }
+                    acc += hb[b];
+                }
+            }
+            if (lane == 0 && wave::readlane(incl, 63) < k)
+                sm.d = 0u;                                    // not found: general path
         }
-        const uint64_t fb = __ballot(finder);
-        general = total < k || fb == 0ull;
-        const int src = general ? 0 : __ffsll((long long)fb) - 1;
-        const uint32_t d = wave::readlane(d_l, src);
-        const uint32_t need = k - wave::readlane(above_l, src);
-        const uint32_t m = wave::readlane(in_l, src);
-        general = general || m > (uint32_t)kCap;
+        __syncthreads();                                                // barrier 3
+        const uint32_t d = sm.d, m = sm.in_d;
+        general = d == 0u || m > (uint32_t)kCap;
 
         if (!general) {
-            // 3. the entries of bin d to LDS; every wave ranks them by counting
-            bool hit[kEntries];
+            // 3. the entries of bin d to LDS (empty slots sit in bin 0)
             uint32_t nd = 0;
 #pragma unroll
-            for (int e = 0; e < kEntries; ++e) {
-                hit[e] = u[e] != 0ull && bins[e] == d;
-                nd += hit[e] ? 1u : 0u;
-            }
+            for (int e = 0; e < kEntries; ++e)
+                nd += bins[e] == d ? 1u : 0u;
             if (nd) {
                 uint32_t o = atomicAdd(&sm.ncand, nd);
 #pragma unroll
                 for (int e = 0; e < kEntries; ++e)
-                    if (hit[e])
+                    if (bins[e] == d)
                         sm.cand[o++] = u[e];
             }
-            __syncthreads();                                            // barrier 3
-            uint64_t kap_l = 0ull;
-            bool found = false;
-            for (uint32_t j = lane; j < m; j += kWave) {
-                const uint64_t c = sm.cand[j];
-                uint32_t r = 0;
+            __syncthreads();                                            // barrier 4
+            if (wv == 0) {
+                // wave 0 ranks them by counting: kappa = the need-th largest
+                const uint32_t need = sm.need;
+                for (uint32_t j = lane; j < m; j += kWave) {
+                    const uint64_t c = sm.cand[j];
+                    uint32_t r = 0;
 #pragma unroll 4
-                for (uint32_t i = 0; i < m; ++i)
-                    r += sm.cand[i] > c ? 1u : 0u;
-                if (r == need - 1) {
-                    kap_l = c;
-                    found = true;
+                    for (uint32_t i = 0; i < m; ++i)
+                        r += sm.cand[i] > c ? 1u : 0u;
+                    if (r == need - 1)
+                        sm.kappa = c;
                 }
             }
-            const int ks = __ffsll((long long)__ballot(found)) - 1;   // exactly one
-            const uint64_t kappa = wave::readlane64(kap_l, ks);
+            __syncthreads();                                            // barrier 5
+            const uint64_t kappa = sm.kappa;
 
-            // 4. winners into the bitmap; exactness check.  The last slot of
-            //    a list is the odd entry of chunks c with (c+1) % (T/2) == 0,
-            //    i.e. of every chunk of threads with (t+1) % (T/2) == 0.
+            // 4. winners into the bitmap (straight from registers, no return
+            //    values awaited); exactness check.  The last slot of a list is
+            //    the odd entry of chunks c with (c+1) % (T/2) == 0, i.e. of
+            //    every chunk of threads with (t+1) % (T/2) == 0.
             bool win[kEntries];
 #pragma unroll
             for (int e = 0; e < kEntries; ++e)
@@ -397,31 +396,30 @@ __device__ void run(const SelectArgs &a, char *lds, Emit emit)
                     const uint32_t id = ~(uint32_t)u[e];
                     atomicOr(&bitmap[id >> 5], 1u << (id & 31));
                 }
-            general = __syncthreads_or(bad ? 1 : 0) != 0;              // barrier 4
+            if (bad)
+                sm.bad = 1u;
+            __syncthreads();                                            // barrier 6
+            general = sm.bad != 0u;
             if (!general) {
-                // 5. word prefix sums: thread t owns words 2t, 2t+1; within the
-                //    wave by DPP scan (to LDS), across waves by the wave totals
+                // 5. thread t owns bitmap words 2t, 2t+1 (ids 64t .. 64t+63):
+                //    its first slot = winners in lower words, by a DPP scan in
+                //    the wave plus the totals of the lower waves
                 const uint2 wd = *own;
-                const uint32_t p0 = (uint32_t)__popc(wd.x), p1 = (uint32_t)__popc(wd.y);
-                const uint32_t wincl = wave::incl_scan_add(p0 + p1);
-                const uint32_t wexcl = wincl - p0 - p1;
-                reinterpret_cast<uint2 *>(wpre)[t] = make_uint2(wexcl, wexcl + p0);
+                const uint32_t pc = (uint32_t)(__popc(wd.x) + __popc(wd.y));
+                const uint32_t wincl = wave::incl_scan_add(pc);
                 if (lane == 63)
                     sm.wtot[wv] = wincl;
-                __syncthreads();                                        // barrier 5
-                // lane i < 16 of every wave: words owned by waves below i
+                __syncthreads();                                        // barrier 7
                 const uint32_t wt = lane < kWaves ? sm.wtot[lane] : 0u;
-                const uint32_t woff = wave::incl_scan_add(wt) - wt;
-#pragma unroll
-                for (int e = 0; e < kEntries; ++e) {
-                    const uint32_t id = ~(uint32_t)u[e];
-                    const uint32_t w = win[e] ? id >> 5 : 0u;
-                    const uint32_t off = (uint32_t)__builtin_amdgcn_ds_bpermute(
-                        (int)((w >> 7) << 2), (int)woff);           // owner wave = w / 128
-                    const uint32_t slot =
-                        off + wpre[w] + (uint32_t)__popc(bitmap[w] & ((1u << (id & 31)) - 1u));
-                    if (win[e] && slot < k)
-                        emit(slot, id);
+                const uint32_t wexcl_all = wave::incl_scan_add(wt) - wt;
+                uint32_t slot = wave::readlane(wexcl_all, wv) + wincl - pc;
+                uint64_t bits = ((uint64_t)wd.y << 32) | wd.x;
+                while (bits) {
+                    const int b = __ffsll((long long)bits) - 1;
+                    bits &= bits - 1;
+                    if (slot < k)
+                        emit(slot, 64u * (uint32_t)t + (uint32_t)b);
+                    ++slot;
                 }
                 return;
             }
