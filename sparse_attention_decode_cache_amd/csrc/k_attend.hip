@@ -240,8 +240,11 @@ __global__ __launch_bounds__(kAT) void k_select_attend(FusedArgs f)
 // Workgroup (h, 64-dim slice), 16 waves, one global latency round: thread s
 // loads m_s while wave w loads (l_s, acc_s[d]) of splits w, w+16, ...; M by
 // a block max; thread s turns m_s into the weight e^(m_s - M) in LDS; each
-// wave sums its splits, and wave 0 sums the 16 wave results in order:
-// a fixed order, bitwise repeatable.
+// wave sums its splits, and wave 0 sums the 16 wave results in order and
+// adds the tail: a fixed order, bitwise repeatable.  The tail (cells
+// 4*nb + j, j < n_tail, when the splits hold only the chosen blocks) is one
+// more partial that wave 0 computes itself: <= 3 logits, its K/V rows
+// loaded with the first round.
 constexpr int kMT = 1024;
 constexpr int kMW = kMT / kWave;
 constexpr int kMRound = 8;                  // splits per wave per load round
@@ -253,6 +256,7 @@ __global__ __launch_bounds__(kMT) void k_merge(AttendArgs a)
     __shared__ float s_w[kMaxSplits];
     __shared__ float s_red[kMW];
     __shared__ float s_l[kMW], s_acc[kMW][kWave];
+    constexpr int QD = DH / kWave;              // dims per lane of a tail logit
     const int h = blockIdx.x;
     const int g = h / G, hh = h % G;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -270,8 +274,51 @@ __global__ __launch_bounds__(kMT) void k_merge(AttendArgs a)
         l[i] = p[G + hh];
         x[i] = p[2 * G + hh * DH + d];
     }
+    // the tail's K and V rows (wave 0): every load issued at once, rows past
+    // the tail clamped to row 0 and masked below
+    const int nt = wave == 0 ? a.n_tail : 0;
+    float kq[3][QD], vt[3], qv[QD];
+    if (nt) {
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const size_t cell = j < nt ? 4 * (size_t)a.nb + j : 0;   // row 0: always there
+            const _Float16 *kr = (const _Float16 *)a.k + (cell * a.kv_heads + g) * DH;
+            const _Float16 *vr = (const _Float16 *)a.v + (cell * a.kv_heads + g) * DH;
+#pragma unroll
+            for (int i = 0; i < QD; ++i)
+                kq[j][i] = (float)kr[lane + kWave * i];
+            vt[j] = (float)vr[d];
+        }
+#pragma unroll
+        for (int i = 0; i < QD; ++i)
+            qv[i] = a.q[(size_t)h * DH + lane + kWave * i];
+    }
+
     const float ms = t < ns ? base[(size_t)t * ps + hh] : -INFINITY;
-    const float wm = wave::reduce_max_f(ms);
+    float wm = wave::reduce_max_f(ms);
+    float mt = -INFINITY, lt = 0.0f, at = 0.0f;
+    if (nt) {
+        // wave-uniform: the tail's logits, max, sum and this lane's dim
+        float xl[3];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            float dp = 0.0f;
+#pragma unroll
+            for (int i = 0; i < QD; ++i)
+                dp = fmaf(qv[i], kq[j][i], dp);
+            xl[j] = a.scale * wave::reduce_add_f(dp);
+            if (j < nt)
+                mt = fmaxf(mt, xl[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            if (j < nt) {
+                const float pj = expf(xl[j] - mt);
+                lt += pj;
+                at = fmaf(pj, vt[j], at);
+            }
+        wm = fmaxf(wm, mt);
+    }
     if (lane == 0)
         s_red[wave] = wm;
     __syncthreads();
@@ -319,6 +366,11 @@ __global__ __launch_bounds__(kMT) void k_merge(AttendArgs a)
         for (int w = 1; w < kMW; ++w) {
             A += s_acc[w][lane];
             L += s_l[w];
+        }
+        if (nt) {
+            const float wt = expf(mt - M);
+            A = fmaf(wt, at, A);
+            L = fmaf(wt, lt, L);
         }
         a.out[(size_t)h * DH + d] = A / L;
     }

@@ -421,7 +421,11 @@ qsa_status qsa_decode_step(const qsa_layer_desc *desc, const qsa_layer_cache *ca
     if (need_select) {
         const int tile_rows = score_tile_rows(desc->idx_dtype == QSA_F16, rowb);
         SelectArgs sa = select_args(wsp, L, nb, K, tile_rows, sel_out);
-        const AttendArgs aa = attend_args(desc, cache, n, nullptr, K, q, out, part);
+        // fused: the splits hold the 4K chosen cells, the merge adds the tail
+        AttendArgs aa = attend_args(desc, cache, n, nullptr, K, q, out, part);
+        aa.n_cells = 4 * K;
+        aa.n_tail = n % 4;
+        aa.n_split = (int32_t)n_splits(aa.n_cells);
         if (sel::fits_fast(sa.ntiles, sa.T) &&
             (int64_t)aa.n_split * aa.kv_heads <= device_cus()) {
             e = launch_select_attend(aa, sa, desc->head_dim, G, stream);

@@ -119,7 +119,8 @@ struct AttendArgs {
     float *out;
     int32_t n_sel_blocks;
     int32_t nb;                 // floor(n_tokens / 4)
-    int32_t n_cells;
+    int32_t n_cells;            // cells of the attention splits
+    int32_t n_tail;             // cells 4*nb + j, j < n_tail, folded in by the merge
     int32_t n_split;
     int32_t kv_heads;
     float scale;
