@@ -105,6 +105,89 @@ def cpu_baseline(w, n_steps):
                       f"{1e3 * statistics.median(steps):.1f} ms"}
 
 
+TRAFFIC_COPY_MB = 256
+
+
+def traffic_run(args):
+    """Short program for the rocprofv3 counter passes: `kernel_reps` score
+    launches at the bench workload (layer 0, same kernel and grid as the
+    roofline timing), then as many plain copies of TRAFFIC_COPY_MB MiB (the
+    reference of known size that scales the counters)."""
+    import torch
+    import sparse_attention_decode_cache_amd as qsa
+    from qsagen import workloads as W
+    w = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    desc = qsa.make_desc(w.idx_heads, w.idx_dim, qsa.QSA_F16 if w.idx_f16 else qsa.QSA_F32,
+                         w.q_heads, w.kv_heads, w.head_dim, w.top_k_tokens, w.rms_eps, w.rope_theta)
+    buf = qsa.LayerBuffers(desc, w.capacity())
+    W.dev_fill_layer_(w, buf, 0, w.n0)
+    qsa.qsa_cache_update(desc, buf.cache, W.dev_gamma(w, 0), 0, w.n0 // 4)
+    inp = W.dev_step_inputs(w, 0, 0, 1)
+    nb = w.n0 // 4
+    scores = torch.empty(nb, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    src = torch.empty(TRAFFIC_COPY_MB << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(args.kernel_reps):
+        qsa.qsa_index_score(desc, buf.cache, nb, inp.q_idx[0], inp.w[0], scores, stream)
+    for _ in range(args.kernel_reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"traffic run: {args.kernel_reps} score launches ({nb} blocks), "
+        f"{args.kernel_reps} copies of {TRAFFIC_COPY_MB} MiB")
+
+
+def traffic_summarize(args):
+    """Turn the two counter passes (FETCH_SIZE, WRITE_SIZE; KiB per dispatch)
+    into bytes per score launch, each scaled by what the same counter reads
+    for the plain copy (TRAFFIC_COPY_MB MiB read and written)."""
+    import csv
+    from qsagen import workloads as W
+    w = W.WORKLOADS[args.workload]
+    fetch_dir, write_dir = args.traffic_summarize
+
+    def per_dispatch(d, counter):
+        vals = {"score": [], "copy": []}
+        for root, _, files in os.walk(d):
+            for f in files:
+                if not f.endswith("counter_collection.csv"):
+                    continue
+                for r in csv.DictReader(open(os.path.join(root, f))):
+                    if r.get("Counter_Name") != counter:
+                        continue
+                    name = r.get("Kernel_Name", "")
+                    key = "score" if "k_score" in name else ("copy" if "copy" in name.lower() else None)
+                    if key:
+                        vals[key].append(float(r["Counter_Value"]))
+        return {k: statistics.mean(v) if v else None for k, v in vals.items()}
+
+    fetch = per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = per_dispatch(write_dir, "WRITE_SIZE")
+    copy_bytes = float(TRAFFIC_COPY_MB << 20)
+    f_scale = copy_bytes / (fetch["copy"] * 1024.0)
+    w_scale = copy_bytes / (write["copy"] * 1024.0)
+    f_bytes = fetch["score"] * 1024.0 * f_scale
+    w_bytes = write["score"] * 1024.0 * w_scale
+    nb = w.n0 // 4
+    src = os.path.join(ROOT, "sparse_attention_decode_cache_amd", "csrc", "k_score.hip")
+    rec = {"workload": w.name, "k_score_sha256_16": source_hash(src), "n_blocks": nb,
+           "algorithmic_bytes": score_kernel_bytes(w, nb),
+           "fetch_kib_per_dispatch": round(fetch["score"], 1),
+           "write_kib_per_dispatch": round(write["score"], 1),
+           "copy_fetch_kib": round(fetch["copy"], 1), "copy_write_kib": round(write["copy"], 1),
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "bytes_per_launch": round(f_bytes + w_bytes)}
+    out = os.path.join(ROOT, "profiles", "score_kernel_traffic.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,7 +197,17 @@ def main():
     ap.add_argument("--cpu-steps", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=8, help="score-kernel timing passes")
+    ap.add_argument("--traffic-run", action="store_true",
+                    help="only launch the score kernel and a plain copy (for rocprofv3 --pmc)")
+    ap.add_argument("--traffic-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/score_kernel_traffic.json from two counter passes")
     args = ap.parse_args()
+    if args.traffic_summarize:
+        traffic_summarize(args)
+        return
+    if args.traffic_run:
+        traffic_run(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus must be 1).", file=sys.stderr)
