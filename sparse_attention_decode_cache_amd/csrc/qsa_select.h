@@ -284,7 +284,7 @@ __device__ void run(const SelectArgs &a, char *lds, Emit emit)
         sm.rmin[wv] = kmin1;
         sm.rmax[wv] = kmax;
     }
-    __syncthreads();                                                    // barrier 1
+    __syncthreads();                                                    // barrier
 #pragma unroll
     for (int i = 0; i < kWaves; i += 4) {
         const uint4 a4 = reinterpret_cast<const uint4 *>(sm.rmin)[i / 4];
@@ -298,52 +298,58 @@ __device__ void run(const SelectArgs &a, char *lds, Emit emit)
     const float scale = (float)kBins / range;
     general = general || kmin1 == 0xFFFFFFFFu || kmin < kKeyFiniteLo || kmax > kKeyFiniteHi ||
               !(range > 0.0f) || !(range < __builtin_inff()) || !(scale < __builtin_inff());
+    // All listed scores >= 0 (the usual case for the tiles' top entries): bins
+    // linear in the key itself, which is linear in the score inside a binade;
+    // otherwise linear in the score (the key space has a wide gap around 0).
+    const bool by_key = kmin >= 0x80000000u;
+    const int kshift = 32 - __clz((int)(kmax - kmin)) - 10;
+    const uint32_t ksh = kshift > 0 ? (uint32_t)kshift : 0u;     // (kmax - kmin) >> ksh < 1024
 
     if (!general) {
-        // 2. linear histogram; an empty slot (NaN score) lands in bin 0, which
-        //    the fast path never resolves (it falls back below)
+        // 2. linear histogram; an empty slot (key 0) lands in bin 0, which the
+        //    fast path never resolves (it falls back below)
         uint32_t bins[kEntries];
 #pragma unroll
         for (int e = 0; e < kEntries; ++e) {
-            const float s = fmaxf(key_score((uint32_t)(u[e] >> 32)), mn);   // in [mn, mx]
-            const uint32_t b = (uint32_t)((s - mn) * scale);                // in [0, 1024]
-            bins[e] = b < (uint32_t)kBins - 1 ? b : (uint32_t)kBins - 1;
-            atomicAdd(&sm.hist[bins[e]], 1u);
+            const uint32_t key = (uint32_t)(u[e] >> 32);
+            uint32_t b;
+            if (by_key) {
+                b = (key > kmin ? key - kmin : 0u) >> ksh;
+            } else {
+                const float s = fmaxf(key_score(key), mn);             // in [mn, mx]
+                b = (uint32_t)((s - mn) * scale);                      // in [0, 1024]
+                b = b < (uint32_t)kBins - 1 ? b : (uint32_t)kBins - 1;
+            }
+            bins[e] = b;
+            atomicAdd(&sm.hist[b], 1u);
         }
-        __syncthreads();                                                // barrier 2
-        if (wv == 0) {
-            // wave 0: lane l scans bins [16l, 16l + 16); the lane whose range
-            // holds the k-th largest finds its bin d
-            uint32_t hb[16];
+        __syncthreads();                                                // barrier
+        // the bin d holding the k-th largest: thread t takes bin 1023 - t, so a
+        // prefix sum over threads is the count of entries in higher bins
+        {
+            const uint32_t h = sm.hist[kBins - 1 - t];
+            const uint32_t incl = wave::incl_scan_add(h);
+            if (lane == 63)
+                sm.wtot[wv] = incl;
+            __syncthreads();                                            // barrier
+            uint32_t off = 0, tot = 0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint4 h4 = reinterpret_cast<const uint4 *>(sm.hist + 16 * lane)[i];
-                hb[4 * i] = h4.x;
-                hb[4 * i + 1] = h4.y;
-                hb[4 * i + 2] = h4.z;
-                hb[4 * i + 3] = h4.w;
+            for (int i = 0; i < kWaves; i += 4) {
+                const uint4 w4 = reinterpret_cast<const uint4 *>(sm.wtot)[i / 4];
+                tot += w4.x + w4.y + w4.z + w4.w;
+                off += (i < wv ? w4.x : 0u) + (i + 1 < wv ? w4.y : 0u) +
+                       (i + 2 < wv ? w4.z : 0u) + (i + 3 < wv ? w4.w : 0u);
             }
-            uint32_t hs = 0;
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                hs += hb[i];
-            const uint32_t incl = wave::incl_scan_add(hs);
-            uint32_t acc = wave::readlane(incl, 63) - incl;   // entries in higher lanes' bins
-            if (acc < k && acc + hs >= k) {
-#pragma unroll
-                for (int b = 15; b >= 0; --b) {
-                    if (acc < k && acc + hb[b] >= k) {
-                        sm.d = 16u * lane + b;
-                        sm.need = k - acc;
-                        sm.in_d = hb[b];
-                    }
-                    acc += hb[b];
-                }
+            const uint32_t above = off + incl - h;
+            if (above < k && above + h >= k) {
+                sm.d = (uint32_t)(kBins - 1 - t);
+                sm.need = k - above;
+                sm.in_d = h;
             }
-            if (lane == 0 && wave::readlane(incl, 63) < k)
+            if (t == 0 && tot < k)
                 sm.d = 0u;                                    // not found: general path
         }
-        __syncthreads();                                                // barrier 3
+        __syncthreads();                                                // barrier
         const uint32_t d = sm.d, m = sm.in_d;
         general = d == 0u || m > (uint32_t)kCap;
 
@@ -360,7 +366,7 @@ __device__ void run(const SelectArgs &a, char *lds, Emit emit)
                     if (bins[e] == d)
                         sm.cand[o++] = u[e];
             }
-            __syncthreads();                                            // barrier 4
+            __syncthreads();                                            // barrier
             if (wv == 0) {
                 // wave 0 ranks them by counting: kappa = the need-th largest
                 const uint32_t need = sm.need;
@@ -374,7 +380,7 @@ __device__ void run(const SelectArgs &a, char *lds, Emit emit)
                         sm.kappa = c;
                 }
             }
-            __syncthreads();                                            // barrier 5
+            __syncthreads();                                            // barrier
             const uint64_t kappa = sm.kappa;
 
             // 4. winners into the bitmap (straight from registers, no return
@@ -398,7 +404,7 @@ __device__ void run(const SelectArgs &a, char *lds, Emit emit)
                 }
             if (bad)
                 sm.bad = 1u;
-            __syncthreads();                                            // barrier 6
+            __syncthreads();                                            // barrier
             general = sm.bad != 0u;
             if (!general) {
                 // 5. thread t owns bitmap words 2t, 2t+1 (ids 64t .. 64t+63):
@@ -409,7 +415,7 @@ __device__ void run(const SelectArgs &a, char *lds, Emit emit)
                 const uint32_t wincl = wave::incl_scan_add(pc);
                 if (lane == 63)
                     sm.wtot[wv] = wincl;
-                __syncthreads();                                        // barrier 7
+                __syncthreads();                                        // barrier
                 const uint32_t wt = lane < kWaves ? sm.wtot[lane] : 0u;
                 const uint32_t wexcl_all = wave::incl_scan_add(wt) - wt;
                 uint32_t slot = wave::readlane(wexcl_all, wv) + wincl - pc;
