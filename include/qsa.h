@@ -182,6 +182,46 @@ qsa_status qsa_decode_step(const qsa_layer_desc *desc, const qsa_layer_cache *ca
                            const float *w, const float *q, float *out, int32_t *sel_out,
                            float *scores_out, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------- batches
+ * Batched variable-length decode: one decode step (as qsa_decode_step) for
+ * each of n_seq independent sequences of the same layer shapes, in one call:
+ * one launch per stage for the whole batch, so short contexts share the GPU
+ * instead of each filling it alone [post 10, "QSA indexer", "selected QSA K/V
+ * gather（COMMON-005）": the same per-sequence step; batching is this
+ * library's].  Sequence s has its own cache caches[s], state states[s] and
+ * I/O io[s]; gamma is the layer's, shared.  Results are those of n_seq
+ * qsa_decode_step calls. */
+#define QSA_MAX_BATCH 8
+
+typedef struct qsa_seq_io {
+    const void *idx_k_row;      /* DEVICE [H_i][D_i] idx_dtype: the appended token's raw key */
+    const uint16_t *k_row;      /* DEVICE [Hkv][Dh] binary16 */
+    const uint16_t *v_row;      /* DEVICE [Hkv][Dh] binary16 */
+    const float *q_idx;         /* DEVICE fp32 [H_i][D_i], 16-byte aligned */
+    const float *w;             /* DEVICE fp32 [H_i] */
+    const float *q;             /* DEVICE fp32 [Hq][Dh], 16-byte aligned */
+    float *out;                 /* DEVICE fp32 [Hq][Dh] */
+    int32_t *sel_out;           /* optional DEVICE int32 [min(K, n/4)] (NULL to skip) */
+} qsa_seq_io;
+
+/* Workspace bytes for qsa_decode_step_batch over sequences of the given
+ * capacities (tokens each); 0 if the desc, n_seq (1..QSA_MAX_BATCH) or a
+ * capacity is invalid. */
+size_t qsa_batch_workspace_bytes(const qsa_layer_desc *desc, int32_t n_seq,
+                                 const int32_t *capacities);
+
+/* One decode step of each of n_seq sequences (HOST arrays of n_seq entries:
+ * caches, states, io).  Each sequence follows qsa_decode_step: it appends at
+ * pos = states[s].n_tokens and on success states[s] becomes {n, n/4}; on any
+ * error no state changes.
+ * Errors: ARG if n_seq is outside [1, QSA_MAX_BATCH], an array or pointer is
+ * null, a position is outside its cache or a pointer is misaligned;
+ * UNSUPPORTED / WORKSPACE as in qsa_decode_step. */
+qsa_status qsa_decode_step_batch(const qsa_layer_desc *desc, int32_t n_seq,
+                                 const qsa_layer_cache *caches, qsa_seq_state *states,
+                                 const qsa_seq_io *io, const float *gamma, void *ws,
+                                 size_t ws_bytes, hipStream_t stream);
+
 /* Static text for a status code. */
 const char *qsa_status_string(qsa_status s);
 

@@ -119,21 +119,28 @@ struct ScoreShape {
     static_assert(V >= 1 && V <= L, "one butterfly finishes the rows");
 };
 
+template <int LPR>
+struct ScoreLds {
+    uint64_t c[ScoreShape<LPR>::R];            // the tile's composites
+    u32x4 fresh[LPR];                          // the row pooled by the fused prologue
+};
+
+// Score tile `tile` of one sequence (256 threads).  `pool_here`: this
+// workgroup runs the fused append + pool (it must hold the last tile).
 template <bool F16, int LPR>
-__global__ __launch_bounds__(256) void k_score(ScoreArgs a)
+__device__ inline void score_tile(const ScoreArgs &a, ScoreLds<LPR> &sl, int tile, bool pool_here)
 {
     using S = ScoreShape<LPR>;
     constexpr int EPL = F16 ? 8 : 4;           // elements per 16-byte chunk
     constexpr int L = S::L, C = S::C, RI = S::RI, V = S::V, R = S::R;
     constexpr int ROWB = LPR * 16;             // row bytes
-    __shared__ uint64_t s_c[R];
-    __shared__ u32x4 s_new[LPR];               // the row pooled by workgroup 0
+    uint64_t *s_c = sl.c;
+    u32x4 *s_new = sl.fresh;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int col = lane % L;                  // lane within its row
     const int sub = lane / L;                  // row within a wave-wide load
-    const int tile = blockIdx.x == 0 ? (int)gridDim.x - 1 : (int)blockIdx.x - 1;
     const int64_t base = (int64_t)tile * R + (int64_t)wave * S::RPW;
 
     // q and w for the C chunks this lane reads of every row (a chunk lies
@@ -164,7 +171,7 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a)
     // Fused stage 1 (workgroup 0, whose tile holds the last row): append,
     // pool the new block into LDS while the loads fly, and hand the pooled
     // row to the lanes that loaded its stale chunks -- no reload, no fence.
-    if (blockIdx.x == 0 && a.fuse) {
+    if (pool_here) {
         if (a.upd.new_idx_row)
             append_rows(a.upd, threadIdx.x, 256);
         if (a.upd.nblk > 0)
@@ -240,6 +247,30 @@ __global__ __launch_bounds__(256) void k_score(ScoreArgs a)
     }
 }
 
+template <bool F16, int LPR>
+__global__ __launch_bounds__(256) void k_score(ScoreArgs a)
+{
+    __shared__ ScoreLds<LPR> sl;
+    // workgroup 0 (dispatched first) takes the last tile: the one holding the new row
+    const int tile = blockIdx.x == 0 ? (int)gridDim.x - 1 : (int)blockIdx.x - 1;
+    score_tile<F16, LPR>(a, sl, tile, blockIdx.x == 0 && a.fuse);
+}
+
+// A batch of sequences in one launch: workgroups [tile0[s], tile0[s+1]) score
+// sequence s, the first of them its last tile (with the fused prologue).
+template <bool F16, int LPR>
+__global__ __launch_bounds__(256) void k_score_batch(ScoreBatchArgs b)
+{
+    __shared__ ScoreLds<LPR> sl;
+    int s = 0;
+    while (s + 1 < b.n && (int)blockIdx.x >= b.tile0[s + 1])
+        ++s;
+    const int local = (int)blockIdx.x - b.tile0[s];
+    const int ntiles = b.tile0[s + 1] - b.tile0[s];
+    const int tile = local == 0 ? ntiles - 1 : local - 1;
+    score_tile<F16, LPR>(b.seq[s], sl, tile, local == 0 && b.seq[s].fuse);
+}
+
 // Keys and tile lists from given fp32 scores (stand-alone top-k), R = 256.
 __global__ __launch_bounds__(kKeysTile) void k_keys(const float *scores, int32_t nb, uint32_t *keys,
                                                     uint64_t *lists)
@@ -300,6 +331,37 @@ hipError_t launch_score(const ScoreArgs &a, bool f16, int row_bytes, hipStream_t
         }
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_score_batch(ScoreBatchArgs &b, bool f16, int row_bytes, hipStream_t s)
+{
+    const int R = score_tile_rows(f16, row_bytes);
+    if (R == 0 || b.n < 1 || b.n > kMaxBatch)
+        return hipErrorInvalidValue;
+    b.tile0[0] = 0;
+    for (int i = 0; i < b.n; ++i) {
+        const int nt = (int)((b.seq[i].nb + R - 1) / R);
+        b.tile0[i + 1] = b.tile0[i] + (nt > 0 ? nt : 1);   // at least one: the fused prologue
+    }
+    const int grid = b.tile0[b.n];
+    const int lpr = row_bytes / 16;
+    if (f16) {
+        switch (lpr) {
+        case 8: hipLaunchKernelGGL((k_score_batch<true, 8>), dim3(grid), dim3(256), 0, s, b); break;
+        case 16: hipLaunchKernelGGL((k_score_batch<true, 16>), dim3(grid), dim3(256), 0, s, b); break;
+        case 32: hipLaunchKernelGGL((k_score_batch<true, 32>), dim3(grid), dim3(256), 0, s, b); break;
+        case 64: hipLaunchKernelGGL((k_score_batch<true, 64>), dim3(grid), dim3(256), 0, s, b); break;
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (lpr) {
+        case 16: hipLaunchKernelGGL((k_score_batch<false, 16>), dim3(grid), dim3(256), 0, s, b); break;
+        case 32: hipLaunchKernelGGL((k_score_batch<false, 32>), dim3(grid), dim3(256), 0, s, b); break;
+        case 64: hipLaunchKernelGGL((k_score_batch<false, 64>), dim3(grid), dim3(256), 0, s, b); break;
+        default: return hipErrorInvalidValue;
+        }
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_keys(const float *scores, int32_t nb, uint32_t *keys, uint64_t *lists,

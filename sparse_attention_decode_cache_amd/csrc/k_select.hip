@@ -14,7 +14,49 @@ __global__ __launch_bounds__(sel::kT) void k_select(SelectArgs a)
     });
 }
 
+// One workgroup per sequence of a batch; a sequence with nb <= k keeps every
+// block (its ids, if asked for, are 0..nb-1).
+__global__ __launch_bounds__(sel::kT) void k_select_batch(SelectBatchArgs b)
+{
+    extern __shared__ uint4 sel_lds[];
+    const SelectArgs &a = b.seq[blockIdx.x];
+    int32_t *out = a.sel;
+    if (a.nb <= a.k) {
+        if (out)
+            for (int i = threadIdx.x; i < a.nb; i += sel::kT)
+                out[i] = i;
+        return;
+    }
+    sel::run(a, reinterpret_cast<char *>(sel_lds), [=](uint32_t slot, uint32_t id) {
+        out[slot] = (int32_t)id;
+    });
+}
+
 }  // namespace
+
+hipError_t launch_select_batch(const SelectBatchArgs &b, hipStream_t s)
+{
+    if (b.n < 1 || b.n > kMaxBatch)
+        return hipErrorInvalidValue;
+    size_t lds = 0;
+    for (int i = 0; i < b.n; ++i) {
+        if (b.seq[i].nb > b.seq[i].k && b.seq[i].T != 8 && b.seq[i].T != 16 && b.seq[i].T != 32)
+            return hipErrorInvalidValue;
+        const size_t l = sel::lds_bytes(b.seq[i].nb);
+        lds = l > lds ? l : lds;
+    }
+    if (lds > sel::kMaxLds)
+        return hipErrorInvalidValue;
+    if (lds > 64 * 1024) {
+        static hipError_t attr = hipFuncSetAttribute((const void *)k_select_batch,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     (int)sel::kMaxLds);
+        if (attr != hipSuccess)
+            return attr;
+    }
+    hipLaunchKernelGGL(k_select_batch, dim3(b.n), dim3(sel::kT), lds, s, b);
+    return hipGetLastError();
+}
 
 hipError_t launch_select(const SelectArgs &a, hipStream_t s)
 {

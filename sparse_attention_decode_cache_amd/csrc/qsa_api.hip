@@ -455,6 +455,135 @@ qsa_status qsa_decode_step(const qsa_layer_desc *desc, const qsa_layer_cache *ca
     return ok();
 }
 
+size_t qsa_batch_workspace_bytes(const qsa_layer_desc *desc, int32_t n_seq,
+                                 const int32_t *capacities)
+{
+    if (check_desc(desc) != QSA_OK || n_seq < 1 || n_seq > QSA_MAX_BATCH || !capacities)
+        return 0;
+    size_t total = 0;
+    for (int32_t i = 0; i < n_seq; ++i) {
+        const int32_t c = capacities[i];
+        if (c < 4 || c % 4 != 0 || c > (1 << 21))
+            return 0;
+        total += align256(decode_layout(desc, c).total);
+    }
+    return total;
+}
+
+qsa_status qsa_decode_step_batch(const qsa_layer_desc *desc, int32_t n_seq,
+                                 const qsa_layer_cache *caches, qsa_seq_state *states,
+                                 const qsa_seq_io *io, const float *gamma, void *ws,
+                                 size_t ws_bytes, hipStream_t stream)
+{
+    qsa_status s;
+    if ((s = check_desc(desc)) != QSA_OK)
+        return s;
+    if (n_seq < 1 || n_seq > QSA_MAX_BATCH)
+        return fail(QSA_ERR_ARG, "n_seq %d outside [1, %d]", n_seq, QSA_MAX_BATCH);
+    if (!caches || !states || !io || !gamma)
+        return fail(QSA_ERR_ARG, "caches / states / io / gamma is NULL");
+    size_t need = 0;
+    for (int32_t i = 0; i < n_seq; ++i) {
+        if ((s = check_cache(&caches[i], true, true, true)) != QSA_OK) {
+            char why[sizeof(tl_err)];
+            snprintf(why, sizeof(why), "%s", tl_err);
+            return fail(s, "sequence %d: %s", i, why);
+        }
+        const qsa_seq_io &x = io[i];
+        if (!x.idx_k_row || !x.k_row || !x.v_row || !x.q_idx || !x.w || !x.q || !x.out)
+            return fail(QSA_ERR_ARG, "sequence %d: an input or output pointer is NULL", i);
+        if (!aligned(x.idx_k_row, 4) || !aligned(x.k_row, 4) || !aligned(x.v_row, 4) ||
+            !aligned(x.q, 16) || !aligned(x.q_idx, 16))
+            return fail(QSA_ERR_ARG, "sequence %d: misaligned pointer", i);
+        const int32_t pos = states[i].n_tokens;
+        if (pos < 0 || pos >= caches[i].capacity)
+            return fail(QSA_ERR_ARG, "sequence %d: position %d outside [0, %d)", i, pos,
+                        caches[i].capacity);
+        if (states[i].n_valid_blocks < 0)
+            return fail(QSA_ERR_ARG, "sequence %d: n_valid_blocks < 0", i);
+        need += align256(decode_layout(desc, caches[i].capacity).total);
+    }
+    if ((s = check_ws(ws, ws_bytes, need)) != QSA_OK)
+        return s;
+
+    const int32_t K = desc->top_k_tokens / 4;
+    const bool f16 = desc->idx_dtype == QSA_F16;
+    const int rowb = desc->idx_heads * desc->idx_dim * elem_bytes(desc->idx_dtype);
+    const int tile_rows = score_tile_rows(f16, rowb);
+    const int G = desc->q_heads / desc->kv_heads;
+    ScoreBatchArgs sb{};
+    SelectBatchArgs selb{};
+    AttendBatchArgs ab{};
+    sb.n = selb.n = ab.n = n_seq;
+    size_t off = 0;
+    hipError_t e;
+    for (int32_t i = 0; i < n_seq; ++i) {
+        const qsa_layer_cache *c = &caches[i];
+        const qsa_seq_io &x = io[i];
+        const WsLayout L = decode_layout(desc, c->capacity);
+        char *wsp = (char *)ws + off;
+        off += align256(L.total);
+        const int32_t pos = states[i].n_tokens;
+        const int32_t n = pos + 1, nb = n / 4;
+        const int32_t b0 = states[i].n_valid_blocks < nb ? states[i].n_valid_blocks : nb;
+        const bool need_select = nb > K;
+
+        UpdateArgs u{};
+        u.idx_k = c->idx_k;
+        u.summary = c->summary;
+        u.k = c->k;
+        u.v = c->v;
+        u.new_idx_row = x.idx_k_row;
+        u.new_k_row = x.k_row;
+        u.new_v_row = x.v_row;
+        u.gamma = gamma;
+        u.idx_row_words = rowb / 4;
+        u.kv_row_words = desc->kv_heads * desc->head_dim / 2;
+        u.pos = pos;
+        u.b0 = b0;
+        u.nblk = nb - b0;
+        u.H = desc->idx_heads;
+        u.D = desc->idx_dim;
+        u.eps = (double)desc->rms_eps;
+        u.theta = (double)desc->rope_theta;
+        const bool fuse = u.nblk <= 1;
+        if (!fuse) {   // a rebuild after invalidation: its own launch first
+            e = launch_update(u, f16, stream);
+            if (e != hipSuccess)
+                return hip_fail(e, "decode_step_batch/update");
+        }
+        ScoreArgs &a = sb.seq[i];
+        a.summary = c->summary;
+        a.q = x.q_idx;
+        a.w = x.w;
+        a.keys = need_select ? (uint32_t *)(wsp + L.keys) : nullptr;
+        a.lists = need_select ? (uint64_t *)(wsp + L.lists) : nullptr;
+        a.nb = need_select ? nb : 0;     // kept-everything sequences only run the prologue
+        a.D = desc->idx_dim;
+        a.fuse = fuse ? 1 : 0;
+        a.upd = u;
+
+        int32_t *sel = need_select ? (x.sel_out ? x.sel_out : (int32_t *)(wsp + L.sel)) : x.sel_out;
+        selb.seq[i] = select_args(wsp, L, nb, K, tile_rows, sel);
+        ab.seq[i] = attend_args(desc, c, n, need_select ? sel : nullptr, need_select ? K : nb,
+                                x.q, x.out, (float *)(wsp + L.part));
+    }
+    e = launch_score_batch(sb, f16, rowb, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "decode_step_batch/score");
+    e = launch_select_batch(selb, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "decode_step_batch/select");
+    e = launch_attend_batch(ab, desc->head_dim, G, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "decode_step_batch/attend");
+    for (int32_t i = 0; i < n_seq; ++i) {
+        states[i].n_tokens += 1;
+        states[i].n_valid_blocks = states[i].n_tokens / 4;
+    }
+    return ok();
+}
+
 const char *qsa_status_string(qsa_status s)
 {
     switch (s) {

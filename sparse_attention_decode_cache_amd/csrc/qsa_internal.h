@@ -81,6 +81,15 @@ struct ScoreArgs {
     UpdateArgs upd;
 };
 hipError_t launch_score(const ScoreArgs &a, bool f16, int row_bytes, hipStream_t s);
+
+// Batched calls: per-sequence arguments travel in the kernel arguments.
+constexpr int kMaxBatch = 8;
+struct ScoreBatchArgs {
+    int32_t n;
+    int32_t tile0[kMaxBatch + 1];   // first workgroup of each sequence (filled by the launcher)
+    ScoreArgs seq[kMaxBatch];
+};
+hipError_t launch_score_batch(ScoreBatchArgs &b, bool f16, int row_bytes, hipStream_t s);
 // Rows per score workgroup (tile) for a given indexer row size.
 int score_tile_rows(bool f16, int row_bytes);
 
@@ -104,6 +113,11 @@ struct SelectArgs {
     int32_t T;
 };
 hipError_t launch_select(const SelectArgs &a, hipStream_t s);
+struct SelectBatchArgs {
+    int32_t n;
+    SelectArgs seq[kMaxBatch];
+};
+hipError_t launch_select_batch(const SelectBatchArgs &b, hipStream_t s);
 
 __host__ __device__ inline uint64_t comp_key(uint32_t key, uint32_t id)
 {
@@ -126,6 +140,12 @@ struct AttendArgs {
     float scale;
 };
 hipError_t launch_attend(const AttendArgs &a, int Dh, int G, hipStream_t s);
+struct AttendBatchArgs {
+    int32_t n;
+    int32_t wg0[kMaxBatch + 1];     // first workgroup of each sequence (filled by the launcher)
+    AttendArgs seq[kMaxBatch];
+};
+hipError_t launch_attend_batch(AttendBatchArgs &b, int Dh, int G, hipStream_t s);
 // Stages 3 + 4 fused: every attention workgroup selects (a.sel is ignored;
 // the chosen ids come from `sa`, sa.sel optionally receives them all).
 hipError_t launch_select_attend(const AttendArgs &a, const SelectArgs &sa, int Dh, int G,

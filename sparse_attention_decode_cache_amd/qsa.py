@@ -21,7 +21,9 @@ QSA_F32, QSA_F16 = 0, 1
 # Entry points declared in include/qsa.h (checked by the ABI test).
 EXPORTS = ("qsa_workspace_bytes", "qsa_state_invalidate", "qsa_state_truncate",
            "qsa_cache_update", "qsa_index_score", "qsa_topk_blocks", "qsa_gather_attend",
-           "qsa_decode_step", "qsa_status_string", "qsa_last_error")
+           "qsa_decode_step", "qsa_batch_workspace_bytes", "qsa_decode_step_batch",
+           "qsa_status_string", "qsa_last_error")
+QSA_MAX_BATCH = 8
 
 
 class QSAError(RuntimeError):
@@ -48,6 +50,12 @@ class qsa_seq_state(ctypes.Structure):
     _fields_ = [("n_tokens", ctypes.c_int32), ("n_valid_blocks", ctypes.c_int32)]
 
 
+class qsa_seq_io(ctypes.Structure):
+    _fields_ = [("idx_k_row", ctypes.c_void_p), ("k_row", ctypes.c_void_p),
+                ("v_row", ctypes.c_void_p), ("q_idx", ctypes.c_void_p), ("w", ctypes.c_void_p),
+                ("q", ctypes.c_void_p), ("out", ctypes.c_void_p), ("sel_out", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -71,8 +79,11 @@ def lib():
         L.qsa_topk_blocks.argtypes = [P, i32, i32, P, P, sz, P]
         L.qsa_gather_attend.argtypes = [D, C, i32, P, i32, P, P, P, sz, P]
         L.qsa_decode_step.argtypes = [D, C, S, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+        L.qsa_batch_workspace_bytes.restype = sz
+        L.qsa_batch_workspace_bytes.argtypes = [D, i32, ctypes.POINTER(i32)]
+        L.qsa_decode_step_batch.argtypes = [D, i32, C, S, ctypes.POINTER(qsa_seq_io), P, P, sz, P]
         for f in ("qsa_cache_update", "qsa_index_score", "qsa_topk_blocks", "qsa_gather_attend",
-                  "qsa_decode_step"):
+                  "qsa_decode_step", "qsa_decode_step_batch"):
             getattr(L, f).restype = ctypes.c_int
         L.qsa_status_string.restype = ctypes.c_char_p
         L.qsa_status_string.argtypes = [ctypes.c_int]
@@ -171,3 +182,32 @@ def qsa_decode_step(desc, cache, state, idx_k_row, k_row, v_row, gamma, q_idx, w
                                  _ptr(idx_k_row), _ptr(k_row), _ptr(v_row), _ptr(gamma), _ptr(q_idx),
                                  _ptr(w), _ptr(q), _ptr(out), _ptr(sel_out), _ptr(scores_out),
                                  p, n, _stream(stream)))
+
+
+def qsa_batch_workspace_bytes(desc, capacities):
+    caps = (ctypes.c_int32 * len(capacities))(*[int(c) for c in capacities])
+    return lib().qsa_batch_workspace_bytes(ctypes.byref(desc), len(capacities), caps)
+
+
+def batch_workspace(desc, capacities, device="cuda"):
+    n = qsa_batch_workspace_bytes(desc, capacities)
+    if n == 0:
+        raise QSAError(QSA_ERR_UNSUPPORTED, "qsa_batch_workspace_bytes rejected the arguments")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def qsa_decode_step_batch(desc, caches, states, io, gamma, ws, stream=None):
+    """caches: list of qsa_layer_cache; states: list of qsa_seq_state (updated in
+    place); io: list of dicts with keys idx_k_row, k_row, v_row, q_idx, w, q, out
+    and optional sel_out (torch tensors)."""
+    n = len(caches)
+    c_arr = (qsa_layer_cache * n)(*caches)
+    s_arr = (qsa_seq_state * n)(*[qsa_seq_state(s.n_tokens, s.n_valid_blocks) for s in states])
+    io_arr = (qsa_seq_io * n)(*[qsa_seq_io(*[None if x.get(k) is None else x[k].data_ptr()
+                                              for k in ("idx_k_row", "k_row", "v_row", "q_idx", "w",
+                                                        "q", "out", "sel_out")]) for x in io])
+    p, nbytes = _ws(ws)
+    _check(lib().qsa_decode_step_batch(ctypes.byref(desc), n, c_arr, s_arr, io_arr, _ptr(gamma), p,
+                                       nbytes, _stream(stream)))
+    for i, st in enumerate(states):
+        st.n_tokens, st.n_valid_blocks = s_arr[i].n_tokens, s_arr[i].n_valid_blocks

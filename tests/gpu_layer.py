@@ -22,7 +22,7 @@ def with_size(w, n0=None, steps=None, **kw):
 
 
 class GpuLayer:
-    def __init__(self, w, layer=0, seq=0, prefill=True):
+    def __init__(self, w, layer=0, seq=0, prefill=True, gamma_seq=None):
         import torch
         import sparse_attention_decode_cache_amd as qsa
         self.qsa = qsa
@@ -34,7 +34,7 @@ class GpuLayer:
                                   w.rms_eps, w.rope_theta)
         self.buf = qsa.LayerBuffers(self.desc, self.cap)
         W.dev_fill_layer_(w, self.buf, layer, w.n0, seq)
-        self.gamma = W.dev_gamma(w, layer, seq)
+        self.gamma = W.dev_gamma(w, layer, seq if gamma_seq is None else gamma_seq)
         self.ws = qsa.workspace(self.desc, self.cap)
         self.state = qsa.qsa_seq_state(w.n0, 0)
         if prefill:
@@ -58,7 +58,7 @@ class GpuLayer:
 
 
 class OracleMirror:
-    def __init__(self, w, layer=0, seq=0):
+    def __init__(self, w, layer=0, seq=0, gamma_seq=None):
         self.w = w
         self.layer = layer
         cap = w.capacity()
@@ -69,7 +69,7 @@ class OracleMirror:
         rows = np.arange(w.n0)
         raw[:w.n0] = W.host_raw_rows(w, rows, layer, seq)
         K[:w.n0], V[:w.n0] = W.host_kv_rows(w, rows, layer, seq)
-        self.gamma = W.host_gamma(w, layer, seq)
+        self.gamma = W.host_gamma(w, layer, seq if gamma_seq is None else gamma_seq)
         self.L = oracle.OracleLayer(raw, K, V, self.gamma, w.rms_eps, w.rope_theta, w.n0, w.k_blocks)
         self.L.rebuild()
         self.seq = seq

@@ -95,6 +95,35 @@ def test_argument_errors_before_launch():
     assert L.qsa_status_string(-3) == b"workspace missing or too small"
 
 
+def test_batch_argument_errors_before_launch():
+    qsa, d, c = _objs()
+    L = qsa.lib()
+    P = ctypes.c_void_p
+    D = ctypes.byref(d)
+    caps = (ctypes.c_int32 * 3)(4096, 8192, 400)
+    one = qsa.qsa_batch_workspace_bytes(d, [4096])
+    assert one == qsa.qsa_workspace_bytes(d, 4096)
+    assert qsa.qsa_batch_workspace_bytes(d, [4096, 8192, 400]) > one
+    assert L.qsa_batch_workspace_bytes(D, 0, caps) == 0
+    assert L.qsa_batch_workspace_bytes(D, 9, caps) == 0
+    assert qsa.qsa_batch_workspace_bytes(d, [4096, 4094]) == 0          # capacity % 4
+    cs = (qsa.qsa_layer_cache * 2)(c, c)
+    sts = (qsa.qsa_seq_state * 2)(qsa.qsa_seq_state(100, 25), qsa.qsa_seq_state(4096, 1024))
+    io = (qsa.qsa_seq_io * 2)(qsa.qsa_seq_io(*[16] * 7, None), qsa.qsa_seq_io(*[16] * 7, None))
+    assert L.qsa_decode_step_batch(D, 0, cs, sts, io, P(16), P(256), 1 << 30, None) == -1
+    assert L.qsa_decode_step_batch(D, 9, cs, sts, io, P(16), P(256), 1 << 30, None) == -1
+    assert L.qsa_decode_step_batch(D, 2, cs, sts, io, None, P(256), 1 << 30, None) == -1
+    # sequence 1 sits at its capacity
+    assert L.qsa_decode_step_batch(D, 2, cs, sts, io, P(16), P(256), 1 << 30, None) == -1
+    assert b"sequence 1" in L.qsa_last_error()
+    sts[1] = qsa.qsa_seq_state(200, 50)
+    io[0].q = 8                                                          # q must be 16-byte aligned
+    assert L.qsa_decode_step_batch(D, 2, cs, sts, io, P(16), P(256), 1 << 30, None) == -1
+    io[0].q = 16
+    assert L.qsa_decode_step_batch(D, 2, cs, sts, io, P(16), P(256), 100, None) == -3
+    assert [(x.n_tokens, x.n_valid_blocks) for x in sts] == [(100, 25), (200, 50)]
+
+
 def test_state_invalidate_and_truncate():
     import sparse_attention_decode_cache_amd as qsa
     st = qsa.qsa_seq_state(1000, 250)
