@@ -222,6 +222,49 @@ qsa_status qsa_decode_step_batch(const qsa_layer_desc *desc, int32_t n_seq,
                                  const qsa_seq_io *io, const float *gamma, void *ws,
                                  size_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------- prefill chunk
+ * n_q consecutive tokens of one sequence in one call, with the results of n_q
+ * qsa_decode_step calls in a row [post 10, "QSA indexer", "incremental
+ * pooled-key cache（COMMON-004）", "selected QSA K/V gather（COMMON-005）": the
+ * per-token step; running a ubatch of tokens through it at once is this
+ * library's].  Token i (0 <= i < n_q) is appended at pos_i = st->n_tokens + i;
+ * its query sees n_i = pos_i + 1 tokens: the floor(n_i / 4) blocks completed
+ * by then (a causal block mask -- never a block completed by a later token of
+ * the chunk), of which it keeps the top K = top_k_tokens / 4 by its own
+ * indexer score, plus its own tail of n_i mod 4 cells.  Every block the chunk
+ * completes (and any below the watermark) is pooled first, in one launch.
+ * Scoring runs as one f16 matrix-core GEMM of all queries against all blocks:
+ * the query q_idx[i][h] * w[i][h] is scaled by a power of two and split into
+ * two f16 halves so that the products keep fp32 accuracy (fp32 summaries are
+ * split likewise).
+ *
+ * idx_k_rows: DEVICE [n_q][H_i][D_i] idx_dtype; k_rows, v_rows: DEVICE
+ * [n_q][Hkv][Dh] binary16; q_idx: DEVICE fp32 [n_q][H_i][D_i]; w: DEVICE fp32
+ * [n_q][H_i]; q: DEVICE fp32 [n_q][Hq][Dh]; out: DEVICE fp32 [n_q][Hq][Dh].
+ * Rows, q_idx and q 16-byte aligned.  sel_out (optional, DEVICE int32
+ * [n_q][K]): row i gets the min(K, floor(n_i/4)) chosen ids ascending, then
+ * -1.  scores_out (optional, DEVICE fp32 [n_q][nb_last], nb_last =
+ * floor((pos_0 + n_q) / 4)): written only when some query has more than K
+ * blocks; entry (i, b) is query i's score of block b for b < floor(n_i / 4),
+ * -INFINITY past it.
+ * On success st becomes {pos_0 + n_q, nb_last}; on any error nothing is
+ * enqueued and st is unchanged.
+ * Errors: ARG if n_q is outside [1, QSA_MAX_CHUNK], a pointer is null or
+ * misaligned, or pos_0 + n_q > capacity; UNSUPPORTED / WORKSPACE as in
+ * qsa_decode_step (workspace >= qsa_chunk_workspace_bytes). */
+#define QSA_MAX_CHUNK 4096
+
+/* Workspace bytes for qsa_chunk_step of up to n_q tokens on a cache of the
+ * given capacity; 0 if the desc, capacity or n_q is invalid. */
+size_t qsa_chunk_workspace_bytes(const qsa_layer_desc *desc, int32_t capacity, int32_t n_q);
+
+qsa_status qsa_chunk_step(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
+                          qsa_seq_state *st, int32_t n_q, const void *idx_k_rows,
+                          const uint16_t *k_rows, const uint16_t *v_rows, const float *gamma,
+                          const float *q_idx, const float *w, const float *q, float *out,
+                          int32_t *sel_out, float *scores_out, void *ws, size_t ws_bytes,
+                          hipStream_t stream);
+
 /* Static text for a status code. */
 const char *qsa_status_string(qsa_status s);
 

@@ -5,4 +5,4 @@ gathered GQA attention -- is hand-written HIP in libqsa.so behind the C ABI of
 include/qsa.h; ``qsa`` is its ctypes binding.
 """
 from .qsa import *  # noqa: F401,F403
-from .qsa import LayerBuffers, QSAError, batch_workspace, lib, make_desc, workspace  # noqa: F401
+from .qsa import LayerBuffers, QSAError, batch_workspace, chunk_workspace, lib, make_desc, workspace  # noqa: F401

@@ -1,0 +1,481 @@
+// k_chunk.hip -- a prefill chunk: n_q consecutive tokens of one sequence in
+// one call, with results equal to n_q decode steps in a row.  Query i sits at
+// position p = n0 + i; it sees the floor((p + 1) / 4) blocks completed by then
+// (the causal block mask), keeps the top k of them and attends to their cells
+// and to its own tail [post 10, "QSA indexer"; "incremental pooled-key
+// cache（COMMON-004）"; "selected QSA K/V gather（COMMON-005）"].
+//
+// Launches (after the caller pools the blocks the chunk completes):
+//   prep    per query: q_idx scaled by the head weights (score = sum over
+//           (h, d) of w_h q_hd khat_hd, one contraction of length H*D), times
+//           a power of two that keeps it in f16 range, split into f16 hi + lo
+//           and written in the matrix-core operand layout;
+//   score   all queries x all blocks as one f16 MFMA GEMM (hi and lo both
+//           multiplied: the products are exact in fp32), epilogue: the
+//           order-preserving key of each score, 0 past the query's blocks;
+//   select  one workgroup per query: the exact radix top-k over its keys,
+//           held in registers;
+//   attend  workgroup (query, split, KV head): the tile routine of the decode
+//           path over the split's 16-cell tiles, folded into a running
+//           (max, sum, acc) in registers; with one split the output is
+//           written directly, otherwise a small merge follows.
+#include "qsa_attend.h"
+#include "qsa_internal.h"
+#include "qsa_select.h"
+#include "qsa_wave.h"
+
+namespace qsa {
+namespace {
+
+using namespace att;
+
+// ------------------------------------------------------------------ append
+
+__global__ __launch_bounds__(256) void k_chunk_append(ChunkArgs c)
+{
+    const size_t ni = (size_t)c.n_q * c.idx_row_bytes / 16;
+    const size_t nk = (size_t)c.n_q * c.kv_row_bytes / 16;
+    uint4 *di = (uint4 *)((char *)c.idx_k + (size_t)c.n0 * c.idx_row_bytes);
+    uint4 *dk = (uint4 *)((char *)c.k + (size_t)c.n0 * c.kv_row_bytes);
+    uint4 *dv = (uint4 *)((char *)c.v + (size_t)c.n0 * c.kv_row_bytes);
+    const uint4 *si = (const uint4 *)c.idx_rows;
+    const uint4 *sk = (const uint4 *)c.k_rows;
+    const uint4 *sv = (const uint4 *)c.v_rows;
+    const size_t total = ni + 2 * nk;
+    for (size_t x = (size_t)blockIdx.x * 256 + threadIdx.x; x < total; x += (size_t)gridDim.x * 256) {
+        if (x < ni)
+            di[x] = si[x];
+        else if (x < ni + nk)
+            dk[x - ni] = sk[x - ni];
+        else
+            dv[x - ni - nk] = sv[x - ni - nk];
+    }
+}
+
+// ------------------------------------------------------------------- prep
+
+typedef float float4v __attribute__((ext_vector_type(4)));
+
+// One wave per query (4 per workgroup).  Lane g owns elements 8g .. 8g+7 of
+// the H*D contraction.  Output: for query tile qt (16 queries) and k-step ks
+// (32 elements), hi then lo, 64 lanes x 8 halves: lane l holds elements
+// 32 ks + 8 (l / 16) .. +8 of query 16 qt + l % 16 -- the B operand of
+// v_mfma_f32_16x16x32_f16.  Queries past n_q (tile padding) are zero.
+__global__ __launch_bounds__(256) void k_chunk_prep(ChunkArgs c)
+{
+    const int lane = threadIdx.x & 63;
+    const int qi = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int QK = c.H * c.D, KS = QK / 32;
+    const bool live = lane < QK / 8;
+    const bool real = qi < c.n_q;
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        x[j] = 0.0f;
+    if (live && real) {
+        const int e0 = 8 * lane;
+        const float wh = c.w[(size_t)qi * c.H + e0 / c.D];
+        const float4 *src = (const float4 *)(c.q_idx + (size_t)qi * QK + e0);
+        const float4 u = src[0], v = src[1];
+        x[0] = wh * u.x; x[1] = wh * u.y; x[2] = wh * u.z; x[3] = wh * u.w;
+        x[4] = wh * v.x; x[5] = wh * v.y; x[6] = wh * v.z; x[7] = wh * v.w;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        amax = fmaxf(amax, fabsf(x[j]));
+    amax = wave::reduce_max_f(amax);
+    // 2^s with amax * 2^s in [2^13, 2^14): far from the f16 limit, lo normal
+    int ex = 0;
+    (void)frexpf(amax, &ex);
+    const int sh = (amax > 0.0f && amax < __builtin_inff()) ? 14 - ex : 0;
+    if (live) {
+        _Float16 hi[8], lo[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float y = ldexpf(x[j], sh);
+            hi[j] = (_Float16)y;
+            lo[j] = (_Float16)(y - (float)hi[j]);
+        }
+        const int ks = lane / 4, kg = lane % 4;
+        const int l = kg * 16 + qi % 16;
+        _Float16 *dst = c.qhl + ((((size_t)(qi / 16) * KS + ks) * 2) * 64 + l) * 8;
+        __builtin_memcpy(dst, hi, 16);
+        __builtin_memcpy(dst + 64 * 8, lo, 16);
+    }
+    if (lane == 0 && real)
+        c.qscale[qi] = ldexpf(1.0f, -sh);
+}
+
+// ------------------------------------------------------------------ score
+
+__device__ inline uint32_t chunk_key(float s)
+{
+    // -0 and +0 compare equal: canonicalise before taking the bits
+    const uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+constexpr int kSQT = 8;                      // query tiles (16 queries) per workgroup
+constexpr int kSRT = 4;                      // block row tiles (16 blocks) per wave
+constexpr int kSBlocks = 4 * kSRT * 16;      // blocks per workgroup (4 waves)
+
+// Workgroup (256 blocks, 128 queries), 4 waves; wave w holds the 64 x 128
+// block-query products of blocks 64w .. 64w+63 in 32 accumulator tiles.  The
+// summary rows are the A operand, loaded straight from memory (lane l: row
+// l % 16, 8 elements at 8 (l / 16)); the queries' operand tiles are staged in
+// LDS, KC k-steps at a time, shared by the 4 waves.
+template <bool F16>
+__global__ __launch_bounds__(256) void k_chunk_score(ChunkArgs c)
+{
+    constexpr int KC = F16 ? 4 : 2;
+    constexpr int ES = F16 ? 2 : 4;
+    __shared__ uint4 sb[kSQT][KC][2][64];
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int QK = c.H * c.D, KS = QK / 32;
+    const int QT = (c.n_q + 15) / 16;
+    const int qt0 = blockIdx.y * kSQT;
+    const int64_t bw = (int64_t)blockIdx.x * kSBlocks + wave * kSRT * 16;
+    const int mr = lane & 15, kg = lane >> 4;
+
+    const char *rowp[kSRT];
+#pragma unroll
+    for (int rt = 0; rt < kSRT; ++rt) {
+        int64_t r = bw + 16 * rt + mr;
+        r = r < c.nb_last ? r : c.nb_last - 1;
+        rowp[rt] = (const char *)c.summary + ((size_t)r * QK + 8 * kg) * ES;
+    }
+    float4v acc[kSRT][kSQT];
+#pragma unroll
+    for (int rt = 0; rt < kSRT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < kSQT; ++ct)
+            acc[rt][ct] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+
+    const uint4 *qsrc = (const uint4 *)c.qhl;
+    for (int k0 = 0; k0 < KS; k0 += KC) {
+        // this chunk's A operands, in flight while the B tiles are staged
+        uint4 ar[kSRT][KC][ES / 2];
+#pragma unroll
+        for (int rt = 0; rt < kSRT; ++rt)
+#pragma unroll
+            for (int kk = 0; kk < KC; ++kk)
+#pragma unroll
+                for (int p = 0; p < ES / 2; ++p)
+                    ar[rt][kk][p] = k0 + kk < KS
+                                        ? *(const uint4 *)(rowp[rt] + (size_t)(32 * (k0 + kk)) * ES + 16 * p)
+                                        : make_uint4(0u, 0u, 0u, 0u);
+        __syncthreads();                 // the previous chunk's B reads are done
+        for (int i = t; i < kSQT * KC * 2 * 64; i += 256) {
+            const int ln = i & 63, hl = (i >> 6) & 1, kk = (i >> 7) % KC, ct = (i >> 7) / KC;
+            const bool ok = qt0 + ct < QT && k0 + kk < KS;
+            sb[ct][kk][hl][ln] =
+                ok ? qsrc[(((size_t)(qt0 + ct) * KS + k0 + kk) * 2 + hl) * 64 + ln] : make_uint4(0u, 0u, 0u, 0u);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk) {
+            if (k0 + kk >= KS)
+                break;
+            half8 ah[kSRT], al[kSRT];
+#pragma unroll
+            for (int rt = 0; rt < kSRT; ++rt) {
+                if constexpr (F16) {
+                    __builtin_memcpy(&ah[rt], &ar[rt][kk][0], 16);
+                } else {
+                    float f[8];
+                    __builtin_memcpy(f, &ar[rt][kk][0], 32);
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        ah[rt][j] = (_Float16)f[j];
+                        al[rt][j] = (_Float16)(f[j] - (float)ah[rt][j]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int ct = 0; ct < kSQT; ++ct) {
+                half8 bh, bl;
+                __builtin_memcpy(&bh, &sb[ct][kk][0][lane], 16);
+                __builtin_memcpy(&bl, &sb[ct][kk][1][lane], 16);
+#pragma unroll
+                for (int rt = 0; rt < kSRT; ++rt) {
+                    acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[rt], bh, acc[rt][ct], 0, 0, 0);
+                    acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[rt], bl, acc[rt][ct], 0, 0, 0);
+                    if constexpr (!F16)
+                        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[rt], bh, acc[rt][ct], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    // lane l holds D[block 4 (l / 16) + j][query l % 16] of each tile
+#pragma unroll
+    for (int ct = 0; ct < kSQT; ++ct) {
+        const int qi = (qt0 + ct) * 16 + mr;
+        if (qi >= c.n_q)
+            continue;
+        const float f = c.qscale[qi];
+        const int64_t nbq = ((int64_t)c.n0 + qi + 1) >> 2;
+#pragma unroll
+        for (int rt = 0; rt < kSRT; ++rt) {
+            const int64_t b = bw + 16 * rt + 4 * kg;
+            float sc[4];
+            uint32_t key[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                sc[j] = acc[rt][ct][j] * f;
+                key[j] = b + j < nbq ? chunk_key(sc[j]) : 0u;
+            }
+            if (b < c.ldk)
+                *(uint4 *)(c.keys + (size_t)qi * c.ldk + b) = make_uint4(key[0], key[1], key[2], key[3]);
+            if (c.scores_out) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (b + j < c.nb_last)
+                        c.scores_out[(size_t)qi * c.nb_last + b + j] = b + j < nbq ? sc[j] : -INFINITY;
+            }
+        }
+    }
+}
+
+// ----------------------------------------------------------------- select
+
+// LDS of the chunk select: Smem, the id bitmap and, when they fit, the keys.
+inline size_t chunk_sel_lds(int32_t nb, bool &cache_keys)
+{
+    const size_t base = sel::lds_bytes(nb);
+    cache_keys = base + 4 * (size_t)nb <= sel::kMaxLds;
+    return cache_keys ? base + 4 * (size_t)nb : base;
+}
+
+__global__ __launch_bounds__(sel::kT) void k_chunk_select(ChunkArgs c)
+{
+    extern __shared__ uint4 sel_lds[];
+    const int i = blockIdx.x, t = threadIdx.x;
+    const int32_t nbq = (int32_t)(((int64_t)c.n0 + i + 1) >> 2);
+    const int32_t keep = nbq < c.kb ? nbq : c.kb;
+    int32_t *row_out = c.sel_out ? c.sel_out + (size_t)i * c.kb : nullptr;
+    if (row_out)
+        for (int j = keep + t; j < c.kb; j += sel::kT)
+            row_out[j] = -1;
+    if (nbq <= c.kb) {
+        if (row_out)
+            for (int j = t; j < nbq; j += sel::kT)
+                row_out[j] = j;
+        return;
+    }
+    SelectArgs a{};
+    a.keys = c.keys + (size_t)i * c.ldk;
+    a.nb = nbq;
+    a.k = c.kb;
+    a.T = 8;
+    int32_t *row = c.sel + (size_t)i * c.kb;
+    char *lds = reinterpret_cast<char *>(sel_lds);
+    sel::Smem &sm = *reinterpret_cast<sel::Smem *>(lds);
+    uint32_t *bitmap = reinterpret_cast<uint32_t *>(lds + (sizeof(sel::Smem) + 15) / 16 * 16);
+    uint32_t *lkeys = c.sel_cache_keys ? reinterpret_cast<uint32_t *>(lds + sel::lds_bytes(c.nb_last)) : nullptr;
+    sel::general_path(a, sm, bitmap, lkeys, [=](uint32_t slot, uint32_t id) {
+        row[slot] = (int32_t)id;
+        if (row_out)
+            row_out[slot] = (int32_t)id;
+    });
+}
+
+// ----------------------------------------------------------------- attend
+
+template <int DH, int G>
+__global__ __launch_bounds__(kAT) void k_chunk_attend(ChunkArgs c)
+{
+    __shared__ AttLds<DH, G> L;
+    __shared__ int32_t ids[kChunkMaxIds];
+    constexpr int R = (G * DH + kAT - 1) / kAT;
+    const int t = threadIdx.x;
+    const int ns = c.n_split;
+    const int i = blockIdx.x / ns, s = blockIdx.x % ns, g = blockIdx.y;
+    const int64_t n = (int64_t)c.n0 + i + 1;
+    const int32_t nbq = (int32_t)(n >> 2);
+    const bool keep_all = nbq <= c.kb;
+    const int32_t nsel = keep_all ? nbq : c.kb;
+    const int32_t ncells = 4 * nsel + (int32_t)(n & 3);
+    const int32_t ntiles = (ncells + kCells - 1) / kCells;
+    const int32_t tps = (ntiles + ns - 1) / ns;
+    const int32_t j0 = s * tps, j1 = j0 + tps < ntiles ? j0 + tps : ntiles;
+    // the split's block ids
+    const int32_t id0 = 4 * j0, id1 = 4 * j1 < nsel ? 4 * j1 : nsel;
+    const int32_t *srow = c.sel + (size_t)i * c.kb;
+    for (int x = id0 + t; x < id1; x += kAT)
+        ids[x - id0] = keep_all ? x : srow[x];
+    __syncthreads();
+
+    AttendArgs a{};
+    a.k = c.k;
+    a.v = c.v;
+    a.q = c.q + (size_t)i * c.kv_heads * G * DH;
+    a.n_sel_blocks = nsel;
+    a.nb = nbq;
+    a.n_cells = ncells;
+    a.kv_heads = c.kv_heads;
+    a.scale = c.scale;
+
+    float m_r[R], l_r[R], acc_r[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        m_r[r] = -INFINITY;
+        l_r[r] = 0.0f;
+        acc_r[r] = 0.0f;
+    }
+    for (int32_t j = j0; j < j1; ++j) {
+        attend_tile<DH, G>(a, L, ids + 4 * (j - j0), kCells * j, g, [&](AttLds<DH, G> &T) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const int idx = t + kAT * r;
+                if (idx < G * DH) {
+                    const int h = idx / DH;
+                    const float mt = T.m[h], lt = T.l[h];
+                    const float at = tile_acc<DH, G>(T, idx);
+                    const float mn = fmaxf(m_r[r], mt);
+                    if (mn != -INFINITY) {
+                        const float wr = m_r[r] == -INFINITY ? 0.0f : expf(m_r[r] - mn);
+                        const float wt = mt == -INFINITY ? 0.0f : expf(mt - mn);
+                        acc_r[r] = acc_r[r] * wr + at * wt;
+                        l_r[r] = l_r[r] * wr + lt * wt;
+                        m_r[r] = mn;
+                    }
+                }
+            }
+        });
+    }
+
+    const size_t ob = (size_t)i * c.kv_heads * G * DH + (size_t)g * G * DH;
+    if (ns == 1) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int idx = t + kAT * r;
+            if (idx < G * DH)
+                c.out[ob + idx] = acc_r[r] / l_r[r];
+        }
+        return;
+    }
+    float *part = c.part + (((size_t)i * c.kv_heads + g) * ns + s) * (size_t)part_stride(G, DH);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int idx = t + kAT * r;
+        if (idx < G * DH) {
+            part[2 * G + idx] = acc_r[r];
+            if (idx % DH == 0) {
+                part[idx / DH] = m_r[r];
+                part[G + idx / DH] = l_r[r];
+            }
+        }
+    }
+}
+
+// Workgroup (query, KV head): out = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s
+// over the splits, in split order.
+template <int DH, int G>
+__global__ __launch_bounds__(256) void k_chunk_merge(ChunkArgs c)
+{
+    const int unit = blockIdx.x;
+    const int ns = c.n_split;
+    const size_t ps = (size_t)part_stride(G, DH);
+    const float *base = c.part + (size_t)unit * ns * ps;
+    float *out = c.out + (size_t)unit * G * DH;
+    for (int idx = threadIdx.x; idx < G * DH; idx += 256) {
+        const int h = idx / DH;
+        float M = -INFINITY;
+        for (int s = 0; s < ns; ++s)
+            M = fmaxf(M, base[s * ps + h]);
+        float A = 0.0f, Ls = 0.0f;
+        for (int s = 0; s < ns; ++s) {
+            const float m = base[s * ps + h];
+            const float w = m == -INFINITY ? 0.0f : expf(m - M);
+            A = fmaf(w, base[s * ps + 2 * G + idx], A);
+            Ls = fmaf(w, base[s * ps + G + h], Ls);
+        }
+        out[idx] = A / Ls;
+    }
+}
+
+template <int DH, int G>
+hipError_t attend_go(const ChunkArgs &c, hipStream_t s)
+{
+    hipLaunchKernelGGL((k_chunk_attend<DH, G>), dim3(c.n_q * c.n_split, c.kv_heads), dim3(kAT), 0, s, c);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || c.n_split == 1)
+        return e;
+    hipLaunchKernelGGL((k_chunk_merge<DH, G>), dim3(c.n_q * c.kv_heads), dim3(256), 0, s, c);
+    return hipGetLastError();
+}
+
+template <int DH>
+hipError_t attend_g(const ChunkArgs &c, int G, hipStream_t s)
+{
+    switch (G) {
+    case 1: return attend_go<DH, 1>(c, s);
+    case 2: return attend_go<DH, 2>(c, s);
+    case 4: return attend_go<DH, 4>(c, s);
+    case 8: return attend_go<DH, 8>(c, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_chunk_append(const ChunkArgs &c, hipStream_t s)
+{
+    if (c.idx_row_bytes % 16 || c.kv_row_bytes % 16)
+        return hipErrorInvalidValue;
+    const size_t total = (size_t)c.n_q * (c.idx_row_bytes + 2 * (size_t)c.kv_row_bytes) / 16;
+    size_t grid = (total + 255) / 256;
+    grid = grid < 1 ? 1 : (grid > 2048 ? 2048 : grid);
+    hipLaunchKernelGGL(k_chunk_append, dim3((unsigned)grid), dim3(256), 0, s, c);
+    return hipGetLastError();
+}
+
+hipError_t launch_chunk_rest(ChunkArgs c, bool f16, int Dh, int G, hipStream_t s)
+{
+    const int QK = c.H * c.D;
+    if (QK % 32 || QK / 8 > 64 || c.kb < 1 || c.kb >= kChunkMaxIds || c.n_split < 1 ||
+        c.n_split > kChunkMaxSplits || c.n_q < 1)
+        return hipErrorInvalidValue;
+    hipError_t e;
+    // scoring and selection only when some query has more blocks than it keeps
+    if (c.nb_last > c.kb) {
+        const int qt = (c.n_q + 15) / 16;
+        hipLaunchKernelGGL(k_chunk_prep, dim3(qt * 4), dim3(256), 0, s, c);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+        const dim3 grid((unsigned)((c.nb_last + kSBlocks - 1) / kSBlocks), (unsigned)((qt + kSQT - 1) / kSQT));
+        if (f16)
+            hipLaunchKernelGGL(k_chunk_score<true>, grid, dim3(256), 0, s, c);
+        else
+            hipLaunchKernelGGL(k_chunk_score<false>, grid, dim3(256), 0, s, c);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+    }
+    if (c.nb_last > c.kb || c.sel_out) {
+        bool cache_keys = false;
+        const size_t lds = chunk_sel_lds(c.nb_last, cache_keys);
+        if (lds > sel::kMaxLds)
+            return hipErrorInvalidValue;
+        c.sel_cache_keys = cache_keys ? 1 : 0;
+        if (lds > 64 * 1024) {
+            static hipError_t attr = hipFuncSetAttribute((const void *)k_chunk_select,
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                         (int)sel::kMaxLds);
+            if (attr != hipSuccess)
+                return attr;
+        }
+        hipLaunchKernelGGL(k_chunk_select, dim3(c.n_q), dim3(sel::kT), lds, s, c);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+    }
+    switch (Dh) {
+    case 64: return attend_g<64>(c, G, s);
+    case 128: return attend_g<128>(c, G, s);
+    case 256: return attend_g<256>(c, G, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace qsa

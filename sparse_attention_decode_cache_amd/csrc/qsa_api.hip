@@ -100,6 +100,34 @@ WsLayout decode_layout(const qsa_layer_desc *d, int32_t capacity)
     return ws_layout(capacity / 4, d->top_k_tokens / 4, decode_part_floats(d));
 }
 
+// Prefill-chunk workspace: folded queries, their scales, the keys of every
+// (query, block), the chosen ids and the attention partials.
+struct ChunkLayout {
+    size_t qhl, qscale, keys, sel, part, total;
+};
+
+ChunkLayout chunk_layout(const qsa_layer_desc *d, int32_t capacity, int32_t n_q)
+{
+    ChunkLayout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = off;
+        off = align256(off + bytes);
+        return o;
+    };
+    const size_t qk = (size_t)d->idx_heads * d->idx_dim;
+    const size_t qpad = ((size_t)n_q + 15) / 16 * 16;
+    const size_t ldk = ((size_t)capacity / 4 + 3) / 4 * 4;
+    const int G = d->q_heads / d->kv_heads;
+    L.qhl = take(qpad * qk * 2 * sizeof(uint16_t));
+    L.qscale = take(sizeof(float) * (size_t)n_q);
+    L.keys = take(sizeof(uint32_t) * (size_t)n_q * ldk);
+    L.sel = take(sizeof(int32_t) * (size_t)n_q * (d->top_k_tokens / 4));
+    L.part = take(sizeof(float) * 2 * (size_t)kChunkWgTarget * part_stride(G, d->head_dim));
+    L.total = off;
+    return L;
+}
+
 qsa_status check_ws(void *ws, size_t ws_bytes, size_t need)
 {
     if (!ws || !aligned(ws, 256))
@@ -581,6 +609,115 @@ qsa_status qsa_decode_step_batch(const qsa_layer_desc *desc, int32_t n_seq,
         states[i].n_tokens += 1;
         states[i].n_valid_blocks = states[i].n_tokens / 4;
     }
+    return ok();
+}
+
+size_t qsa_chunk_workspace_bytes(const qsa_layer_desc *desc, int32_t capacity, int32_t n_q)
+{
+    if (check_desc(desc) != QSA_OK || capacity < 4 || capacity % 4 != 0 || capacity > (1 << 21) ||
+        n_q < 1 || n_q > QSA_MAX_CHUNK)
+        return 0;
+    return chunk_layout(desc, capacity, n_q).total;
+}
+
+qsa_status qsa_chunk_step(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
+                          qsa_seq_state *st, int32_t n_q, const void *idx_k_rows,
+                          const uint16_t *k_rows, const uint16_t *v_rows, const float *gamma,
+                          const float *q_idx, const float *w, const float *q, float *out,
+                          int32_t *sel_out, float *scores_out, void *ws, size_t ws_bytes,
+                          hipStream_t stream)
+{
+    qsa_status s;
+    if ((s = check_desc(desc)) != QSA_OK || (s = check_cache(cache, true, true, true)) != QSA_OK)
+        return s;
+    if (!st)
+        return fail(QSA_ERR_ARG, "state is NULL");
+    if (n_q < 1 || n_q > QSA_MAX_CHUNK)
+        return fail(QSA_ERR_ARG, "n_q %d outside [1, %d]", n_q, QSA_MAX_CHUNK);
+    if (!idx_k_rows || !k_rows || !v_rows || !gamma || !q_idx || !w || !q || !out)
+        return fail(QSA_ERR_ARG, "an input or output pointer is NULL");
+    if (!aligned(idx_k_rows, 16) || !aligned(k_rows, 16) || !aligned(v_rows, 16) ||
+        !aligned(q_idx, 16) || !aligned(q, 16))
+        return fail(QSA_ERR_ARG, "row, q_idx or q pointer not 16-byte aligned");
+    const int32_t n0 = st->n_tokens;
+    if (n0 < 0 || (int64_t)n0 + n_q > cache->capacity)
+        return fail(QSA_ERR_ARG, "positions [%d, %lld) outside [0, %d)", n0,
+                    (long long)n0 + n_q, cache->capacity);
+    if (st->n_valid_blocks < 0)
+        return fail(QSA_ERR_ARG, "n_valid_blocks < 0");
+    const ChunkLayout L = chunk_layout(desc, cache->capacity, n_q);
+    if ((s = check_ws(ws, ws_bytes, L.total)) != QSA_OK)
+        return s;
+
+    const bool f16 = desc->idx_dtype == QSA_F16;
+    const int rowb = desc->idx_heads * desc->idx_dim * elem_bytes(desc->idx_dtype);
+    const int G = desc->q_heads / desc->kv_heads;
+    const int32_t K = desc->top_k_tokens / 4;
+    const int32_t n_end = n0 + n_q, nb_last = n_end / 4;
+    char *wsp = (char *)ws;
+
+    ChunkArgs c{};
+    c.idx_k = cache->idx_k;
+    c.summary = cache->summary;
+    c.k = cache->k;
+    c.v = cache->v;
+    c.idx_rows = idx_k_rows;
+    c.k_rows = k_rows;
+    c.v_rows = v_rows;
+    c.idx_row_bytes = rowb;
+    c.kv_row_bytes = desc->kv_heads * desc->head_dim * 2;
+    c.q_idx = q_idx;
+    c.w = w;
+    c.q = q;
+    c.out = out;
+    c.sel_out = sel_out;
+    c.scores_out = scores_out;
+    c.qhl = (_Float16 *)(wsp + L.qhl);
+    c.qscale = (float *)(wsp + L.qscale);
+    c.keys = (uint32_t *)(wsp + L.keys);
+    c.sel = (int32_t *)(wsp + L.sel);
+    c.part = (float *)(wsp + L.part);
+    c.ldk = ((int64_t)nb_last + 3) / 4 * 4;
+    c.n0 = n0;
+    c.n_q = n_q;
+    c.nb_last = nb_last;
+    c.kb = K;
+    c.H = desc->idx_heads;
+    c.D = desc->idx_dim;
+    c.kv_heads = desc->kv_heads;
+    c.scale = attn_scale(desc);
+    // few queries: split each query's tiles so that the chip is still filled
+    const int64_t units = (int64_t)n_q * desc->kv_heads;
+    const int64_t max_tiles = n_splits(4 * (int64_t)K + 3);
+    int64_t ns = units >= kChunkWgTarget ? 1 : (kChunkWgTarget + units - 1) / units;
+    ns = ns < max_tiles ? ns : max_tiles;
+    ns = ns < kChunkMaxSplits ? ns : kChunkMaxSplits;
+    c.n_split = (int32_t)ns;
+
+    hipError_t e = launch_chunk_append(c, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "chunk_step/append");
+    const int32_t b0 = st->n_valid_blocks < nb_last ? st->n_valid_blocks : nb_last;
+    if (nb_last > b0) {
+        UpdateArgs u{};
+        u.idx_k = cache->idx_k;
+        u.summary = cache->summary;
+        u.gamma = gamma;
+        u.b0 = b0;
+        u.nblk = nb_last - b0;
+        u.H = desc->idx_heads;
+        u.D = desc->idx_dim;
+        u.eps = (double)desc->rms_eps;
+        u.theta = (double)desc->rope_theta;
+        e = launch_update(u, f16, stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "chunk_step/pool");
+    }
+    e = launch_chunk_rest(c, f16, desc->head_dim, G, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "chunk_step");
+    st->n_tokens = n_end;
+    st->n_valid_blocks = nb_last;
     return ok();
 }
 

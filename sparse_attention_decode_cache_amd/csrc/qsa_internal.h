@@ -151,4 +151,43 @@ hipError_t launch_attend_batch(AttendBatchArgs &b, int Dh, int G, hipStream_t s)
 hipError_t launch_select_attend(const AttendArgs &a, const SelectArgs &sa, int Dh, int G,
                                 hipStream_t s);
 
+// ------------------------------------------------------------ prefill chunk
+// n_q consecutive tokens of one sequence in one call: query i sits at position
+// n0 + i and sees the blocks completed by then.
+constexpr int kChunkWgTarget = 512;     // attention workgroups aimed at when queries are few
+constexpr int kChunkMaxSplits = 64;
+constexpr int kChunkMaxIds = 4096;      // block ids of one query (k <= 4095)
+
+struct ChunkArgs {
+    void *idx_k;                // cache: raw indexer keys, summaries, K, V
+    const void *summary;
+    uint16_t *k;
+    uint16_t *v;
+    const void *idx_rows;       // [n_q] appended rows
+    const uint16_t *k_rows;
+    const uint16_t *v_rows;
+    int32_t idx_row_bytes;
+    int32_t kv_row_bytes;
+    const float *q_idx;         // [n_q][H][D]
+    const float *w;             // [n_q][H]
+    const float *q;             // [n_q][Hq][Dh]
+    float *out;                 // [n_q][Hq][Dh]
+    int32_t *sel_out;           // optional [n_q][kb]
+    float *scores_out;          // optional [n_q][nb_last]
+    _Float16 *qhl;              // workspace: folded queries, MFMA operand layout
+    float *qscale;              // workspace: [n_q] power-of-two factors
+    uint32_t *keys;             // workspace: [n_q][ldk]
+    int32_t *sel;               // workspace: [n_q][kb]
+    float *part;                // workspace: attention partials (n_split > 1)
+    int64_t ldk;
+    int32_t n0, n_q, nb_last, kb;   // kb: blocks kept per query
+    int32_t H, D;
+    int32_t kv_heads, n_split;
+    int32_t sel_cache_keys;     // the select keeps each query's keys in LDS (set by the launcher)
+    float scale;
+};
+// Append, then (after the caller's pooling launch) score, select and attend.
+hipError_t launch_chunk_append(const ChunkArgs &c, hipStream_t s);
+hipError_t launch_chunk_rest(ChunkArgs c, bool f16, int Dh, int G, hipStream_t s);
+
 }  // namespace qsa

@@ -67,7 +67,7 @@ struct Smem {
 };
 
 // Dynamic LDS of run(): Smem and the id bitmap.
-inline size_t lds_bytes(int32_t nb)
+__host__ __device__ inline size_t lds_bytes(int32_t nb)
 {
     const size_t nwords = (size_t)(nb + 31) / 32;
     const size_t bm = nwords > (size_t)kFastWords ? nwords : (size_t)kFastWords;
@@ -229,6 +229,82 @@ __device__ void refine_and_mark(Smem &sm, ForEach for_each, Mark mark, uint32_t 
     }
 }
 
+// The exact top-k over every key (radix refinement, bitmap, popcount slots).
+// lkeys (LDS, nb words, or null): the keys are copied there first and every
+// pass reads them from LDS instead of memory.  Whole workgroup calls;
+// `bitmap` holds (nb + 31) / 32 words; emit as in run().
+template <class Emit>
+__device__ void general_path(const SelectArgs &a, Smem &sm, uint32_t *bitmap, uint32_t *lkeys,
+                             Emit emit)
+{
+    const uint32_t nb = (uint32_t)a.nb;
+    const uint32_t k = (uint32_t)a.k;
+    const uint32_t nwords = (nb + 31) >> 5;
+    const int t = threadIdx.x;
+    for (uint32_t i = t; i < nwords; i += kT)
+        bitmap[i] = 0u;
+    if (lkeys) {
+        for (uint32_t base = 0; base < nb; base += kT * 4) {
+            uint32_t kk[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t e = base + q * kT + t;
+                kk[q] = a.keys[e < nb ? e : nb - 1];
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t e = base + q * kT + t;
+                if (e < nb)
+                    lkeys[e] = kk[q];
+            }
+        }
+    }
+    __syncthreads();
+    auto each_key = [&](auto f) {
+        if (lkeys) {
+            for (uint32_t e = t; e < nb; e += kT)
+                f(comp_key(lkeys[e], e));
+            return;
+        }
+        for (uint32_t base = 0; base < nb; base += kT * 8) {
+            uint32_t kk[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const uint32_t e = base + q * kT + t;
+                kk[q] = a.keys[e < nb ? e : nb - 1];
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const uint32_t e = base + q * kT + t;
+                if (e < nb)
+                    f(comp_key(kk[q], e));
+            }
+        }
+    };
+    refine_and_mark(sm, each_key, [&](uint64_t c) {
+        const uint32_t id = ~(uint32_t)c;
+        atomicOr(&bitmap[id >> 5], 1u << (id & 31));
+    }, k);
+    __syncthreads();
+    const uint32_t per = (nwords + kT - 1) / kT;
+    const uint32_t w0 = t * per;
+    const uint32_t w1 = w0 + per < nwords ? w0 + per : nwords;
+    uint32_t c = 0;
+    for (uint32_t w = w0; w < w1; ++w)
+        c += (uint32_t)__popc(bitmap[w]);
+    uint32_t o = block_excl_scan(c, sm, nullptr);
+    for (uint32_t w = w0; w < w1; ++w) {
+        uint32_t bits = bitmap[w];
+        while (bits) {
+            const int b = __ffs(bits) - 1;
+            bits &= bits - 1;
+            if (o < k)
+                emit(o, w * 32 + (uint32_t)b);
+            ++o;
+        }
+    }
+}
+
 // ------------------------------------------------------------------ routine
 
 // Whole workgroup (kT threads) calls; `lds` holds lds_bytes(a.nb) bytes.
@@ -257,17 +333,23 @@ __device__ void run(const SelectArgs &a, char *lds, Emit emit)
     }
 
     // chunks t + 1024q of U (2 composites each), all loads in flight together
+    // (no lists: the general path over the keys)
+    general = general || !a.lists;
     uint64_t u[kEntries];
-    {
+    if (!general) {
         const uint4 *src = reinterpret_cast<const uint4 *>(a.lists);
 #pragma unroll
         for (int q = 0; q < kChunks; ++q) {
             const uint32_t c = (uint32_t)t + (uint32_t)(kT * q);
             const uint4 v = src[c < nchunks ? c : nchunks - 1];
-            const bool in = !general && c < nchunks;
+            const bool in = c < nchunks;
             u[2 * q] = in ? ((uint64_t)v.y << 32) | v.x : 0ull;
             u[2 * q + 1] = in ? ((uint64_t)v.w << 32) | v.z : 0ull;
         }
+    } else {
+#pragma unroll
+        for (int e = 0; e < kEntries; ++e)
+            u[e] = 0ull;
     }
     // 1. key range of the listed entries (an empty slot has key 0: it wraps
     //    to the top in key - 1 and is the bottom for the maximum)
@@ -434,47 +516,7 @@ __device__ void run(const SelectArgs &a, char *lds, Emit emit)
 
     // ---------------------------------------------------------- general path
     __syncthreads();
-    for (uint32_t i = t; i < nwords; i += kT)
-        bitmap[i] = 0u;
-    __syncthreads();
-    auto each_key = [&](auto f) {
-        for (uint32_t base = 0; base < nb; base += kT * 8) {
-            uint32_t kk[8];
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const uint32_t e = base + q * kT + t;
-                kk[q] = a.keys[e < nb ? e : nb - 1];
-            }
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const uint32_t e = base + q * kT + t;
-                if (e < nb)
-                    f(comp_key(kk[q], e));
-            }
-        }
-    };
-    refine_and_mark(sm, each_key, [&](uint64_t c) {
-        const uint32_t id = ~(uint32_t)c;
-        atomicOr(&bitmap[id >> 5], 1u << (id & 31));
-    }, k);
-    __syncthreads();
-    const uint32_t per = (nwords + kT - 1) / kT;
-    const uint32_t w0 = t * per;
-    const uint32_t w1 = w0 + per < nwords ? w0 + per : nwords;
-    uint32_t c = 0;
-    for (uint32_t w = w0; w < w1; ++w)
-        c += (uint32_t)__popc(bitmap[w]);
-    uint32_t o = block_excl_scan(c, sm, nullptr);
-    for (uint32_t w = w0; w < w1; ++w) {
-        uint32_t bits = bitmap[w];
-        while (bits) {
-            const int b = __ffs(bits) - 1;
-            bits &= bits - 1;
-            if (o < k)
-                emit(o, w * 32 + (uint32_t)b);
-            ++o;
-        }
-    }
+    general_path(a, sm, bitmap, nullptr, emit);
 }
 
 }  // namespace sel

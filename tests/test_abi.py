@@ -138,3 +138,30 @@ def test_state_invalidate_and_truncate():
     assert (st.n_tokens, st.n_valid_blocks) == (601, 150)
     qsa.qsa_state_truncate(st, -5)
     assert (st.n_tokens, st.n_valid_blocks) == (0, 0)
+
+
+def test_chunk_argument_errors_before_launch():
+    qsa, d, c = _objs()
+    L = qsa.lib()
+    P = ctypes.c_void_p
+    D = ctypes.byref(d)
+    one = qsa.qsa_chunk_workspace_bytes(d, 4096, 64)
+    assert one > 0 and qsa.qsa_chunk_workspace_bytes(d, 4096, 1024) > one
+    assert qsa.qsa_chunk_workspace_bytes(d, 4096, 0) == 0
+    assert qsa.qsa_chunk_workspace_bytes(d, 4096, qsa.QSA_MAX_CHUNK + 1) == 0
+    assert qsa.qsa_chunk_workspace_bytes(d, 4094, 16) == 0
+
+    def call(st, n_q, q=16, ws_bytes=1 << 40, gamma=16):
+        return L.qsa_chunk_step(D, ctypes.byref(c), ctypes.byref(st), n_q, P(16), P(16), P(16),
+                                P(gamma) if gamma else None, P(16), P(16), P(q), P(16), None, None,
+                                P(256), ws_bytes, None)
+
+    st = qsa.qsa_seq_state(4000, 1000)
+    assert call(st, 0) == -1
+    assert call(st, qsa.QSA_MAX_CHUNK + 1) == -1
+    assert call(st, 97) == -1                       # 4000 + 97 > capacity 4096
+    assert b"outside" in L.qsa_last_error()
+    assert call(st, 16, q=8) == -1                  # q must be 16-byte aligned
+    assert call(st, 16, gamma=0) == -1
+    assert call(st, 16, ws_bytes=100) == -3
+    assert (st.n_tokens, st.n_valid_blocks) == (4000, 1000)
