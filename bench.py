@@ -13,6 +13,9 @@ Prints ONE JSON line.  `value` is QSA-layer decode steps per second.
 `roofline` is for the dominant kernel (the block-score stream), timed with HIP
 events around passes of back-to-back launches on the stream it runs on.  `cpu_baseline` times
 the CPU oracle on a bounded sample of the same workload (rank 0, N = 1 only).
+`batch_and_chunk` (after the headline, outside its timed region): batched
+decode of 8 sequences of mixed context in one call per step, and one prefill
+chunk of 1024 tokens at 126,253 tokens of context, on the same layer shapes.
 """
 import argparse
 import hashlib
@@ -106,6 +109,133 @@ def cpu_baseline(w, n_steps):
 
 
 TRAFFIC_COPY_MB = 256
+MFMA_F16_PEAK_TFLOPS = 2500.0      # MI355X dense f16 matrix-core peak
+
+
+def chunk_bytes(w, n_q):
+    """Algorithmic HBM bytes of a prefill chunk: appended rows, the blocks it
+    pools, one read of every summary, and each query's gathered K/V rows."""
+    idx_row = w.idx_heads * w.idx_dim * (2 if w.idx_f16 else 4)
+    kv_row = w.kv_heads * w.head_dim * 2
+    nb_last = (w.n0 + n_q) // 4
+    new_blocks = nb_last - w.n0 // 4
+    gathered = 0
+    for i in range(n_q):
+        n = w.n0 + i + 1
+        gathered += 2 * kv_row * (4 * min(w.k_blocks, n // 4) + n % 4)
+    queries = 4 * n_q * (w.idx_heads * w.idx_dim + w.idx_heads + 2 * w.q_heads * w.head_dim)
+    return n_q * (idx_row + 2 * kv_row) + 5 * idx_row * new_blocks + idx_row * nb_last + gathered + queries
+
+
+def chunk_flops(w, n_q):
+    """Matrix-core flops of the chunk's score GEMM as run: every query against
+    every block (the causal mask is applied in the epilogue), both f16 halves
+    of the query."""
+    nb_last = (w.n0 + n_q) // 4
+    return 2 * 2 * n_q * nb_last * w.idx_heads * w.idx_dim
+
+
+def bench_batch_and_chunk(args, torch, qsa, W, stream, dev):
+    """Batched decode of 8 mixed-context sequences, and one 1024-token prefill
+    chunk at 128k, on the headline layer shapes."""
+    import ctypes
+    import dataclasses
+    lib = qsa.lib()
+    res = {}
+
+    # ---- batched decode
+    base = W.BATCH
+    total = args.batch_warmup + args.batch_steps
+    desc = qsa.make_desc(base.idx_heads, base.idx_dim, qsa.QSA_F16, base.q_heads, base.kv_heads,
+                         base.head_dim, base.top_k_tokens, base.rms_eps, base.rope_theta)
+    seqs = []
+    gamma = W.dev_gamma(base, 0)
+    for i, n0 in enumerate(W.BATCH_CONTEXTS):
+        w = dataclasses.replace(base, n0=n0, steps=total)
+        buf = qsa.LayerBuffers(desc, w.capacity())
+        W.dev_fill_layer_(w, buf, 0, n0, seq=i)
+        qsa.qsa_cache_update(desc, buf.cache, gamma, 0, n0 // 4)
+        seqs.append({"w": w, "buf": buf, "inp": W.dev_step_inputs(w, 0, 0, total, seq=i),
+                     "out": torch.empty((w.q_heads, w.head_dim), dtype=torch.float32, device=dev)})
+    n = len(seqs)
+    ws = qsa.batch_workspace(desc, [x["w"].capacity() for x in seqs])
+    c_arr = (qsa.qsa_layer_cache * n)(*[x["buf"].cache for x in seqs])
+    s_arr = (qsa.qsa_seq_state * n)(*[qsa.qsa_seq_state(x["w"].n0, x["w"].n0 // 4) for x in seqs])
+    io = []
+    for st in range(total):      # marshalled ahead: the timed loop only calls the library
+        io.append((qsa.qsa_seq_io * n)(*[qsa.qsa_seq_io(
+            x["inp"].raw[st].data_ptr(), x["inp"].k[st].data_ptr(), x["inp"].v[st].data_ptr(),
+            x["inp"].q_idx[st].data_ptr(), x["inp"].w[st].data_ptr(), x["inp"].q[st].data_ptr(),
+            x["out"].data_ptr(), None) for x in seqs]))
+    D = ctypes.byref(desc)
+    g = ctypes.c_void_p(gamma.data_ptr())
+    wp, wn = ctypes.c_void_p(ws.data_ptr()), ws.numel()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def bstep(st):
+        r = lib.qsa_decode_step_batch(D, n, c_arr, s_arr, io[st], g, wp, wn, sp)
+        if r != 0:
+            raise qsa.QSAError(r, lib.qsa_last_error().decode())
+
+    torch.cuda.synchronize()
+    for st in range(args.batch_warmup):
+        bstep(st)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    nbytes = 0
+    e0.record(stream)
+    for i in range(args.batch_steps):
+        for j, x in enumerate(seqs):
+            nbytes += layer_step_bytes(x["w"], s_arr[j].n_tokens + 1)
+        bstep(args.batch_warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    per = ms / args.batch_steps
+    gbs = nbytes / (ms / 1e3) / 1e9
+    log(f"batched decode: {per * 1e3:.1f} us per step of {n} sequences, {gbs:.0f} GB/s")
+    res["batch_decode"] = {
+        "workload": base.name, "contexts": list(W.BATCH_CONTEXTS), "steps": args.batch_steps,
+        "warmup": args.batch_warmup, "us_per_batched_step": round(1e3 * per, 2),
+        "tokens_per_s": round(n / (per / 1e3), 1),
+        "hbm": {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_step": round(nbytes / args.batch_steps)}}
+    del seqs, ws, io
+    torch.cuda.empty_cache()
+
+    # ---- prefill chunk
+    w = W.CHUNK128K
+    n_q = w.steps
+    cdesc = qsa.make_desc(w.idx_heads, w.idx_dim, qsa.QSA_F16, w.q_heads, w.kv_heads, w.head_dim,
+                          w.top_k_tokens, w.rms_eps, w.rope_theta)
+    buf = qsa.LayerBuffers(cdesc, w.capacity())
+    W.dev_fill_layer_(w, buf, 0, w.n0)
+    cg = W.dev_gamma(w, 0)
+    qsa.qsa_cache_update(cdesc, buf.cache, cg, 0, w.n0 // 4)
+    inp = W.dev_step_inputs(w, 0, 0, n_q)
+    out = torch.empty((n_q, w.q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    cws = qsa.chunk_workspace(cdesc, w.capacity(), n_q)
+    state = qsa.qsa_seq_state(w.n0, w.n0 // 4)
+    times = []
+    for rep in range(args.chunk_reps + 1):
+        qsa.qsa_state_truncate(state, w.n0)      # the same chunk again: re-append, re-pool
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        qsa.qsa_chunk_step(cdesc, buf.cache, state, n_q, inp.raw, inp.k, inp.v, cg, inp.q_idx, inp.w,
+                           inp.q, out, None, None, cws, stream)
+        b.record(stream)
+        times.append((a, b))
+    torch.cuda.synchronize()
+    cms = [a.elapsed_time(b) for a, b in times[1:]]
+    c_ms = statistics.median(cms)
+    cb = chunk_bytes(w, n_q)
+    log(f"prefill chunk: {c_ms:.3f} ms for {n_q} tokens at n0={w.n0}")
+    res["chunk"] = {
+        "workload": w.name, "n0": w.n0, "n_q": n_q, "reps": args.chunk_reps,
+        "ms": round(c_ms, 4), "tokens_per_s": round(n_q / (c_ms / 1e3), 1),
+        "algorithmic_gbs": round(cb / (c_ms / 1e3) / 1e9, 1), "bytes": cb,
+        "score_gemm_flops": chunk_flops(w, n_q), "mfma_f16_peak_tflops": MFMA_F16_PEAK_TFLOPS}
+    return res
 
 
 def traffic_run(args):
@@ -197,6 +327,11 @@ def main():
     ap.add_argument("--cpu-steps", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=8, help="score-kernel timing passes")
+    ap.add_argument("--no-batch", action="store_true", help="skip the batched-decode / chunk leg")
+    ap.add_argument("--batch-steps", type=int, default=48)
+    ap.add_argument("--batch-warmup", type=int, default=4)
+    ap.add_argument("--chunk-reps", type=int, default=5)
+    ap.add_argument("--batch-only", action="store_true", help="only the batched-decode / chunk leg")
     ap.add_argument("--traffic-run", action="store_true",
                     help="only launch the score kernel and a plain copy (for rocprofv3 --pmc)")
     ap.add_argument("--traffic-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -216,6 +351,13 @@ def main():
     import torch
     import sparse_attention_decode_cache_amd as qsa
     from qsagen import workloads as W
+
+    if args.batch_only:
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        print(json.dumps(bench_batch_and_chunk(args, torch, qsa, W, torch.cuda.current_stream(), dev)),
+              flush=True)
+        return
 
     w0 = W.WORKLOADS[args.workload]
     total = args.warmup + args.steps
@@ -327,7 +469,12 @@ def main():
                      "traffic": traffic, "bytes_per_launch": kbytes,
                      "avg_launch_us": round(1e6 * k_avg_s, 3)},
         "cpu_baseline": None,
+        "batch_and_chunk": None,
     }
+    if not args.no_batch:
+        del layers, ws
+        torch.cuda.empty_cache()
+        result["batch_and_chunk"] = bench_batch_and_chunk(args, torch, qsa, W, stream, dev)
     if not args.no_cpu_baseline:
         log("cpu baseline ...")
         result["cpu_baseline"] = cpu_baseline(w0, args.cpu_steps)

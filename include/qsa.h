@@ -241,7 +241,7 @@ qsa_status qsa_decode_step_batch(const qsa_layer_desc *desc, int32_t n_seq,
  * idx_k_rows: DEVICE [n_q][H_i][D_i] idx_dtype; k_rows, v_rows: DEVICE
  * [n_q][Hkv][Dh] binary16; q_idx: DEVICE fp32 [n_q][H_i][D_i]; w: DEVICE fp32
  * [n_q][H_i]; q: DEVICE fp32 [n_q][Hq][Dh]; out: DEVICE fp32 [n_q][Hq][Dh].
- * Rows, q_idx and q 16-byte aligned.  sel_out (optional, DEVICE int32
+ * Rows, q_idx, q and out 16-byte aligned.  sel_out (optional, DEVICE int32
  * [n_q][K]): row i gets the min(K, floor(n_i/4)) chosen ids ascending, then
  * -1.  scores_out (optional, DEVICE fp32 [n_q][nb_last], nb_last =
  * floor((pos_0 + n_q) / 4)): written only when some query has more than K

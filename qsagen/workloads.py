@@ -64,6 +64,13 @@ CTX128K = Workload("qsa-128k", 2, 1, 126253, 128, 4, 128, True, 16, 2, 256, 2048
 CTX256K = Workload("qsa-256k-12layers", 3, 12, 255181, 64, 4, 128, True, 16, 2, 256, 2048)
 WORKLOADS = {w.name: w for w in (TINY, CTX64K, CTX128K, CTX256K)}
 
+# Batched decode + prefill chunk, same layer shapes: eight sequences of mixed
+# context (16k / 32k / 64k / 128k / 256k inputs, the last three repeated), and
+# one 1024-token chunk (the post's ubatch size) at the 128k input size.
+BATCH_CONTEXTS = (16381, 29453, 61789, 126253, 255181, 16381, 29453, 61789)
+BATCH = Workload("qsa-batch8-mixed", 4, 1, 16381, 64, 4, 128, True, 16, 2, 256, 2048)
+CHUNK128K = Workload("qsa-chunk1024-128k", 5, 1, 126253, 1024, 4, 128, True, 16, 2, 256, 2048)
+
 
 def ids(layer, seq=0):
     return {k: tensor_id(k, layer=layer, seq=seq) for k in (KIND_RAW, KIND_K, KIND_V, KIND_GAMMA)}

@@ -19,6 +19,8 @@
 //           path over the split's 16-cell tiles, folded into a running
 //           (max, sum, acc) in registers; with one split the output is
 //           written directly, otherwise a small merge follows.
+#include <type_traits>
+
 #include "qsa_attend.h"
 #include "qsa_internal.h"
 #include "qsa_select.h"
@@ -282,14 +284,80 @@ __global__ __launch_bounds__(sel::kT) void k_chunk_select(ChunkArgs c)
 }
 
 // ----------------------------------------------------------------- attend
+//
+// Workgroup (query, split, KV head), 1024 threads, 64 cells per iteration.
+// Every thread loads K and V chunks of the iteration (coalesced: consecutive
+// threads read consecutive 16 bytes of a row) ahead of use -- K one
+// iteration, V two (double-buffered registers) where the registers allow;
+// K goes to an LDS tile, where waves 0-3 take the
+// 64 x G logits on the matrix cores (q as two f16 halves); waves h < G run
+// the online softmax of head h over the 64 cells; each thread then adds the
+// G x 8 products of its own V chunks to accumulators it keeps for the whole
+// split.  The accumulators of threads sharing a chunk are summed once at the
+// end (xor shuffles in the wave, a fixed tree over the waves).
+
+constexpr int kCI = 64;                      // cells per iteration
+
+// Up to two 16-byte registers named at compile time (arrays indexed in a
+// loop that spans the iteration loop end up in scratch memory).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+struct Regs2 {
+    u32x4 x0, x1;
+    template <int R>
+    __device__ __forceinline__ u32x4 &at()
+    {
+        if constexpr (R == 0)
+            return x0;
+        else
+            return x1;
+    }
+};
+
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (N > 0) {
+        static_for<N - 1>(f);
+        f(std::integral_constant<int, N - 1>{});
+    }
+}
+
+template <int DH, int G>
+struct CAShape {
+    static constexpr int CH = DH / 8;                     // 16-byte chunks of a row
+    static constexpr int PAIRS = kCI * CH;                // (cell, chunk) pairs of an iteration
+    static constexpr int LR = (PAIRS + kAT - 1) / kAT;    // pairs per thread
+    static constexpr int KS = DH / 32;                    // MFMA k-steps of a row
+    static constexpr int KROW = 2 * DH + 16;              // padded LDS bytes of a K row
+    static constexpr int LPW = CH < kWave ? CH : kWave;   // lanes holding distinct chunks
+    static constexpr int GP = G < 4 ? 4 : G;
+    // V two iterations ahead (double-buffered) unless the accumulators of 8
+    // heads leave no room: then one ahead, like K
+    static constexpr int VAHEAD = (G == 8 && LR == 2) ? 1 : 2;
+    static_assert(kAT % CH == 0 && PAIRS % kWave == 0 && LR <= 2, "shape");
+};
+
+template <int DH, int G>
+struct CALds {
+    using S = CAShape<DH, G>;
+    alignas(16) unsigned char ktile[kCI * S::KROW];
+    alignas(16) uint4 qb[S::KS][2][kWave];
+    float lg[kCI][G + 1];
+    alignas(16) float p[kCI][S::GP];
+    float sc[G], mrow[G], lrow[G];
+    int32_t ids[kChunkMaxIds];
+    alignas(16) float red[8 * G * 8 * S::LPW];
+};
 
 template <int DH, int G>
 __global__ __launch_bounds__(kAT) void k_chunk_attend(ChunkArgs c)
 {
-    __shared__ AttLds<DH, G> L;
-    __shared__ int32_t ids[kChunkMaxIds];
-    constexpr int R = (G * DH + kAT - 1) / kAT;
-    const int t = threadIdx.x;
+    using S = CAShape<DH, G>;
+    constexpr int CH = S::CH, LR = S::LR, KS = S::KS, KROW = S::KROW, LPW = S::LPW;
+    extern __shared__ uint4 ca_lds[];
+    CALds<DH, G> &L = *reinterpret_cast<CALds<DH, G> *>(ca_lds);
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int ns = c.n_split;
     const int i = blockIdx.x / ns, s = blockIdx.x % ns, g = blockIdx.y;
     const int64_t n = (int64_t)c.n0 + i + 1;
@@ -297,75 +365,235 @@ __global__ __launch_bounds__(kAT) void k_chunk_attend(ChunkArgs c)
     const bool keep_all = nbq <= c.kb;
     const int32_t nsel = keep_all ? nbq : c.kb;
     const int32_t ncells = 4 * nsel + (int32_t)(n & 3);
-    const int32_t ntiles = (ncells + kCells - 1) / kCells;
-    const int32_t tps = (ntiles + ns - 1) / ns;
-    const int32_t j0 = s * tps, j1 = j0 + tps < ntiles ? j0 + tps : ntiles;
-    // the split's block ids
-    const int32_t id0 = 4 * j0, id1 = 4 * j1 < nsel ? 4 * j1 : nsel;
+    const int32_t nit = (ncells + kCI - 1) / kCI;
+    const int32_t ipw = (nit + ns - 1) / ns;
+    const int32_t it0 = s * ipw, it1 = it0 + ipw < nit ? it0 + ipw : nit;
+    // the split's block ids (16 per iteration)
+    const int32_t id0 = (kCI / 4) * it0;
+    const int32_t id1 = (kCI / 4) * it1 < nsel ? (kCI / 4) * it1 : nsel;
     const int32_t *srow = c.sel + (size_t)i * c.kb;
     for (int x = id0 + t; x < id1; x += kAT)
-        ids[x - id0] = keep_all ? x : srow[x];
+        L.ids[x - id0] = keep_all ? x : srow[x];
+    // q as the B operand of the logit MFMA: lane l of k-step ks holds
+    // q[head l % 16][32 ks + 8 (l / 16) .. +8] (zero past G), hi and lo
+    const float *qg = c.q + ((size_t)i * c.kv_heads + g) * G * DH;
+    for (int x = t; x < KS * kWave; x += kAT) {
+        const int ks = x / kWave, l = x % kWave, h = l % 16, d0 = 32 * ks + 8 * (l / 16);
+        half8 hi, lo;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float v = h < G ? qg[h * DH + d0 + j] : 0.0f;
+            hi[j] = (_Float16)v;
+            lo[j] = (_Float16)(v - (float)hi[j]);
+        }
+        __builtin_memcpy(&L.qb[ks][0][l], &hi, 16);
+        __builtin_memcpy(&L.qb[ks][1][l], &lo, 16);
+    }
     __syncthreads();
 
-    AttendArgs a{};
-    a.k = c.k;
-    a.v = c.v;
-    a.q = c.q + (size_t)i * c.kv_heads * G * DH;
-    a.n_sel_blocks = nsel;
-    a.nb = nbq;
-    a.n_cells = ncells;
-    a.kv_heads = c.kv_heads;
-    a.scale = c.scale;
+    // Row of local cell lc of iteration it; invalid cells read row 0, masked.
+    auto cell_row = [&](int it, int lc, bool &valid) __attribute__((always_inline)) -> size_t {
+        const int32_t e = kCI * it + lc;
+        valid = e < ncells;
+        int64_t cell;
+        if (e < 4 * nsel) {
+            const int32_t b = L.ids[(e >> 2) - id0];
+            valid = valid && (uint32_t)b < (uint32_t)nbq;
+            cell = 4 * (int64_t)b + (e & 3);
+        } else {
+            cell = 4 * (int64_t)nbq + (e - 4 * nsel);
+        }
+        return valid ? (size_t)cell : 0;
+    };
+    auto row_off = [&](int it, int r) __attribute__((always_inline)) -> size_t {
+        const int pr = t + kAT * r;
+        bool v;
+        const size_t row = cell_row(it, pr / CH, v);
+        return (row * c.kv_heads + g) * DH + 8 * (pr % CH);
+    };
+    auto load_k = [&](int it, Regs2 &kr) __attribute__((always_inline)) {
+        static_for<LR>([&](auto rc) __attribute__((always_inline)) {
+            constexpr int r = decltype(rc)::value;
+            if (t + kAT * r < S::PAIRS)
+                kr.template at<r>() = *(const u32x4 *)(c.k + row_off(it, r));
+        });
+    };
+    auto load_v = [&](int it, Regs2 &vr) __attribute__((always_inline)) {
+        static_for<LR>([&](auto rc) __attribute__((always_inline)) {
+            constexpr int r = decltype(rc)::value;
+            if (t + kAT * r < S::PAIRS)
+                vr.template at<r>() = *(const u32x4 *)(c.v + row_off(it, r));
+        });
+    };
 
-    float m_r[R], l_r[R], acc_r[R];
+    float acc[G][8];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        m_r[r] = -INFINITY;
-        l_r[r] = 0.0f;
-        acc_r[r] = 0.0f;
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            acc[h][j] = 0.0f;
+    float m_run = -INFINITY, l_run = 0.0f;          // wave h < G: head h
+    // K one iteration ahead (it leaves the registers for LDS first thing),
+    // V VAHEAD iterations ahead
+    constexpr int VA = S::VAHEAD;
+    Regs2 kA{}, vA{}, vB{};
+    if (it0 < it1) {
+        load_k(it0, kA);
+        load_v(it0, vA);
     }
-    for (int32_t j = j0; j < j1; ++j) {
-        attend_tile<DH, G>(a, L, ids + 4 * (j - j0), kCells * j, g, [&](AttLds<DH, G> &T) {
+    if (VA == 2 && it0 + 1 < it1)
+        load_v(it0 + 1, vB);
+
+    auto body = [&](int it, Regs2 &kr, Regs2 &vr) __attribute__((always_inline)) {
+        static_for<LR>([&](auto rc) __attribute__((always_inline)) {
+            constexpr int r = decltype(rc)::value;
+            const int pr = t + kAT * r;
+            if (pr < S::PAIRS)
+                *(u32x4 *)(L.ktile + (pr / CH) * KROW + 16 * (pr % CH)) = kr.template at<r>();
+        });
+        if (it + 1 < it1)
+            load_k(it + 1, kr);
+        __syncthreads();
+        if (wave < kCI / 16) {
+            // D[cell][head] = K[cell][:] . q[head][:], 16 cells per wave
+            const int mc = lane & 15, kg = lane >> 4;
+            float4v d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const int idx = t + kAT * r;
-                if (idx < G * DH) {
-                    const int h = idx / DH;
-                    const float mt = T.m[h], lt = T.l[h];
-                    const float at = tile_acc<DH, G>(T, idx);
-                    const float mn = fmaxf(m_r[r], mt);
-                    if (mn != -INFINITY) {
-                        const float wr = m_r[r] == -INFINITY ? 0.0f : expf(m_r[r] - mn);
-                        const float wt = mt == -INFINITY ? 0.0f : expf(mt - mn);
-                        acc_r[r] = acc_r[r] * wr + at * wt;
-                        l_r[r] = l_r[r] * wr + lt * wt;
-                        m_r[r] = mn;
-                    }
+            for (int ks = 0; ks < KS; ++ks) {
+                half8 a, bh, bl;
+                __builtin_memcpy(&a, L.ktile + (16 * wave + mc) * KROW + 2 * (32 * ks + 8 * kg), 16);
+                __builtin_memcpy(&bh, &L.qb[ks][0][lane], 16);
+                __builtin_memcpy(&bl, &L.qb[ks][1][lane], 16);
+                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bh, d, 0, 0, 0);
+                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bl, d, 0, 0, 0);
+            }
+            if (mc < G) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int lc = 16 * wave + 4 * kg + j;
+                    bool v;
+                    (void)cell_row(it, lc, v);
+                    L.lg[lc][mc] = v ? c.scale * d[j] : -INFINITY;
                 }
             }
+        }
+        __syncthreads();
+        if (wave < G) {
+            // online softmax of head `wave` over the 64 cells (lane = cell)
+            const float x = L.lg[lane][wave];
+            const float mn = fmaxf(m_run, wave::reduce_max_f(x));
+            float sc = 1.0f, pv = 0.0f;
+            if (mn != -INFINITY) {
+                sc = m_run == -INFINITY ? 0.0f : expf(m_run - mn);
+                pv = x == -INFINITY ? 0.0f : expf(x - mn);
+            }
+            l_run = l_run * sc + wave::reduce_add_f(pv);
+            m_run = mn;
+            L.p[lane][wave] = pv;
+            if (lane == 0)
+                L.sc[wave] = sc;
+        }
+        __syncthreads();
+        float scv[G];
+        bool any = false;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            scv[h] = L.sc[h];
+            any = any || scv[h] != 1.0f;
+        }
+        if (any) {
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    acc[h][j] *= scv[h];
+        }
+        static_for<LR>([&](auto rc) __attribute__((always_inline)) {
+            constexpr int r = decltype(rc)::value;
+            const int pr = t + kAT * r;
+            if (pr < S::PAIRS) {
+                const int lc = pr / CH;
+                float ph[G];
+#pragma unroll
+                for (int h = 0; h < G; ++h)
+                    ph[h] = L.p[lc][h];
+                half8 vh;
+                __builtin_memcpy(&vh, &vr.template at<r>(), 16);
+#pragma unroll
+                for (int h = 0; h < G; ++h)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        acc[h][j] = fmaf(ph[h], (float)vh[j], acc[h][j]);
+            }
         });
+        if (it + VA < it1)
+            load_v(it + VA, vr);
+    };
+
+    for (int32_t it = it0; it < it1; ++it) {
+        body(it, kA, vA);              // reloads kA with iteration it + 1, vA with it + VA
+        if constexpr (VA == 2) {
+            const Regs2 tv = vA;
+            vA = vB;
+            vB = tv;
+        }
     }
 
-    const size_t ob = (size_t)i * c.kv_heads * G * DH + (size_t)g * G * DH;
-    if (ns == 1) {
+    if (wave < G && lane == 0) {
+        L.mrow[wave] = m_run;
+        L.lrow[wave] = l_run;
+    }
+    // sum over the threads of a chunk: lanes l ^ CH, l ^ 2CH, ... in the wave,
+    // then a fixed tree over the 16 waves
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const int idx = t + kAT * r;
-            if (idx < G * DH)
-                c.out[ob + idx] = acc_r[r] / l_r[r];
+    for (int off = CH; off < kWave; off <<= 1)
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc[h][j] += __shfl_xor(acc[h][j], off);
+#pragma unroll
+    for (int half = kAT / kWave / 2; half >= 1; half >>= 1) {
+        if (wave >= half && wave < 2 * half && lane < LPW) {
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    L.red[((wave - half) * G * 8 + h * 8 + j) * LPW + lane] = acc[h][j];
+        }
+        __syncthreads();
+        if (wave < half && lane < LPW) {
+#pragma unroll
+            for (int h = 0; h < G; ++h)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    acc[h][j] += L.red[(wave * G * 8 + h * 8 + j) * LPW + lane];
+        }
+        __syncthreads();
+    }
+    if (wave != 0 || lane >= LPW)
+        return;
+    const int k8 = 8 * lane;                       // this lane's 8 dims
+    if (ns == 1) {
+        float *o = c.out + ((size_t)i * c.kv_heads + g) * G * DH;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float l = L.lrow[h];
+            float4 *dst = (float4 *)(o + h * DH + k8);
+            dst[0] = make_float4(acc[h][0] / l, acc[h][1] / l, acc[h][2] / l, acc[h][3] / l);
+            dst[1] = make_float4(acc[h][4] / l, acc[h][5] / l, acc[h][6] / l, acc[h][7] / l);
         }
         return;
     }
     float *part = c.part + (((size_t)i * c.kv_heads + g) * ns + s) * (size_t)part_stride(G, DH);
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int idx = t + kAT * r;
-        if (idx < G * DH) {
-            part[2 * G + idx] = acc_r[r];
-            if (idx % DH == 0) {
-                part[idx / DH] = m_r[r];
-                part[G + idx / DH] = l_r[r];
-            }
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)                // a partial's stride is not a multiple of 4
+            part[2 * G + h * DH + k8 + j] = acc[h][j];
+        if (lane == 0) {
+            part[h] = L.mrow[h];
+            part[G + h] = L.lrow[h];
         }
     }
 }
@@ -399,7 +627,14 @@ __global__ __launch_bounds__(256) void k_chunk_merge(ChunkArgs c)
 template <int DH, int G>
 hipError_t attend_go(const ChunkArgs &c, hipStream_t s)
 {
-    hipLaunchKernelGGL((k_chunk_attend<DH, G>), dim3(c.n_q * c.n_split, c.kv_heads), dim3(kAT), 0, s, c);
+    const size_t lds = sizeof(CALds<DH, G>);
+    if (lds > 64 * 1024) {
+        static hipError_t attr = hipFuncSetAttribute((const void *)k_chunk_attend<DH, G>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (attr != hipSuccess)
+            return attr;
+    }
+    hipLaunchKernelGGL((k_chunk_attend<DH, G>), dim3(c.n_q * c.n_split, c.kv_heads), dim3(kAT), lds, s, c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || c.n_split == 1)
         return e;

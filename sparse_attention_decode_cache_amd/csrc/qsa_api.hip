@@ -637,8 +637,8 @@ qsa_status qsa_chunk_step(const qsa_layer_desc *desc, const qsa_layer_cache *cac
     if (!idx_k_rows || !k_rows || !v_rows || !gamma || !q_idx || !w || !q || !out)
         return fail(QSA_ERR_ARG, "an input or output pointer is NULL");
     if (!aligned(idx_k_rows, 16) || !aligned(k_rows, 16) || !aligned(v_rows, 16) ||
-        !aligned(q_idx, 16) || !aligned(q, 16))
-        return fail(QSA_ERR_ARG, "row, q_idx or q pointer not 16-byte aligned");
+        !aligned(q_idx, 16) || !aligned(q, 16) || !aligned(out, 16))
+        return fail(QSA_ERR_ARG, "row, q_idx, q or out pointer not 16-byte aligned");
     const int32_t n0 = st->n_tokens;
     if (n0 < 0 || (int64_t)n0 + n_q > cache->capacity)
         return fail(QSA_ERR_ARG, "positions [%d, %lld) outside [0, %d)", n0,

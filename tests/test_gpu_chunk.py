@@ -167,3 +167,14 @@ def test_chunk_128k_1024_queries_sampled():
     nb_last = g.state.n_valid_blocks
     assert o.L.n // 4 == nb_last
     check_summaries(g.buf.summary[nb_last - 300:nb_last].cpu().numpy(), o.L.summary[nb_last - 300:nb_last])
+
+
+@pytest.mark.parametrize("q_heads,kv_heads,head_dim,n_q", [
+    (2, 2, 128, 21), (4, 2, 64, 37), (8, 2, 128, 19), (16, 2, 64, 23), (4, 4, 256, 17),
+    (2, 2, 64, 2), (16, 2, 128, 3)])
+def test_chunk_attention_shapes(q_heads, kv_heads, head_dim, n_q):
+    """GQA groups of 1, 2, 4 and 8 heads, head dims 64 / 128 / 256; the last two
+    cases have so few queries that each query is split and merged."""
+    base = with_size(W.CTX64K, q_heads=q_heads, kv_heads=kv_heads, head_dim=head_dim)
+    st = _run_full(base, 3001, n_q)
+    assert st["exact"] + st["threshold"] == n_q
