@@ -285,32 +285,40 @@ __global__ __launch_bounds__(sel::kT) void k_chunk_select(ChunkArgs c)
 
 // ----------------------------------------------------------------- attend
 //
-// Workgroup (query, split, KV head), 1024 threads, 64 cells per iteration.
-// Every thread loads K and V chunks of the iteration (coalesced: consecutive
-// threads read consecutive 16 bytes of a row) ahead of use -- K one
-// iteration, V two (double-buffered registers) where the registers allow;
-// K goes to an LDS tile, where waves 0-3 take the
+// Workgroup (query, split, KV head), 512 threads (two workgroups per CU, so
+// that one computes while the other waits), 64 cells per iteration.  Every
+// thread loads K and V chunks of the iteration (coalesced: consecutive
+// threads read consecutive bytes of a row) one iteration ahead; K goes to an
+// LDS tile, where waves 0-3 take the
 // 64 x G logits on the matrix cores (q as two f16 halves); waves h < G run
 // the online softmax of head h over the 64 cells; each thread then adds the
-// G x 8 products of its own V chunks to accumulators it keeps for the whole
-// split.  The accumulators of threads sharing a chunk are summed once at the
-// end (xor shuffles in the wave, a fixed tree over the waves).
+// G x 4 products of its own 8-byte V chunks to accumulators it keeps for the
+// whole split.  The accumulators of threads sharing a chunk are summed once
+// at the end (xor shuffles in the wave, a fixed tree over the waves).
 
 constexpr int kCI = 64;                      // cells per iteration
+constexpr int kCAT = 512;                    // threads (two workgroups share a CU)
+constexpr int kCAW = kCAT / kWave;
 
-// Up to two 16-byte registers named at compile time (arrays indexed in a
-// loop that spans the iteration loop end up in scratch memory).
+// Up to eight registers named at compile time (arrays indexed in a loop that
+// spans the iteration loop end up in scratch memory).
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-struct Regs2 {
-    u32x4 x0, x1;
+template <class T>
+struct Regs8 {
+    T x0, x1, x2, x3, x4, x5, x6, x7;
     template <int R>
-    __device__ __forceinline__ u32x4 &at()
+    __device__ __forceinline__ T &at()
     {
-        if constexpr (R == 0)
-            return x0;
-        else
-            return x1;
+        if constexpr (R == 0) return x0;
+        else if constexpr (R == 1) return x1;
+        else if constexpr (R == 2) return x2;
+        else if constexpr (R == 3) return x3;
+        else if constexpr (R == 4) return x4;
+        else if constexpr (R == 5) return x5;
+        else if constexpr (R == 6) return x6;
+        else return x7;
     }
 };
 
@@ -323,38 +331,44 @@ __device__ __forceinline__ void static_for(F &&f)
     }
 }
 
+// K moves in 16-byte chunks (to the LDS tile), V in 8-byte chunks (a thread
+// keeps 4 dims x G heads of accumulators).
 template <int DH, int G>
 struct CAShape {
-    static constexpr int CH = DH / 8;                     // 16-byte chunks of a row
-    static constexpr int PAIRS = kCI * CH;                // (cell, chunk) pairs of an iteration
-    static constexpr int LR = (PAIRS + kAT - 1) / kAT;    // pairs per thread
+    static constexpr int KCH = DH / 8;                    // 16-byte chunks of a K row
+    static constexpr int KPAIRS = kCI * KCH;
+    static constexpr int KR = (KPAIRS + kCAT - 1) / kCAT; // K chunks per thread
+    static constexpr int VCH = DH / 4;                    // 8-byte chunks of a V row
+    static constexpr int VPAIRS = kCI * VCH;
+    static constexpr int VR = (VPAIRS + kCAT - 1) / kCAT; // V chunks (cells) per thread
     static constexpr int KS = DH / 32;                    // MFMA k-steps of a row
     static constexpr int KROW = 2 * DH + 16;              // padded LDS bytes of a K row
-    static constexpr int LPW = CH < kWave ? CH : kWave;   // lanes holding distinct chunks
+    static constexpr int LPW = VCH < kWave ? VCH : kWave; // lanes holding distinct V chunks
     static constexpr int GP = G < 4 ? 4 : G;
-    // V two iterations ahead (double-buffered) unless the accumulators of 8
-    // heads leave no room: then one ahead, like K
-    static constexpr int VAHEAD = (G == 8 && LR == 2) ? 1 : 2;
-    static_assert(kAT % CH == 0 && PAIRS % kWave == 0 && LR <= 2, "shape");
+    static constexpr int RED = (kCAW / 2) * G * 4 * LPW;  // floats of the reduction tree
+    static_assert(kCAT % KCH == 0 && kCAT % VCH == 0 && KPAIRS % kWave == 0 && VPAIRS % kWave == 0 &&
+                  KR <= 8 && VR <= 8 && G <= kCAW && kCI / 16 <= kCAW, "shape");
 };
 
 template <int DH, int G>
 struct CALds {
     using S = CAShape<DH, G>;
-    alignas(16) unsigned char ktile[kCI * S::KROW];
+    // the K tile during the loop, the reduction tree after it
+    static constexpr int KT = kCI * S::KROW, RB = 4 * S::RED;
+    alignas(16) unsigned char ktile[KT > RB ? KT : RB];
     alignas(16) uint4 qb[S::KS][2][kWave];
     float lg[kCI][G + 1];
     alignas(16) float p[kCI][S::GP];
     float sc[G], mrow[G], lrow[G];
     int32_t ids[kChunkMaxIds];
-    alignas(16) float red[8 * G * 8 * S::LPW];
 };
 
 template <int DH, int G>
-__global__ __launch_bounds__(kAT) void k_chunk_attend(ChunkArgs c)
+__global__ __launch_bounds__(kCAT, 2) void k_chunk_attend(ChunkArgs c)
 {
     using S = CAShape<DH, G>;
-    constexpr int CH = S::CH, LR = S::LR, KS = S::KS, KROW = S::KROW, LPW = S::LPW;
+    constexpr int KCH = S::KCH, VCH = S::VCH, KR = S::KR, VR = S::VR, KS = S::KS, KROW = S::KROW,
+                  LPW = S::LPW;
     extern __shared__ uint4 ca_lds[];
     CALds<DH, G> &L = *reinterpret_cast<CALds<DH, G> *>(ca_lds);
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -372,19 +386,24 @@ __global__ __launch_bounds__(kAT) void k_chunk_attend(ChunkArgs c)
     const int32_t id0 = (kCI / 4) * it0;
     const int32_t id1 = (kCI / 4) * it1 < nsel ? (kCI / 4) * it1 : nsel;
     const int32_t *srow = c.sel + (size_t)i * c.kb;
-    for (int x = id0 + t; x < id1; x += kAT)
+    for (int x = id0 + t; x < id1; x += kCAT)
         L.ids[x - id0] = keep_all ? x : srow[x];
     // q as the B operand of the logit MFMA: lane l of k-step ks holds
     // q[head l % 16][32 ks + 8 (l / 16) .. +8] (zero past G), hi and lo
     const float *qg = c.q + ((size_t)i * c.kv_heads + g) * G * DH;
-    for (int x = t; x < KS * kWave; x += kAT) {
+    for (int x = t; x < KS * kWave; x += kCAT) {
         const int ks = x / kWave, l = x % kWave, h = l % 16, d0 = 32 * ks + 8 * (l / 16);
+        float4 u = make_float4(0.0f, 0.0f, 0.0f, 0.0f), v = u;
+        if (h < G) {
+            u = *(const float4 *)(qg + h * DH + d0);
+            v = *(const float4 *)(qg + h * DH + d0 + 4);
+        }
+        const float qf[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
         half8 hi, lo;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float v = h < G ? qg[h * DH + d0 + j] : 0.0f;
-            hi[j] = (_Float16)v;
-            lo[j] = (_Float16)(v - (float)hi[j]);
+            hi[j] = (_Float16)qf[j];
+            lo[j] = (_Float16)(qf[j] - (float)hi[j]);
         }
         __builtin_memcpy(&L.qb[ks][0][l], &hi, 16);
         __builtin_memcpy(&L.qb[ks][1][l], &lo, 16);
@@ -405,51 +424,49 @@ __global__ __launch_bounds__(kAT) void k_chunk_attend(ChunkArgs c)
         }
         return valid ? (size_t)cell : 0;
     };
-    auto row_off = [&](int it, int r) __attribute__((always_inline)) -> size_t {
-        const int pr = t + kAT * r;
+    auto row_base = [&](int it, int lc) __attribute__((always_inline)) -> size_t {
         bool v;
-        const size_t row = cell_row(it, pr / CH, v);
-        return (row * c.kv_heads + g) * DH + 8 * (pr % CH);
+        return (cell_row(it, lc, v) * c.kv_heads + g) * DH;
     };
-    auto load_k = [&](int it, Regs2 &kr) __attribute__((always_inline)) {
-        static_for<LR>([&](auto rc) __attribute__((always_inline)) {
+    auto load_k = [&](int it, Regs8<u32x4> &kr) __attribute__((always_inline)) {
+        static_for<KR>([&](auto rc) __attribute__((always_inline)) {
             constexpr int r = decltype(rc)::value;
-            if (t + kAT * r < S::PAIRS)
-                kr.template at<r>() = *(const u32x4 *)(c.k + row_off(it, r));
+            const int pr = t + kCAT * r;
+            if (pr < S::KPAIRS)
+                kr.template at<r>() = *(const u32x4 *)(c.k + row_base(it, pr / KCH) + 8 * (pr % KCH));
         });
     };
-    auto load_v = [&](int it, Regs2 &vr) __attribute__((always_inline)) {
-        static_for<LR>([&](auto rc) __attribute__((always_inline)) {
+    auto load_v = [&](int it, Regs8<u32x2> &vr) __attribute__((always_inline)) {
+        static_for<VR>([&](auto rc) __attribute__((always_inline)) {
             constexpr int r = decltype(rc)::value;
-            if (t + kAT * r < S::PAIRS)
-                vr.template at<r>() = *(const u32x4 *)(c.v + row_off(it, r));
+            const int pr = t + kCAT * r;
+            if (pr < S::VPAIRS)
+                vr.template at<r>() = *(const u32x2 *)(c.v + row_base(it, pr / VCH) + 4 * (pr % VCH));
         });
     };
 
-    float acc[G][8];
+    float acc[G][4];
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
+        for (int j = 0; j < 4; ++j)
             acc[h][j] = 0.0f;
     float m_run = -INFINITY, l_run = 0.0f;          // wave h < G: head h
-    // K one iteration ahead (it leaves the registers for LDS first thing),
-    // V VAHEAD iterations ahead
-    constexpr int VA = S::VAHEAD;
-    Regs2 kA{}, vA{}, vB{};
+    // K and V one iteration ahead (K leaves the registers for the LDS tile
+    // first thing, V after the products)
+    Regs8<u32x4> kr;
+    Regs8<u32x2> vr;
     if (it0 < it1) {
-        load_k(it0, kA);
-        load_v(it0, vA);
+        load_k(it0, kr);
+        load_v(it0, vr);
     }
-    if (VA == 2 && it0 + 1 < it1)
-        load_v(it0 + 1, vB);
 
-    auto body = [&](int it, Regs2 &kr, Regs2 &vr) __attribute__((always_inline)) {
-        static_for<LR>([&](auto rc) __attribute__((always_inline)) {
+    for (int32_t it = it0; it < it1; ++it) {
+        static_for<KR>([&](auto rc) __attribute__((always_inline)) {
             constexpr int r = decltype(rc)::value;
-            const int pr = t + kAT * r;
-            if (pr < S::PAIRS)
-                *(u32x4 *)(L.ktile + (pr / CH) * KROW + 16 * (pr % CH)) = kr.template at<r>();
+            const int pr = t + kCAT * r;
+            if (pr < S::KPAIRS)
+                *(u32x4 *)(L.ktile + (pr / KCH) * KROW + 16 * (pr % KCH)) = kr.template at<r>();
         });
         if (it + 1 < it1)
             load_k(it + 1, kr);
@@ -457,7 +474,7 @@ __global__ __launch_bounds__(kAT) void k_chunk_attend(ChunkArgs c)
         if (wave < kCI / 16) {
             // D[cell][head] = K[cell][:] . q[head][:], 16 cells per wave
             const int mc = lane & 15, kg = lane >> 4;
-            float4v d = {0.0f, 0.0f, 0.0f, 0.0f};
+            float4v d = {0.0f, 0.0f, 0.0f, 0.0f}, e = d;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 half8 a, bh, bl;
@@ -465,7 +482,7 @@ __global__ __launch_bounds__(kAT) void k_chunk_attend(ChunkArgs c)
                 __builtin_memcpy(&bh, &L.qb[ks][0][lane], 16);
                 __builtin_memcpy(&bl, &L.qb[ks][1][lane], 16);
                 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bh, d, 0, 0, 0);
-                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bl, d, 0, 0, 0);
+                e = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bl, e, 0, 0, 0);
             }
             if (mc < G) {
 #pragma unroll
@@ -473,7 +490,7 @@ __global__ __launch_bounds__(kAT) void k_chunk_attend(ChunkArgs c)
                     const int lc = 16 * wave + 4 * kg + j;
                     bool v;
                     (void)cell_row(it, lc, v);
-                    L.lg[lc][mc] = v ? c.scale * d[j] : -INFINITY;
+                    L.lg[lc][mc] = v ? c.scale * (d[j] + e[j]) : -INFINITY;
                 }
             }
         }
@@ -505,83 +522,74 @@ __global__ __launch_bounds__(kAT) void k_chunk_attend(ChunkArgs c)
 #pragma unroll
             for (int h = 0; h < G; ++h)
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
+                for (int j = 0; j < 4; ++j)
                     acc[h][j] *= scv[h];
         }
-        static_for<LR>([&](auto rc) __attribute__((always_inline)) {
+        static_for<VR>([&](auto rc) __attribute__((always_inline)) {
             constexpr int r = decltype(rc)::value;
-            const int pr = t + kAT * r;
-            if (pr < S::PAIRS) {
-                const int lc = pr / CH;
+            const int pr = t + kCAT * r;
+            if (pr < S::VPAIRS) {
+                const int lc = pr / VCH;
                 float ph[G];
 #pragma unroll
                 for (int h = 0; h < G; ++h)
                     ph[h] = L.p[lc][h];
-                half8 vh;
-                __builtin_memcpy(&vh, &vr.template at<r>(), 16);
+                _Float16 vh[4];
+                __builtin_memcpy(vh, &vr.template at<r>(), 8);
 #pragma unroll
                 for (int h = 0; h < G; ++h)
 #pragma unroll
-                    for (int j = 0; j < 8; ++j)
+                    for (int j = 0; j < 4; ++j)
                         acc[h][j] = fmaf(ph[h], (float)vh[j], acc[h][j]);
             }
         });
-        if (it + VA < it1)
-            load_v(it + VA, vr);
-    };
-
-    for (int32_t it = it0; it < it1; ++it) {
-        body(it, kA, vA);              // reloads kA with iteration it + 1, vA with it + VA
-        if constexpr (VA == 2) {
-            const Regs2 tv = vA;
-            vA = vB;
-            vB = tv;
-        }
+        if (it + 1 < it1)
+            load_v(it + 1, vr);
     }
 
     if (wave < G && lane == 0) {
         L.mrow[wave] = m_run;
         L.lrow[wave] = l_run;
     }
-    // sum over the threads of a chunk: lanes l ^ CH, l ^ 2CH, ... in the wave,
-    // then a fixed tree over the 16 waves
+    // sum over the threads of a V chunk: lanes l ^ VCH, l ^ 2 VCH, ... in the
+    // wave, then a fixed tree over the waves (in the K tile's LDS, free now:
+    // every wave has passed the last iteration's logit barrier)
 #pragma unroll
-    for (int off = CH; off < kWave; off <<= 1)
+    for (int off = VCH; off < kWave; off <<= 1)
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < 4; ++j)
                 acc[h][j] += __shfl_xor(acc[h][j], off);
+    float *red = reinterpret_cast<float *>(L.ktile);
 #pragma unroll
-    for (int half = kAT / kWave / 2; half >= 1; half >>= 1) {
+    for (int half = kCAW / 2; half >= 1; half >>= 1) {
         if (wave >= half && wave < 2 * half && lane < LPW) {
 #pragma unroll
             for (int h = 0; h < G; ++h)
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    L.red[((wave - half) * G * 8 + h * 8 + j) * LPW + lane] = acc[h][j];
+                for (int j = 0; j < 4; ++j)
+                    red[((wave - half) * G * 4 + h * 4 + j) * LPW + lane] = acc[h][j];
         }
         __syncthreads();
         if (wave < half && lane < LPW) {
 #pragma unroll
             for (int h = 0; h < G; ++h)
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    acc[h][j] += L.red[(wave * G * 8 + h * 8 + j) * LPW + lane];
+                for (int j = 0; j < 4; ++j)
+                    acc[h][j] += red[(wave * G * 4 + h * 4 + j) * LPW + lane];
         }
         __syncthreads();
     }
     if (wave != 0 || lane >= LPW)
         return;
-    const int k8 = 8 * lane;                       // this lane's 8 dims
+    const int k4 = 4 * lane;                       // this lane's 4 dims
     if (ns == 1) {
         float *o = c.out + ((size_t)i * c.kv_heads + g) * G * DH;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             const float l = L.lrow[h];
-            float4 *dst = (float4 *)(o + h * DH + k8);
-            dst[0] = make_float4(acc[h][0] / l, acc[h][1] / l, acc[h][2] / l, acc[h][3] / l);
-            dst[1] = make_float4(acc[h][4] / l, acc[h][5] / l, acc[h][6] / l, acc[h][7] / l);
+            *(float4 *)(o + h * DH + k4) = make_float4(acc[h][0] / l, acc[h][1] / l, acc[h][2] / l, acc[h][3] / l);
         }
         return;
     }
@@ -589,8 +597,8 @@ __global__ __launch_bounds__(kAT) void k_chunk_attend(ChunkArgs c)
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)                // a partial's stride is not a multiple of 4
-            part[2 * G + h * DH + k8 + j] = acc[h][j];
+        for (int j = 0; j < 4; ++j)                // a partial's stride is not a multiple of 4
+            part[2 * G + h * DH + k4 + j] = acc[h][j];
         if (lane == 0) {
             part[h] = L.mrow[h];
             part[G + h] = L.lrow[h];
@@ -634,7 +642,7 @@ hipError_t attend_go(const ChunkArgs &c, hipStream_t s)
         if (attr != hipSuccess)
             return attr;
     }
-    hipLaunchKernelGGL((k_chunk_attend<DH, G>), dim3(c.n_q * c.n_split, c.kv_heads), dim3(kAT), lds, s, c);
+    hipLaunchKernelGGL((k_chunk_attend<DH, G>), dim3(c.n_q * c.n_split, c.kv_heads), dim3(kCAT), lds, s, c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || c.n_split == 1)
         return e;
