@@ -13,8 +13,8 @@
 //   score   all queries x all blocks as one f16 MFMA GEMM (hi and lo both
 //           multiplied: the products are exact in fp32), epilogue: the
 //           order-preserving key of each score, 0 past the query's blocks;
-//   select  one workgroup per query: the exact radix top-k over its keys,
-//           held in registers;
+//   select  one workgroup per query: the exact top-k over its keys, held
+//           in LDS (a linear histogram, then the boundary bin ranked);
 //   attend  workgroup (query, split, KV head): the tile routine of the decode
 //           path over the split's 16-cell tiles, folded into a running
 //           (max, sum, acc) in registers; with one split the output is
@@ -118,26 +118,48 @@ __device__ inline uint32_t chunk_key(float s)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+constexpr int kXcds = 8;                     // accelerator dies of an MI355X, each with its own L2
 constexpr int kSQT = 8;                      // query tiles (16 queries) per workgroup
 constexpr int kSRT = 4;                      // block row tiles (16 blocks) per wave
 constexpr int kSBlocks = 4 * kSRT * 16;      // blocks per workgroup (4 waves)
+
+template <bool F16, int KS>
+struct ScShape {
+    static constexpr int KC = (F16 ? 4 : 2) < KS ? (F16 ? 4 : 2) : KS;   // k-steps per stage
+    static constexpr int NST = KS / KC;                                   // stages
+    static constexpr int ES = F16 ? 2 : 4;                                // summary element bytes
+    static constexpr int AP = ES / 2;                                     // 16-byte A loads per k-step
+    static constexpr int BSEG = kSQT * KC * 2;                            // 1 KB B segments per stage
+    static constexpr int BPT = BSEG * 64 / 256;                           // 16-byte B loads per thread
+};
 
 // Workgroup (256 blocks, 128 queries), 4 waves; wave w holds the 64 x 128
 // block-query products of blocks 64w .. 64w+63 in 32 accumulator tiles.  The
 // summary rows are the A operand, loaded straight from memory (lane l: row
 // l % 16, 8 elements at 8 (l / 16)); the queries' operand tiles are staged in
-// LDS, KC k-steps at a time, shared by the 4 waves.
-template <bool F16>
+// LDS, KC k-steps at a time, shared by the 4 waves.  Both operands of stage
+// s + 1 are loaded while stage s runs on the matrix cores.
+template <bool F16, int KS>
 __global__ __launch_bounds__(256) void k_chunk_score(ChunkArgs c)
 {
-    constexpr int KC = F16 ? 4 : 2;
-    constexpr int ES = F16 ? 2 : 4;
-    __shared__ uint4 sb[kSQT][KC][2][64];
+    using S = ScShape<F16, KS>;
+    constexpr int KC = S::KC, NST = S::NST, ES = S::ES, AP = S::AP, BPT = S::BPT;
+    extern __shared__ uint4 sc_lds[];
+    uint4 (*sb)[KC][2][64] = reinterpret_cast<uint4 (*)[KC][2][64]>(sc_lds);   // [kSQT][KC][2][64]
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int QK = c.H * c.D, KS = QK / 32;
+    constexpr int QK = 32 * KS;
     const int QT = (c.n_q + 15) / 16;
-    const int qt0 = blockIdx.y * kSQT;
-    const int64_t bw = (int64_t)blockIdx.x * kSBlocks + wave * kSRT * 16;
+    // XCD-aware order: workgroups are dealt to the 8 XCDs in turn, so the
+    // query groups of one block tile are made consecutive on one XCD -- the
+    // tile's summary rows come from that XCD's L2 after the first read
+    const int nqg = (QT + kSQT - 1) / kSQT;
+    const int nbt = (c.nb_last + kSBlocks - 1) / kSBlocks;
+    const int xcd = (int)blockIdx.x % kXcds, j = (int)blockIdx.x / kXcds;
+    const int bt = (j / nqg) * kXcds + xcd, qg = j % nqg;
+    if (bt >= nbt)
+        return;
+    const int qt0 = qg * kSQT;
+    const int64_t bw = (int64_t)bt * kSBlocks + wave * kSRT * 16;
     const int mr = lane & 15, kg = lane >> 4;
 
     const char *rowp[kSRT];
@@ -155,38 +177,54 @@ __global__ __launch_bounds__(256) void k_chunk_score(ChunkArgs c)
             acc[rt][ct] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
 
     const uint4 *qsrc = (const uint4 *)c.qhl;
-    for (int k0 = 0; k0 < KS; k0 += KC) {
-        // this chunk's A operands, in flight while the B tiles are staged
-        uint4 ar[kSRT][KC][ES / 2];
+    auto load_a = [&](int st, uint4 (&ar)[kSRT][KC][AP]) __attribute__((always_inline)) {
 #pragma unroll
         for (int rt = 0; rt < kSRT; ++rt)
 #pragma unroll
             for (int kk = 0; kk < KC; ++kk)
 #pragma unroll
-                for (int p = 0; p < ES / 2; ++p)
-                    ar[rt][kk][p] = k0 + kk < KS
-                                        ? *(const uint4 *)(rowp[rt] + (size_t)(32 * (k0 + kk)) * ES + 16 * p)
-                                        : make_uint4(0u, 0u, 0u, 0u);
-        __syncthreads();                 // the previous chunk's B reads are done
-        for (int i = t; i < kSQT * KC * 2 * 64; i += 256) {
+                for (int p = 0; p < AP; ++p)
+                    ar[rt][kk][p] = *(const uint4 *)(rowp[rt] + (size_t)(32 * (st * KC + kk)) * ES + 16 * p);
+    };
+    // B segment x = (ct, kk, hl): 64 consecutive 16-byte operand slots
+    auto load_b = [&](int st, uint4 (&br)[BPT]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) {
+            const int i = t + 256 * u;
             const int ln = i & 63, hl = (i >> 6) & 1, kk = (i >> 7) % KC, ct = (i >> 7) / KC;
-            const bool ok = qt0 + ct < QT && k0 + kk < KS;
-            sb[ct][kk][hl][ln] =
-                ok ? qsrc[(((size_t)(qt0 + ct) * KS + k0 + kk) * 2 + hl) * 64 + ln] : make_uint4(0u, 0u, 0u, 0u);
+            br[u] = qt0 + ct < QT ? qsrc[(((size_t)(qt0 + ct) * KS + st * KC + kk) * 2 + hl) * 64 + ln]
+                                  : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+
+    uint4 a_cur[kSRT][KC][AP], a_nxt[kSRT][KC][AP], b_nxt[BPT];
+    load_a(0, a_cur);
+    load_b(0, b_nxt);
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+        if (st > 0)
+            __syncthreads();             // stage st-1's B reads are done
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) {
+            const int i = t + 256 * u;
+            const int ln = i & 63, hl = (i >> 6) & 1, kk = (i >> 7) % KC, ct = (i >> 7) / KC;
+            sb[ct][kk][hl][ln] = b_nxt[u];
         }
         __syncthreads();
+        if (st + 1 < NST) {
+            load_a(st + 1, a_nxt);
+            load_b(st + 1, b_nxt);
+        }
 #pragma unroll
         for (int kk = 0; kk < KC; ++kk) {
-            if (k0 + kk >= KS)
-                break;
             half8 ah[kSRT], al[kSRT];
 #pragma unroll
             for (int rt = 0; rt < kSRT; ++rt) {
                 if constexpr (F16) {
-                    __builtin_memcpy(&ah[rt], &ar[rt][kk][0], 16);
+                    __builtin_memcpy(&ah[rt], &a_cur[rt][kk][0], 16);
                 } else {
                     float f[8];
-                    __builtin_memcpy(f, &ar[rt][kk][0], 32);
+                    __builtin_memcpy(f, &a_cur[rt][kk][0], 32);
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
                         ah[rt][j] = (_Float16)f[j];
@@ -207,6 +245,15 @@ __global__ __launch_bounds__(256) void k_chunk_score(ChunkArgs c)
                         acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[rt], bh, acc[rt][ct], 0, 0, 0);
                 }
             }
+        }
+        if (st + 1 < NST) {
+#pragma unroll
+            for (int rt = 0; rt < kSRT; ++rt)
+#pragma unroll
+                for (int kk = 0; kk < KC; ++kk)
+#pragma unroll
+                    for (int p = 0; p < AP; ++p)
+                        a_cur[rt][kk][p] = a_nxt[rt][kk][p];
         }
     }
 
@@ -238,6 +285,33 @@ __global__ __launch_bounds__(256) void k_chunk_score(ChunkArgs c)
             }
         }
     }
+}
+
+template <bool F16, int KS>
+hipError_t score_go(const ChunkArgs &c, dim3 grid, hipStream_t s)
+{
+    using S = ScShape<F16, KS>;
+    const size_t lds = sizeof(uint4) * kSQT * S::KC * 2 * 64;
+    if (lds > 64 * 1024) {
+        static hipError_t attr = hipFuncSetAttribute((const void *)k_chunk_score<F16, KS>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (attr != hipSuccess)
+            return attr;
+    }
+    hipLaunchKernelGGL((k_chunk_score<F16, KS>), grid, dim3(256), lds, s, c);
+    return hipGetLastError();
+}
+
+template <bool F16>
+hipError_t score_ks(const ChunkArgs &c, dim3 grid, hipStream_t s)
+{
+    switch (c.H * c.D / 32) {
+    case 2: return score_go<F16, 2>(c, grid, s);
+    case 4: return score_go<F16, 4>(c, grid, s);
+    case 8: return score_go<F16, 8>(c, grid, s);
+    case 16: return score_go<F16, 16>(c, grid, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 // ----------------------------------------------------------------- select
@@ -276,7 +350,7 @@ __global__ __launch_bounds__(sel::kT) void k_chunk_select(ChunkArgs c)
     sel::Smem &sm = *reinterpret_cast<sel::Smem *>(lds);
     uint32_t *bitmap = reinterpret_cast<uint32_t *>(lds + (sizeof(sel::Smem) + 15) / 16 * 16);
     uint32_t *lkeys = c.sel_cache_keys ? reinterpret_cast<uint32_t *>(lds + sel::lds_bytes(c.nb_last)) : nullptr;
-    sel::general_path(a, sm, bitmap, lkeys, [=](uint32_t slot, uint32_t id) {
+    sel::keys_path(a, sm, bitmap, lkeys, [=](uint32_t slot, uint32_t id) {
         row[slot] = (int32_t)id;
         if (row_out)
             row_out[slot] = (int32_t)id;
@@ -688,12 +762,10 @@ hipError_t launch_chunk_rest(ChunkArgs c, bool f16, int Dh, int G, hipStream_t s
         hipLaunchKernelGGL(k_chunk_prep, dim3(qt * 4), dim3(256), 0, s, c);
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
-        const dim3 grid((unsigned)((c.nb_last + kSBlocks - 1) / kSBlocks), (unsigned)((qt + kSQT - 1) / kSQT));
-        if (f16)
-            hipLaunchKernelGGL(k_chunk_score<true>, grid, dim3(256), 0, s, c);
-        else
-            hipLaunchKernelGGL(k_chunk_score<false>, grid, dim3(256), 0, s, c);
-        if ((e = hipGetLastError()) != hipSuccess)
+        const int nbt = (c.nb_last + kSBlocks - 1) / kSBlocks, nqg = (qt + kSQT - 1) / kSQT;
+        const dim3 grid((unsigned)(kXcds * ((nbt + kXcds - 1) / kXcds) * nqg));
+        e = f16 ? score_ks<true>(c, grid, s) : score_ks<false>(c, grid, s);
+        if (e != hipSuccess)
             return e;
     }
     if (c.nb_last > c.kb || c.sel_out) {

@@ -33,8 +33,10 @@
 //      to emit(slot, id) in ascending order.
 // Anything the fast path cannot decide exactly -- fewer than k listed
 // entries, non-finite or all-equal scores, a crowded bin, a tile that may
-// hide winners, N > 65,536 -- takes the general path: radix refinement over
-// every key, marked in the same bitmap, slots by a popcount prefix sum.
+// hide winners, N > 65,536 -- runs the same histogram / rank / mark steps
+// over every key (four passes), and where those cannot decide either, a
+// radix refinement over every key; both mark the same bitmap, slots by a
+// popcount prefix sum.
 #pragma once
 #include "qsa_internal.h"
 #include "qsa_wave.h"
@@ -229,6 +231,31 @@ __device__ void refine_and_mark(Smem &sm, ForEach for_each, Mark mark, uint32_t 
     }
 }
 
+// Emit the k ids marked in the bitmap, ascending (thread t owns a run of
+// words; a block prefix sum of their popcounts gives its first slot).
+template <class Emit>
+__device__ void emit_bitmap(Smem &sm, const uint32_t *bitmap, uint32_t nwords, uint32_t k, Emit emit)
+{
+    const int t = threadIdx.x;
+    const uint32_t per = (nwords + kT - 1) / kT;
+    const uint32_t w0 = t * per;
+    const uint32_t w1 = w0 + per < nwords ? w0 + per : nwords;
+    uint32_t c = 0;
+    for (uint32_t w = w0; w < w1; ++w)
+        c += (uint32_t)__popc(bitmap[w]);
+    uint32_t o = block_excl_scan(c, sm, nullptr);
+    for (uint32_t w = w0; w < w1; ++w) {
+        uint32_t bits = bitmap[w];
+        while (bits) {
+            const int b = __ffs(bits) - 1;
+            bits &= bits - 1;
+            if (o < k)
+                emit(o, w * 32 + (uint32_t)b);
+            ++o;
+        }
+    }
+}
+
 // The exact top-k over every key (radix refinement, bitmap, popcount slots).
 // lkeys (LDS, nb words, or null): the keys are copied there first and every
 // pass reads them from LDS instead of memory.  Whole workgroup calls;
@@ -286,23 +313,143 @@ __device__ void general_path(const SelectArgs &a, Smem &sm, uint32_t *bitmap, ui
         atomicOr(&bitmap[id >> 5], 1u << (id & 31));
     }, k);
     __syncthreads();
-    const uint32_t per = (nwords + kT - 1) / kT;
-    const uint32_t w0 = t * per;
-    const uint32_t w1 = w0 + per < nwords ? w0 + per : nwords;
-    uint32_t c = 0;
-    for (uint32_t w = w0; w < w1; ++w)
-        c += (uint32_t)__popc(bitmap[w]);
-    uint32_t o = block_excl_scan(c, sm, nullptr);
-    for (uint32_t w = w0; w < w1; ++w) {
-        uint32_t bits = bitmap[w];
-        while (bits) {
-            const int b = __ffs(bits) - 1;
-            bits &= bits - 1;
-            if (o < k)
-                emit(o, w * 32 + (uint32_t)b);
-            ++o;
+    emit_bitmap(sm, bitmap, nwords, k, emit);
+}
+
+// The exact top-k over every key in four passes: min / max, a 1024-bin
+// histogram linear in the score (or in the key when every score is >= 0),
+// the entries of the bin holding the k-th ranked by counting (kappa = the
+// k-th largest composite), the composites >= kappa marked.  Non-finite
+// scores or a crowded bin fall back to the radix refinement.  lkeys (LDS, nb
+// words, or null): the keys are read from memory once and kept there.
+// Requires nb > k.  Whole workgroup calls; emit as in run().
+template <class Emit>
+__device__ void keys_path(const SelectArgs &a, Smem &sm, uint32_t *bitmap, uint32_t *lkeys, Emit emit)
+{
+    const uint32_t nb = (uint32_t)a.nb;
+    const uint32_t k = (uint32_t)a.k;
+    const uint32_t nwords = (nb + 31) >> 5;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    for (uint32_t i = t; i < nwords; i += kT)
+        bitmap[i] = 0u;
+    sm.hist[t] = 0u;
+    if (t == 0) {
+        sm.ncand = 0u;
+        sm.d = 0xFFFFFFFFu;
+    }
+    // 1. keys (to LDS when asked) and their range
+    uint32_t kmin1 = 0xFFFFFFFFu, kmax = 0u;
+    for (uint32_t base = 0; base < nb; base += kT * 4) {
+        uint32_t kk[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t e = base + q * kT + t;
+            kk[q] = a.keys[e < nb ? e : nb - 1];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t e = base + q * kT + t;
+            if (e < nb) {
+                if (lkeys)
+                    lkeys[e] = kk[q];
+                kmin1 = min(kmin1, kk[q] - 1u);
+                kmax = max(kmax, kk[q]);
+            }
         }
     }
+    kmin1 = wave::reduce_min_u32(kmin1);
+    kmax = wave::reduce_max_u32(kmax);
+    if (lane == 0) {
+        sm.rmin[wv] = kmin1;
+        sm.rmax[wv] = kmax;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kWaves; i += 4) {
+        const uint4 a4 = reinterpret_cast<const uint4 *>(sm.rmin)[i / 4];
+        const uint4 b4 = reinterpret_cast<const uint4 *>(sm.rmax)[i / 4];
+        kmin1 = min(min(kmin1, a4.x), min(a4.y, min(a4.z, a4.w)));
+        kmax = max(max(kmax, b4.x), max(b4.y, max(b4.z, b4.w)));
+    }
+    const uint32_t kmin = kmin1 + 1u;
+    const float mn = key_score(kmin), mx = key_score(kmax);
+    const float range = mx - mn;
+    const float scale = (float)kBins / range;
+    bool general = kmin < kKeyFiniteLo || kmax > kKeyFiniteHi || !(range > 0.0f) ||
+                   !(range < __builtin_inff()) || !(scale < __builtin_inff());
+    const bool by_key = kmin >= 0x80000000u;
+    const int kshift = 32 - __clz((int)(kmax - kmin)) - 10;
+    const uint32_t ksh = kshift > 0 ? (uint32_t)kshift : 0u;
+    auto key_at = [&](uint32_t e) -> uint32_t { return lkeys ? lkeys[e] : a.keys[e]; };
+    auto bin_of = [&](uint32_t key) -> uint32_t {
+        if (by_key)
+            return (key > kmin ? key - kmin : 0u) >> ksh;
+        const float sc = fmaxf(key_score(key), mn);
+        const uint32_t b = (uint32_t)((sc - mn) * scale);
+        return b < (uint32_t)kBins - 1 ? b : (uint32_t)kBins - 1;
+    };
+    if (!general) {
+        // 2. histogram
+        for (uint32_t e = t; e < nb; e += kT)
+            atomicAdd(&sm.hist[bin_of(key_at(e))], 1u);
+        __syncthreads();
+        // the bin d holding the k-th largest (thread t takes bin 1023 - t)
+        {
+            const uint32_t h = sm.hist[kBins - 1 - t];
+            const uint32_t incl = wave::incl_scan_add(h);
+            if (lane == 63)
+                sm.wtot[wv] = incl;
+            __syncthreads();
+            uint32_t off = 0;
+#pragma unroll
+            for (int i = 0; i < kWaves; i += 4) {
+                const uint4 w4 = reinterpret_cast<const uint4 *>(sm.wtot)[i / 4];
+                off += (i < wv ? w4.x : 0u) + (i + 1 < wv ? w4.y : 0u) + (i + 2 < wv ? w4.z : 0u) +
+                       (i + 3 < wv ? w4.w : 0u);
+            }
+            const uint32_t above = off + incl - h;
+            if (above < k && above + h >= k) {
+                sm.d = (uint32_t)(kBins - 1 - t);
+                sm.need = k - above;
+                sm.in_d = h;
+            }
+        }
+        __syncthreads();
+        const uint32_t d = sm.d, m = sm.in_d;
+        general = d == 0xFFFFFFFFu || m > (uint32_t)kCap;
+        if (!general) {
+            // 3. the entries of bin d, ranked by counting in wave 0
+            for (uint32_t e = t; e < nb; e += kT) {
+                const uint32_t key = key_at(e);
+                if (bin_of(key) == d)
+                    sm.cand[atomicAdd(&sm.ncand, 1u)] = comp_key(key, e);
+            }
+            __syncthreads();
+            if (wv == 0) {
+                const uint32_t need = sm.need;
+                for (uint32_t j = lane; j < m; j += kWave) {
+                    const uint64_t c = sm.cand[j];
+                    uint32_t r = 0;
+#pragma unroll 4
+                    for (uint32_t i = 0; i < m; ++i)
+                        r += sm.cand[i] > c ? 1u : 0u;
+                    if (r == need - 1)
+                        sm.kappa = c;
+                }
+            }
+            __syncthreads();
+            // 4. the winners: composites >= kappa (exactly k of them)
+            const uint64_t kappa = sm.kappa;
+            for (uint32_t e = t; e < nb; e += kT)
+                if (comp_key(key_at(e), e) >= kappa)
+                    atomicOr(&bitmap[e >> 5], 1u << (e & 31));
+            __syncthreads();
+            emit_bitmap(sm, bitmap, nwords, k, emit);
+            return;
+        }
+    }
+    __syncthreads();
+    general_path(a, sm, bitmap, lkeys, emit);
 }
 
 // ------------------------------------------------------------------ routine
@@ -516,7 +663,7 @@ __device__ void run(const SelectArgs &a, char *lds, Emit emit)
 
     // ---------------------------------------------------------- general path
     __syncthreads();
-    general_path(a, sm, bitmap, nullptr, emit);
+    keys_path(a, sm, bitmap, nullptr, emit);
 }
 
 }  // namespace sel

@@ -178,3 +178,12 @@ def test_chunk_attention_shapes(q_heads, kv_heads, head_dim, n_q):
     base = with_size(W.CTX64K, q_heads=q_heads, kv_heads=kv_heads, head_dim=head_dim)
     st = _run_full(base, 3001, n_q)
     assert st["exact"] + st["threshold"] == n_q
+
+
+@pytest.mark.parametrize("idx_heads,idx_dim,idx_f16", [
+    (1, 128, True), (4, 64, False), (1, 64, True), (1, 128, False)])
+def test_chunk_indexer_shapes(idx_heads, idx_dim, idx_f16):
+    """Indexer contractions of 64 .. 512 elements, f16 and fp32 summaries."""
+    base = with_size(W.CTX64K, idx_heads=idx_heads, idx_dim=idx_dim, idx_f16=idx_f16)
+    st = _run_full(base, 4001, 33)
+    assert st["exact"] + st["threshold"] == 33
