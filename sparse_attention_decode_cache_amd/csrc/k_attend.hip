@@ -238,26 +238,8 @@ __global__ __launch_bounds__(kMT) void k_merge(AttendArgs a)
     merge_unit<DH, G>(a, ml, blockIdx.x, blockIdx.y);
 }
 
-// A batch: workgroups [wg0[s], wg0[s+1]) are sequence s's (split, KV head)
-// pairs; the merge grid is (sequence x query head, 64-dim slice).
-template <int DH, int G>
-__global__ __launch_bounds__(kAT) void k_attend_batch(AttendBatchArgs b)
-{
-    __shared__ AttLds<DH, G> L;
-    int s = 0;
-    while (s + 1 < b.n && (int)blockIdx.x >= b.wg0[s + 1])
-        ++s;
-    const AttendArgs &a = b.seq[s];
-    const int local = (int)blockIdx.x - b.wg0[s];
-    const int split = local % a.n_split, g = local / a.n_split;
-    if (threadIdx.x < kCells / 4) {
-        const int i = split * (kCells / 4) + threadIdx.x;
-        L.blk[threadIdx.x] = !a.sel ? i : (i < a.n_sel_blocks ? a.sel[i] : -1);
-    }
-    __syncthreads();
-    attend_split<DH, G>(a, L, split, g);
-}
-
+// A batch: grid (sequence x query head, 64-dim slice), over each sequence's
+// split partials.
 template <int DH, int G>
 __global__ __launch_bounds__(kMT) void k_merge_batch(AttendBatchArgs b)
 {
@@ -265,24 +247,6 @@ __global__ __launch_bounds__(kMT) void k_merge_batch(AttendBatchArgs b)
     const int hq = b.seq[0].kv_heads * G;
     const int s = (int)blockIdx.x / hq;
     merge_unit<DH, G>(b.seq[s], ml, (int)blockIdx.x % hq, blockIdx.y);
-}
-
-template <int DH, int G>
-hipError_t go_batch(AttendBatchArgs &b, hipStream_t s)
-{
-    b.wg0[0] = 0;
-    for (int i = 0; i < b.n; ++i) {
-        if (b.seq[i].n_split < 1 || b.seq[i].n_split > kMaxSplits || b.seq[i].kv_heads != b.seq[0].kv_heads)
-            return hipErrorInvalidValue;
-        b.wg0[i + 1] = b.wg0[i] + b.seq[i].n_split * b.seq[i].kv_heads;
-    }
-    hipLaunchKernelGGL((k_attend_batch<DH, G>), dim3(b.wg0[b.n]), dim3(kAT), 0, s, b);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    hipLaunchKernelGGL((k_merge_batch<DH, G>), dim3(b.n * b.seq[0].kv_heads * G, DH / kWave),
-                       dim3(kMT), 0, s, b);
-    return hipGetLastError();
 }
 
 template <int DH, int G>
@@ -349,25 +313,31 @@ hipError_t launch_attend(const AttendArgs &a, int Dh, int G, hipStream_t s)
     return dispatch(a, nullptr, Dh, G, s);
 }
 
-hipError_t launch_attend_batch(AttendBatchArgs &b, int Dh, int G, hipStream_t s)
+hipError_t launch_merge_batch(const AttendBatchArgs &b, int Dh, int G, hipStream_t s)
 {
     if (b.n < 1 || b.n > kMaxBatch)
         return hipErrorInvalidValue;
-#define QSA_BATCH_G(DHV)                                   \
-    switch (G) {                                           \
-    case 1: return go_batch<DHV, 1>(b, s);                 \
-    case 2: return go_batch<DHV, 2>(b, s);                 \
-    case 4: return go_batch<DHV, 4>(b, s);                 \
-    case 8: return go_batch<DHV, 8>(b, s);                 \
-    }                                                      \
-    return hipErrorInvalidValue;
+    for (int i = 0; i < b.n; ++i)
+        if (b.seq[i].n_split < 1 || b.seq[i].n_split > kMaxSplits || b.seq[i].kv_heads != b.seq[0].kv_heads)
+            return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(b.n * b.seq[0].kv_heads * G), (unsigned)(Dh / kWave));
+#define QSA_MERGE_G(DHV)                                                                \
+    switch (G) {                                                                        \
+    case 1: hipLaunchKernelGGL((k_merge_batch<DHV, 1>), grid, dim3(kMT), 0, s, b); break; \
+    case 2: hipLaunchKernelGGL((k_merge_batch<DHV, 2>), grid, dim3(kMT), 0, s, b); break; \
+    case 4: hipLaunchKernelGGL((k_merge_batch<DHV, 4>), grid, dim3(kMT), 0, s, b); break; \
+    case 8: hipLaunchKernelGGL((k_merge_batch<DHV, 8>), grid, dim3(kMT), 0, s, b); break; \
+    default: return hipErrorInvalidValue;                                               \
+    }                                                                                   \
+    break;
     switch (Dh) {
-    case 64: QSA_BATCH_G(64)
-    case 128: QSA_BATCH_G(128)
-    case 256: QSA_BATCH_G(256)
+    case 64: QSA_MERGE_G(64)
+    case 128: QSA_MERGE_G(128)
+    case 256: QSA_MERGE_G(256)
+    default: return hipErrorInvalidValue;
     }
-#undef QSA_BATCH_G
-    return hipErrorInvalidValue;
+#undef QSA_MERGE_G
+    return hipGetLastError();
 }
 
 hipError_t launch_select_attend(const AttendArgs &a, const SelectArgs &sa, int Dh, int G,

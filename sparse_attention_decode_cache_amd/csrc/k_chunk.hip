@@ -1,5 +1,6 @@
 // k_chunk.hip -- a prefill chunk: n_q consecutive tokens of one sequence in
-// one call, with results equal to n_q decode steps in a row.  Query i sits at
+// one call, with results equal to n_q decode steps in a row; its attention
+// also serves the batched decode (one unit per sequence).  Query i sits at
 // position p = n0 + i; it sees the floor((p + 1) / 4) blocks completed by then
 // (the causal block mask), keeps the top k of them and attends to their cells
 // and to its own tail [post 10, "QSA indexer"; "incremental pooled-key
@@ -437,20 +438,31 @@ struct CALds {
     int32_t ids[kChunkMaxIds];
 };
 
+// One attention unit: a query of one sequence, one KV head, one split.
+struct QueryUnit {
+    const uint16_t *k, *v;      // the sequence's K / V cache
+    const int32_t *sel;         // its chosen block ids, ascending (null: every block kept)
+    const float *q;             // [Hq][Dh]
+    float *out;                 // [Hq][Dh], written when ns == 1
+    float *part;                // [Hkv][ns] partials, written when ns > 1
+    int64_t n;                  // tokens seen, the current one included
+    int32_t kb;                 // blocks kept at most
+    int32_t kv_heads, ns;
+    int32_t direct;             // ns == 1 and the output is written here, normalised
+    float scale;
+};
+
 template <int DH, int G>
-__global__ __launch_bounds__(kCAT, 2) void k_chunk_attend(ChunkArgs c)
+__device__ void attend_unit(const QueryUnit &c, CALds<DH, G> &L, int s, int g)
 {
     using S = CAShape<DH, G>;
     constexpr int KCH = S::KCH, VCH = S::VCH, KR = S::KR, VR = S::VR, KS = S::KS, KROW = S::KROW,
                   LPW = S::LPW;
-    extern __shared__ uint4 ca_lds[];
-    CALds<DH, G> &L = *reinterpret_cast<CALds<DH, G> *>(ca_lds);
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int ns = c.n_split;
-    const int i = blockIdx.x / ns, s = blockIdx.x % ns, g = blockIdx.y;
-    const int64_t n = (int64_t)c.n0 + i + 1;
+    const int ns = c.ns;
+    const int64_t n = c.n;
     const int32_t nbq = (int32_t)(n >> 2);
-    const bool keep_all = nbq <= c.kb;
+    const bool keep_all = !c.sel || nbq <= c.kb;
     const int32_t nsel = keep_all ? nbq : c.kb;
     const int32_t ncells = 4 * nsel + (int32_t)(n & 3);
     const int32_t nit = (ncells + kCI - 1) / kCI;
@@ -459,12 +471,12 @@ __global__ __launch_bounds__(kCAT, 2) void k_chunk_attend(ChunkArgs c)
     // the split's block ids (16 per iteration)
     const int32_t id0 = (kCI / 4) * it0;
     const int32_t id1 = (kCI / 4) * it1 < nsel ? (kCI / 4) * it1 : nsel;
-    const int32_t *srow = c.sel + (size_t)i * c.kb;
+    const int32_t *srow = c.sel;
     for (int x = id0 + t; x < id1; x += kCAT)
         L.ids[x - id0] = keep_all ? x : srow[x];
     // q as the B operand of the logit MFMA: lane l of k-step ks holds
     // q[head l % 16][32 ks + 8 (l / 16) .. +8] (zero past G), hi and lo
-    const float *qg = c.q + ((size_t)i * c.kv_heads + g) * G * DH;
+    const float *qg = c.q + (size_t)g * G * DH;
     for (int x = t; x < KS * kWave; x += kCAT) {
         const int ks = x / kWave, l = x % kWave, h = l % 16, d0 = 32 * ks + 8 * (l / 16);
         float4 u = make_float4(0.0f, 0.0f, 0.0f, 0.0f), v = u;
@@ -658,8 +670,8 @@ __global__ __launch_bounds__(kCAT, 2) void k_chunk_attend(ChunkArgs c)
     if (wave != 0 || lane >= LPW)
         return;
     const int k4 = 4 * lane;                       // this lane's 4 dims
-    if (ns == 1) {
-        float *o = c.out + ((size_t)i * c.kv_heads + g) * G * DH;
+    if (c.direct) {
+        float *o = c.out + (size_t)g * G * DH;
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             const float l = L.lrow[h];
@@ -667,7 +679,7 @@ __global__ __launch_bounds__(kCAT, 2) void k_chunk_attend(ChunkArgs c)
         }
         return;
     }
-    float *part = c.part + (((size_t)i * c.kv_heads + g) * ns + s) * (size_t)part_stride(G, DH);
+    float *part = c.part + ((size_t)g * ns + s) * (size_t)part_stride(G, DH);
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
@@ -680,16 +692,63 @@ __global__ __launch_bounds__(kCAT, 2) void k_chunk_attend(ChunkArgs c)
     }
 }
 
-// Workgroup (query, KV head): out = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s
-// over the splits, in split order.
 template <int DH, int G>
-__global__ __launch_bounds__(256) void k_chunk_merge(ChunkArgs c)
+__global__ __launch_bounds__(kCAT, 2) void k_chunk_attend(ChunkArgs c)
 {
-    const int unit = blockIdx.x;
+    extern __shared__ uint4 ca_lds[];
+    CALds<DH, G> &L = *reinterpret_cast<CALds<DH, G> *>(ca_lds);
     const int ns = c.n_split;
+    const int i = blockIdx.x / ns;
+    QueryUnit u;
+    u.k = c.k;
+    u.v = c.v;
+    u.sel = c.sel + (size_t)i * c.kb;
+    u.q = c.q + (size_t)i * c.kv_heads * G * DH;
+    u.out = c.out + (size_t)i * c.kv_heads * G * DH;
+    u.part = c.part + (size_t)i * c.kv_heads * ns * part_stride(G, DH);
+    u.n = (int64_t)c.n0 + i + 1;
+    u.kb = c.kb;
+    u.kv_heads = c.kv_heads;
+    u.ns = ns;
+    u.direct = ns == 1;
+    u.scale = c.scale;
+    attend_unit<DH, G>(u, L, blockIdx.x % ns, blockIdx.y);
+}
+
+// Batched decode: workgroups [wg0[s], wg0[s+1]) are sequence s's (split, KV
+// head) units.
+template <int DH, int G>
+__global__ __launch_bounds__(kCAT, 2) void k_batch_attend(AttendBatchArgs b)
+{
+    extern __shared__ uint4 ca_lds[];
+    CALds<DH, G> &L = *reinterpret_cast<CALds<DH, G> *>(ca_lds);
+    int sq = 0;
+    while (sq + 1 < b.n && (int)blockIdx.x >= b.wg0[sq + 1])
+        ++sq;
+    const AttendArgs &a = b.seq[sq];
+    const int local = (int)blockIdx.x - b.wg0[sq];
+    QueryUnit u;
+    u.k = a.k;
+    u.v = a.v;
+    u.sel = a.sel;
+    u.q = a.q;
+    u.out = a.out;
+    u.part = a.part;
+    u.n = 4 * (int64_t)a.nb + (a.n_cells - 4 * (int64_t)a.n_sel_blocks);
+    u.kb = a.n_sel_blocks;
+    u.kv_heads = a.kv_heads;
+    u.ns = a.n_split;
+    u.direct = 0;                                  // the merge kernel writes the output
+    u.scale = a.scale;
+    attend_unit<DH, G>(u, L, local % a.n_split, local / a.n_split);
+}
+
+// out = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s over the ns split
+// partials of one (query, KV head), in split order.  Whole workgroup calls.
+template <int DH, int G>
+__device__ void merge_partials(const float *base, int ns, float *out)
+{
     const size_t ps = (size_t)part_stride(G, DH);
-    const float *base = c.part + (size_t)unit * ns * ps;
-    float *out = c.out + (size_t)unit * G * DH;
     for (int idx = threadIdx.x; idx < G * DH; idx += 256) {
         const int h = idx / DH;
         float M = -INFINITY;
@@ -704,6 +763,16 @@ __global__ __launch_bounds__(256) void k_chunk_merge(ChunkArgs c)
         }
         out[idx] = A / Ls;
     }
+}
+
+// Workgroup (query, KV head): out = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s
+// over the splits, in split order.
+template <int DH, int G>
+__global__ __launch_bounds__(256) void k_chunk_merge(ChunkArgs c)
+{
+    const int unit = blockIdx.x;
+    merge_partials<DH, G>(c.part + (size_t)unit * c.n_split * part_stride(G, DH), c.n_split,
+                          c.out + (size_t)unit * G * DH);
 }
 
 template <int DH, int G>
@@ -724,6 +793,34 @@ hipError_t attend_go(const ChunkArgs &c, hipStream_t s)
     return hipGetLastError();
 }
 
+template <int DH, int G>
+hipError_t batch_go(AttendBatchArgs &b, hipStream_t s)
+{
+    b.wg0[0] = 0;
+    for (int i = 0; i < b.n; ++i) {
+        AttendArgs &a = b.seq[i];
+        if (a.kv_heads != b.seq[0].kv_heads || a.n_cells < 1)
+            return hipErrorInvalidValue;
+        // one 64-cell iteration per workgroup: the batch fills the chip
+        const int nit = (a.n_cells + kCI - 1) / kCI;
+        a.n_split = nit < kChunkMaxSplits ? nit : kChunkMaxSplits;
+        b.wg0[i + 1] = b.wg0[i] + a.n_split * a.kv_heads;
+    }
+    const size_t lds = sizeof(CALds<DH, G>);
+    if (lds > 64 * 1024) {
+        static hipError_t attr = hipFuncSetAttribute((const void *)k_batch_attend<DH, G>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (attr != hipSuccess)
+            return attr;
+    }
+    hipLaunchKernelGGL((k_batch_attend<DH, G>), dim3(b.wg0[b.n]), dim3(kCAT), lds, s, b);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    // sequences kept in one split still take the merge (it divides by l)
+    return launch_merge_batch(b, DH, G, s);
+}
+
 template <int DH>
 hipError_t attend_g(const ChunkArgs &c, int G, hipStream_t s)
 {
@@ -737,6 +834,27 @@ hipError_t attend_g(const ChunkArgs &c, int G, hipStream_t s)
 }
 
 }  // namespace
+
+hipError_t launch_attend_batch(AttendBatchArgs &b, int Dh, int G, hipStream_t s)
+{
+    if (b.n < 1 || b.n > kMaxBatch)
+        return hipErrorInvalidValue;
+#define QSA_BATCH_G(DHV)                                   \
+    switch (G) {                                           \
+    case 1: return batch_go<DHV, 1>(b, s);                 \
+    case 2: return batch_go<DHV, 2>(b, s);                 \
+    case 4: return batch_go<DHV, 4>(b, s);                 \
+    case 8: return batch_go<DHV, 8>(b, s);                 \
+    }                                                      \
+    return hipErrorInvalidValue;
+    switch (Dh) {
+    case 64: QSA_BATCH_G(64)
+    case 128: QSA_BATCH_G(128)
+    case 256: QSA_BATCH_G(256)
+    }
+#undef QSA_BATCH_G
+    return hipErrorInvalidValue;
+}
 
 hipError_t launch_chunk_append(const ChunkArgs &c, hipStream_t s)
 {

@@ -145,7 +145,11 @@ struct AttendBatchArgs {
     int32_t wg0[kMaxBatch + 1];     // first workgroup of each sequence (filled by the launcher)
     AttendArgs seq[kMaxBatch];
 };
+// The batch's attention: each sequence's cells in 64-cell iterations, one
+// per workgroup, then a merge of the partials (n_split is set here).
 hipError_t launch_attend_batch(AttendBatchArgs &b, int Dh, int G, hipStream_t s);
+// The merge of a batch's split partials (one load round per output slice).
+hipError_t launch_merge_batch(const AttendBatchArgs &b, int Dh, int G, hipStream_t s);
 // Stages 3 + 4 fused: every attention workgroup selects (a.sel is ignored;
 // the chosen ids come from `sa`, sa.sel optionally receives them all).
 hipError_t launch_select_attend(const AttendArgs &a, const SelectArgs &sa, int Dh, int G,

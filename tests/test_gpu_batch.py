@@ -70,8 +70,10 @@ def test_batch_tiny_eight_sequences():
 
 
 def test_batch_single_sequence_matches_decode_step():
-    """A batch of one gives the same bits as qsa_decode_step on the same inputs
-    whenever both keep every block (the same kernels then run on both paths)."""
+    """A batch of one agrees with qsa_decode_step on the same inputs whenever
+    both keep every block: the same summary bits (the same pooling), and the
+    same attention up to summation order (the batch attends in 64-cell
+    iterations, the single step in 16-cell splits) -- far inside 2e-3."""
     import torch
     import sparse_attention_decode_cache_amd as qsa
     w = with_size(W.TINY, n0=40, steps=4, top_k_tokens=256)
@@ -82,5 +84,5 @@ def test_batch_single_sequence_matches_decode_step():
         b.step(s)
         nb = a.state.n_tokens // 4
         assert a.state.n_tokens == b.state.n_tokens
-        assert torch.equal(a.out, b.out)
+        torch.testing.assert_close(a.out, b.out, rtol=0.0, atol=1e-5)
         assert torch.equal(a.buf.summary[:nb], b.buf.summary[:nb])
