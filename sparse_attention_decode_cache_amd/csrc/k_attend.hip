@@ -264,7 +264,8 @@ hipError_t go(const AttendArgs &a, const SelectArgs *sa, hipStream_t s)
     if (!sa) {
         hipLaunchKernelGGL((k_attend<DH, G>), dim3(a.n_split, a.kv_heads), dim3(kAT), 0, s, a);
     } else {
-        const size_t lds = sel::lds_bytes(sa->nb);
+        SelectArgs sc = *sa;
+        const size_t lds = sel::lds_with_cache(sc, sc.nb, sel::kMaxLds - sizeof(AttLds<DH, G>));
         if (lds + sizeof(AttLds<DH, G>) > sel::kMaxLds)
             return hipErrorInvalidValue;
         if (lds > 32 * 1024) {
@@ -274,7 +275,7 @@ hipError_t go(const AttendArgs &a, const SelectArgs *sa, hipStream_t s)
             if (attr != hipSuccess)
                 return attr;
         }
-        FusedArgs f{a, *sa};
+        FusedArgs f{a, sc};
         hipLaunchKernelGGL((k_select_attend<DH, G>), dim3(a.n_split, a.kv_heads), dim3(kAT), lds, s,
                            f);
     }

@@ -34,17 +34,22 @@ __global__ __launch_bounds__(sel::kT) void k_select_batch(SelectBatchArgs b)
 
 }  // namespace
 
-hipError_t launch_select_batch(const SelectBatchArgs &b, hipStream_t s)
+hipError_t launch_select_batch(const SelectBatchArgs &bin, hipStream_t s)
 {
+    SelectBatchArgs b = bin;
     if (b.n < 1 || b.n > kMaxBatch)
         return hipErrorInvalidValue;
-    size_t lds = 0;
+    int32_t nb_max = 0;
     for (int i = 0; i < b.n; ++i) {
         if (b.seq[i].nb > b.seq[i].k && b.seq[i].T != 8 && b.seq[i].T != 16 && b.seq[i].T != 32)
             return hipErrorInvalidValue;
-        const size_t l = sel::lds_bytes(b.seq[i].nb);
-        lds = l > lds ? l : lds;
+        nb_max = b.seq[i].nb > nb_max ? b.seq[i].nb : nb_max;
     }
+    // one layout for every sequence: Smem, the bitmap of the longest, and
+    // (when it fits) a key cache as long as the longest
+    size_t lds = 0;
+    for (int i = 0; i < b.n; ++i)
+        lds = sel::lds_with_cache(b.seq[i], nb_max, sel::kMaxLds);
     if (lds > sel::kMaxLds)
         return hipErrorInvalidValue;
     if (lds > 64 * 1024) {
@@ -58,11 +63,12 @@ hipError_t launch_select_batch(const SelectBatchArgs &b, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_select(const SelectArgs &a, hipStream_t s)
+hipError_t launch_select(const SelectArgs &ain, hipStream_t s)
 {
+    SelectArgs a = ain;
     if (a.T != 8 && a.T != 16 && a.T != 32)
         return hipErrorInvalidValue;
-    const size_t lds = sel::lds_bytes(a.nb);
+    const size_t lds = sel::lds_with_cache(a, a.nb, sel::kMaxLds);
     if (lds > sel::kMaxLds)
         return hipErrorInvalidValue;
     if (lds > 64 * 1024) {

@@ -111,6 +111,8 @@ struct SelectArgs {
     int32_t k;
     int32_t ntiles;
     int32_t T;
+    int32_t lkeys_off;          // byte offset of an nb-word key cache in the dynamic LDS (0: none;
+                                // set by the launchers when it fits)
 };
 hipError_t launch_select(const SelectArgs &a, hipStream_t s);
 struct SelectBatchArgs {

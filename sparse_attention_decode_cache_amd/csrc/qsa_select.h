@@ -68,12 +68,24 @@ struct Smem {
     uint32_t gtot, bin, gabove;
 };
 
+// Dynamic LDS of run() with a key cache of nb words at lds_bytes(nb_max)
+// when the total stays within `cap` (else without one).  Sets a.lkeys_off.
+inline size_t lds_with_cache(SelectArgs &a, int32_t nb_max, size_t cap);
+
 // Dynamic LDS of run(): Smem and the id bitmap.
 __host__ __device__ inline size_t lds_bytes(int32_t nb)
 {
     const size_t nwords = (size_t)(nb + 31) / 32;
     const size_t bm = nwords > (size_t)kFastWords ? nwords : (size_t)kFastWords;
     return (sizeof(Smem) + 15) / 16 * 16 + 4 * bm;
+}
+
+inline size_t lds_with_cache(SelectArgs &a, int32_t nb_max, size_t cap)
+{
+    const size_t base = lds_bytes(nb_max);
+    const size_t with = base + 4 * (size_t)nb_max;
+    a.lkeys_off = with <= cap ? (int32_t)base : 0;
+    return with <= cap ? with : base;
 }
 
 // True when the fast path can hold the lists of N blocks in T-entry lists.
@@ -468,7 +480,9 @@ __device__ void run(const SelectArgs &a, char *lds, Emit emit)
     uint32_t *bitmap = reinterpret_cast<uint32_t *>(lds + (sizeof(Smem) + 15) / 16 * 16);
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const uint32_t nchunks = (uint32_t)a.ntiles * (uint32_t)a.T / 2;
-    bool general = nchunks > (uint32_t)(kT * kChunks);
+    // the lists decide only when they hold well over k entries: with fewer
+    // than 4k the tiles' lists are full of winners and the check fails
+    bool general = nchunks > (uint32_t)(kT * kChunks) || 2ull * nchunks < 4ull * k;
 
     // clear: histogram, bitmap words 2t and 2t+1, the counters
     sm.hist[t] = 0u;
@@ -663,7 +677,7 @@ __device__ void run(const SelectArgs &a, char *lds, Emit emit)
 
     // ---------------------------------------------------------- general path
     __syncthreads();
-    keys_path(a, sm, bitmap, nullptr, emit);
+    keys_path(a, sm, bitmap, a.lkeys_off ? reinterpret_cast<uint32_t *>(lds + a.lkeys_off) : nullptr, emit);
 }
 
 }  // namespace sel
