@@ -13,7 +13,8 @@
 //           and written in the matrix-core operand layout;
 //   score   all queries x all blocks as one f16 MFMA GEMM (hi and lo both
 //           multiplied: the products are exact in fp32), epilogue: the
-//           order-preserving key of each score, 0 past the query's blocks;
+//           order-preserving key of each (scaled) score, 0 past the query's
+//           blocks;
 //   select  one workgroup per query: the exact top-k over its keys, held
 //           in LDS (a linear histogram, then the boundary bin ranked);
 //   attend  workgroup (query, split, KV head): the tile routine of the decode
@@ -58,6 +59,8 @@ __global__ __launch_bounds__(256) void k_chunk_append(ChunkArgs c)
 // ------------------------------------------------------------------- prep
 
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 // One wave per query (4 per workgroup).  Lane g owns elements 8g .. 8g+7 of
 // the H*D contraction.  Output: for query tile qt (16 queries) and k-step ks
@@ -119,170 +122,169 @@ __device__ inline uint32_t chunk_key(float s)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-constexpr int kXcds = 8;                     // accelerator dies of an MI355X, each with its own L2
-constexpr int kSQT = 8;                      // query tiles (16 queries) per workgroup
-constexpr int kSRT = 4;                      // block row tiles (16 blocks) per wave
+constexpr int kSQT = 8;                      // query tiles (16 queries) per LDS stage
+constexpr int kSRT = 2;                      // block row tiles (16 blocks) per wave
 constexpr int kSBlocks = 4 * kSRT * 16;      // blocks per workgroup (4 waves)
 
 template <bool F16, int KS>
 struct ScShape {
-    static constexpr int KC = (F16 ? 4 : 2) < KS ? (F16 ? 4 : 2) : KS;   // k-steps per stage
-    static constexpr int NST = KS / KC;                                   // stages
+    static constexpr int KC = (F16 ? 4 : 2) < KS ? (F16 ? 4 : 2) : KS;   // k-steps per LDS stage
+    static constexpr int NST = KS / KC;                                   // stages per query group
     static constexpr int ES = F16 ? 2 : 4;                                // summary element bytes
-    static constexpr int AP = ES / 2;                                     // 16-byte A loads per k-step
-    static constexpr int BSEG = kSQT * KC * 2;                            // 1 KB B segments per stage
-    static constexpr int BPT = BSEG * 64 / 256;                           // 16-byte B loads per thread
 };
 
-// Workgroup (256 blocks, 128 queries), 4 waves; wave w holds the 64 x 128
-// block-query products of blocks 64w .. 64w+63 in 32 accumulator tiles.  The
-// summary rows are the A operand, loaded straight from memory (lane l: row
-// l % 16, 8 elements at 8 (l / 16)); the queries' operand tiles are staged in
-// LDS, KC k-steps at a time, shared by the 4 waves.  Both operands of stage
-// s + 1 are loaded while stage s runs on the matrix cores.
+// Workgroup = 128 blocks x every query, 4 waves.  Wave w keeps the A operand
+// of its 32 blocks (two 16-row tiles, every k-step, f16 hi -- and lo for fp32
+// summaries) in registers for the whole kernel: the summaries are read once.
+// The queries stream through LDS, 128 queries x KC k-steps per stage, the
+// next stage loaded straight into the other LDS buffer while the current one
+// runs on the matrix cores; each B fragment read from LDS feeds both row tiles.  After the last
+// stage of a query group, the epilogue writes its keys.
 template <bool F16, int KS>
 __global__ __launch_bounds__(256) void k_chunk_score(ChunkArgs c)
 {
     using S = ScShape<F16, KS>;
-    constexpr int KC = S::KC, NST = S::NST, ES = S::ES, AP = S::AP, BPT = S::BPT;
+    constexpr int KC = S::KC, NST = S::NST, ES = S::ES;
     extern __shared__ uint4 sc_lds[];
-    uint4 (*sb)[KC][2][64] = reinterpret_cast<uint4 (*)[KC][2][64]>(sc_lds);   // [kSQT][KC][2][64]
+    uint4 (*sb)[kSQT][KC][2][64] = reinterpret_cast<uint4 (*)[kSQT][KC][2][64]>(sc_lds);   // [2][kSQT][KC][2][64]
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     constexpr int QK = 32 * KS;
     const int QT = (c.n_q + 15) / 16;
-    // XCD-aware order: workgroups are dealt to the 8 XCDs in turn, so the
-    // query groups of one block tile are made consecutive on one XCD -- the
-    // tile's summary rows come from that XCD's L2 after the first read
     const int nqg = (QT + kSQT - 1) / kSQT;
-    const int nbt = (c.nb_last + kSBlocks - 1) / kSBlocks;
-    const int xcd = (int)blockIdx.x % kXcds, j = (int)blockIdx.x / kXcds;
-    const int bt = (j / nqg) * kXcds + xcd, qg = j % nqg;
-    if (bt >= nbt)
-        return;
-    const int qt0 = qg * kSQT;
-    const int64_t bw = (int64_t)bt * kSBlocks + wave * kSRT * 16;
+    const int64_t bw = (int64_t)blockIdx.x * kSBlocks + wave * kSRT * 16;
     const int mr = lane & 15, kg = lane >> 4;
 
-    const char *rowp[kSRT];
+    // A: lane l holds row l % 16 of each row tile, elements 32 ks + 8 (l / 16) .. +8
+    half8 ah[kSRT][KS], al[kSRT][F16 ? 1 : KS];
 #pragma unroll
     for (int rt = 0; rt < kSRT; ++rt) {
         int64_t r = bw + 16 * rt + mr;
         r = r < c.nb_last ? r : c.nb_last - 1;
-        rowp[rt] = (const char *)c.summary + ((size_t)r * QK + 8 * kg) * ES;
+        const char *row = (const char *)c.summary + ((size_t)r * QK + 8 * kg) * ES;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if constexpr (F16) {
+                const uint4 v = *(const uint4 *)(row + (size_t)(32 * ks) * ES);
+                __builtin_memcpy(&ah[rt][ks], &v, 16);
+            } else {
+                float f[8];
+                const uint4 v0 = *(const uint4 *)(row + (size_t)(32 * ks) * ES);
+                const uint4 v1 = *(const uint4 *)(row + (size_t)(32 * ks) * ES + 16);
+                __builtin_memcpy(f, &v0, 16);
+                __builtin_memcpy(f + 4, &v1, 16);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    ah[rt][ks][j] = (_Float16)f[j];
+                    al[rt][ks][j] = (_Float16)(f[j] - (float)ah[rt][ks][j]);
+                }
+            }
+        }
     }
-    float4v acc[kSRT][kSQT];
-#pragma unroll
-    for (int rt = 0; rt < kSRT; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < kSQT; ++ct)
-            acc[rt][ct] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
 
+    // B stages: 128 queries x KC k-steps, 64 segments (ct, kk, hl) of 64
+    // 16-byte operand slots, double-buffered in LDS and filled straight from
+    // memory (global_load_lds: lane l's 16 bytes land at the segment base +
+    // 16 l); wave w issues segments w, w + 4, ...  The query operand buffer is
+    // padded with zeros to whole groups of 128 queries.
     const uint4 *qsrc = (const uint4 *)c.qhl;
-    auto load_a = [&](int st, uint4 (&ar)[kSRT][KC][AP]) __attribute__((always_inline)) {
+    constexpr int NSEG = kSQT * KC * 2;
+    auto issue_b = [&](int qg, int kc, int buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < NSEG / 4; ++u) {
+            const int seg = wave + 4 * u;
+            const int hl = seg & 1, kk = (seg >> 1) % KC, ct = (seg >> 1) / KC;
+            const int qt = qg * kSQT + ct;
+            const uint4 *src = qsrc + (((size_t)qt * KS + kc * KC + kk) * 2 + hl) * 64 + lane;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                             (__attribute__((address_space(3))) void *)&sb[buf][ct][kk][hl][0],
+                                             16, 0, 0);
+        }
+    };
+
+    const int nst = nqg * NST;
+    issue_b(0, 0, 0);
+    for (int qg = 0; qg < nqg; ++qg) {
+        float4v acc[kSRT][kSQT];
 #pragma unroll
         for (int rt = 0; rt < kSRT; ++rt)
 #pragma unroll
-            for (int kk = 0; kk < KC; ++kk)
+            for (int ct = 0; ct < kSQT; ++ct)
+                acc[rt][ct] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int p = 0; p < AP; ++p)
-                    ar[rt][kk][p] = *(const uint4 *)(rowp[rt] + (size_t)(32 * (st * KC + kk)) * ES + 16 * p);
-    };
-    // B segment x = (ct, kk, hl): 64 consecutive 16-byte operand slots
-    auto load_b = [&](int st, uint4 (&br)[BPT]) __attribute__((always_inline)) {
+        for (int kc = 0; kc < NST; ++kc) {
+            const int gs = qg * NST + kc, buf = gs & 1;
+            // this stage's segments (every wave's) have landed, and every
+            // wave is done with the other buffer (read in stage gs - 1)
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            if (gs + 1 < nst)
+                issue_b(kc + 1 < NST ? qg : qg + 1, kc + 1 < NST ? kc + 1 : 0, buf ^ 1);
+            // fragments f = (kk, hl, ct) in this order, read from LDS FD
+            // ahead of their two MFMAs (both row tiles); the order is pinned so
+            // that the reads stay ahead, and a tile's hi and lo products are
+            // 16 MFMAs apart
+            constexpr int NF = KC * 2 * kSQT, FD = 4;
+            auto frag = [&](int f) __attribute__((always_inline)) -> half8 {
+                const int ct = f % kSQT, hl = (f / kSQT) & 1, kk = f / (2 * kSQT);
+                half8 x;
+                __builtin_memcpy(&x, &sb[buf][ct][kk][hl][lane], 16);
+                return x;
+            };
+            half8 fr[FD];
 #pragma unroll
-        for (int u = 0; u < BPT; ++u) {
-            const int i = t + 256 * u;
-            const int ln = i & 63, hl = (i >> 6) & 1, kk = (i >> 7) % KC, ct = (i >> 7) / KC;
-            br[u] = qt0 + ct < QT ? qsrc[(((size_t)(qt0 + ct) * KS + st * KC + kk) * 2 + hl) * 64 + ln]
-                                  : make_uint4(0u, 0u, 0u, 0u);
-        }
-    };
-
-    uint4 a_cur[kSRT][KC][AP], a_nxt[kSRT][KC][AP], b_nxt[BPT];
-    load_a(0, a_cur);
-    load_b(0, b_nxt);
+            for (int f = 0; f < FD; ++f)
+                fr[f] = frag(f);
 #pragma unroll
-    for (int st = 0; st < NST; ++st) {
-        if (st > 0)
-            __syncthreads();             // stage st-1's B reads are done
+            for (int f = 0; f < NF; ++f) {
+                const int ct = f % kSQT, hl = (f / kSQT) & 1, ks = kc * KC + f / (2 * kSQT);
 #pragma unroll
-        for (int u = 0; u < BPT; ++u) {
-            const int i = t + 256 * u;
-            const int ln = i & 63, hl = (i >> 6) & 1, kk = (i >> 7) % KC, ct = (i >> 7) / KC;
-            sb[ct][kk][hl][ln] = b_nxt[u];
-        }
-        __syncthreads();
-        if (st + 1 < NST) {
-            load_a(st + 1, a_nxt);
-            load_b(st + 1, b_nxt);
-        }
+                for (int rt = 0; rt < kSRT; ++rt)
+                    acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[rt][ks], fr[f % FD], acc[rt][ct], 0, 0, 0);
+                if constexpr (!F16) {
+                    if (hl == 0) {
 #pragma unroll
-        for (int kk = 0; kk < KC; ++kk) {
-            half8 ah[kSRT], al[kSRT];
-#pragma unroll
-            for (int rt = 0; rt < kSRT; ++rt) {
-                if constexpr (F16) {
-                    __builtin_memcpy(&ah[rt], &a_cur[rt][kk][0], 16);
-                } else {
-                    float f[8];
-                    __builtin_memcpy(f, &a_cur[rt][kk][0], 32);
-#pragma unroll
-                    for (int j = 0; j < 8; ++j) {
-                        ah[rt][j] = (_Float16)f[j];
-                        al[rt][j] = (_Float16)(f[j] - (float)ah[rt][j]);
+                        for (int rt = 0; rt < kSRT; ++rt)
+                            acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[rt][ks], fr[f % FD], acc[rt][ct], 0, 0, 0);
                     }
                 }
-            }
-#pragma unroll
-            for (int ct = 0; ct < kSQT; ++ct) {
-                half8 bh, bl;
-                __builtin_memcpy(&bh, &sb[ct][kk][0][lane], 16);
-                __builtin_memcpy(&bl, &sb[ct][kk][1][lane], 16);
-#pragma unroll
-                for (int rt = 0; rt < kSRT; ++rt) {
-                    acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[rt], bh, acc[rt][ct], 0, 0, 0);
-                    acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[rt], bl, acc[rt][ct], 0, 0, 0);
-                    if constexpr (!F16)
-                        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[rt], bh, acc[rt][ct], 0, 0, 0);
-                }
+                if (f + FD < NF)
+                    fr[f % FD] = frag(f + FD);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-        if (st + 1 < NST) {
-#pragma unroll
-            for (int rt = 0; rt < kSRT; ++rt)
-#pragma unroll
-                for (int kk = 0; kk < KC; ++kk)
-#pragma unroll
-                    for (int p = 0; p < AP; ++p)
-                        a_cur[rt][kk][p] = a_nxt[rt][kk][p];
-        }
-    }
 
-    // lane l holds D[block 4 (l / 16) + j][query l % 16] of each tile
+        // lane l holds D[block 4 (l / 16) + j][query l % 16] of each tile.
+        // The keys are taken on the scaled sums: a query's keys are compared
+        // only with each other, and its power-of-two factor is exact, so it
+        // changes neither their order nor their ties; only the optional fp32
+        // scores are scaled back.
 #pragma unroll
-    for (int ct = 0; ct < kSQT; ++ct) {
-        const int qi = (qt0 + ct) * 16 + mr;
-        if (qi >= c.n_q)
-            continue;
-        const float f = c.qscale[qi];
-        const int64_t nbq = ((int64_t)c.n0 + qi + 1) >> 2;
+        for (int ct = 0; ct < kSQT; ++ct) {
+            const int qi = (qg * kSQT + ct) * 16 + mr;
+            if (qi >= c.n_q)
+                continue;
+            const int64_t nbq = ((int64_t)c.n0 + qi + 1) >> 2;
 #pragma unroll
-        for (int rt = 0; rt < kSRT; ++rt) {
-            const int64_t b = bw + 16 * rt + 4 * kg;
-            float sc[4];
-            uint32_t key[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                sc[j] = acc[rt][ct][j] * f;
-                key[j] = b + j < nbq ? chunk_key(sc[j]) : 0u;
-            }
-            if (b < c.ldk)
-                *(uint4 *)(c.keys + (size_t)qi * c.ldk + b) = make_uint4(key[0], key[1], key[2], key[3]);
-            if (c.scores_out) {
+            for (int rt = 0; rt < kSRT; ++rt) {
+                const int64_t b = bw + 16 * rt + 4 * kg;
+                u32x4 key;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    if (b + j < c.nb_last)
-                        c.scores_out[(size_t)qi * c.nb_last + b + j] = b + j < nbq ? sc[j] : -INFINITY;
+                    key[j] = b + j < nbq ? chunk_key(acc[rt][ct][j]) : 0u;
+                if (b < c.ldk)
+                    *(u32x4 *)(c.keys + (size_t)qi * c.ldk + b) = key;
+            }
+            if (c.scores_out) {
+                const float f = c.qscale[qi];
+#pragma unroll
+                for (int rt = 0; rt < kSRT; ++rt) {
+                    const int64_t b = bw + 16 * rt + 4 * kg;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (b + j < c.nb_last)
+                            c.scores_out[(size_t)qi * c.nb_last + b + j] =
+                                b + j < nbq ? acc[rt][ct][j] * f : -INFINITY;
+                }
             }
         }
     }
@@ -292,7 +294,7 @@ template <bool F16, int KS>
 hipError_t score_go(const ChunkArgs &c, dim3 grid, hipStream_t s)
 {
     using S = ScShape<F16, KS>;
-    const size_t lds = sizeof(uint4) * kSQT * S::KC * 2 * 64;
+    const size_t lds = 2 * sizeof(uint4) * kSQT * S::KC * 2 * 64;
     if (lds > 64 * 1024) {
         static hipError_t attr = hipFuncSetAttribute((const void *)k_chunk_score<F16, KS>,
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -310,7 +312,10 @@ hipError_t score_ks(const ChunkArgs &c, dim3 grid, hipStream_t s)
     case 2: return score_go<F16, 2>(c, grid, s);
     case 4: return score_go<F16, 4>(c, grid, s);
     case 8: return score_go<F16, 8>(c, grid, s);
-    case 16: return score_go<F16, 16>(c, grid, s);
+    case 16:   // fp32 rows are at most 1 KB: 256 elements
+        if constexpr (F16)
+            return score_go<F16, 16>(c, grid, s);
+        break;
     }
     return hipErrorInvalidValue;
 }
@@ -377,8 +382,6 @@ constexpr int kCAW = kCAT / kWave;
 
 // Up to eight registers named at compile time (arrays indexed in a loop that
 // spans the iteration loop end up in scratch memory).
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 template <class T>
 struct Regs8 {
@@ -876,12 +879,13 @@ hipError_t launch_chunk_rest(ChunkArgs c, bool f16, int Dh, int G, hipStream_t s
     hipError_t e;
     // scoring and selection only when some query has more blocks than it keeps
     if (c.nb_last > c.kb) {
+        // query tiles padded to whole groups of kSQT (zero-filled by the prep)
         const int qt = (c.n_q + 15) / 16;
-        hipLaunchKernelGGL(k_chunk_prep, dim3(qt * 4), dim3(256), 0, s, c);
+        const int qt_pad = (qt + kSQT - 1) / kSQT * kSQT;
+        hipLaunchKernelGGL(k_chunk_prep, dim3(qt_pad * 4), dim3(256), 0, s, c);
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
-        const int nbt = (c.nb_last + kSBlocks - 1) / kSBlocks, nqg = (qt + kSQT - 1) / kSQT;
-        const dim3 grid((unsigned)(kXcds * ((nbt + kXcds - 1) / kXcds) * nqg));
+        const dim3 grid((unsigned)((c.nb_last + kSBlocks - 1) / kSBlocks));
         e = f16 ? score_ks<true>(c, grid, s) : score_ks<false>(c, grid, s);
         if (e != hipSuccess)
             return e;

@@ -116,7 +116,7 @@ ChunkLayout chunk_layout(const qsa_layer_desc *d, int32_t capacity, int32_t n_q)
         return o;
     };
     const size_t qk = (size_t)d->idx_heads * d->idx_dim;
-    const size_t qpad = ((size_t)n_q + 15) / 16 * 16;
+    const size_t qpad = ((size_t)n_q + 127) / 128 * 128;   // whole groups of 128 queries
     const size_t ldk = ((size_t)capacity / 4 + 3) / 4 * 4;
     const int G = d->q_heads / d->kv_heads;
     L.qhl = take(qpad * qk * 2 * sizeof(uint16_t));
