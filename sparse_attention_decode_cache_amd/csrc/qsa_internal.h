@@ -137,7 +137,7 @@ struct AttendArgs {
     int32_t nb;                 // floor(n_tokens / 4)
     int32_t n_cells;            // cells of the attention splits
     int32_t n_tail;             // cells 4*nb + j, j < n_tail, folded in by the merge
-    int32_t n_split;
+    int32_t n_split;            // splits per KV head (partials [kv_heads][n_split])
     int32_t kv_heads;
     float scale;
 };
@@ -180,7 +180,8 @@ struct ChunkArgs {
     float *out;                 // [n_q][Hq][Dh]
     int32_t *sel_out;           // optional [n_q][kb]
     float *scores_out;          // optional [n_q][nb_last]
-    _Float16 *qhl;              // workspace: folded queries, MFMA operand layout
+    _Float16 *qhl;              // workspace: folded queries, MFMA operand layout, padded with
+                                // zeros to whole groups of 128 queries
     float *qscale;              // workspace: [n_q] power-of-two factors
     uint32_t *keys;             // workspace: [n_q][ldk]
     int32_t *sel;               // workspace: [n_q][kb]
