@@ -236,7 +236,9 @@ qsa_status qsa_decode_step_batch(const qsa_layer_desc *desc, int32_t n_seq,
  * Scoring runs as one f16 matrix-core GEMM of all queries against all blocks:
  * the query q_idx[i][h] * w[i][h] is scaled by a power of two and split into
  * two f16 halves so that the products keep fp32 accuracy (fp32 summaries are
- * split likewise).
+ * split likewise).  A chunk of at most QSA_MAX_MULTI tokens runs as
+ * qsa_decode_step_multi instead (same results; scores_out then written
+ * whenever nb_last > 0).
  *
  * idx_k_rows: DEVICE [n_q][H_i][D_i] idx_dtype; k_rows, v_rows: DEVICE
  * [n_q][Hkv][Dh] binary16; q_idx: DEVICE fp32 [n_q][H_i][D_i]; w: DEVICE fp32
@@ -264,6 +266,52 @@ qsa_status qsa_chunk_step(const qsa_layer_desc *desc, const qsa_layer_cache *cac
                           const float *q_idx, const float *w, const float *q, float *out,
                           int32_t *sel_out, float *scores_out, void *ws, size_t ws_bytes,
                           hipStream_t stream);
+
+/* ------------------------------------------------ multi-query decode
+ * Speculative verification: the token at pos_0 = st->n_tokens and up to
+ * QSA_MAX_MULTI - 1 drafted tokens after it, decoded in one call with the
+ * results of n_q qsa_decode_step calls in a row [post 10, "QSA indexer",
+ * "incremental pooled-key cache（COMMON-004）", "selected QSA K/V gather
+ * （COMMON-005）": the per-token step; running a few tokens of one sequence
+ * through it together is this library's].  Token i is appended at pos_i =
+ * pos_0 + i and its query sees n_i = pos_i + 1 tokens: the floor(n_i / 4)
+ * blocks completed by then (never a block completed by a later token of the
+ * call), its own top K = top_k_tokens / 4 of them by its own indexer score,
+ * and its tail of n_i mod 4 cells.  Every summary row is read once for all
+ * queries; the top-k and the gather-attention run per query.
+ *
+ * Rejected drafts [dirty-range protection; post 10, COMMON-004 section: the
+ * cache is invalidated on a sequence edit]: after accepting a tokens of the
+ * call, qsa_state_truncate(st, pos_0 + a) drops the rest and lowers the
+ * summary watermark below any block that held a dropped token, so the next
+ * step that completes that block pools it again from the rows then in the
+ * cache.  Rows of dropped tokens are overwritten by the next appends.
+ *
+ * Arguments and layouts as in qsa_chunk_step (idx_k_rows [n_q][H_i][D_i],
+ * k_rows / v_rows [n_q][Hkv][Dh], q_idx [n_q][H_i][D_i], w [n_q][H_i], q and
+ * out [n_q][Hq][Dh], all DEVICE, rows, q_idx, q and out 16-byte aligned).
+ * sel_out (optional, DEVICE int32 [n_q][K]): row i gets the min(K,
+ * floor(n_i/4)) chosen ids ascending, then -1.  scores_out (optional, DEVICE
+ * fp32 [n_q][nb_last], nb_last = floor((pos_0 + n_q) / 4)): entry (i, b) is
+ * query i's score of block b for b < floor(n_i / 4), -INFINITY past it
+ * (written whenever nb_last > 0).  Workspace >= qsa_multi_workspace_bytes.
+ * On success st becomes {pos_0 + n_q, nb_last}; on any error nothing is
+ * enqueued and st is unchanged.
+ * Errors: ARG if n_q is outside [1, QSA_MAX_MULTI], a pointer is null or
+ * misaligned, or pos_0 + n_q > capacity; UNSUPPORTED / WORKSPACE as in
+ * qsa_decode_step. */
+#define QSA_MAX_MULTI 4
+
+/* Workspace bytes for qsa_decode_step_multi of up to n_q tokens on a cache of
+ * the given capacity; 0 if the desc, capacity or n_q is invalid. */
+size_t qsa_multi_workspace_bytes(const qsa_layer_desc *desc, int32_t capacity, int32_t n_q);
+
+qsa_status qsa_decode_step_multi(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
+                                 qsa_seq_state *st, int32_t n_q, const void *idx_k_rows,
+                                 const uint16_t *k_rows, const uint16_t *v_rows,
+                                 const float *gamma, const float *q_idx, const float *w,
+                                 const float *q, float *out, int32_t *sel_out, float *scores_out,
+                                 void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Static text for a status code. */
 const char *qsa_status_string(qsa_status s);

@@ -249,6 +249,29 @@ __global__ __launch_bounds__(kMT) void k_merge_batch(AttendBatchArgs b)
     merge_unit<DH, G>(b.seq[s], ml, (int)blockIdx.x % hq, blockIdx.y);
 }
 
+// Prefill chunk with few queries: grid (query x query head, 64-dim slice);
+// query i's partials are [kv_heads][n_split] at part + i * kv_heads * n_split
+// partials, its output [Hq][DH] at out + i * Hq * DH.
+struct ChunkMergeArgs {
+    float *part;
+    float *out;
+    int32_t kv_heads, n_split;
+};
+
+template <int DH, int G>
+__global__ __launch_bounds__(kMT) void k_merge_chunk(ChunkMergeArgs m)
+{
+    __shared__ MergeLds ml;
+    const int hq = m.kv_heads * G;
+    const int i = (int)blockIdx.x / hq;
+    AttendArgs a{};
+    a.part = m.part + (size_t)i * m.kv_heads * m.n_split * part_stride(G, DH);
+    a.out = m.out + (size_t)i * hq * DH;
+    a.n_split = m.n_split;
+    a.kv_heads = m.kv_heads;
+    merge_unit<DH, G>(a, ml, (int)blockIdx.x % hq, blockIdx.y);
+}
+
 template <int DH, int G>
 hipError_t merge(const AttendArgs &a, hipStream_t s)
 {
@@ -312,6 +335,32 @@ hipError_t dispatch(const AttendArgs &a, const SelectArgs *sa, int Dh, int G, hi
 hipError_t launch_attend(const AttendArgs &a, int Dh, int G, hipStream_t s)
 {
     return dispatch(a, nullptr, Dh, G, s);
+}
+
+hipError_t launch_merge_chunk(float *part, float *out, int n_q, int kv_heads, int n_split, int Dh,
+                              int G, hipStream_t s)
+{
+    if (n_q < 1 || n_split < 1 || n_split > kMaxSplits)
+        return hipErrorInvalidValue;
+    const ChunkMergeArgs m{part, out, kv_heads, n_split};
+    const dim3 grid((unsigned)(n_q * kv_heads * G), (unsigned)(Dh / kWave));
+#define QSA_MERGE_G(DHV)                                                                \
+    switch (G) {                                                                        \
+    case 1: hipLaunchKernelGGL((k_merge_chunk<DHV, 1>), grid, dim3(kMT), 0, s, m); break; \
+    case 2: hipLaunchKernelGGL((k_merge_chunk<DHV, 2>), grid, dim3(kMT), 0, s, m); break; \
+    case 4: hipLaunchKernelGGL((k_merge_chunk<DHV, 4>), grid, dim3(kMT), 0, s, m); break; \
+    case 8: hipLaunchKernelGGL((k_merge_chunk<DHV, 8>), grid, dim3(kMT), 0, s, m); break; \
+    default: return hipErrorInvalidValue;                                               \
+    }                                                                                   \
+    break;
+    switch (Dh) {
+    case 64: QSA_MERGE_G(64)
+    case 128: QSA_MERGE_G(128)
+    case 256: QSA_MERGE_G(256)
+    default: return hipErrorInvalidValue;
+    }
+#undef QSA_MERGE_G
+    return hipGetLastError();
 }
 
 hipError_t launch_merge_batch(const AttendBatchArgs &b, int Dh, int G, hipStream_t s)

@@ -746,38 +746,6 @@ __global__ __launch_bounds__(kCAT, 2) void k_batch_attend(AttendBatchArgs b)
     attend_unit<DH, G>(u, L, local % a.n_split, local / a.n_split);
 }
 
-// out = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s over the ns split
-// partials of one (query, KV head), in split order.  Whole workgroup calls.
-template <int DH, int G>
-__device__ void merge_partials(const float *base, int ns, float *out)
-{
-    const size_t ps = (size_t)part_stride(G, DH);
-    for (int idx = threadIdx.x; idx < G * DH; idx += 256) {
-        const int h = idx / DH;
-        float M = -INFINITY;
-        for (int s = 0; s < ns; ++s)
-            M = fmaxf(M, base[s * ps + h]);
-        float A = 0.0f, Ls = 0.0f;
-        for (int s = 0; s < ns; ++s) {
-            const float m = base[s * ps + h];
-            const float w = m == -INFINITY ? 0.0f : expf(m - M);
-            A = fmaf(w, base[s * ps + 2 * G + idx], A);
-            Ls = fmaf(w, base[s * ps + G + h], Ls);
-        }
-        out[idx] = A / Ls;
-    }
-}
-
-// Workgroup (query, KV head): out = sum_s e^(m_s - M) acc_s / sum_s e^(m_s - M) l_s
-// over the splits, in split order.
-template <int DH, int G>
-__global__ __launch_bounds__(256) void k_chunk_merge(ChunkArgs c)
-{
-    const int unit = blockIdx.x;
-    merge_partials<DH, G>(c.part + (size_t)unit * c.n_split * part_stride(G, DH), c.n_split,
-                          c.out + (size_t)unit * G * DH);
-}
-
 template <int DH, int G>
 hipError_t attend_go(const ChunkArgs &c, hipStream_t s)
 {
@@ -792,8 +760,7 @@ hipError_t attend_go(const ChunkArgs &c, hipStream_t s)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || c.n_split == 1)
         return e;
-    hipLaunchKernelGGL((k_chunk_merge<DH, G>), dim3(c.n_q * c.kv_heads), dim3(256), 0, s, c);
-    return hipGetLastError();
+    return launch_merge_chunk(c.part, c.out, c.n_q, c.kv_heads, c.n_split, DH, G, s);
 }
 
 template <int DH, int G>

@@ -271,6 +271,194 @@ __global__ __launch_bounds__(256) void k_score_batch(ScoreBatchArgs b)
     score_tile<F16, LPR>(b.seq[s], sl, tile, local == 0 && b.seq[s].fuse);
 }
 
+// Q queries of one sequence in one pass (speculative verify): the tile's
+// rows are loaded once, as in score_tile, and every 16-byte chunk is
+// widened once and dotted with all Q queries.  The folded queries w[h] q[h]
+// sit in LDS and are read one chunk position at a time, so the registers
+// hold the row loads, one chunk of every query and Q x V sums whatever Q
+// is.  Query i sees the rows below a.nbq[i]; the rest get no key, no list
+// entry and a score of -inf.  The butterfly, keys and lists are those of the
+// single query, once per query.
+template <int LPR, int Q, int EPL>
+struct ScoreMultiLds {
+    float qw[Q][LPR * EPL];
+    uint64_t c[Q][ScoreShape<LPR>::R];
+    u32x4 fresh[LPR];
+};
+
+template <bool F16, int LPR, int Q>
+__global__ __launch_bounds__(256) void k_score_multi(ScoreMultiArgs a)
+{
+    using S = ScoreShape<LPR>;
+    constexpr int EPL = F16 ? 8 : 4;
+    constexpr int L = S::L, C = S::C, RI = S::RI, V = S::V, R = S::R;
+    constexpr int ROWB = LPR * 16;
+    constexpr int HD = LPR * EPL;              // elements of a row
+    constexpr int QPT = (Q * HD / 4 + 255) / 256;   // float4 groups of queries per thread
+    __shared__ ScoreMultiLds<LPR, Q, EPL> sl;
+
+    // workgroup 0 (dispatched first) takes the last tile: the one holding the new row
+    const int tile = blockIdx.x == 0 ? (int)gridDim.x - 1 : (int)blockIdx.x - 1;
+    const bool pool_here = blockIdx.x == 0 && a.fuse;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int col = lane % L;
+    const int sub = lane / L;
+    const int64_t base = (int64_t)tile * R + (int64_t)wave * S::RPW;
+
+    // the queries' float4 groups this thread folds into LDS, loaded ahead of the rows
+    float4 qraw[QPT];
+    float wraw[QPT];
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+        const int g4 = (int)threadIdx.x + 256 * j;
+        if (g4 < Q * HD / 4) {
+            const int qi = g4 / (HD / 4), e0 = 4 * (g4 % (HD / 4));
+            qraw[j] = ((const float4 *)(a.q[qi] + e0))[0];
+            wraw[j] = a.w[qi][e0 / a.D];
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    const char *rows = (const char *)a.summary;
+    u32x4 buf[S::LOADS];
+#pragma unroll
+    for (int i = 0; i < S::LOADS; ++i) {
+        const int64_t r = base + (int64_t)(i / C) * RI + sub;
+        const u32x4 *src = (const u32x4 *)(rows + (r < a.nb ? r : 0) * ROWB) + col + L * (i % C);
+        buf[i] = __builtin_nontemporal_load(src);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+        const int g4 = (int)threadIdx.x + 256 * j;
+        if (g4 < Q * HD / 4) {
+            const int qi = g4 / (HD / 4), e0 = 4 * (g4 % (HD / 4));
+            float4 f = qraw[j];
+            f.x *= wraw[j];
+            f.y *= wraw[j];
+            f.z *= wraw[j];
+            f.w *= wraw[j];
+            *(float4 *)&sl.qw[qi][e0] = f;
+        }
+    }
+
+    if (pool_here) {
+        if (a.upd.new_idx_row)
+            append_rows(a.upd, threadIdx.x, 256);
+        if (a.upd.nblk > 0)
+            pool_row<F16>(a.upd, a.upd.b0, threadIdx.x, sl.fresh);
+    }
+    __syncthreads();
+    if (pool_here && a.upd.nblk > 0) {
+#pragma unroll
+        for (int i = 0; i < S::LOADS; ++i) {
+            const int64_t r = base + (int64_t)(i / C) * RI + sub;
+            if (r == a.upd.b0)
+                buf[i] = sl.fresh[col + L * (i % C)];
+        }
+    }
+
+    float v[Q][V];
+#pragma unroll
+    for (int qi = 0; qi < Q; ++qi)
+#pragma unroll
+        for (int g = 0; g < V; ++g)
+            v[qi][g] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int e0 = (col + L * c) * EPL;
+        float qw[Q][EPL];
+#pragma unroll
+        for (int qi = 0; qi < Q; ++qi)
+#pragma unroll
+            for (int k4 = 0; k4 < EPL / 4; ++k4) {
+                const float4 f = *(const float4 *)&sl.qw[qi][e0 + 4 * k4];
+                qw[qi][4 * k4] = f.x;
+                qw[qi][4 * k4 + 1] = f.y;
+                qw[qi][4 * k4 + 2] = f.z;
+                qw[qi][4 * k4 + 3] = f.w;
+            }
+#pragma unroll
+        for (int g = 0; g < V; ++g) {
+            const u32x4 &b = buf[g * C + c];
+            if constexpr (F16) {
+                half8 h;
+                __builtin_memcpy(&h, &b, 16);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const float x = (float)h[k];
+#pragma unroll
+                    for (int qi = 0; qi < Q; ++qi)
+                        v[qi][g] = fmaf(qw[qi][k], x, v[qi][g]);
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const float x = __uint_as_float(b[k]);
+#pragma unroll
+                    for (int qi = 0; qi < Q; ++qi)
+                        v[qi][g] = fmaf(qw[qi][k], x, v[qi][g]);
+                }
+            }
+        }
+    }
+
+    int toff = 0;
+#pragma unroll
+    for (int qi = 0; qi < Q; ++qi) {
+        int t = 0;
+        Butterfly<L / 2, V>::run(v[qi], lane, t);
+        toff = t;                              // the same for every query
+    }
+
+    constexpr int OWN = L / V;
+    const int local = wave * S::RPW + toff * RI + sub;
+    const int64_t r = (int64_t)tile * R + local;
+    if (col % OWN == 0) {
+#pragma unroll
+        for (int qi = 0; qi < Q; ++qi) {
+            uint64_t c = 0;
+            if (r < a.nbq[qi]) {
+                const float sc = v[qi][0];
+                if (a.scores)
+                    a.scores[qi * a.ld_scores + r] = sc;
+                if (a.keys[qi]) {
+                    const uint32_t key = score_key(sc);
+                    a.keys[qi][r] = key;
+                    c = comp_key(key, (uint32_t)r);
+                }
+            } else if (r < a.nb && a.scores) {
+                a.scores[qi * a.ld_scores + r] = -__builtin_inff();
+            }
+            sl.c[qi][local] = c;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int qi = 0; qi < Q; ++qi) {
+        if (a.lists[qi]) {
+            const int64_t valid = a.nbq[qi] - (int64_t)tile * R;
+            write_tile_list<R, R / kListDiv>(sl.c[qi], a.lists[qi], tile,
+                                             (int)(valid < 0 ? 0 : (valid < R ? valid : R)));
+        }
+    }
+}
+
+template <bool F16, int LPR>
+hipError_t go_multi(const ScoreMultiArgs &a, int n_q, hipStream_t s)
+{
+    const int grid = (int)((a.nb + ScoreShape<LPR>::R - 1) / ScoreShape<LPR>::R);
+    switch (n_q) {
+    case 2: hipLaunchKernelGGL((k_score_multi<F16, LPR, 2>), dim3(grid), dim3(256), 0, s, a); break;
+    case 3: hipLaunchKernelGGL((k_score_multi<F16, LPR, 3>), dim3(grid), dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_score_multi<F16, LPR, 4>), dim3(grid), dim3(256), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 // Keys and tile lists from given fp32 scores (stand-alone top-k), R = 256.
 __global__ __launch_bounds__(kKeysTile) void k_keys(const float *scores, int32_t nb, uint32_t *keys,
                                                     uint64_t *lists)
@@ -362,6 +550,29 @@ hipError_t launch_score_batch(ScoreBatchArgs &b, bool f16, int row_bytes, hipStr
         }
     }
     return hipGetLastError();
+}
+
+hipError_t launch_score_multi(const ScoreMultiArgs &a, int n_q, bool f16, int row_bytes,
+                              hipStream_t s)
+{
+    if (a.nb <= 0)
+        return hipSuccess;
+    const int lpr = row_bytes / 16;
+    if (f16) {
+        switch (lpr) {
+        case 8: return go_multi<true, 8>(a, n_q, s);
+        case 16: return go_multi<true, 16>(a, n_q, s);
+        case 32: return go_multi<true, 32>(a, n_q, s);
+        case 64: return go_multi<true, 64>(a, n_q, s);
+        }
+    } else {
+        switch (lpr) {
+        case 16: return go_multi<false, 16>(a, n_q, s);
+        case 32: return go_multi<false, 32>(a, n_q, s);
+        case 64: return go_multi<false, 64>(a, n_q, s);
+        }
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_keys(const float *scores, int32_t nb, uint32_t *keys, uint64_t *lists,

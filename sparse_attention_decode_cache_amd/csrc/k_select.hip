@@ -15,7 +15,7 @@ __global__ __launch_bounds__(sel::kT) void k_select(SelectArgs a)
 }
 
 // One workgroup per sequence of a batch; a sequence with nb <= k keeps every
-// block (its ids, if asked for, are 0..nb-1).
+// block (its ids, if asked for, are 0..nb-1, then -1 up to pad_to).
 __global__ __launch_bounds__(sel::kT) void k_select_batch(SelectBatchArgs b)
 {
     extern __shared__ uint4 sel_lds[];
@@ -23,8 +23,8 @@ __global__ __launch_bounds__(sel::kT) void k_select_batch(SelectBatchArgs b)
     int32_t *out = a.sel;
     if (a.nb <= a.k) {
         if (out)
-            for (int i = threadIdx.x; i < a.nb; i += sel::kT)
-                out[i] = i;
+            for (int i = threadIdx.x; i < a.nb || i < a.pad_to; i += sel::kT)
+                out[i] = i < a.nb ? i : -1;
         return;
     }
     sel::run(a, reinterpret_cast<char *>(sel_lds), [=](uint32_t slot, uint32_t id) {

@@ -406,6 +406,7 @@ qsa_status qsa_decode_step(const qsa_layer_desc *desc, const qsa_layer_cache *ca
     u.idx_row_words = rowb / 4;
     u.kv_row_words = desc->kv_heads * desc->head_dim / 2;
     u.pos = pos;
+    u.n_new = 1;
     u.b0 = b0;
     u.nblk = nb - b0;
     u.H = desc->idx_heads;
@@ -568,6 +569,7 @@ qsa_status qsa_decode_step_batch(const qsa_layer_desc *desc, int32_t n_seq,
         u.idx_row_words = rowb / 4;
         u.kv_row_words = desc->kv_heads * desc->head_dim / 2;
         u.pos = pos;
+        u.n_new = 1;
         u.b0 = b0;
         u.nblk = nb - b0;
         u.H = desc->idx_heads;
@@ -612,12 +614,158 @@ qsa_status qsa_decode_step_batch(const qsa_layer_desc *desc, int32_t n_seq,
     return ok();
 }
 
+size_t qsa_multi_workspace_bytes(const qsa_layer_desc *desc, int32_t capacity, int32_t n_q)
+{
+    if (check_desc(desc) != QSA_OK || capacity < 4 || capacity % 4 != 0 || capacity > (1 << 21) ||
+        n_q < 1 || n_q > QSA_MAX_MULTI)
+        return 0;
+    return (size_t)n_q * align256(decode_layout(desc, capacity).total);
+}
+
+qsa_status qsa_decode_step_multi(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
+                                 qsa_seq_state *st, int32_t n_q, const void *idx_k_rows,
+                                 const uint16_t *k_rows, const uint16_t *v_rows,
+                                 const float *gamma, const float *q_idx, const float *w,
+                                 const float *q, float *out, int32_t *sel_out, float *scores_out,
+                                 void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    qsa_status s;
+    if ((s = check_desc(desc)) != QSA_OK || (s = check_cache(cache, true, true, true)) != QSA_OK)
+        return s;
+    if (!st)
+        return fail(QSA_ERR_ARG, "state is NULL");
+    if (n_q < 1 || n_q > QSA_MAX_MULTI)
+        return fail(QSA_ERR_ARG, "n_q %d outside [1, %d]", n_q, QSA_MAX_MULTI);
+    if (!idx_k_rows || !k_rows || !v_rows || !gamma || !q_idx || !w || !q || !out)
+        return fail(QSA_ERR_ARG, "an input or output pointer is NULL");
+    if (!aligned(idx_k_rows, 16) || !aligned(k_rows, 16) || !aligned(v_rows, 16) ||
+        !aligned(q_idx, 16) || !aligned(q, 16) || !aligned(out, 16))
+        return fail(QSA_ERR_ARG, "row, q_idx, q or out pointer not 16-byte aligned");
+    const int32_t n0 = st->n_tokens;
+    if (n0 < 0 || (int64_t)n0 + n_q > cache->capacity)
+        return fail(QSA_ERR_ARG, "positions [%d, %lld) outside [0, %d)", n0,
+                    (long long)n0 + n_q, cache->capacity);
+    if (st->n_valid_blocks < 0)
+        return fail(QSA_ERR_ARG, "n_valid_blocks < 0");
+    const WsLayout L = decode_layout(desc, cache->capacity);
+    const size_t slot = align256(L.total);
+    if ((s = check_ws(ws, ws_bytes, (size_t)n_q * slot)) != QSA_OK)
+        return s;
+
+    const int32_t K = desc->top_k_tokens / 4;
+    const int32_t n_end = n0 + n_q, nb_last = n_end / 4;
+    const bool f16 = desc->idx_dtype == QSA_F16;
+    const int rowb = desc->idx_heads * desc->idx_dim * elem_bytes(desc->idx_dtype);
+    const int G = desc->q_heads / desc->kv_heads;
+    const int qk = desc->idx_heads * desc->idx_dim;
+    const int64_t qa = (int64_t)desc->q_heads * desc->head_dim;
+    const int32_t b0 = st->n_valid_blocks < nb_last ? st->n_valid_blocks : nb_last;
+    const bool any_select = nb_last > K;       // the last query sees the most blocks
+
+    // 1. append the n_q rows, pool [b0, nb_last): inside the score kernel's
+    //    first workgroup when at most one row is new, else in its own launch
+    UpdateArgs u{};
+    u.idx_k = cache->idx_k;
+    u.summary = cache->summary;
+    u.k = cache->k;
+    u.v = cache->v;
+    u.new_idx_row = idx_k_rows;
+    u.new_k_row = k_rows;
+    u.new_v_row = v_rows;
+    u.gamma = gamma;
+    u.idx_row_words = rowb / 4;
+    u.kv_row_words = desc->kv_heads * desc->head_dim / 2;
+    u.pos = n0;
+    u.n_new = n_q;
+    u.b0 = b0;
+    u.nblk = nb_last - b0;
+    u.H = desc->idx_heads;
+    u.D = desc->idx_dim;
+    u.eps = (double)desc->rms_eps;
+    u.theta = (double)desc->rope_theta;
+    const bool score = nb_last > 0 && (any_select || scores_out);
+    const bool fuse = score && u.nblk <= 1;
+    hipError_t e;
+    if (!fuse) {
+        e = launch_update(u, f16, stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "decode_step_multi/update");
+    }
+
+    // 2. one pass over the summaries for every query
+    const int tile_rows = score_tile_rows(f16, rowb);
+    SelectBatchArgs selb{};
+    AttendBatchArgs ab{};
+    selb.n = ab.n = n_q;
+    ScoreMultiArgs sm{};
+    sm.summary = cache->summary;
+    sm.nb = nb_last;
+    sm.D = desc->idx_dim;
+    sm.fuse = fuse ? 1 : 0;
+    sm.upd = u;
+    sm.scores = scores_out;
+    sm.ld_scores = nb_last;
+    for (int32_t i = 0; i < n_q; ++i) {
+        char *wsp = (char *)ws + (size_t)i * slot;
+        const int32_t n = n0 + i + 1, nb = n / 4;
+        const bool need_select = nb > K;
+        sm.nbq[i] = nb;
+        sm.q[i] = q_idx + (size_t)i * qk;
+        sm.w[i] = w + (size_t)i * desc->idx_heads;
+        sm.keys[i] = need_select ? (uint32_t *)(wsp + L.keys) : nullptr;
+        sm.lists[i] = need_select ? (uint64_t *)(wsp + L.lists) : nullptr;
+        int32_t *sel = sel_out ? sel_out + (size_t)i * K : (int32_t *)(wsp + L.sel);
+        selb.seq[i] = select_args(wsp, L, nb, K, tile_rows, need_select || sel_out ? sel : nullptr);
+        selb.seq[i].pad_to = sel_out ? K : 0;
+        ab.seq[i] = attend_args(desc, cache, n, need_select ? sel : nullptr, need_select ? K : nb,
+                                q + (size_t)i * qa, out + (size_t)i * qa,
+                                (float *)(wsp + L.part));
+    }
+    if (score) {
+        if (n_q == 1) {
+            ScoreArgs a{};
+            a.summary = sm.summary;
+            a.q = sm.q[0];
+            a.w = sm.w[0];
+            a.scores = scores_out;
+            a.keys = sm.keys[0];
+            a.lists = sm.lists[0];
+            a.nb = nb_last;
+            a.D = sm.D;
+            a.fuse = sm.fuse;
+            a.upd = u;
+            e = launch_score(a, f16, rowb, stream);
+        } else {
+            e = launch_score_multi(sm, n_q, f16, rowb, stream);
+        }
+        if (e != hipSuccess)
+            return hip_fail(e, "decode_step_multi/score");
+    }
+
+    // 3. per-query top-k (one workgroup per query), 4. per-query attention
+    if (any_select || sel_out) {
+        e = launch_select_batch(selb, stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "decode_step_multi/select");
+    }
+    e = launch_attend_batch(ab, desc->head_dim, G, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "decode_step_multi/attend");
+    st->n_tokens = n_end;
+    st->n_valid_blocks = nb_last;
+    return ok();
+}
+
 size_t qsa_chunk_workspace_bytes(const qsa_layer_desc *desc, int32_t capacity, int32_t n_q)
 {
     if (check_desc(desc) != QSA_OK || capacity < 4 || capacity % 4 != 0 || capacity > (1 << 21) ||
         n_q < 1 || n_q > QSA_MAX_CHUNK)
         return 0;
-    return chunk_layout(desc, capacity, n_q).total;
+    const size_t chunk = chunk_layout(desc, capacity, n_q).total;
+    if (n_q > QSA_MAX_MULTI)
+        return chunk;
+    const size_t multi = qsa_multi_workspace_bytes(desc, capacity, n_q);
+    return multi > chunk ? multi : chunk;
 }
 
 qsa_status qsa_chunk_step(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
@@ -645,6 +793,11 @@ qsa_status qsa_chunk_step(const qsa_layer_desc *desc, const qsa_layer_cache *cac
                     (long long)n0 + n_q, cache->capacity);
     if (st->n_valid_blocks < 0)
         return fail(QSA_ERR_ARG, "n_valid_blocks < 0");
+    // a few tokens: one pass over the summaries scores them all, without the
+    // GEMM's query preparation and its keys matrix
+    if (n_q <= QSA_MAX_MULTI)
+        return qsa_decode_step_multi(desc, cache, st, n_q, idx_k_rows, k_rows, v_rows, gamma, q_idx,
+                                     w, q, out, sel_out, scores_out, ws, ws_bytes, stream);
     const ChunkLayout L = chunk_layout(desc, cache->capacity, n_q);
     if ((s = check_ws(ws, ws_bytes, L.total)) != QSA_OK)
         return s;

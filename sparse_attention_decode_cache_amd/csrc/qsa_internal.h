@@ -62,6 +62,7 @@ struct UpdateArgs {
     int32_t idx_row_words;      // 32-bit words in one raw indexer-key row
     int32_t kv_row_words;       // 32-bit words in one K (or V) row
     int64_t pos;                // append position (ignored without new_idx_row)
+    int32_t n_new;              // rows appended at pos .. pos + n_new - 1 (with new_idx_row)
     int32_t b0, nblk;           // pool blocks [b0, b0 + nblk)
     int32_t H, D;
     double eps, theta;
@@ -93,6 +94,27 @@ hipError_t launch_score_batch(ScoreBatchArgs &b, bool f16, int row_bytes, hipStr
 // Rows per score workgroup (tile) for a given indexer row size.
 int score_tile_rows(bool f16, int row_bytes);
 
+// Several queries of one sequence (consecutive tokens: speculative verify)
+// scored in one pass over the summary rows.  Query i sees blocks [0, nbq[i]);
+// every summary row is loaded once and dotted with every query.
+constexpr int kMaxMulti = 4;
+struct ScoreMultiArgs {
+    const void *summary;
+    int32_t nb;                     // rows streamed: the last query's blocks
+    int32_t D;
+    int32_t fuse;                   // workgroup 0 first runs `upd` (append, pool <= 1 row)
+    UpdateArgs upd;
+    int32_t nbq[kMaxMulti];         // blocks seen by query i (<= nb)
+    const float *q[kMaxMulti];      // [H][D] fp32 per query
+    const float *w[kMaxMulti];      // [H] per query
+    uint32_t *keys[kMaxMulti];      // optional per query: [nb] order-preserving keys
+    uint64_t *lists[kMaxMulti];     // optional per query: per-tile top-T composites
+    float *scores;                  // optional [n_q][ld_scores]: -inf at b >= nbq[i]
+    int64_t ld_scores;
+};
+hipError_t launch_score_multi(const ScoreMultiArgs &a, int n_q, bool f16, int row_bytes,
+                              hipStream_t s);
+
 // Keys and per-tile lists (R = 256) from given fp32 scores.
 constexpr int kKeysTile = 256;
 hipError_t launch_keys(const float *scores, int32_t nb, uint32_t *keys, uint64_t *lists,
@@ -113,6 +135,7 @@ struct SelectArgs {
     int32_t T;
     int32_t lkeys_off;          // byte offset of an nb-word key cache in the dynamic LDS (0: none;
                                 // set by the launchers when it fits)
+    int32_t pad_to;             // batch select, nb <= k: slots [nb, pad_to) of sel get -1
 };
 hipError_t launch_select(const SelectArgs &a, hipStream_t s);
 struct SelectBatchArgs {
@@ -152,6 +175,9 @@ struct AttendBatchArgs {
 hipError_t launch_attend_batch(AttendBatchArgs &b, int Dh, int G, hipStream_t s);
 // The merge of a batch's split partials (one load round per output slice).
 hipError_t launch_merge_batch(const AttendBatchArgs &b, int Dh, int G, hipStream_t s);
+// The same merge for a prefill chunk of n_q queries split n_split ways each.
+hipError_t launch_merge_chunk(float *part, float *out, int n_q, int kv_heads, int n_split, int Dh,
+                              int G, hipStream_t s);
 // Stages 3 + 4 fused: every attention workgroup selects (a.sel is ignored;
 // the chosen ids come from `sa`, sa.sel optionally receives them all).
 hipError_t launch_select_attend(const AttendArgs &a, const SelectArgs &sa, int Dh, int G,

@@ -47,19 +47,21 @@ __device__ inline double load_idx(const void *p, size_t i)
         return (double)((const float *)p)[i];
 }
 
-// Copy the appended token's raw indexer-key, K and V rows into the caches
-// (threads of one workgroup, any count).
+// Copy the n_new appended tokens' raw indexer-key, K and V rows (consecutive
+// in their sources) into the caches (threads of one workgroup, any count).
 __device__ inline void append_rows(const UpdateArgs &a, int t, int nthreads)
 {
     const uint32_t *src = (const uint32_t *)a.new_idx_row;
     uint32_t *dst = (uint32_t *)a.idx_k + (size_t)a.pos * a.idx_row_words;
-    for (int i = t; i < a.idx_row_words; i += nthreads)
+    const int iw = a.n_new * a.idx_row_words;
+    for (int i = t; i < iw; i += nthreads)
         dst[i] = src[i];
     const uint32_t *sk = (const uint32_t *)a.new_k_row;
     const uint32_t *sv = (const uint32_t *)a.new_v_row;
     uint32_t *dk = (uint32_t *)a.k + (size_t)a.pos * a.kv_row_words;
     uint32_t *dv = (uint32_t *)a.v + (size_t)a.pos * a.kv_row_words;
-    for (int i = t; i < a.kv_row_words; i += nthreads) {
+    const int kw = a.n_new * a.kv_row_words;
+    for (int i = t; i < kw; i += nthreads) {
         dk[i] = sk[i];
         dv[i] = sv[i];
     }
@@ -87,10 +89,10 @@ __device__ inline void pool_row(const UpdateArgs &a, int64_t b, int t, void *lds
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int64_t tok = 4 * b + r;
-            // The row being appended by this same launch is read from its source.
-            const bool fresh = a.new_idx_row && tok == a.pos;
+            // Rows being appended by this same launch are read from their source.
+            const bool fresh = a.new_idx_row && tok >= a.pos && tok < a.pos + a.n_new;
             const void *src = fresh ? a.new_idx_row : a.idx_k;
-            const size_t base = fresh ? 0 : (size_t)tok * row;
+            const size_t base = (size_t)(fresh ? tok - a.pos : tok) * row;
             s_lo += load_idx<F16>(src, base + e_lo);
             s_hi += load_idx<F16>(src, base + e_hi);
         }

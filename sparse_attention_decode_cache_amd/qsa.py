@@ -22,9 +22,11 @@ QSA_F32, QSA_F16 = 0, 1
 EXPORTS = ("qsa_workspace_bytes", "qsa_state_invalidate", "qsa_state_truncate",
            "qsa_cache_update", "qsa_index_score", "qsa_topk_blocks", "qsa_gather_attend",
            "qsa_decode_step", "qsa_batch_workspace_bytes", "qsa_decode_step_batch",
-           "qsa_chunk_workspace_bytes", "qsa_chunk_step", "qsa_status_string", "qsa_last_error")
+           "qsa_chunk_workspace_bytes", "qsa_chunk_step", "qsa_multi_workspace_bytes",
+           "qsa_decode_step_multi", "qsa_status_string", "qsa_last_error")
 QSA_MAX_BATCH = 8
 QSA_MAX_CHUNK = 4096
+QSA_MAX_MULTI = 4
 
 
 class QSAError(RuntimeError):
@@ -86,8 +88,12 @@ def lib():
         L.qsa_chunk_workspace_bytes.restype = sz
         L.qsa_chunk_workspace_bytes.argtypes = [D, i32, i32]
         L.qsa_chunk_step.argtypes = [D, C, S, i32, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+        L.qsa_multi_workspace_bytes.restype = sz
+        L.qsa_multi_workspace_bytes.argtypes = [D, i32, i32]
+        L.qsa_decode_step_multi.argtypes = [D, C, S, i32, P, P, P, P, P, P, P, P, P, P, P, sz, P]
         for f in ("qsa_cache_update", "qsa_index_score", "qsa_topk_blocks", "qsa_gather_attend",
-                  "qsa_decode_step", "qsa_decode_step_batch"):
+                  "qsa_decode_step", "qsa_decode_step_batch", "qsa_chunk_step",
+                  "qsa_decode_step_multi"):
             getattr(L, f).restype = ctypes.c_int
         L.qsa_status_string.restype = ctypes.c_char_p
         L.qsa_status_string.argtypes = [ctypes.c_int]
@@ -235,3 +241,23 @@ def qsa_chunk_step(desc, cache, state, n_q, idx_k_rows, k_rows, v_rows, gamma, q
                                 _ptr(idx_k_rows), _ptr(k_rows), _ptr(v_rows), _ptr(gamma), _ptr(q_idx),
                                 _ptr(w), _ptr(q), _ptr(out), _ptr(sel_out), _ptr(scores_out),
                                 p, n, _stream(stream)))
+
+
+def qsa_multi_workspace_bytes(desc, capacity, n_q):
+    return lib().qsa_multi_workspace_bytes(ctypes.byref(desc), int(capacity), int(n_q))
+
+
+def multi_workspace(desc, capacity, n_q, device="cuda"):
+    n = qsa_multi_workspace_bytes(desc, capacity, n_q)
+    if n == 0:
+        raise QSAError(QSA_ERR_UNSUPPORTED, "qsa_multi_workspace_bytes rejected the arguments")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def qsa_decode_step_multi(desc, cache, state, n_q, idx_k_rows, k_rows, v_rows, gamma, q_idx, w, q,
+                          out, sel_out=None, scores_out=None, ws=None, stream=None):
+    p, n = _ws(ws)
+    _check(lib().qsa_decode_step_multi(ctypes.byref(desc), ctypes.byref(cache), ctypes.byref(state),
+                                       int(n_q), _ptr(idx_k_rows), _ptr(k_rows), _ptr(v_rows),
+                                       _ptr(gamma), _ptr(q_idx), _ptr(w), _ptr(q), _ptr(out),
+                                       _ptr(sel_out), _ptr(scores_out), p, n, _stream(stream)))

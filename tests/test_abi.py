@@ -165,3 +165,33 @@ def test_chunk_argument_errors_before_launch():
     assert call(st, 16, gamma=0) == -1
     assert call(st, 16, ws_bytes=100) == -3
     assert (st.n_tokens, st.n_valid_blocks) == (4000, 1000)
+
+
+def test_multi_argument_errors_before_launch():
+    qsa, d, c = _objs()
+    L = qsa.lib()
+    P = ctypes.c_void_p
+    D = ctypes.byref(d)
+    one = qsa.qsa_multi_workspace_bytes(d, 4096, 1)
+    assert one == qsa.qsa_workspace_bytes(d, 4096)
+    assert qsa.qsa_multi_workspace_bytes(d, 4096, 4) == 4 * one
+    assert qsa.qsa_multi_workspace_bytes(d, 4096, 0) == 0
+    assert qsa.qsa_multi_workspace_bytes(d, 4096, qsa.QSA_MAX_MULTI + 1) == 0
+    assert qsa.qsa_multi_workspace_bytes(d, 4094, 2) == 0
+    # a chunk of at most QSA_MAX_MULTI tokens runs the multi-query path
+    assert qsa.qsa_chunk_workspace_bytes(d, 4096, 3) >= qsa.qsa_multi_workspace_bytes(d, 4096, 3)
+
+    def call(st, n_q, q=16, ws_bytes=1 << 40, rows=16):
+        return L.qsa_decode_step_multi(D, ctypes.byref(c), ctypes.byref(st), n_q, P(rows), P(16),
+                                       P(16), P(16), P(16), P(16), P(q), P(16), None, None, P(256),
+                                       ws_bytes, None)
+
+    st = qsa.qsa_seq_state(4093, 1023)
+    assert call(st, 0) == -1
+    assert call(st, qsa.QSA_MAX_MULTI + 1) == -1
+    assert call(st, 4) == -1                        # 4093 + 4 > capacity 4096
+    assert b"outside" in L.qsa_last_error()
+    assert call(st, 3, q=8) == -1                   # q must be 16-byte aligned
+    assert call(st, 3, rows=0) == -1                # null rows
+    assert call(st, 3, ws_bytes=100) == -3
+    assert (st.n_tokens, st.n_valid_blocks) == (4093, 1023)

@@ -100,7 +100,13 @@ def test_chunk_fp32_indexer():
 
 
 def test_chunk_few_queries_split_and_merge():
-    """3 queries: each query's tiles are split over many workgroups and merged."""
+    """6 queries: each query's tiles are split over many workgroups and merged."""
+    st = _run_full(W.CTX64K, 20003, 6)
+    assert st["exact"] + st["threshold"] == 6
+
+
+def test_chunk_of_three_runs_the_multi_query_path():
+    """3 queries (at most QSA_MAX_MULTI): the multi-query path, same results."""
     st = _run_full(W.CTX64K, 20003, 3)
     assert st["exact"] + st["threshold"] == 3
 
@@ -171,7 +177,7 @@ def test_chunk_128k_1024_queries_sampled():
 
 @pytest.mark.parametrize("q_heads,kv_heads,head_dim,n_q", [
     (2, 2, 128, 21), (4, 2, 64, 37), (8, 2, 128, 19), (16, 2, 64, 23), (4, 4, 256, 17),
-    (2, 2, 64, 2), (16, 2, 128, 3)])
+    (2, 2, 64, 5), (16, 2, 128, 7)])
 def test_chunk_attention_shapes(q_heads, kv_heads, head_dim, n_q):
     """GQA groups of 1, 2, 4 and 8 heads, head dims 64 / 128 / 256; the last two
     cases have so few queries that each query is split and merged."""
