@@ -10,7 +10,8 @@
 // any is used (non-temporal: the rows are not reused in this step).  Each
 // lane ends with the partial dots of V rows; a transposing butterfly inside
 // the 16-lane row (DPP moves only: row mirror, half mirror, quad swaps)
-// finishes V rows in log2(L) rounds.  w[h] is folded into q_idx once per lane.
+// finishes V rows in log2(L) rounds.  w[h] is folded into q_idx once per
+// workgroup, into LDS.
 //
 // Outputs (all optional, plain stores, no atomics): fp32 scores; the
 // order-preserving 32-bit key of every score; and, for the top-k, each tile's
@@ -119,166 +120,16 @@ struct ScoreShape {
     static_assert(V >= 1 && V <= L, "one butterfly finishes the rows");
 };
 
-template <int LPR>
-struct ScoreLds {
-    uint64_t c[ScoreShape<LPR>::R];            // the tile's composites
-    u32x4 fresh[LPR];                          // the row pooled by the fused prologue
-};
-
-// Score tile `tile` of one sequence (256 threads).  `pool_here`: this
-// workgroup runs the fused append + pool (it must hold the last tile).
-template <bool F16, int LPR>
-__device__ inline void score_tile(const ScoreArgs &a, ScoreLds<LPR> &sl, int tile, bool pool_here)
-{
-    using S = ScoreShape<LPR>;
-    constexpr int EPL = F16 ? 8 : 4;           // elements per 16-byte chunk
-    constexpr int L = S::L, C = S::C, RI = S::RI, V = S::V, R = S::R;
-    constexpr int ROWB = LPR * 16;             // row bytes
-    uint64_t *s_c = sl.c;
-    u32x4 *s_new = sl.fresh;
-
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int col = lane % L;                  // lane within its row
-    const int sub = lane / L;                  // row within a wave-wide load
-    const int64_t base = (int64_t)tile * R + (int64_t)wave * S::RPW;
-
-    // q and w for the C chunks this lane reads of every row (a chunk lies
-    // inside one head: D is a multiple of 8), loaded ahead of the row stream
-    float4 qraw[C][EPL / 4];
-    float wraw[C];
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-        const int e0 = (col + L * c) * EPL;
-#pragma unroll
-        for (int k4 = 0; k4 < EPL / 4; ++k4)
-            qraw[c][k4] = ((const float4 *)(a.q + e0))[k4];
-        wraw[c] = a.w[e0 / a.D];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // load i: row group g = i / C, chunk col + L*(i % C) of row base + g*RI + sub
-    const char *rows = (const char *)a.summary;
-    u32x4 buf[S::LOADS];
-#pragma unroll
-    for (int i = 0; i < S::LOADS; ++i) {
-        const int64_t r = base + (int64_t)(i / C) * RI + sub;
-        const u32x4 *src = (const u32x4 *)(rows + (r < a.nb ? r : 0) * ROWB) + col + L * (i % C);
-        buf[i] = __builtin_nontemporal_load(src);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // Fused stage 1 (workgroup 0, whose tile holds the last row): append,
-    // pool the new block into LDS while the loads fly, and hand the pooled
-    // row to the lanes that loaded its stale chunks -- no reload, no fence.
-    if (pool_here) {
-        if (a.upd.new_idx_row)
-            append_rows(a.upd, threadIdx.x, 256);
-        if (a.upd.nblk > 0)
-            pool_row<F16>(a.upd, a.upd.b0, threadIdx.x, s_new);
-        __syncthreads();
-        if (a.upd.nblk > 0) {
-#pragma unroll
-            for (int i = 0; i < S::LOADS; ++i) {
-                const int64_t r = base + (int64_t)(i / C) * RI + sub;
-                if (r == a.upd.b0)
-                    buf[i] = s_new[col + L * (i % C)];
-            }
-        }
-    }
-
-    float qw[C][EPL];
-#pragma unroll
-    for (int c = 0; c < C; ++c)
-#pragma unroll
-        for (int k4 = 0; k4 < EPL / 4; ++k4) {
-            qw[c][4 * k4] = qraw[c][k4].x * wraw[c];
-            qw[c][4 * k4 + 1] = qraw[c][k4].y * wraw[c];
-            qw[c][4 * k4 + 2] = qraw[c][k4].z * wraw[c];
-            qw[c][4 * k4 + 3] = qraw[c][k4].w * wraw[c];
-        }
-
-    float v[V];
-#pragma unroll
-    for (int g = 0; g < V; ++g) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int c = 0; c < C; ++c) {
-            const u32x4 &b = buf[g * C + c];
-            if constexpr (F16) {
-                half8 h;
-                __builtin_memcpy(&h, &b, 16);
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    acc = fmaf(qw[c][k], (float)h[k], acc);
-            } else {
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    acc = fmaf(qw[c][k], __uint_as_float(b[k]), acc);
-            }
-        }
-        v[g] = acc;
-    }
-
-    int toff = 0;
-    Butterfly<L / 2, V>::run(v, lane, toff);
-
-    constexpr int OWN = L / V;                 // lanes sharing one final sum
-    const int local = wave * S::RPW + toff * RI + sub;
-    const int64_t r = (int64_t)tile * R + local;
-    if (col % OWN == 0) {
-        uint64_t c = 0;
-        if (r < a.nb) {
-            const float sc = v[0];
-            if (a.scores)
-                a.scores[r] = sc;
-            if (a.keys) {
-                const uint32_t key = score_key(sc);
-                a.keys[r] = key;
-                c = comp_key(key, (uint32_t)r);
-            }
-        }
-        s_c[local] = c;
-    }
-    if (a.lists) {
-        __syncthreads();
-        const int64_t valid = a.nb - (int64_t)tile * R;
-        write_tile_list<R, R / kListDiv>(s_c, a.lists, tile, (int)(valid < R ? valid : R));
-    }
-}
-
-template <bool F16, int LPR>
-__global__ __launch_bounds__(256) void k_score(ScoreArgs a)
-{
-    __shared__ ScoreLds<LPR> sl;
-    // workgroup 0 (dispatched first) takes the last tile: the one holding the new row
-    const int tile = blockIdx.x == 0 ? (int)gridDim.x - 1 : (int)blockIdx.x - 1;
-    score_tile<F16, LPR>(a, sl, tile, blockIdx.x == 0 && a.fuse);
-}
-
-// A batch of sequences in one launch: workgroups [tile0[s], tile0[s+1]) score
-// sequence s, the first of them its last tile (with the fused prologue).
-template <bool F16, int LPR>
-__global__ __launch_bounds__(256) void k_score_batch(ScoreBatchArgs b)
-{
-    __shared__ ScoreLds<LPR> sl;
-    int s = 0;
-    while (s + 1 < b.n && (int)blockIdx.x >= b.tile0[s + 1])
-        ++s;
-    const int local = (int)blockIdx.x - b.tile0[s];
-    const int ntiles = b.tile0[s + 1] - b.tile0[s];
-    const int tile = local == 0 ? ntiles - 1 : local - 1;
-    score_tile<F16, LPR>(b.seq[s], sl, tile, local == 0 && b.seq[s].fuse);
-}
-
-// Q queries of one sequence in one pass (speculative verify): the tile's
-// rows are loaded once, as in score_tile, and every 16-byte chunk is
-// widened once and dotted with all Q queries.  The folded queries w[h] q[h]
-// sit in LDS and are read one chunk position at a time, so the registers
-// hold the row loads, one chunk of every query and Q x V sums whatever Q
-// is.  Query i sees the rows below a.nbq[i]; the rest get no key, no list
-// entry and a score of -inf.  The butterfly, keys and lists are those of the
-// single query, once per query.
+// One tile for Q queries of one sequence (Q = 1: the decode step; Q > 1:
+// speculative verify of consecutive tokens): the tile's rows are loaded
+// once and every 16-byte chunk is widened once and dotted with all Q
+// queries.  The folded queries w[h] q[h] sit in LDS and are read one chunk
+// position at a time, so the registers hold the row loads, one chunk of
+// every query and Q x V sums whatever Q is (122 VGPRs for 1 KB rows: four
+// workgroups per CU, so a 256k-context grid of ~1000 tiles is resident at
+// once).  Query i sees the rows below a.nbq[i]; the rest get no key, no
+// list entry and a score of -inf.  The butterfly, keys and lists run once
+// per query.
 template <int LPR, int Q, int EPL>
 struct ScoreMultiLds {
     float qw[Q][LPR * EPL];
@@ -287,7 +138,13 @@ struct ScoreMultiLds {
 };
 
 template <bool F16, int LPR, int Q>
-__global__ __launch_bounds__(256) void k_score_multi(ScoreMultiArgs a)
+using ScoreLdsOf = ScoreMultiLds<LPR, Q, F16 ? 8 : 4>;
+
+// Score tile `tile` for Q queries (256 threads).  `pool_here`: this
+// workgroup runs the fused append + pool (it must hold the last tile).
+template <bool F16, int LPR, int Q>
+__device__ inline void score_tile(const ScoreMultiArgs &a, ScoreLdsOf<F16, LPR, Q> &sl, int tile,
+                                  bool pool_here)
 {
     using S = ScoreShape<LPR>;
     constexpr int EPL = F16 ? 8 : 4;
@@ -295,11 +152,7 @@ __global__ __launch_bounds__(256) void k_score_multi(ScoreMultiArgs a)
     constexpr int ROWB = LPR * 16;
     constexpr int HD = LPR * EPL;              // elements of a row
     constexpr int QPT = (Q * HD / 4 + 255) / 256;   // float4 groups of queries per thread
-    __shared__ ScoreMultiLds<LPR, Q, EPL> sl;
 
-    // workgroup 0 (dispatched first) takes the last tile: the one holding the new row
-    const int tile = blockIdx.x == 0 ? (int)gridDim.x - 1 : (int)blockIdx.x - 1;
-    const bool pool_here = blockIdx.x == 0 && a.fuse;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int col = lane % L;
@@ -446,11 +299,63 @@ __global__ __launch_bounds__(256) void k_score_multi(ScoreMultiArgs a)
     }
 }
 
+template <bool F16, int LPR, int Q>
+__global__ __launch_bounds__(256) void k_score_multi(ScoreMultiArgs a)
+{
+    __shared__ ScoreLdsOf<F16, LPR, Q> sl;
+    // workgroup 0 (dispatched first) takes the last tile: the one holding the new row
+    const int tile = blockIdx.x == 0 ? (int)gridDim.x - 1 : (int)blockIdx.x - 1;
+    score_tile<F16, LPR, Q>(a, sl, tile, blockIdx.x == 0 && a.fuse);
+}
+
+// One query: the same tile routine.
+__device__ inline ScoreMultiArgs single(const ScoreArgs &a)
+{
+    ScoreMultiArgs m{};
+    m.summary = a.summary;
+    m.nb = a.nb;
+    m.D = a.D;
+    m.fuse = a.fuse;
+    m.upd = a.upd;
+    m.nbq[0] = a.nb;
+    m.q[0] = a.q;
+    m.w[0] = a.w;
+    m.keys[0] = a.keys;
+    m.lists[0] = a.lists;
+    m.scores = a.scores;
+    m.ld_scores = 0;
+    return m;
+}
+
+template <bool F16, int LPR>
+__global__ __launch_bounds__(256) void k_score(ScoreArgs a)
+{
+    __shared__ ScoreLdsOf<F16, LPR, 1> sl;
+    const int tile = blockIdx.x == 0 ? (int)gridDim.x - 1 : (int)blockIdx.x - 1;
+    score_tile<F16, LPR, 1>(single(a), sl, tile, blockIdx.x == 0 && a.fuse);
+}
+
+// A batch of sequences in one launch: workgroups [tile0[s], tile0[s+1]) score
+// sequence s, the first of them its last tile (with the fused prologue).
+template <bool F16, int LPR>
+__global__ __launch_bounds__(256) void k_score_batch(ScoreBatchArgs b)
+{
+    __shared__ ScoreLdsOf<F16, LPR, 1> sl;
+    int s = 0;
+    while (s + 1 < b.n && (int)blockIdx.x >= b.tile0[s + 1])
+        ++s;
+    const int local = (int)blockIdx.x - b.tile0[s];
+    const int ntiles = b.tile0[s + 1] - b.tile0[s];
+    const int tile = local == 0 ? ntiles - 1 : local - 1;
+    score_tile<F16, LPR, 1>(single(b.seq[s]), sl, tile, local == 0 && b.seq[s].fuse);
+}
+
 template <bool F16, int LPR>
 hipError_t go_multi(const ScoreMultiArgs &a, int n_q, hipStream_t s)
 {
     const int grid = (int)((a.nb + ScoreShape<LPR>::R - 1) / ScoreShape<LPR>::R);
     switch (n_q) {
+    case 1: hipLaunchKernelGGL((k_score_multi<F16, LPR, 1>), dim3(grid), dim3(256), 0, s, a); break;
     case 2: hipLaunchKernelGGL((k_score_multi<F16, LPR, 2>), dim3(grid), dim3(256), 0, s, a); break;
     case 3: hipLaunchKernelGGL((k_score_multi<F16, LPR, 3>), dim3(grid), dim3(256), 0, s, a); break;
     case 4: hipLaunchKernelGGL((k_score_multi<F16, LPR, 4>), dim3(grid), dim3(256), 0, s, a); break;

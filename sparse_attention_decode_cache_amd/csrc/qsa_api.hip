@@ -722,22 +722,7 @@ qsa_status qsa_decode_step_multi(const qsa_layer_desc *desc, const qsa_layer_cac
                                 (float *)(wsp + L.part));
     }
     if (score) {
-        if (n_q == 1) {
-            ScoreArgs a{};
-            a.summary = sm.summary;
-            a.q = sm.q[0];
-            a.w = sm.w[0];
-            a.scores = scores_out;
-            a.keys = sm.keys[0];
-            a.lists = sm.lists[0];
-            a.nb = nb_last;
-            a.D = sm.D;
-            a.fuse = sm.fuse;
-            a.upd = u;
-            e = launch_score(a, f16, rowb, stream);
-        } else {
-            e = launch_score_multi(sm, n_q, f16, rowb, stream);
-        }
+        e = launch_score_multi(sm, n_q, f16, rowb, stream);
         if (e != hipSuccess)
             return hip_fail(e, "decode_step_multi/score");
     }
