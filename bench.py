@@ -13,7 +13,9 @@ Prints ONE JSON line.  `value` is QSA-layer decode steps per second.
 `roofline` is for the dominant kernel (the block-score stream), timed with HIP
 events around passes of back-to-back launches on the stream it runs on.  `cpu_baseline` times
 the CPU oracle on a bounded sample of the same workload (rank 0, N = 1 only).
-`batch_and_chunk` (after the headline, outside its timed region): batched
+`multi_decode` (after the headline, outside its timed region): speculative
+verify, one call of 4 tokens per layer on the same 12 caches.
+`batch_and_chunk` (after that, also outside the headline's timed region): batched
 decode of 8 sequences of mixed context in one call per step, and one prefill
 chunk of 1024 tokens at 126,253 tokens of context, on the same layer shapes.
 """
@@ -109,6 +111,7 @@ def cpu_baseline(w, n_steps):
 
 
 TRAFFIC_COPY_MB = 256
+MULTI_Q = 4                        # tokens per speculative-verify call (the token + 3 drafts)
 MFMA_F16_PEAK_TFLOPS = 2500.0      # MI355X dense f16 matrix-core peak
 
 
@@ -133,6 +136,63 @@ def chunk_flops(w, n_q):
     of the query."""
     nb_last = (w.n0 + n_q) // 4
     return 2 * 2 * n_q * nb_last * w.idx_heads * w.idx_dim
+
+
+def multi_call_bytes(w, n0, n_q):
+    """Algorithmic HBM bytes of one multi-query call of n_q tokens at n0: one
+    read of every summary for all queries, each query's gathered K/V rows, the
+    appended rows, the blocks pooled and the queries."""
+    idx_row = w.idx_heads * w.idx_dim * (2 if w.idx_f16 else 4)
+    kv_row = w.kv_heads * w.head_dim * 2
+    nb_last = (n0 + n_q) // 4
+    new_blocks = nb_last - n0 // 4
+    gathered = sum(2 * kv_row * (4 * min(w.k_blocks, (n0 + i + 1) // 4) + (n0 + i + 1) % 4)
+                   for i in range(n_q))
+    queries = 4 * n_q * (w.idx_heads * w.idx_dim + w.idx_heads + 2 * w.q_heads * w.head_dim)
+    return idx_row * nb_last + gathered + n_q * (idx_row + 2 * kv_row) + 5 * idx_row * new_blocks + queries
+
+
+def bench_multi(args, torch, qsa, w, desc, layers, stream, dev, decode_us):
+    """Speculative verify on the headline caches: one qsa_decode_step_multi
+    call of MULTI_Q tokens (the token and its drafts) per layer, the 12 layers
+    round-robin; after each call the drafts are dropped (qsa_state_truncate
+    back to the original context), so every call appends, pools one block,
+    streams every summary once for all queries, selects and attends per query."""
+    n_q = MULTI_Q
+    n0 = w.n0
+    ws = qsa.multi_workspace(desc, layers[0]["buf"].capacity, n_q)
+    outs = torch.empty((n_q, w.q_heads, w.head_dim), dtype=torch.float32, device=dev)
+
+    def call(L):
+        inp = L["inp"]
+        qsa.qsa_decode_step_multi(desc, L["buf"].cache, L["state"], n_q, inp.raw[:n_q], inp.k[:n_q],
+                                  inp.v[:n_q], L["gamma"], inp.q_idx[:n_q], inp.w[:n_q],
+                                  inp.q[:n_q], outs, None, None, ws, stream)
+        qsa.qsa_state_truncate(L["state"], n0)
+
+    for L in layers:
+        qsa.qsa_state_truncate(L["state"], n0)
+    for _ in range(2):
+        for L in layers:
+            call(L)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.multi_reps):
+        for L in layers:
+            call(L)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    calls = args.multi_reps * len(layers)
+    us = 1e3 * e0.elapsed_time(e1) / calls
+    nbytes = multi_call_bytes(w, n0, n_q)
+    gbs = nbytes / (us / 1e6) / 1e9
+    log(f"multi-query decode: {us:.1f} us per call of {n_q} tokens at n0={n0}, {gbs:.0f} GB/s")
+    return {"workload": f"qsa-verify{n_q}-256k-12layers", "n0": n0, "n_q": n_q, "calls": calls,
+            "us_per_call": round(us, 2), "tokens_per_s": round(n_q / (us / 1e6), 1),
+            "vs_decode_steps": round(n_q * decode_us / us, 3),
+            "hbm": {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_call": nbytes}}
 
 
 def bench_batch_and_chunk(args, torch, qsa, W, stream, dev):
@@ -331,6 +391,8 @@ def main():
     ap.add_argument("--batch-steps", type=int, default=48)
     ap.add_argument("--batch-warmup", type=int, default=4)
     ap.add_argument("--chunk-reps", type=int, default=5)
+    ap.add_argument("--multi-reps", type=int, default=8, help="rounds of multi-query calls")
+    ap.add_argument("--no-multi", action="store_true", help="skip the multi-query decode leg")
     ap.add_argument("--batch-only", action="store_true", help="only the batched-decode / chunk leg")
     ap.add_argument("--traffic-run", action="store_true",
                     help="only launch the score kernel and a plain copy (for rocprofv3 --pmc)")
@@ -471,6 +533,9 @@ def main():
         "cpu_baseline": None,
         "batch_and_chunk": None,
     }
+    if not args.no_multi:
+        result["multi_decode"] = bench_multi(args, torch, qsa, w, desc, layers, stream, dev,
+                                             result["layer_step_us"]["median"])
     if not args.no_batch:
         del layers, ws
         torch.cuda.empty_cache()
