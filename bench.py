@@ -15,6 +15,8 @@ events around passes of back-to-back launches on the stream it runs on.  `cpu_ba
 the CPU oracle on a bounded sample of the same workload (rank 0, N = 1 only).
 `multi_decode` (after the headline, outside its timed region): speculative
 verify, one call of 4 tokens per layer on the same 12 caches.
+`ablations` (after that): the page's comparisons timed on the same caches -- pooled-key cache
+off, cell-level top-k, gather off -- beside the calls they stand for.
 `batch_and_chunk` (after that, also outside the headline's timed region): batched
 decode of 8 sequences of mixed context in one call per step, and one prefill
 chunk of 1024 tokens at 126,253 tokens of context, on the same layer shapes.
@@ -193,6 +195,77 @@ def bench_multi(args, torch, qsa, w, desc, layers, stream, dev, decode_us):
             "vs_decode_steps": round(n_q * decode_us / us, 3),
             "hbm": {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_call": nbytes}}
+
+
+def bench_ablations(args, torch, qsa, w, desc, layers, ws, stream, dev, decode_us):
+    """The page's own comparisons on the headline caches (12 layers at 256k,
+    round-robin so every pass reads HBM), each timed with HIP events on the
+    library's stream:
+      pooled-key cache off: qsa_state_invalidate(st, 0) before a decode step,
+        so every block is pooled again (the step then drops its token);
+      cell-level top-k: qsa_topk_cells (scores expanded to cells, top-k over
+        cells) against qsa_topk_blocks on the same scores;
+      gather off: qsa_attend_masked (every cached row read, the selection as a
+        mask) against qsa_gather_attend with the same ids."""
+    n0 = w.n0
+    nb = n0 // 4
+    K = w.k_blocks
+    aws = qsa.ablation_workspace(desc, layers[0]["buf"].capacity)
+    scores = [torch.empty(nb, dtype=torch.float32, device=dev) for _ in layers]
+    sels = [torch.empty(K, dtype=torch.int32, device=dev) for _ in layers]
+    cells = torch.empty(w.top_k_tokens + 4, dtype=torch.int32, device=dev)
+    out = torch.empty((w.q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    for L in layers:
+        qsa.qsa_state_truncate(L["state"], n0)
+    for i, L in enumerate(layers):
+        inp = L["inp"]
+        qsa.qsa_index_score(desc, L["buf"].cache, nb, inp.q_idx[0], inp.w[0], scores[i], stream)
+        qsa.qsa_topk_blocks(scores[i], nb, K, sels[i], ws, stream)
+
+    def timed(fn, reps):
+        for i, L in enumerate(layers):      # warm
+            fn(i, L)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            for i, L in enumerate(layers):
+                fn(i, L)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return 1e3 * a.elapsed_time(b) / (reps * len(layers))
+
+    def cache_off(i, L):
+        inp = L["inp"]
+        qsa.qsa_state_invalidate(L["state"], 0)
+        qsa.qsa_decode_step(desc, L["buf"].cache, L["state"], inp.raw[0], inp.k[0], inp.v[0],
+                            L["gamma"], inp.q_idx[0], inp.w[0], inp.q[0], L["out"], None, None, ws,
+                            stream)
+        qsa.qsa_state_truncate(L["state"], n0)
+
+    def topk_blocks(i, L):
+        qsa.qsa_topk_blocks(scores[i], nb, K, sels[i], ws, stream)
+
+    def topk_cells(i, L):
+        qsa.qsa_topk_cells(scores[i], n0, w.top_k_tokens, cells, aws, stream)
+
+    def gathered(i, L):
+        qsa.qsa_gather_attend(desc, L["buf"].cache, n0, sels[i], K, L["inp"].q[0], out, ws, stream)
+
+    def masked(i, L):
+        qsa.qsa_attend_masked(desc, L["buf"].cache, n0, sels[i], K, L["inp"].q[0], out, aws, stream)
+
+    r = args.ablation_reps
+    res = {"workload": f"{w.name} (n0={n0}, {len(layers)} layers round-robin)",
+           "cache_on_layer_step_us": decode_us,
+           "cache_off_layer_step_us": round(timed(cache_off, max(1, r // 4)), 2),
+           "topk_blocks_us": round(timed(topk_blocks, r), 2),
+           "topk_cells_us": round(timed(topk_cells, r), 2),
+           "gather_attend_us": round(timed(gathered, r), 2),
+           "masked_attend_us": round(timed(masked, r), 2)}
+    kv_all = 2 * w.kv_heads * w.head_dim * 2 * n0
+    res["masked_attend_gbs"] = round(kv_all / (res["masked_attend_us"] / 1e6) / 1e9, 1)
+    log(f"ablations: {res}")
+    return res
 
 
 def bench_batch_and_chunk(args, torch, qsa, W, stream, dev):
@@ -393,6 +466,8 @@ def main():
     ap.add_argument("--chunk-reps", type=int, default=5)
     ap.add_argument("--multi-reps", type=int, default=8, help="rounds of multi-query calls")
     ap.add_argument("--no-multi", action="store_true", help="skip the multi-query decode leg")
+    ap.add_argument("--ablation-reps", type=int, default=8)
+    ap.add_argument("--no-ablations", action="store_true", help="skip the ablation leg")
     ap.add_argument("--batch-only", action="store_true", help="only the batched-decode / chunk leg")
     ap.add_argument("--traffic-run", action="store_true",
                     help="only launch the score kernel and a plain copy (for rocprofv3 --pmc)")
@@ -536,6 +611,9 @@ def main():
     if not args.no_multi:
         result["multi_decode"] = bench_multi(args, torch, qsa, w, desc, layers, stream, dev,
                                              result["layer_step_us"]["median"])
+    if not args.no_ablations:
+        result["ablations"] = bench_ablations(args, torch, qsa, w, desc, layers, ws, stream, dev,
+                                              result["layer_step_us"]["median"])
     if not args.no_batch:
         del layers, ws
         torch.cuda.empty_cache()

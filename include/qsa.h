@@ -313,6 +313,49 @@ qsa_status qsa_decode_step_multi(const qsa_layer_desc *desc, const qsa_layer_cac
                                  const float *q, float *out, int32_t *sel_out, float *scores_out,
                                  void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------ ablations
+ * The page's comparisons of its own changes, reproduced as library calls so
+ * that each can be timed on this hardware against the path above.  (The
+ * third, the pooled-key cache switched off, needs no call of its own:
+ * qsa_state_invalidate(st, 0) before a qsa_decode_step pools every block
+ * again.) */
+
+/* Workspace bytes for qsa_topk_cells and qsa_attend_masked on a cache of the
+ * given capacity; 0 for an invalid descriptor or capacity. */
+size_t qsa_ablation_workspace_bytes(const qsa_layer_desc *desc, int32_t capacity);
+
+/* The selection as the page made it before its block-domain top-k [post 10,
+ * "block-domain top-k（COMMON-006）実装は見送り": block scores copied to every
+ * cell of the block, then a top-k over the cells]: cell 4b + j gets s[b];
+ * the top_k_tokens cells ranked first by (score descending, cell
+ * ascending), in ascending order, then the tail cells 4 floor(n/4) .. n-1.
+ * Because the 4 cells of a block tie and are consecutive, these are the
+ * cells of the blocks qsa_topk_blocks chooses with k = top_k_tokens / 4.
+ * block_scores: DEVICE fp32 [floor(n_tokens/4)]; cells: DEVICE int32
+ * [min(top_k_tokens, 4 floor(n/4)) + n mod 4].  Workspace >=
+ * qsa_ablation_workspace_bytes of any descriptor whose capacity >= n_tokens.
+ * Errors: ARG if n_tokens < 1, floor(n_tokens/4) > 2^17, top_k_tokens is
+ * not a positive multiple of 4 or a pointer is null; WORKSPACE as in
+ * qsa_topk_blocks. */
+qsa_status qsa_topk_cells(const float *block_scores, int32_t n_tokens, int32_t top_k_tokens,
+                          int32_t *cells, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* The attention with the gather switched off [post 10, "selected QSA K/V
+ * gather（COMMON-005）": before it, flash attention ran over the whole cache
+ * with the unselected cells masked]: reads every cached K / V row of the n
+ * tokens; cells of blocks outside sel get no weight, the tail cells always
+ * take part.  The result is that of qsa_gather_attend with the same
+ * arguments (up to summation order).  sel: DEVICE int32 [n_sel_blocks],
+ * ascending, each < floor(n_tokens/4); q, out: DEVICE fp32 [Hq][Dh],
+ * 16-byte aligned.  Workspace >= qsa_ablation_workspace_bytes.
+ * Errors: ARG if n_tokens is outside [1, capacity], n_sel_blocks outside
+ * [0, floor(n_tokens/4)], sel is null with n_sel_blocks > 0, or q / out is
+ * null or misaligned; UNSUPPORTED / WORKSPACE as in qsa_gather_attend. */
+qsa_status qsa_attend_masked(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
+                             int32_t n_tokens, const int32_t *sel, int32_t n_sel_blocks,
+                             const float *q, float *out, void *ws, size_t ws_bytes,
+                             hipStream_t stream);
+
 /* Static text for a status code. */
 const char *qsa_status_string(qsa_status s);
 

@@ -453,9 +453,13 @@ struct QueryUnit {
     int32_t kv_heads, ns;
     int32_t direct;             // ns == 1 and the output is written here, normalised
     float scale;
+    const uint32_t *mask;       // MASKED units: bit b set = block b takes part (every row is read)
 };
 
-template <int DH, int G>
+// MASKED: every block is kept for the loads (each cached K / V row is read,
+// as a dense flash-decode over the whole cache would), and the logits of
+// blocks whose mask bit is clear are -inf: the selection applied as a mask.
+template <int DH, int G, bool MASKED = false>
 __device__ void attend_unit(const QueryUnit &c, CALds<DH, G> &L, int s, int g)
 {
     using S = CAShape<DH, G>;
@@ -475,8 +479,12 @@ __device__ void attend_unit(const QueryUnit &c, CALds<DH, G> &L, int s, int g)
     const int32_t id0 = (kCI / 4) * it0;
     const int32_t id1 = (kCI / 4) * it1 < nsel ? (kCI / 4) * it1 : nsel;
     const int32_t *srow = c.sel;
-    for (int x = id0 + t; x < id1; x += kCAT)
-        L.ids[x - id0] = keep_all ? x : srow[x];
+    for (int x = id0 + t; x < id1; x += kCAT) {
+        if constexpr (MASKED)   // the id, its sign bit set when the block is masked out
+            L.ids[x - id0] = x | (((c.mask[x >> 5] >> (x & 31)) & 1u) ? 0 : (int32_t)0x80000000);
+        else
+            L.ids[x - id0] = keep_all ? x : srow[x];
+    }
     // q as the B operand of the logit MFMA: lane l of k-step ks holds
     // q[head l % 16][32 ks + 8 (l / 16) .. +8] (zero past G), hi and lo
     const float *qg = c.q + (size_t)g * G * DH;
@@ -505,7 +513,14 @@ __device__ void attend_unit(const QueryUnit &c, CALds<DH, G> &L, int s, int g)
         valid = e < ncells;
         int64_t cell;
         if (e < 4 * nsel) {
-            const int32_t b = L.ids[(e >> 2) - id0];
+            int32_t b = L.ids[(e >> 2) - id0];
+            if constexpr (MASKED) {     // a masked-out row is still loaded, its logit is -inf
+                const bool live = valid;
+                valid = valid && b >= 0;
+                b &= 0x7FFFFFFF;
+                cell = 4 * (int64_t)b + (e & 3);
+                return live ? (size_t)cell : 0;
+            }
             valid = valid && (uint32_t)b < (uint32_t)nbq;
             cell = 4 * (int64_t)b + (e & 3);
         } else {
@@ -702,7 +717,7 @@ __global__ __launch_bounds__(kCAT, 2) void k_chunk_attend(ChunkArgs c)
     CALds<DH, G> &L = *reinterpret_cast<CALds<DH, G> *>(ca_lds);
     const int ns = c.n_split;
     const int i = blockIdx.x / ns;
-    QueryUnit u;
+    QueryUnit u{};
     u.k = c.k;
     u.v = c.v;
     u.sel = c.sel + (size_t)i * c.kb;
@@ -730,7 +745,7 @@ __global__ __launch_bounds__(kCAT, 2) void k_batch_attend(AttendBatchArgs b)
         ++sq;
     const AttendArgs &a = b.seq[sq];
     const int local = (int)blockIdx.x - b.wg0[sq];
-    QueryUnit u;
+    QueryUnit u{};
     u.k = a.k;
     u.v = a.v;
     u.sel = a.sel;
@@ -744,6 +759,68 @@ __global__ __launch_bounds__(kCAT, 2) void k_batch_attend(AttendBatchArgs b)
     u.direct = 0;                                  // the merge kernel writes the output
     u.scale = a.scale;
     attend_unit<DH, G>(u, L, local % a.n_split, local / a.n_split);
+}
+
+// The selection as a bitmap over the blocks (bit b of word b / 32): one
+// thread per word finds its first id by binary search in the ascending ids.
+__global__ __launch_bounds__(256) void k_sel_bitmap(const int32_t *sel, int32_t n_sel, int32_t nb,
+                                                    uint32_t *bitmap)
+{
+    const int32_t wd = blockIdx.x * 256 + threadIdx.x;
+    if (wd >= (nb + 31) / 32)
+        return;
+    const int32_t lo_id = 32 * wd;
+    int32_t lo = 0, hi = n_sel;
+    while (lo < hi) {
+        const int32_t mid = (lo + hi) >> 1;
+        if (sel[mid] < lo_id)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    uint32_t bits = 0;
+    for (int32_t i = lo; i < n_sel && sel[i] < lo_id + 32; ++i)
+        bits |= 1u << (sel[i] - lo_id);
+    bitmap[wd] = bits;
+}
+
+template <int DH, int G>
+__global__ __launch_bounds__(kCAT, 2) void k_masked_attend(MaskedArgs m)
+{
+    extern __shared__ uint4 ca_lds[];
+    CALds<DH, G> &L = *reinterpret_cast<CALds<DH, G> *>(ca_lds);
+    QueryUnit u{};
+    u.k = m.k;
+    u.v = m.v;
+    u.sel = nullptr;
+    u.q = m.q;
+    u.out = m.out;
+    u.part = m.part;
+    u.n = m.n_tokens;
+    u.kb = (int32_t)(m.n_tokens / 4);
+    u.kv_heads = m.kv_heads;
+    u.ns = m.n_split;
+    u.direct = m.n_split == 1;
+    u.scale = m.scale;
+    u.mask = m.bitmap;
+    attend_unit<DH, G, true>(u, L, blockIdx.x, blockIdx.y);
+}
+
+template <int DH, int G>
+hipError_t masked_go(const MaskedArgs &m, hipStream_t s)
+{
+    const size_t lds = sizeof(CALds<DH, G>);
+    if (lds > 64 * 1024) {
+        static hipError_t attr = hipFuncSetAttribute((const void *)k_masked_attend<DH, G>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (attr != hipSuccess)
+            return attr;
+    }
+    hipLaunchKernelGGL((k_masked_attend<DH, G>), dim3(m.n_split, m.kv_heads), dim3(kCAT), lds, s, m);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || m.n_split == 1)
+        return e;
+    return launch_merge_chunk(m.part, m.out, 1, m.kv_heads, m.n_split, DH, G, s);
 }
 
 template <int DH, int G>
@@ -823,6 +900,43 @@ hipError_t launch_attend_batch(AttendBatchArgs &b, int Dh, int G, hipStream_t s)
     case 256: QSA_BATCH_G(256)
     }
 #undef QSA_BATCH_G
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_masked_attend(MaskedArgs m, int Dh, int G, hipStream_t s)
+{
+    const int32_t nb = (int32_t)(m.n_tokens / 4);
+    const int32_t nit = (int32_t)((m.n_tokens + kCI - 1) / kCI);
+    // enough splits to fill the chip twice over (two workgroups per CU), each
+    // holding whole iterations and at most kChunkMaxIds block ids
+    int32_t ns = nit < kMaskedSplits ? nit : kMaskedSplits;
+    while ((int64_t)((nit + ns - 1) / ns) * (kCI / 4) > kChunkMaxIds)
+        ++ns;
+    if (ns > kMaskedMaxSplits)
+        return hipErrorInvalidValue;
+    m.n_split = ns;
+    if (nb > 0) {
+        const int words = (nb + 31) / 32;
+        hipLaunchKernelGGL(k_sel_bitmap, dim3((words + 255) / 256), dim3(256), 0, s, m.sel,
+                           m.n_sel_blocks, nb, m.bitmap);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+#define QSA_MASKED_G(DHV)                          \
+    switch (G) {                                   \
+    case 1: return masked_go<DHV, 1>(m, s);        \
+    case 2: return masked_go<DHV, 2>(m, s);        \
+    case 4: return masked_go<DHV, 4>(m, s);        \
+    case 8: return masked_go<DHV, 8>(m, s);        \
+    }                                              \
+    return hipErrorInvalidValue;
+    switch (Dh) {
+    case 64: QSA_MASKED_G(64)
+    case 128: QSA_MASKED_G(128)
+    case 256: QSA_MASKED_G(256)
+    }
+#undef QSA_MASKED_G
     return hipErrorInvalidValue;
 }
 

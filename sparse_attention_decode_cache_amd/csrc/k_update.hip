@@ -35,7 +35,35 @@ __global__ __launch_bounds__(256) void k_iota(int32_t *p, int32_t n)
         p[i] = i;
 }
 
+// Block scores expanded to every cell of a block (cell 4b + j gets s[b]).
+__global__ __launch_bounds__(256) void k_expand_cells(const float *scores, int32_t nb, float *cells)
+{
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < 4 * nb; i += gridDim.x * 256)
+        cells[i] = scores[i >> 2];
+}
+
+// The tail cells 4 nb .. 4 nb + tail - 1 after the first `at` entries.
+__global__ void k_tail_cells(int32_t *cells, int32_t at, int32_t nb, int32_t tail)
+{
+    if ((int)threadIdx.x < tail)
+        cells[at + threadIdx.x] = 4 * nb + (int)threadIdx.x;
+}
+
 }  // namespace
+
+hipError_t launch_expand_cells(const float *scores, int32_t nb, float *cells, hipStream_t s)
+{
+    int grid = (4 * nb + 255) / 256;
+    grid = grid < 1 ? 1 : (grid > 2048 ? 2048 : grid);
+    hipLaunchKernelGGL(k_expand_cells, dim3(grid), dim3(256), 0, s, scores, nb, cells);
+    return hipGetLastError();
+}
+
+hipError_t launch_tail_cells(int32_t *cells, int32_t at, int32_t nb, int32_t tail, hipStream_t s)
+{
+    hipLaunchKernelGGL(k_tail_cells, dim3(1), dim3(64), 0, s, cells, at, nb, tail);
+    return hipGetLastError();
+}
 
 hipError_t launch_update(const UpdateArgs &a, bool f16, hipStream_t s)
 {

@@ -859,6 +859,89 @@ qsa_status qsa_chunk_step(const qsa_layer_desc *desc, const qsa_layer_cache *cac
     return ok();
 }
 
+size_t qsa_ablation_workspace_bytes(const qsa_layer_desc *desc, int32_t capacity)
+{
+    if (check_desc(desc) != QSA_OK || capacity < 4 || capacity % 4 != 0 || capacity > (1 << 21))
+        return 0;
+    const int32_t nb = capacity / 4;
+    const int G = desc->q_heads / desc->kv_heads;
+    // qsa_attend_masked: the block bitmap, then the split partials
+    const size_t masked = align256(sizeof(uint32_t) * (size_t)((nb + 31) / 32)) +
+                          align256(sizeof(float) * (size_t)desc->kv_heads * kMaskedMaxSplits *
+                                   part_stride(G, desc->head_dim));
+    // qsa_topk_cells: the expanded scores, then the keys and tile lists of the cells
+    const size_t cells = align256(sizeof(float) * 4 * (size_t)nb) + ws_layout(4 * (int64_t)nb, 0, 0).total;
+    return masked > cells ? masked : cells;
+}
+
+qsa_status qsa_topk_cells(const float *block_scores, int32_t n_tokens, int32_t top_k_tokens,
+                          int32_t *cells, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (n_tokens < 1 || n_tokens / 4 > (1 << 17) || top_k_tokens < 4 || top_k_tokens % 4 != 0)
+        return fail(QSA_ERR_ARG, "n_tokens %d / top_k_tokens %d out of range", n_tokens, top_k_tokens);
+    const int32_t nb = n_tokens / 4, tail = n_tokens % 4;
+    if ((nb > 0 && !block_scores) || !cells)
+        return fail(QSA_ERR_ARG, "block_scores / cells is NULL");
+    const size_t off = align256(sizeof(float) * 4 * (size_t)nb);
+    const WsLayout L = ws_layout(4 * (int64_t)nb, 0, 0);
+    qsa_status st = check_ws(ws, ws_bytes, off + L.total);
+    if (st != QSA_OK)
+        return st;
+    hipError_t e = hipSuccess;
+    const int32_t nc = 4 * nb;
+    int32_t kept = nc;
+    if (nc > top_k_tokens) {
+        char *w = (char *)ws;
+        float *cs = (float *)w;
+        e = launch_expand_cells(block_scores, nb, cs, stream);
+        if (e == hipSuccess)
+            e = launch_keys(cs, nc, (uint32_t *)(w + off + L.keys), (uint64_t *)(w + off + L.lists),
+                            stream);
+        if (e == hipSuccess)
+            e = launch_select(select_args(w + off, L, nc, top_k_tokens, kKeysTile, cells), stream);
+        kept = top_k_tokens;
+    } else if (nc > 0) {
+        e = launch_iota(cells, nc, stream);
+    }
+    if (e == hipSuccess && tail > 0)
+        e = launch_tail_cells(cells, kept, nb, tail, stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "topk_cells");
+}
+
+qsa_status qsa_attend_masked(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
+                             int32_t n_tokens, const int32_t *sel, int32_t n_sel_blocks,
+                             const float *q, float *out, void *ws, size_t ws_bytes,
+                             hipStream_t stream)
+{
+    qsa_status s;
+    if ((s = check_desc(desc)) != QSA_OK || (s = check_cache(cache, false, false, true)) != QSA_OK)
+        return s;
+    const int32_t nb = n_tokens / 4;
+    if (n_tokens < 1 || n_tokens > cache->capacity)
+        return fail(QSA_ERR_ARG, "n_tokens %d outside [1, %d]", n_tokens, cache->capacity);
+    if (n_sel_blocks < 0 || n_sel_blocks > nb || (n_sel_blocks > 0 && !sel))
+        return fail(QSA_ERR_ARG, "n_sel_blocks %d outside [0, %d] or sel NULL", n_sel_blocks, nb);
+    if (!q || !out || !aligned(q, 16) || !aligned(out, 16))
+        return fail(QSA_ERR_ARG, "q / out NULL or not 16-byte aligned");
+    const size_t need = qsa_ablation_workspace_bytes(desc, cache->capacity);
+    if ((s = check_ws(ws, ws_bytes, need)) != QSA_OK)
+        return s;
+    MaskedArgs m{};
+    m.k = cache->k;
+    m.v = cache->v;
+    m.sel = sel;
+    m.q = q;
+    m.out = out;
+    m.bitmap = (uint32_t *)ws;
+    m.part = (float *)((char *)ws + align256(sizeof(uint32_t) * (size_t)((cache->capacity / 4 + 31) / 32)));
+    m.n_tokens = n_tokens;
+    m.n_sel_blocks = n_sel_blocks;
+    m.kv_heads = desc->kv_heads;
+    m.scale = attn_scale(desc);
+    hipError_t e = launch_masked_attend(m, desc->head_dim, desc->q_heads / desc->kv_heads, stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "attend_masked");
+}
+
 const char *qsa_status_string(qsa_status s)
 {
     switch (s) {

@@ -120,6 +120,9 @@ constexpr int kKeysTile = 256;
 hipError_t launch_keys(const float *scores, int32_t nb, uint32_t *keys, uint64_t *lists,
                        hipStream_t s);
 hipError_t launch_fill_zero(uint32_t *p, int32_t words, hipStream_t s);
+// The former cell-level path: block scores expanded to cells; tail cells appended.
+hipError_t launch_expand_cells(const float *scores, int32_t nb, float *cells, hipStream_t s);
+hipError_t launch_tail_cells(int32_t *cells, int32_t at, int32_t nb, int32_t tail, hipStream_t s);
 hipError_t launch_iota(int32_t *p, int32_t n, hipStream_t s);
 
 // Per-tile candidate lists: a tile of R consecutive blocks keeps its T = R/8
@@ -219,6 +222,27 @@ struct ChunkArgs {
     int32_t sel_cache_keys;     // the select keeps each query's keys in LDS (set by the launcher)
     float scale;
 };
+// The gather switched off (an ablation of the selected K/V gather): flash-
+// decode over every cached K / V row, the blocks outside `sel` masked out of
+// the softmax.  Same cells as the gathered attention.
+constexpr int kMaskedSplits = 256;      // per KV head: 512 workgroups for two KV heads
+constexpr int kMaskedMaxSplits = 1024;
+struct MaskedArgs {
+    const uint16_t *k;
+    const uint16_t *v;
+    const int32_t *sel;         // [n_sel_blocks] ascending
+    const float *q;
+    float *out;
+    float *part;                // [kv_heads][n_split] partials
+    uint32_t *bitmap;           // [ceil(nb / 32)] words, written by the launch
+    int64_t n_tokens;
+    int32_t n_sel_blocks;
+    int32_t kv_heads;
+    int32_t n_split;            // set by the launcher
+    float scale;
+};
+hipError_t launch_masked_attend(MaskedArgs m, int Dh, int G, hipStream_t s);
+
 // Append, then (after the caller's pooling launch) score, select and attend.
 hipError_t launch_chunk_append(const ChunkArgs &c, hipStream_t s);
 hipError_t launch_chunk_rest(ChunkArgs c, bool f16, int Dh, int G, hipStream_t s);

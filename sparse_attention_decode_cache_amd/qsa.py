@@ -23,7 +23,8 @@ EXPORTS = ("qsa_workspace_bytes", "qsa_state_invalidate", "qsa_state_truncate",
            "qsa_cache_update", "qsa_index_score", "qsa_topk_blocks", "qsa_gather_attend",
            "qsa_decode_step", "qsa_batch_workspace_bytes", "qsa_decode_step_batch",
            "qsa_chunk_workspace_bytes", "qsa_chunk_step", "qsa_multi_workspace_bytes",
-           "qsa_decode_step_multi", "qsa_status_string", "qsa_last_error")
+           "qsa_decode_step_multi", "qsa_ablation_workspace_bytes", "qsa_topk_cells",
+           "qsa_attend_masked", "qsa_status_string", "qsa_last_error")
 QSA_MAX_BATCH = 8
 QSA_MAX_CHUNK = 4096
 QSA_MAX_MULTI = 4
@@ -91,9 +92,13 @@ def lib():
         L.qsa_multi_workspace_bytes.restype = sz
         L.qsa_multi_workspace_bytes.argtypes = [D, i32, i32]
         L.qsa_decode_step_multi.argtypes = [D, C, S, i32, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+        L.qsa_ablation_workspace_bytes.restype = sz
+        L.qsa_ablation_workspace_bytes.argtypes = [D, i32]
+        L.qsa_topk_cells.argtypes = [P, i32, i32, P, P, sz, P]
+        L.qsa_attend_masked.argtypes = [D, C, i32, P, i32, P, P, P, sz, P]
         for f in ("qsa_cache_update", "qsa_index_score", "qsa_topk_blocks", "qsa_gather_attend",
                   "qsa_decode_step", "qsa_decode_step_batch", "qsa_chunk_step",
-                  "qsa_decode_step_multi"):
+                  "qsa_decode_step_multi", "qsa_topk_cells", "qsa_attend_masked"):
             getattr(L, f).restype = ctypes.c_int
         L.qsa_status_string.restype = ctypes.c_char_p
         L.qsa_status_string.argtypes = [ctypes.c_int]
@@ -261,3 +266,26 @@ def qsa_decode_step_multi(desc, cache, state, n_q, idx_k_rows, k_rows, v_rows, g
                                        int(n_q), _ptr(idx_k_rows), _ptr(k_rows), _ptr(v_rows),
                                        _ptr(gamma), _ptr(q_idx), _ptr(w), _ptr(q), _ptr(out),
                                        _ptr(sel_out), _ptr(scores_out), p, n, _stream(stream)))
+
+
+def qsa_ablation_workspace_bytes(desc, capacity):
+    return lib().qsa_ablation_workspace_bytes(ctypes.byref(desc), int(capacity))
+
+
+def ablation_workspace(desc, capacity, device="cuda"):
+    n = qsa_ablation_workspace_bytes(desc, capacity)
+    if n == 0:
+        raise QSAError(QSA_ERR_UNSUPPORTED, "qsa_ablation_workspace_bytes rejected the arguments")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def qsa_topk_cells(block_scores, n_tokens, top_k_tokens, cells, ws, stream=None):
+    p, n = _ws(ws)
+    _check(lib().qsa_topk_cells(_ptr(block_scores), int(n_tokens), int(top_k_tokens), _ptr(cells),
+                                p, n, _stream(stream)))
+
+
+def qsa_attend_masked(desc, cache, n_tokens, sel, n_sel_blocks, q, out, ws, stream=None):
+    p, n = _ws(ws)
+    _check(lib().qsa_attend_masked(ctypes.byref(desc), ctypes.byref(cache), int(n_tokens), _ptr(sel),
+                                   int(n_sel_blocks), _ptr(q), _ptr(out), p, n, _stream(stream)))

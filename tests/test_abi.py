@@ -195,3 +195,26 @@ def test_multi_argument_errors_before_launch():
     assert call(st, 3, rows=0) == -1                # null rows
     assert call(st, 3, ws_bytes=100) == -3
     assert (st.n_tokens, st.n_valid_blocks) == (4093, 1023)
+
+
+def test_ablation_argument_errors_before_launch():
+    qsa, d, c = _objs()
+    L = qsa.lib()
+    P = ctypes.c_void_p
+    D, C = ctypes.byref(d), ctypes.byref(c)
+    need = qsa.qsa_ablation_workspace_bytes(d, 4096)
+    assert need > 0 and need % 256 == 0
+    assert qsa.qsa_ablation_workspace_bytes(d, 4094) == 0
+    # cell-level top-k
+    assert L.qsa_topk_cells(P(16), 0, 2048, P(16), P(256), need, None) == -1
+    assert L.qsa_topk_cells(P(16), 4096, 2046, P(16), P(256), need, None) == -1
+    assert L.qsa_topk_cells(None, 4096, 2048, P(16), P(256), need, None) == -1
+    assert L.qsa_topk_cells(P(16), 4 * (1 << 17) + 4, 2048, P(16), P(256), 1 << 40, None) == -1
+    assert L.qsa_topk_cells(P(16), 4096, 2048, P(16), P(256), 64, None) == -3
+    # masked attention
+    assert L.qsa_attend_masked(D, C, 0, P(16), 0, P(16), P(16), P(256), need, None) == -1
+    assert L.qsa_attend_masked(D, C, 4097, P(16), 0, P(16), P(16), P(256), need, None) == -1
+    assert L.qsa_attend_masked(D, C, 4096, None, 5, P(16), P(16), P(256), need, None) == -1
+    assert L.qsa_attend_masked(D, C, 4096, P(16), 1025, P(16), P(16), P(256), need, None) == -1
+    assert L.qsa_attend_masked(D, C, 4096, P(16), 5, P(8), P(16), P(256), need, None) == -1
+    assert L.qsa_attend_masked(D, C, 4096, P(16), 5, P(16), P(16), P(256), need - 256, None) == -3
