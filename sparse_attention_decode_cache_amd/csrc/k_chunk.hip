@@ -371,10 +371,12 @@ __global__ __launch_bounds__(sel::kT) void k_chunk_select(ChunkArgs c)
 // threads read consecutive bytes of a row) one iteration ahead; K goes to an
 // LDS tile, where waves 0-3 take the
 // 64 x G logits on the matrix cores (q as two f16 halves); waves h < G run
-// the online softmax of head h over the 64 cells; each thread then adds the
-// G x 4 products of its own 8-byte V chunks to accumulators it keeps for the
-// whole split.  The accumulators of threads sharing a chunk are summed once
-// at the end (xor shuffles in the wave, a fixed tree over the waves).
+// the online softmax of head h over the 64 cells and leave its weights in LDS
+// as two f16 halves (hi + lo: V times either half is exact in fp32); V then
+// takes the K tile's place, and P.V also runs on the matrix cores: out^T
+// (dims x heads) += V^T (dims x cells) . P (cells x heads), wave w owning the
+// 16-dim tiles w, w + 8, ... for the whole split, so no cross-wave sum is
+// left at the end.
 
 constexpr int kCI = 64;                      // cells per iteration
 constexpr int kCAT = 512;                    // threads (two workgroups share a CU)
@@ -409,8 +411,7 @@ __device__ __forceinline__ void static_for(F &&f)
     }
 }
 
-// K moves in 16-byte chunks (to the LDS tile), V in 8-byte chunks (a thread
-// keeps 4 dims x G heads of accumulators).
+// K moves in 16-byte chunks, V in 8-byte chunks, both through the LDS tile.
 template <int DH, int G>
 struct CAShape {
     static constexpr int KCH = DH / 8;                    // 16-byte chunks of a K row
@@ -420,10 +421,9 @@ struct CAShape {
     static constexpr int VPAIRS = kCI * VCH;
     static constexpr int VR = (VPAIRS + kCAT - 1) / kCAT; // V chunks (cells) per thread
     static constexpr int KS = DH / 32;                    // MFMA k-steps of a row
-    static constexpr int KROW = 2 * DH + 16;              // padded LDS bytes of a K row
-    static constexpr int LPW = VCH < kWave ? VCH : kWave; // lanes holding distinct V chunks
-    static constexpr int GP = G < 4 ? 4 : G;
-    static constexpr int RED = (kCAW / 2) * G * 4 * LPW;  // floats of the reduction tree
+    static constexpr int KROW = 2 * DH + 16;              // padded LDS bytes of a K (or V) row
+    static constexpr int NT = DH / 16;                    // 16-dim output tiles of P.V
+    static constexpr int TPW = (NT + kCAW - 1) / kCAW;    // tiles per wave
     static_assert(kCAT % KCH == 0 && kCAT % VCH == 0 && KPAIRS % kWave == 0 && VPAIRS % kWave == 0 &&
                   KR <= 8 && VR <= 8 && G <= kCAW && kCI / 16 <= kCAW, "shape");
 };
@@ -431,12 +431,12 @@ struct CAShape {
 template <int DH, int G>
 struct CALds {
     using S = CAShape<DH, G>;
-    // the K tile during the loop, the reduction tree after it
-    static constexpr int KT = kCI * S::KROW, RB = 4 * S::RED;
-    alignas(16) unsigned char ktile[KT > RB ? KT : RB];
+    // the K tile, then (after the logits) the V tile of the iteration
+    static constexpr int KT = kCI * S::KROW;
+    alignas(16) unsigned char ktile[KT];
     alignas(16) uint4 qb[S::KS][2][kWave];
     float lg[kCI][G + 1];
-    alignas(16) float p[kCI][S::GP];
+    alignas(16) _Float16 pt[2][G][kCI];        // softmax weights, hi and lo halves, [head][cell]
     float sc[G], mrow[G], lrow[G];
     int32_t ids[kChunkMaxIds];
 };
@@ -464,7 +464,7 @@ __device__ void attend_unit(const QueryUnit &c, CALds<DH, G> &L, int s, int g)
 {
     using S = CAShape<DH, G>;
     constexpr int KCH = S::KCH, VCH = S::VCH, KR = S::KR, VR = S::VR, KS = S::KS, KROW = S::KROW,
-                  LPW = S::LPW;
+                  NT = S::NT, TPW = S::TPW;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int ns = c.ns;
     const int64_t n = c.n;
@@ -549,15 +549,16 @@ __device__ void attend_unit(const QueryUnit &c, CALds<DH, G> &L, int s, int g)
         });
     };
 
-    float acc[G][4];
+    // P.V accumulators: wave w owns the 16-dim tiles w, w + kCAW, ...; lane l
+    // holds out^T[dim 16 tile + 4 (l / 16) + j][head l % 16], j < 4
+    const int hn = lane & 15, kq = lane >> 4;
+    float4v acc[TPW];
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[h][j] = 0.0f;
+    for (int i = 0; i < TPW; ++i)
+        acc[i] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
     float m_run = -INFINITY, l_run = 0.0f;          // wave h < G: head h
-    // K and V one iteration ahead (K leaves the registers for the LDS tile
-    // first thing, V after the products)
+    // K and V one iteration ahead: K leaves the registers for the LDS tile
+    // first thing, V when the tile is free again (after the logits)
     Regs8<u32x4> kr;
     Regs8<u32x2> vr;
     if (it0 < it1) {
@@ -610,103 +611,81 @@ __device__ void attend_unit(const QueryUnit &c, CALds<DH, G> &L, int s, int g)
             }
             l_run = l_run * sc + wave::reduce_add_f(pv);
             m_run = mn;
-            L.p[lane][wave] = pv;
+            const _Float16 ph = (_Float16)pv;
+            L.pt[0][wave][lane] = ph;
+            L.pt[1][wave][lane] = (_Float16)(pv - (float)ph);
             if (lane == 0)
                 L.sc[wave] = sc;
         }
-        __syncthreads();
-        float scv[G];
-        bool any = false;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            scv[h] = L.sc[h];
-            any = any || scv[h] != 1.0f;
-        }
-        if (any) {
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[h][j] *= scv[h];
-        }
+        // V into the tile (every read of K was before the barrier above)
         static_for<VR>([&](auto rc) __attribute__((always_inline)) {
             constexpr int r = decltype(rc)::value;
             const int pr = t + kCAT * r;
-            if (pr < S::VPAIRS) {
-                const int lc = pr / VCH;
-                float ph[G];
-#pragma unroll
-                for (int h = 0; h < G; ++h)
-                    ph[h] = L.p[lc][h];
-                _Float16 vh[4];
-                __builtin_memcpy(vh, &vr.template at<r>(), 8);
-#pragma unroll
-                for (int h = 0; h < G; ++h)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc[h][j] = fmaf(ph[h], (float)vh[j], acc[h][j]);
-            }
+            if (pr < S::VPAIRS)
+                *(u32x2 *)(L.ktile + (pr / VCH) * KROW + 8 * (pr % VCH)) = vr.template at<r>();
         });
         if (it + 1 < it1)
             load_v(it + 1, vr);
+        __syncthreads();
+        // out^T = out^T * sc + V^T P: A = 16 dims x 32 cells read down the V
+        // tile's columns, B = 32 cells x 16 heads (zero past G), hi and lo
+        const float scl = hn < G ? L.sc[hn] : 1.0f;
+#pragma unroll
+        for (int i = 0; i < TPW; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] *= scl;
+#pragma unroll
+        for (int ks = 0; ks < kCI / 32; ++ks) {
+            half8 bh = {}, bl = {};
+            if (hn < G) {
+                __builtin_memcpy(&bh, &L.pt[0][hn][32 * ks + 8 * kq], 16);
+                __builtin_memcpy(&bl, &L.pt[1][hn][32 * ks + 8 * kq], 16);
+            }
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                const int tile = wave + kCAW * i;
+                if (NT % kCAW == 0 || tile < NT) {
+                    half8 a;
+                    const unsigned char *col = L.ktile + (32 * ks + 8 * kq) * KROW + 2 * (16 * tile + hn);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        a[e] = *(const _Float16 *)(col + e * KROW);
+                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bh, acc[i], 0, 0, 0);
+                    acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bl, acc[i], 0, 0, 0);
+                }
+            }
+        }
+        __syncthreads();   // the tile takes the next iteration's K
     }
 
     if (wave < G && lane == 0) {
         L.mrow[wave] = m_run;
         L.lrow[wave] = l_run;
     }
-    // sum over the threads of a V chunk: lanes l ^ VCH, l ^ 2 VCH, ... in the
-    // wave, then a fixed tree over the waves (in the K tile's LDS, free now:
-    // every wave has passed the last iteration's logit barrier)
-#pragma unroll
-    for (int off = VCH; off < kWave; off <<= 1)
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[h][j] += __shfl_xor(acc[h][j], off);
-    float *red = reinterpret_cast<float *>(L.ktile);
-#pragma unroll
-    for (int half = kCAW / 2; half >= 1; half >>= 1) {
-        if (wave >= half && wave < 2 * half && lane < LPW) {
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    red[((wave - half) * G * 4 + h * 4 + j) * LPW + lane] = acc[h][j];
-        }
-        __syncthreads();
-        if (wave < half && lane < LPW) {
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[h][j] += red[(wave * G * 4 + h * 4 + j) * LPW + lane];
-        }
-        __syncthreads();
-    }
-    if (wave != 0 || lane >= LPW)
-        return;
-    const int k4 = 4 * lane;                       // this lane's 4 dims
-    if (c.direct) {
-        float *o = c.out + (size_t)g * G * DH;
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            const float l = L.lrow[h];
-            *(float4 *)(o + h * DH + k4) = make_float4(acc[h][0] / l, acc[h][1] / l, acc[h][2] / l, acc[h][3] / l);
-        }
-        return;
-    }
+    __syncthreads();
     float *part = c.part + ((size_t)g * ns + s) * (size_t)part_stride(G, DH);
+    if (hn < G) {
+        const float l = L.lrow[hn];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+        for (int i = 0; i < TPW; ++i) {
+            const int tile = wave + kCAW * i;
+            if (NT % kCAW != 0 && tile >= NT)
+                continue;
+            const int d0 = 16 * tile + 4 * kq;
+            if (c.direct) {
+                float *o = c.out + ((size_t)g * G + hn) * DH + d0;
+                *(float4 *)o = make_float4(acc[i][0] / l, acc[i][1] / l, acc[i][2] / l, acc[i][3] / l);
+            } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)                // a partial's stride is not a multiple of 4
-            part[2 * G + h * DH + k4 + j] = acc[h][j];
-        if (lane == 0) {
-            part[h] = L.mrow[h];
-            part[G + h] = L.lrow[h];
+                for (int j = 0; j < 4; ++j)            // a partial's stride is not a multiple of 4
+                    part[2 * G + hn * DH + d0 + j] = acc[i][j];
+            }
         }
+    }
+    if (!c.direct && wave == 0 && lane < G) {
+        part[lane] = L.mrow[lane];
+        part[G + lane] = L.lrow[lane];
     }
 }
 
