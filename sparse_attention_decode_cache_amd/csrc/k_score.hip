@@ -77,13 +77,15 @@ __device__ inline uint32_t score_key(float s)
 }
 
 // Tile list: the T largest of the R composites in s_c (0 = no row), written
-// descending to lists[tile*T ...]; slots past the tile's rows get 0.  Ranks
+// descending to lists[tile*T ...]; slots past the tile's rows get 0.  T <= R
+// is chosen per call (longer lists where a tile holds more winners).  Ranks
 // are exact because composites are unique and nonzero.  All 256 threads
 // work: P = 256/R consecutive threads share an entry, each counting the
 // larger composites in 1/P of the tile, summed with DPP quad moves.  Whole
 // workgroup calls (uniform control flow: DPP reads neighbouring lanes).
-template <int R, int T>
-__device__ inline void write_tile_list(const uint64_t *s_c, uint64_t *lists, int tile, int valid_rows)
+template <int R>
+__device__ inline void write_tile_list(const uint64_t *s_c, uint64_t *lists, int tile, int valid_rows,
+                                       int T)
 {
     static_assert(R == 64 || R == 128 || R == 256, "tile rows");
     constexpr int P = 256 / R;
@@ -293,8 +295,8 @@ __device__ inline void score_tile(const ScoreMultiArgs &a, ScoreLdsOf<F16, LPR, 
     for (int qi = 0; qi < Q; ++qi) {
         if (a.lists[qi]) {
             const int64_t valid = a.nbq[qi] - (int64_t)tile * R;
-            write_tile_list<R, R / kListDiv>(sl.c[qi], a.lists[qi], tile,
-                                             (int)(valid < 0 ? 0 : (valid < R ? valid : R)));
+            write_tile_list<R>(sl.c[qi], a.lists[qi], tile,
+                               (int)(valid < 0 ? 0 : (valid < R ? valid : R)), a.list_t);
         }
     }
 }
@@ -324,6 +326,7 @@ __device__ inline ScoreMultiArgs single(const ScoreArgs &a)
     m.lists[0] = a.lists;
     m.scores = a.scores;
     m.ld_scores = 0;
+    m.list_t = a.list_t;
     return m;
 }
 
@@ -379,8 +382,8 @@ __global__ __launch_bounds__(kKeysTile) void k_keys(const float *scores, int32_t
     s_c[threadIdx.x] = c;
     __syncthreads();
     const int valid = nb - (int)blockIdx.x * kKeysTile;
-    write_tile_list<kKeysTile, kKeysTile / kListDiv>(s_c, lists, blockIdx.x,
-                                                     valid < kKeysTile ? valid : kKeysTile);
+    write_tile_list<kKeysTile>(s_c, lists, blockIdx.x, valid < kKeysTile ? valid : kKeysTile,
+                               kKeysTile / kListDiv);
 }
 
 template <bool F16, int LPR>

@@ -190,8 +190,41 @@ qsa_status do_attend(const qsa_layer_desc *d, const qsa_layer_cache *c, int32_t 
 }
 
 // Top-k arguments over the keys and tile lists already in the workspace.
+// Entries T of each R-block tile list for nb blocks and k kept: a tile can
+// hide a winner from the lists only if it holds T or more of the k winners.
+// With winners spread at random, a tile holds X ~ Poisson(R k / nb) of them;
+// T is the shortest of R/8, R/4, R/2 (at most 32) for which the expected
+// number of such tiles, ntiles P(X >= T), is below 1e-4, within what the
+// fast path of the top-k holds.  (Failing the check costs time, not
+// exactness: the top-k then runs over every key.)
+int32_t list_len(int32_t tile_rows, int64_t nb, int32_t k)
+{
+    const int32_t base = tile_rows / kListDiv;
+    if (nb <= 0)
+        return base;
+    const int64_t ntiles = (nb + tile_rows - 1) / tile_rows;
+    const double lam = (double)tile_rows * (double)(k < nb ? k : nb) / (double)nb;
+    int32_t best = base;
+    for (int32_t T = base; T <= 32 && T <= tile_rows / 2; T *= 2) {
+        if (!sel::fits_fast((int32_t)ntiles, T))
+            break;
+        best = T;
+        double term = exp(-lam);            // P(X = x), x = 0 ..
+        for (int32_t x = 0; x < T; ++x)
+            term *= lam / (double)(x + 1);
+        double tail = 0.0;                  // P(X >= T)
+        for (int32_t x = T; x < T + 200 && term > 0.0; ++x) {
+            tail += term;
+            term *= lam / (double)(x + 1);
+        }
+        if ((double)ntiles * tail < 1e-4)
+            break;
+    }
+    return best;
+}
+
 SelectArgs select_args(char *ws, const WsLayout &L, int32_t nb, int32_t k, int32_t tile_rows,
-                       int32_t *sel)
+                       int32_t list_t, int32_t *sel)
 {
     SelectArgs s{};
     s.keys = (const uint32_t *)(ws + L.keys);
@@ -200,14 +233,15 @@ SelectArgs select_args(char *ws, const WsLayout &L, int32_t nb, int32_t k, int32
     s.nb = nb;
     s.k = k;
     s.ntiles = (nb + tile_rows - 1) / tile_rows;
-    s.T = tile_rows / kListDiv;
+    s.T = list_t;
     return s;
 }
 
 qsa_status do_select(char *ws, const WsLayout &L, int32_t nb, int32_t k, int32_t tile_rows,
                      int32_t *sel, hipStream_t stream)
 {
-    hipError_t e = launch_select(select_args(ws, L, nb, k, tile_rows, sel), stream);
+    hipError_t e = launch_select(select_args(ws, L, nb, k, tile_rows, tile_rows / kListDiv, sel),
+                                 stream);
     if (e != hipSuccess)
         return hip_fail(e, "select");
     return QSA_OK;
@@ -423,6 +457,8 @@ qsa_status qsa_decode_step(const qsa_layer_desc *desc, const qsa_layer_cache *ca
     }
 
     // 2. score every completed block (keys for the top-k)
+    const int tile_rows = score_tile_rows(desc->idx_dtype == QSA_F16, rowb);
+    const int32_t list_t = list_len(tile_rows, nb, K);
     if (score) {
         ScoreArgs a{};
         a.summary = cache->summary;
@@ -431,6 +467,7 @@ qsa_status qsa_decode_step(const qsa_layer_desc *desc, const qsa_layer_cache *ca
         a.scores = scores_out;
         a.keys = need_select ? (uint32_t *)(wsp + L.keys) : nullptr;
         a.lists = need_select ? (uint64_t *)(wsp + L.lists) : nullptr;
+        a.list_t = list_t;
         a.nb = nb;
         a.D = desc->idx_dim;
         a.fuse = fuse ? 1 : 0;
@@ -448,8 +485,7 @@ qsa_status qsa_decode_step(const qsa_layer_desc *desc, const qsa_layer_cache *ca
     float *part = (float *)(wsp + L.part);
     const int G = desc->q_heads / desc->kv_heads;
     if (need_select) {
-        const int tile_rows = score_tile_rows(desc->idx_dtype == QSA_F16, rowb);
-        SelectArgs sa = select_args(wsp, L, nb, K, tile_rows, sel_out);
+        SelectArgs sa = select_args(wsp, L, nb, K, tile_rows, list_t, sel_out);
         // fused: the splits hold the 4K chosen cells, the merge adds the tail
         AttendArgs aa = attend_args(desc, cache, n, nullptr, K, q, out, part);
         aa.n_cells = 4 * K;
@@ -588,13 +624,14 @@ qsa_status qsa_decode_step_batch(const qsa_layer_desc *desc, int32_t n_seq,
         a.w = x.w;
         a.keys = need_select ? (uint32_t *)(wsp + L.keys) : nullptr;
         a.lists = need_select ? (uint64_t *)(wsp + L.lists) : nullptr;
+        a.list_t = list_len(tile_rows, nb, K);
         a.nb = need_select ? nb : 0;     // kept-everything sequences only run the prologue
         a.D = desc->idx_dim;
         a.fuse = fuse ? 1 : 0;
         a.upd = u;
 
         int32_t *sel = need_select ? (x.sel_out ? x.sel_out : (int32_t *)(wsp + L.sel)) : x.sel_out;
-        selb.seq[i] = select_args(wsp, L, nb, K, tile_rows, sel);
+        selb.seq[i] = select_args(wsp, L, nb, K, tile_rows, a.list_t, sel);
         ab.seq[i] = attend_args(desc, c, n, need_select ? sel : nullptr, need_select ? K : nb,
                                 x.q, x.out, (float *)(wsp + L.part));
     }
@@ -705,6 +742,7 @@ qsa_status qsa_decode_step_multi(const qsa_layer_desc *desc, const qsa_layer_cac
     sm.upd = u;
     sm.scores = scores_out;
     sm.ld_scores = nb_last;
+    sm.list_t = list_len(tile_rows, nb_last, K);   // one list length for every query
     for (int32_t i = 0; i < n_q; ++i) {
         char *wsp = (char *)ws + (size_t)i * slot;
         const int32_t n = n0 + i + 1, nb = n / 4;
@@ -715,7 +753,8 @@ qsa_status qsa_decode_step_multi(const qsa_layer_desc *desc, const qsa_layer_cac
         sm.keys[i] = need_select ? (uint32_t *)(wsp + L.keys) : nullptr;
         sm.lists[i] = need_select ? (uint64_t *)(wsp + L.lists) : nullptr;
         int32_t *sel = sel_out ? sel_out + (size_t)i * K : (int32_t *)(wsp + L.sel);
-        selb.seq[i] = select_args(wsp, L, nb, K, tile_rows, need_select || sel_out ? sel : nullptr);
+        selb.seq[i] = select_args(wsp, L, nb, K, tile_rows, sm.list_t,
+                                  need_select || sel_out ? sel : nullptr);
         selb.seq[i].pad_to = sel_out ? K : 0;
         ab.seq[i] = attend_args(desc, cache, n, need_select ? sel : nullptr, need_select ? K : nb,
                                 q + (size_t)i * qa, out + (size_t)i * qa,
@@ -898,7 +937,9 @@ qsa_status qsa_topk_cells(const float *block_scores, int32_t n_tokens, int32_t t
             e = launch_keys(cs, nc, (uint32_t *)(w + off + L.keys), (uint64_t *)(w + off + L.lists),
                             stream);
         if (e == hipSuccess)
-            e = launch_select(select_args(w + off, L, nc, top_k_tokens, kKeysTile, cells), stream);
+            e = launch_select(select_args(w + off, L, nc, top_k_tokens, kKeysTile,
+                                          kKeysTile / kListDiv, cells),
+                              stream);
         kept = top_k_tokens;
     } else if (nc > 0) {
         e = launch_iota(cells, nc, stream);

@@ -10,7 +10,7 @@
 namespace qsa {
 
 constexpr int kWave = 64;           // CDNA wavefront width
-constexpr int kListDiv = 8;         // per-tile top-k lists keep R / 8 entries
+constexpr int kListDiv = 8;         // per-tile top-k lists keep R / 8 entries or more (up to R / 2)
 
 // Workspace carve-up.
 struct WsLayout {
@@ -29,7 +29,7 @@ inline WsLayout ws_layout(int64_t max_blocks, int64_t sel_entries, int64_t part_
         return o;
     };
     L.keys = take(sizeof(uint32_t) * (size_t)max_blocks);
-    L.lists = take(sizeof(uint64_t) * (size_t)((max_blocks + kListDiv - 1) / kListDiv + 64));
+    L.lists = take(sizeof(uint64_t) * (size_t)((max_blocks + 1) / 2 + 64));
     L.sel = take(sizeof(int32_t) * (size_t)sel_entries);
     L.part = take(sizeof(float) * (size_t)part_floats);
     L.total = off;
@@ -76,6 +76,7 @@ struct ScoreArgs {
     float *scores;              // optional fp32 scores
     uint32_t *keys;             // optional order-preserving keys
     uint64_t *lists;            // optional per-tile top-T composites (with keys)
+    int32_t list_t;             // T: entries per tile list (with lists)
     int32_t nb;
     int32_t D;
     int32_t fuse;               // workgroup 0 first runs `upd` (append, pool <= 1 row)
@@ -111,6 +112,7 @@ struct ScoreMultiArgs {
     uint64_t *lists[kMaxMulti];     // optional per query: per-tile top-T composites
     float *scores;                  // optional [n_q][ld_scores]: -inf at b >= nbq[i]
     int64_t ld_scores;
+    int32_t list_t;                 // T: entries per tile list (with lists)
 };
 hipError_t launch_score_multi(const ScoreMultiArgs &a, int n_q, bool f16, int row_bytes,
                               hipStream_t s);
