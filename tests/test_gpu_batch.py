@@ -86,3 +86,11 @@ def test_batch_single_sequence_matches_decode_step():
         assert a.state.n_tokens == b.state.n_tokens
         torch.testing.assert_close(a.out, b.out, rtol=0.0, atol=1e-5)
         assert torch.equal(a.buf.summary[:nb], b.buf.summary[:nb])
+
+
+def test_batch_full_size_mixed_contexts():
+    """The benchmarked batch (8 sequences of 16,381 .. 255,181 tokens, the
+    headline layer shapes): tile lists of 32, 16 and 8 entries side by side in
+    one select launch; every sequence checked against its own oracle."""
+    st = _run_batch(W.BATCH, list(W.BATCH_CONTEXTS), steps=2)
+    assert st["exact"] + st["threshold"] == 16
