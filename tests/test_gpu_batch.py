@@ -94,3 +94,36 @@ def test_batch_full_size_mixed_contexts():
     one select launch; every sequence checked against its own oracle."""
     st = _run_batch(W.BATCH, list(W.BATCH_CONTEXTS), steps=2)
     assert st["exact"] + st["threshold"] == 16
+
+
+def test_batch_winners_clustered_in_a_few_tiles():
+    """The batched select with every winner of two sequences inside a few
+    consecutive tiles (tile lists of 16 and 32 entries): the per-sequence
+    fallback over every key, beside a sequence the lists decide."""
+    import torch
+    import sparse_attention_decode_cache_amd as qsa
+    contexts, clusters = [61789, 29453, 126253], [(3000, 3700), (100, 900), None]
+    ws_ = [with_size(W.CTX64K, n0=n0, steps=1) for n0 in contexts]
+    gs = [GpuLayer(w, seq=i, gamma_seq=0) for i, w in enumerate(ws_)]
+    os_ = [OracleMirror(w, seq=i, gamma_seq=0) for i, w in enumerate(ws_)]
+    for w, g, o, cl in zip(ws_, gs, os_, clusters):
+        if cl:
+            qi, _, _ = W.host_step_inputs(w, 0, 0, o.seq)
+            rows = np.stack([(qi * (4.0 + 0.01 * (b - cl[0]))).astype(np.float16)
+                             for b in range(*cl)])
+            o.L.summary[cl[0]:cl[1]] = rows
+            g.buf.summary[cl[0]:cl[1]] = torch.from_numpy(rows).cuda()
+    desc = gs[0].desc
+    ws = qsa.batch_workspace(desc, [g.cap for g in gs])
+    sels = [torch.full((W.CTX64K.k_blocks,), -1, dtype=torch.int32, device="cuda") for _ in gs]
+    qsa.qsa_decode_step_batch(desc, [g.buf.cache for g in gs], [g.state for g in gs],
+                              [_batch_io(g, 0, sels[i]) for i, g in enumerate(gs)], gs[0].gamma, ws)
+    for i, (g, o, cl) in enumerate(zip(gs, os_, clusters)):
+        ro = o.step(0)
+        n = g.state.n_tokens
+        sel = sels[i].cpu().numpy()
+        branch = check_topk(sel, ro["scores"], ro["scale"], W.CTX64K.k_blocks)
+        if cl:
+            assert branch == "exact" and np.array_equal(sel, np.arange(cl[1] - 512, cl[1]))
+        ref = oracle.attend(ro["q"], o.L.K, o.L.V, oracle.cells(sel, n))
+        check_attention(g.out.cpu().numpy().astype(np.float64), ref)

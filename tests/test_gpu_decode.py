@@ -110,3 +110,32 @@ def test_decode_is_bitwise_repeatable():
         ra, rb = a.step(s), b.step(s)
         assert np.array_equal(ra["out"], rb["out"]) and np.array_equal(ra["sel"], rb["sel"])
         assert np.array_equal(ra["scores"], rb["scores"])
+
+
+def _cluster_rows(w, lo, hi):
+    """Summary rows for blocks [lo, hi) that outscore every other block for the
+    step-0 query, increasing with the block id (no ties): f16 copies of
+    q_idx scaled by 4 + 0.01 (b - lo)."""
+    qi, _, _ = W.host_step_inputs(w, 0, 0)
+    dt = np.float16 if w.idx_f16 else np.float32
+    return np.stack([(qi * (4.0 + 0.01 * (b - lo))).astype(dt) for b in range(lo, hi)])
+
+
+@pytest.mark.parametrize("n0,lo,hi", [(61789, 3000, 3700), (29453, 100, 900), (255181, 40000, 40600)])
+def test_decode_winners_clustered_in_a_few_tiles(n0, lo, hi):
+    """Every winner inside a few consecutive tiles, so those tiles' lists are
+    full with their last entries above the k-th: the list fast path cannot
+    decide and the top-k runs over every key (tile lists of 16, 32 and 8
+    entries at these contexts).  The cluster's summary rows are written into
+    the GPU cache and the oracle's alike."""
+    import torch
+    w = with_size(W.CTX64K, n0=n0, steps=1)
+    g = GpuLayer(w)
+    o = OracleMirror(w)
+    rows = _cluster_rows(w, lo, hi)
+    o.L.summary[lo:hi] = rows
+    g.buf.summary[lo:hi] = torch.from_numpy(rows).cuda()
+    stats = {"ulp_diffs": 0, "exact": 0, "threshold": 0, "attn_err": 0.0}
+    rg, ro = _compare_step(g, o, 0, stats)
+    assert stats["exact"] == 1
+    assert np.array_equal(rg["sel"], np.arange(hi - w.k_blocks, hi))
