@@ -328,13 +328,18 @@ __device__ void general_path(const SelectArgs &a, Smem &sm, uint32_t *bitmap, ui
     emit_bitmap(sm, bitmap, nwords, k, emit);
 }
 
-// The exact top-k over every key in four passes: min / max, a 1024-bin
-// histogram linear in the score (or in the key when every score is >= 0),
-// the entries of the bin holding the k-th ranked by counting (kappa = the
-// k-th largest composite), the composites >= kappa marked.  Non-finite
-// scores or a crowded bin fall back to the radix refinement.  lkeys (LDS, nb
-// words, or null): the keys are read from memory once and kept there.
-// Requires nb > k.  Whole workgroup calls; emit as in run().
+// The exact top-k over every key: min / max, a 1024-bin histogram linear in
+// the score (or in the key when every score is >= 0), the entries of the bin
+// holding the k-th ranked by counting (kappa = the k-th largest composite),
+// the composites >= kappa marked.  A lower bound tau <= kappa prunes the
+// later passes: each thread's largest key is one of the keys, so if k of
+// these maxima are >= tau, at least k keys are, and the k-th largest is too.
+// tau is the k-th largest maximum (found by the same histogram / rank steps
+// on the 1024 maxima), and only keys >= tau -- a few per cent -- enter the
+// histogram, the boundary bin and the marks.  Non-finite scores or a
+// crowded bin fall back to the radix refinement.  lkeys (LDS, nb words, or
+// null): the keys are read from memory once and kept there.  Requires
+// nb > k.  Whole workgroup calls; emit as in run().
 template <class Emit>
 __device__ void keys_path(const SelectArgs &a, Smem &sm, uint32_t *bitmap, uint32_t *lkeys, Emit emit)
 {
@@ -349,7 +354,7 @@ __device__ void keys_path(const SelectArgs &a, Smem &sm, uint32_t *bitmap, uint3
         sm.ncand = 0u;
         sm.d = 0xFFFFFFFFu;
     }
-    // 1. keys (to LDS when asked) and their range
+    // 1. keys (to LDS when asked), their range, and this thread's largest
     uint32_t kmin1 = 0xFFFFFFFFu, kmax = 0u;
     for (uint32_t base = 0; base < nb; base += kT * 4) {
         uint32_t kk[4];
@@ -369,6 +374,7 @@ __device__ void keys_path(const SelectArgs &a, Smem &sm, uint32_t *bitmap, uint3
             }
         }
     }
+    const uint32_t tmax = kmax;                 // this thread's largest key (it holds one iff t < nb)
     kmin1 = wave::reduce_min_u32(kmin1);
     kmax = wave::reduce_max_u32(kmax);
     if (lane == 0) {
@@ -400,61 +406,100 @@ __device__ void keys_path(const SelectArgs &a, Smem &sm, uint32_t *bitmap, uint3
         const uint32_t b = (uint32_t)((sc - mn) * scale);
         return b < (uint32_t)kBins - 1 ? b : (uint32_t)kBins - 1;
     };
-    if (!general) {
-        // 2. histogram
-        for (uint32_t e = t; e < nb; e += kT)
-            atomicAdd(&sm.hist[bin_of(key_at(e))], 1u);
+    // The bin holding the need-th largest of the histogram (thread t takes
+    // bin 1023 - t): sm.d, sm.need (rank inside the bin), sm.in_d.
+    auto kth_bin = [&](uint32_t need) {
+        const uint32_t h = sm.hist[kBins - 1 - t];
+        const uint32_t incl = wave::incl_scan_add(h);
+        if (lane == 63)
+            sm.wtot[wv] = incl;
         __syncthreads();
-        // the bin d holding the k-th largest (thread t takes bin 1023 - t)
-        {
-            const uint32_t h = sm.hist[kBins - 1 - t];
-            const uint32_t incl = wave::incl_scan_add(h);
-            if (lane == 63)
-                sm.wtot[wv] = incl;
-            __syncthreads();
-            uint32_t off = 0;
+        uint32_t off = 0;
 #pragma unroll
-            for (int i = 0; i < kWaves; i += 4) {
-                const uint4 w4 = reinterpret_cast<const uint4 *>(sm.wtot)[i / 4];
-                off += (i < wv ? w4.x : 0u) + (i + 1 < wv ? w4.y : 0u) + (i + 2 < wv ? w4.z : 0u) +
-                       (i + 3 < wv ? w4.w : 0u);
-            }
-            const uint32_t above = off + incl - h;
-            if (above < k && above + h >= k) {
-                sm.d = (uint32_t)(kBins - 1 - t);
-                sm.need = k - above;
-                sm.in_d = h;
+        for (int i = 0; i < kWaves; i += 4) {
+            const uint4 w4 = reinterpret_cast<const uint4 *>(sm.wtot)[i / 4];
+            off += (i < wv ? w4.x : 0u) + (i + 1 < wv ? w4.y : 0u) + (i + 2 < wv ? w4.z : 0u) +
+                   (i + 3 < wv ? w4.w : 0u);
+        }
+        const uint32_t above = off + incl - h;
+        if (above < need && above + h >= need) {
+            sm.d = (uint32_t)(kBins - 1 - t);
+            sm.need = need - above;
+            sm.in_d = h;
+        }
+        __syncthreads();
+    };
+    // wave 0 ranks the m candidates by counting: sm.kappa = the need-th largest
+    auto rank_cand = [&](uint32_t m, uint32_t need) {
+        if (wv == 0) {
+            for (uint32_t j = lane; j < m; j += kWave) {
+                const uint64_t c = sm.cand[j];
+                uint32_t r = 0;
+#pragma unroll 4
+                for (uint32_t i = 0; i < m; ++i)
+                    r += sm.cand[i] > c ? 1u : 0u;
+                if (r == need - 1)
+                    sm.kappa = c;
             }
         }
         __syncthreads();
+    };
+    uint32_t tau = 0u;                          // keys below it cannot be among the k largest
+    if (!general && k <= (uint32_t)kT) {
+        // 2a. the k-th largest of the threads' maxima (composites: unique)
+        if ((uint32_t)t < nb)
+            atomicAdd(&sm.hist[bin_of(tmax)], 1u);
+        __syncthreads();
+        kth_bin(k);
+        const uint32_t dt = sm.d, mt = sm.in_d, need_t = sm.need;
+        if (dt != 0xFFFFFFFFu && mt <= (uint32_t)kCap) {
+            if ((uint32_t)t < nb && bin_of(tmax) == dt)
+                sm.cand[atomicAdd(&sm.ncand, 1u)] = comp_key(tmax, (uint32_t)t);
+            __syncthreads();
+            rank_cand(mt, need_t);
+            tau = (uint32_t)(sm.kappa >> 32);
+        }
+        sm.hist[t] = 0u;
+        if (t == 0) {
+            sm.ncand = 0u;
+            sm.d = 0xFFFFFFFFu;
+        }
+        __syncthreads();
+    }
+    if (!general) {
+        // 2. histogram of the keys >= tau
+        for (uint32_t e = t; e < nb; e += kT) {
+            const uint32_t key = key_at(e);
+            if (key >= tau)
+                atomicAdd(&sm.hist[bin_of(key)], 1u);
+        }
+        __syncthreads();
+        kth_bin(k);
         const uint32_t d = sm.d, m = sm.in_d;
         general = d == 0xFFFFFFFFu || m > (uint32_t)kCap;
         if (!general) {
-            // 3. the entries of bin d, ranked by counting in wave 0
+            // 3. keys above bin d are winners; bin d's entries are ranked
             for (uint32_t e = t; e < nb; e += kT) {
                 const uint32_t key = key_at(e);
-                if (bin_of(key) == d)
-                    sm.cand[atomicAdd(&sm.ncand, 1u)] = comp_key(key, e);
-            }
-            __syncthreads();
-            if (wv == 0) {
-                const uint32_t need = sm.need;
-                for (uint32_t j = lane; j < m; j += kWave) {
-                    const uint64_t c = sm.cand[j];
-                    uint32_t r = 0;
-#pragma unroll 4
-                    for (uint32_t i = 0; i < m; ++i)
-                        r += sm.cand[i] > c ? 1u : 0u;
-                    if (r == need - 1)
-                        sm.kappa = c;
+                if (key >= tau) {
+                    const uint32_t b = bin_of(key);
+                    if (b > d)
+                        atomicOr(&bitmap[e >> 5], 1u << (e & 31));
+                    else if (b == d)
+                        sm.cand[atomicAdd(&sm.ncand, 1u)] = comp_key(key, e);
                 }
             }
             __syncthreads();
-            // 4. the winners: composites >= kappa (exactly k of them)
+            rank_cand(m, sm.need);
+            // 4. bin d's winners: its composites >= kappa
             const uint64_t kappa = sm.kappa;
-            for (uint32_t e = t; e < nb; e += kT)
-                if (comp_key(key_at(e), e) >= kappa)
+            for (uint32_t j = t; j < m; j += kT) {
+                const uint64_t c = sm.cand[j];
+                if (c >= kappa) {
+                    const uint32_t e = ~(uint32_t)c;
                     atomicOr(&bitmap[e >> 5], 1u << (e & 31));
+                }
+            }
             __syncthreads();
             emit_bitmap(sm, bitmap, nwords, k, emit);
             return;
