@@ -354,17 +354,19 @@ __device__ void keys_path(const SelectArgs &a, Smem &sm, uint32_t *bitmap, uint3
         sm.ncand = 0u;
         sm.d = 0xFFFFFFFFu;
     }
-    // 1. keys (to LDS when asked), their range, and this thread's largest
+    // 1. keys (to LDS when asked), their range, and this thread's largest;
+    //    16 loads in flight per thread (each round waits one memory latency)
+    constexpr int kRound = 16;
     uint32_t kmin1 = 0xFFFFFFFFu, kmax = 0u;
-    for (uint32_t base = 0; base < nb; base += kT * 4) {
-        uint32_t kk[4];
+    for (uint32_t base = 0; base < nb; base += kT * kRound) {
+        uint32_t kk[kRound];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < kRound; ++q) {
             const uint32_t e = base + q * kT + t;
             kk[q] = a.keys[e < nb ? e : nb - 1];
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < kRound; ++q) {
             const uint32_t e = base + q * kT + t;
             if (e < nb) {
                 if (lkeys)
