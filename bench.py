@@ -17,6 +17,8 @@ the CPU oracle on a bounded sample of the same workload (rank 0, N = 1 only).
 verify, one call of 4 tokens per layer on the same 12 caches.
 `ablations` (after that): the page's comparisons timed on the same caches -- pooled-key cache
 off, cell-level top-k, gather off -- beside the calls they stand for.
+`context_sweep` (after that): the same 12-layer decode at 61,789 and 126,253 tokens beside the
+256k headline, each split into the score kernel's time and the rest of the step.
 `batch_and_chunk` (after that, also outside the headline's timed region): batched
 decode of 8 sequences of mixed context in one call per step, and one prefill
 chunk of 1024 tokens at 126,253 tokens of context, on the same layer shapes.
@@ -152,6 +154,76 @@ def multi_call_bytes(w, n0, n_q):
                    for i in range(n_q))
     queries = 4 * n_q * (w.idx_heads * w.idx_dim + w.idx_heads + 2 * w.q_heads * w.head_dim)
     return idx_row * nb_last + gathered + n_q * (idx_row + 2 * kv_row) + 5 * idx_row * new_blocks + queries
+
+
+def time_decode(torch, qsa, W, w, desc, stream, dev, steps, warmup, kernel_reps):
+    """12 layers of workload w (independent caches, round-robin): median
+    layer-step time over `steps` decode steps, and the score kernel's own time
+    (passes of back-to-back qsa_index_score launches over the same caches)."""
+    import dataclasses
+    w = dataclasses.replace(w, steps=warmup + steps)
+    cap = w.capacity()
+    layers = []
+    for li in range(w.layers):
+        buf = qsa.LayerBuffers(desc, cap)
+        W.dev_fill_layer_(w, buf, li, w.n0)
+        gamma = W.dev_gamma(w, li)
+        qsa.qsa_cache_update(desc, buf.cache, gamma, 0, w.n0 // 4)
+        layers.append((buf, gamma, W.dev_step_inputs(w, li, 0, w.steps),
+                       qsa.qsa_seq_state(w.n0, w.n0 // 4)))
+    ws = qsa.workspace(desc, cap)
+    out = torch.empty((w.q_heads, w.head_dim), dtype=torch.float32, device=dev)
+    for s in range(warmup):
+        for buf, gamma, inp, st in layers:
+            qsa.qsa_decode_step(desc, buf.cache, st, inp.raw[s], inp.k[s], inp.v[s], gamma,
+                                inp.q_idx[s], inp.w[s], inp.q[s], out, None, None, ws, stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(steps):
+        s = warmup + i
+        for buf, gamma, inp, st in layers:
+            qsa.qsa_decode_step(desc, buf.cache, st, inp.raw[s], inp.k[s], inp.v[s], gamma,
+                                inp.q_idx[s], inp.w[s], inp.q[s], out, None, None, ws, stream)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    step_us = statistics.median(1e3 * ev[i].elapsed_time(ev[i + 1]) / len(layers) for i in range(steps))
+    nb = layers[0][3].n_tokens // 4
+    scores = torch.empty(nb, dtype=torch.float32, device=dev)
+    durs = []
+    for rep in range(kernel_reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for buf, gamma, inp, st in layers:
+            qsa.qsa_index_score(desc, buf.cache, nb, inp.q_idx[0], inp.w[0], scores, stream)
+        b.record(stream)
+        durs.append((a, b))
+    torch.cuda.synchronize()
+    score_us = statistics.mean(1e3 * a.elapsed_time(b) / len(layers) for a, b in durs[1:])
+    del layers, ws
+    torch.cuda.empty_cache()
+    return step_us, score_us
+
+
+def bench_context_sweep(args, torch, qsa, W, w256, desc, stream, dev, head):
+    """The same 12-layer decode at 61,789 and 126,253 tokens beside the 256k
+    headline: the score pass grows with the context (one read of every
+    summary), the rest of the step (top-k over the tile lists, gather +
+    attention of at most 2,051 cells, merge) should not."""
+    import dataclasses
+    res = {}
+    for n0 in (61789, 126253):
+        w = dataclasses.replace(w256, n0=n0)
+        step_us, score_us = time_decode(torch, qsa, W, w, desc, stream, dev, args.sweep_steps, 4,
+                                        args.kernel_reps)
+        res[str(n0)] = {"layer_step_us": round(step_us, 2), "score_us": round(score_us, 2),
+                        "rest_us": round(step_us - score_us, 2)}
+    res[str(w256.n0)] = {"layer_step_us": head["layer_step_us"]["median"],
+                         "score_us": head["roofline"]["avg_launch_us"],
+                         "rest_us": round(head["layer_step_us"]["median"] - head["roofline"]["avg_launch_us"], 2)}
+    log(f"context sweep: {res}")
+    return {"workload": "12 layers x {61789, 126253, 255181} tokens, headline layer shapes", "by_context": res,
+            "note": "rest_us = layer step - score kernel (the score kernel's own time, scores only)"}
 
 
 def bench_multi(args, torch, qsa, w, desc, layers, stream, dev, decode_us):
@@ -467,6 +539,8 @@ def main():
     ap.add_argument("--multi-reps", type=int, default=8, help="rounds of multi-query calls")
     ap.add_argument("--no-multi", action="store_true", help="skip the multi-query decode leg")
     ap.add_argument("--ablation-reps", type=int, default=8)
+    ap.add_argument("--sweep-steps", type=int, default=16, help="decode steps per context of the sweep")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the 64k / 128k context sweep")
     ap.add_argument("--no-ablations", action="store_true", help="skip the ablation leg")
     ap.add_argument("--batch-only", action="store_true", help="only the batched-decode / chunk leg")
     ap.add_argument("--traffic-run", action="store_true",
@@ -607,6 +681,7 @@ def main():
                      "avg_launch_us": round(1e6 * k_avg_s, 3)},
         "cpu_baseline": None,
         "batch_and_chunk": None,
+        "context_sweep": None,
     }
     if not args.no_multi:
         result["multi_decode"] = bench_multi(args, torch, qsa, w, desc, layers, stream, dev,
@@ -614,9 +689,11 @@ def main():
     if not args.no_ablations:
         result["ablations"] = bench_ablations(args, torch, qsa, w, desc, layers, ws, stream, dev,
                                               result["layer_step_us"]["median"])
+    del layers, ws                      # the 256k caches: the legs below allocate their own
+    torch.cuda.empty_cache()
+    if not args.no_sweep:
+        result["context_sweep"] = bench_context_sweep(args, torch, qsa, W, w0, desc, stream, dev, result)
     if not args.no_batch:
-        del layers, ws
-        torch.cuda.empty_cache()
         result["batch_and_chunk"] = bench_batch_and_chunk(args, torch, qsa, W, stream, dev)
     if not args.no_cpu_baseline:
         log("cpu baseline ...")
