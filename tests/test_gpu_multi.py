@@ -247,3 +247,23 @@ def test_multi_argument_errors():
         g.qsa.qsa_decode_step_multi(g.desc, g.buf.cache, g.state, 3, raw, k, v, g.gamma, qi, wt, q,
                                     out, None, None, ws)
     assert g.state.n_tokens == g.cap - 2
+
+
+def test_multi_after_invalidation_rebuilds():
+    """The watermark far below the call (a state load): the call appends its
+    rows and rebuilds every distrusted block in its own launch before the one
+    pass over the summaries."""
+    w = with_size(W.CTX64K, n0=5002, steps=4)
+    g = GpuLayer(w)
+    o = OracleMirror(w)
+    g.qsa.qsa_state_invalidate(g.state, 1003)
+    o.L.invalidate(1003)
+    toks = _host_tokens(w, range(w.n0, w.n0 + 4), [0] * 4, range(4))
+    res = _multi(g, toks)
+    stats = {"exact": 0, "threshold": 0, "attn_err": 0.0}
+    for i in range(4):
+        _oracle_take(o.L, toks, i)
+        _check(i, o.L, toks, res, w.k_blocks, stats)
+    nb = g.state.n_valid_blocks
+    check_summaries(g.buf.summary[:nb].cpu().numpy(), o.L.summary[:nb])
+    assert stats["exact"] + stats["threshold"] == 4
