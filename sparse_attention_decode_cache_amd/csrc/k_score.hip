@@ -15,13 +15,17 @@
 //
 // Outputs (all optional, plain stores, no atomics): fp32 scores; the
 // order-preserving 32-bit key of every score; and, for the top-k, each tile's
-// T = R/8 largest composite keys (key << 32 | ~block), sorted descending.
+// T largest composite keys (key << 32 | ~block), sorted descending (T is
+// chosen per call, R/8 .. R/2).  Up to 4 queries of one sequence (the tokens
+// of a speculative-verify call) share one pass: every chunk is loaded once
+// and dotted with each query, each query with its own causal block limit.
 //
 // Fused stage 1: in a decode step at most one summary row is new.  Workgroup 0
 // (dispatched first) scores the LAST tile -- the one holding the new row --
-// and, while its loads are in flight, appends the token's rows and pools that
-// block straight into LDS; the lanes that loaded the row's stale chunks take
-// the pooled ones from there.  The pooling latency hides under the stream.
+// and, while its loads are in flight, appends the token's rows (all of a
+// verify call's) and pools that block straight into LDS; the lanes that
+// loaded the row's stale chunks take the pooled ones from there.  The
+// pooling latency hides under the stream.
 #include "qsa_pool.h"
 #include "qsa_wave.h"
 

@@ -137,7 +137,6 @@ qsa_status check_ws(void *ws, size_t ws_bytes, size_t need)
     return QSA_OK;
 }
 
-// Stage 4 launch shared by qsa_gather_attend and qsa_decode_step.
 // Compute units of the current device (cached per device).
 int64_t device_cus()
 {
@@ -178,6 +177,7 @@ AttendArgs attend_args(const qsa_layer_desc *d, const qsa_layer_cache *c, int32_
     return a;
 }
 
+// Stage 4 launch shared by qsa_gather_attend and qsa_decode_step.
 qsa_status do_attend(const qsa_layer_desc *d, const qsa_layer_cache *c, int32_t n_tokens,
                      const int32_t *sel, int32_t n_sel_blocks, const float *q, float *out,
                      float *part, hipStream_t stream)
@@ -189,7 +189,6 @@ qsa_status do_attend(const qsa_layer_desc *d, const qsa_layer_cache *c, int32_t 
     return QSA_OK;
 }
 
-// Top-k arguments over the keys and tile lists already in the workspace.
 // Entries T of each R-block tile list for nb blocks and k kept: a tile can
 // hide a winner from the lists only if it holds T or more of the k winners.
 // With winners spread at random, a tile holds X ~ Poisson(R k / nb) of them;
@@ -223,6 +222,8 @@ int32_t list_len(int32_t tile_rows, int64_t nb, int32_t k)
     return best;
 }
 
+// Top-k arguments over the keys and tile lists (T entries each) already in
+// the workspace.
 SelectArgs select_args(char *ws, const WsLayout &L, int32_t nb, int32_t k, int32_t tile_rows,
                        int32_t list_t, int32_t *sel)
 {
