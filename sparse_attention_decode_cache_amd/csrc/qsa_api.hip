@@ -189,6 +189,34 @@ qsa_status do_attend(const qsa_layer_desc *d, const qsa_layer_cache *c, int32_t 
     return QSA_OK;
 }
 
+// Stage 1 arguments: append n_new rows (consecutive in their sources) at
+// pos, then pool blocks [b0, b1).  rows may be null (no append).
+UpdateArgs update_args(const qsa_layer_desc *d, const qsa_layer_cache *c, const float *gamma,
+                       const void *idx_rows, const uint16_t *k_rows, const uint16_t *v_rows,
+                       int64_t pos, int32_t n_new, int32_t b0, int32_t b1)
+{
+    UpdateArgs u{};
+    u.idx_k = c->idx_k;
+    u.summary = c->summary;
+    u.k = c->k;
+    u.v = c->v;
+    u.new_idx_row = idx_rows;
+    u.new_k_row = k_rows;
+    u.new_v_row = v_rows;
+    u.gamma = gamma;
+    u.idx_row_words = d->idx_heads * d->idx_dim * elem_bytes(d->idx_dtype) / 4;
+    u.kv_row_words = d->kv_heads * d->head_dim / 2;
+    u.pos = pos;
+    u.n_new = n_new;
+    u.b0 = b0;
+    u.nblk = b1 - b0;
+    u.H = d->idx_heads;
+    u.D = d->idx_dim;
+    u.eps = (double)d->rms_eps;
+    u.theta = (double)d->rope_theta;
+    return u;
+}
+
 // Entries T of each R-block tile list for nb blocks and k kept: a tile can
 // hide a winner from the lists only if it holds T or more of the k winners.
 // With winners spread at random, a tile holds X ~ Poisson(R k / nb) of them;
@@ -295,16 +323,8 @@ qsa_status qsa_cache_update(const qsa_layer_desc *desc, const qsa_layer_cache *c
                     cache->capacity / 4);
     if (blk_end == blk_begin)
         return ok();
-    UpdateArgs a{};
-    a.idx_k = cache->idx_k;
-    a.summary = cache->summary;
-    a.gamma = gamma;
-    a.b0 = blk_begin;
-    a.nblk = blk_end - blk_begin;
-    a.H = desc->idx_heads;
-    a.D = desc->idx_dim;
-    a.eps = (double)desc->rms_eps;
-    a.theta = (double)desc->rope_theta;
+    const UpdateArgs a =
+        update_args(desc, cache, gamma, nullptr, nullptr, nullptr, 0, 0, blk_begin, blk_end);
     hipError_t e = launch_update(a, desc->idx_dtype == QSA_F16, stream);
     if (e != hipSuccess)
         return hip_fail(e, "cache_update");
@@ -429,25 +449,7 @@ qsa_status qsa_decode_step(const qsa_layer_desc *desc, const qsa_layer_cache *ca
 
     // 1. append + pool [b0, nb).  One new row (the usual decode step) is pooled
     //    by the score kernel's first workgroup; anything else runs on its own.
-    UpdateArgs u{};
-    u.idx_k = cache->idx_k;
-    u.summary = cache->summary;
-    u.k = cache->k;
-    u.v = cache->v;
-    u.new_idx_row = idx_k_row;
-    u.new_k_row = k_row;
-    u.new_v_row = v_row;
-    u.gamma = gamma;
-    u.idx_row_words = rowb / 4;
-    u.kv_row_words = desc->kv_heads * desc->head_dim / 2;
-    u.pos = pos;
-    u.n_new = 1;
-    u.b0 = b0;
-    u.nblk = nb - b0;
-    u.H = desc->idx_heads;
-    u.D = desc->idx_dim;
-    u.eps = (double)desc->rms_eps;
-    u.theta = (double)desc->rope_theta;
+    const UpdateArgs u = update_args(desc, cache, gamma, idx_k_row, k_row, v_row, pos, 1, b0, nb);
     const bool score = nb > 0 && (need_select || scores_out);
     const bool fuse = score && u.nblk <= 1;
     hipError_t e;
@@ -594,25 +596,8 @@ qsa_status qsa_decode_step_batch(const qsa_layer_desc *desc, int32_t n_seq,
         const int32_t b0 = states[i].n_valid_blocks < nb ? states[i].n_valid_blocks : nb;
         const bool need_select = nb > K;
 
-        UpdateArgs u{};
-        u.idx_k = c->idx_k;
-        u.summary = c->summary;
-        u.k = c->k;
-        u.v = c->v;
-        u.new_idx_row = x.idx_k_row;
-        u.new_k_row = x.k_row;
-        u.new_v_row = x.v_row;
-        u.gamma = gamma;
-        u.idx_row_words = rowb / 4;
-        u.kv_row_words = desc->kv_heads * desc->head_dim / 2;
-        u.pos = pos;
-        u.n_new = 1;
-        u.b0 = b0;
-        u.nblk = nb - b0;
-        u.H = desc->idx_heads;
-        u.D = desc->idx_dim;
-        u.eps = (double)desc->rms_eps;
-        u.theta = (double)desc->rope_theta;
+        const UpdateArgs u =
+            update_args(desc, c, gamma, x.idx_k_row, x.k_row, x.v_row, pos, 1, b0, nb);
         const bool fuse = u.nblk <= 1;
         if (!fuse) {   // a rebuild after invalidation: its own launch first
             e = launch_update(u, f16, stream);
@@ -702,25 +687,8 @@ qsa_status qsa_decode_step_multi(const qsa_layer_desc *desc, const qsa_layer_cac
 
     // 1. append the n_q rows, pool [b0, nb_last): inside the score kernel's
     //    first workgroup when at most one row is new, else in its own launch
-    UpdateArgs u{};
-    u.idx_k = cache->idx_k;
-    u.summary = cache->summary;
-    u.k = cache->k;
-    u.v = cache->v;
-    u.new_idx_row = idx_k_rows;
-    u.new_k_row = k_rows;
-    u.new_v_row = v_rows;
-    u.gamma = gamma;
-    u.idx_row_words = rowb / 4;
-    u.kv_row_words = desc->kv_heads * desc->head_dim / 2;
-    u.pos = n0;
-    u.n_new = n_q;
-    u.b0 = b0;
-    u.nblk = nb_last - b0;
-    u.H = desc->idx_heads;
-    u.D = desc->idx_dim;
-    u.eps = (double)desc->rms_eps;
-    u.theta = (double)desc->rope_theta;
+    const UpdateArgs u =
+        update_args(desc, cache, gamma, idx_k_rows, k_rows, v_rows, n0, n_q, b0, nb_last);
     const bool score = nb_last > 0 && (any_select || scores_out);
     const bool fuse = score && u.nblk <= 1;
     hipError_t e;
@@ -877,16 +845,8 @@ qsa_status qsa_chunk_step(const qsa_layer_desc *desc, const qsa_layer_cache *cac
         return hip_fail(e, "chunk_step/append");
     const int32_t b0 = st->n_valid_blocks < nb_last ? st->n_valid_blocks : nb_last;
     if (nb_last > b0) {
-        UpdateArgs u{};
-        u.idx_k = cache->idx_k;
-        u.summary = cache->summary;
-        u.gamma = gamma;
-        u.b0 = b0;
-        u.nblk = nb_last - b0;
-        u.H = desc->idx_heads;
-        u.D = desc->idx_dim;
-        u.eps = (double)desc->rms_eps;
-        u.theta = (double)desc->rope_theta;
+        const UpdateArgs u =
+            update_args(desc, cache, gamma, nullptr, nullptr, nullptr, 0, 0, b0, nb_last);
         e = launch_update(u, f16, stream);
         if (e != hipSuccess)
             return hip_fail(e, "chunk_step/pool");
