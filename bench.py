@@ -12,7 +12,9 @@ incremental pool, score of every cached block, top-k, gather + attention.
 Prints ONE JSON line.  `value` is QSA-layer decode steps per second.
 `roofline` is for the dominant kernel (the block-score stream), timed with HIP
 events around passes of back-to-back launches on the stream it runs on.  `cpu_baseline` times
-the CPU oracle on a bounded sample of the same workload (rank 0, N = 1 only).
+the CPU oracle on a bounded sample of the same workload (rank 0, N = 1 only);
+the other legs carry the oracle's time beside theirs (`cpu_oracle`), also on
+bounded samples.
 `multi_decode` (after the headline, outside its timed region): speculative
 verify, one call of 4 tokens per layer on the same 12 caches.
 `ablations` (after that): the page's comparisons timed on the same caches -- pooled-key cache
@@ -112,6 +114,61 @@ def cpu_baseline(w, n_steps):
             "sample": f"{n_steps} decode steps of layer 0 of {w.name} (n0={w.n0}), fp64 C oracle "
                       f"with OpenMP over blocks; cache build excluded; median step "
                       f"{1e3 * statistics.median(steps):.1f} ms"}
+
+
+def oracle_step_ms(w, n0, n_steps, seq=0):
+    """Median time (ms) of the CPU oracle's decode step on one layer of
+    workload w at n0 tokens (seeded rows of stream `seq`), over n_steps
+    steps; the oracle's cache build is not timed."""
+    import numpy as np
+    import oracle
+    from qsagen import workloads as W
+    cap = n0 + n_steps
+    dt = np.float16 if w.idx_f16 else np.float32
+    raw = np.zeros((cap,) + w.idx_row, dt)
+    K = np.zeros((cap,) + w.kv_row, np.float16)
+    V = np.zeros_like(K)
+    rows = np.arange(n0)
+    raw[:n0] = W.host_raw_rows(w, rows, 0, seq)
+    K[:n0], V[:n0] = W.host_kv_rows(w, rows, 0, seq)
+    L = oracle.OracleLayer(raw, K, V, W.host_gamma(w, 0), w.rms_eps, w.rope_theta, n0, w.k_blocks)
+    L.rebuild()
+    times = []
+    for s in range(n_steps):
+        pos = n0 + s
+        rr = W.host_raw_rows(w, [pos], 0, seq)[0]
+        kr, vr = (x[0] for x in W.host_kv_rows(w, [pos], 0, seq))
+        qi, wt, q = W.host_step_inputs(w, 0, s, seq)
+        t = time.perf_counter()
+        L.step(rr, kr, vr, qi, wt, q)
+        times.append(time.perf_counter() - t)
+    return 1e3 * statistics.median(times)
+
+
+def oracle_beside_legs(result, w256, cpu_step_ms):
+    """The CPU oracle beside the other legs, on bounded samples: a verify call
+    is n_q oracle decode steps; a batched step is one oracle step per
+    sequence (one step each, timed on that sequence's own context); a chunk
+    is n_q oracle steps, estimated from 4 steps at the chunk's context."""
+    from qsagen import workloads as W
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    md = result.get("multi_decode")
+    if md:
+        md["cpu_oracle"] = {"ms_per_call": round(md["n_q"] * cpu_step_ms, 1), "cores": threads,
+                            "sample": f"{md['n_q']} x the median oracle decode step at n0={w256.n0} "
+                                      f"({cpu_step_ms:.1f} ms, cpu_baseline's sample)"}
+    bc = result.get("batch_and_chunk")
+    if bc:
+        b = W.BATCH
+        per = [oracle_step_ms(b, n0, 1, seq=i) for i, n0 in enumerate(W.BATCH_CONTEXTS)]
+        bc["batch_decode"]["cpu_oracle"] = {
+            "ms_per_batched_step": round(sum(per), 1), "cores": threads,
+            "sample": "one oracle decode step per sequence, each at its own context"}
+        c = W.CHUNK128K
+        ms = oracle_step_ms(c, c.n0, 4)
+        bc["chunk"]["cpu_oracle"] = {
+            "ms_per_chunk": round(ms * c.steps, 1), "cores": threads,
+            "sample": f"{c.steps} x the median of 4 oracle decode steps at n0={c.n0} ({ms:.1f} ms)"}
 
 
 TRAFFIC_COPY_MB = 256
@@ -698,6 +755,8 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline ...")
         result["cpu_baseline"] = cpu_baseline(w0, args.cpu_steps)
+        step_ms = float(result["cpu_baseline"]["sample"].split("median step ")[1].split(" ms")[0])
+        oracle_beside_legs(result, w0, step_ms)
     print(json.dumps(result), flush=True)
 
 
