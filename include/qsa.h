@@ -158,7 +158,8 @@ qsa_status qsa_topk_blocks(const float *scores, int32_t n_blocks, int32_t k_bloc
  * Split-context flash-decode: partial softmax states go to the workspace and
  * are merged in a fixed order, so results are bitwise repeatable.
  * Errors: ARG if n_tokens < 1, n_tokens > capacity, n_sel_blocks outside
- * [0, min(top_k_tokens/4, floor(n_tokens/4))] or a pointer is null;
+ * [0, min(top_k_tokens/4, floor(n_tokens/4))], no cell to attend
+ * (n_sel_blocks = 0 and n_tokens a multiple of 4) or a pointer is null;
  * WORKSPACE as above. */
 qsa_status qsa_gather_attend(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
                              int32_t n_tokens, const int32_t *sel, int32_t n_sel_blocks,
@@ -349,8 +350,9 @@ qsa_status qsa_topk_cells(const float *block_scores, int32_t n_tokens, int32_t t
  * ascending, each < floor(n_tokens/4); q, out: DEVICE fp32 [Hq][Dh],
  * 16-byte aligned.  Workspace >= qsa_ablation_workspace_bytes.
  * Errors: ARG if n_tokens is outside [1, capacity], n_sel_blocks outside
- * [0, floor(n_tokens/4)], sel is null with n_sel_blocks > 0, or q / out is
- * null or misaligned; UNSUPPORTED / WORKSPACE as in qsa_gather_attend. */
+ * [0, floor(n_tokens/4)], no cell to attend (n_sel_blocks = 0 and n_tokens a
+ * multiple of 4), sel is null with n_sel_blocks > 0, or q / out is null or
+ * misaligned; UNSUPPORTED / WORKSPACE as in qsa_gather_attend. */
 qsa_status qsa_attend_masked(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
                              int32_t n_tokens, const int32_t *sel, int32_t n_sel_blocks,
                              const float *q, float *out, void *ws, size_t ws_bytes,

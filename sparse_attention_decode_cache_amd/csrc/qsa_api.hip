@@ -402,6 +402,8 @@ qsa_status qsa_gather_attend(const qsa_layer_desc *desc, const qsa_layer_cache *
         return fail(QSA_ERR_ARG, "n_sel_blocks %d outside [0, min(%d, %d)]", n_sel_blocks, K, nb);
     if (!sel && n_sel_blocks != nb)
         return fail(QSA_ERR_ARG, "sel may be NULL only when every block is kept");
+    if (n_sel_blocks == 0 && n_tokens % 4 == 0)
+        return fail(QSA_ERR_ARG, "no cell to attend (no block and no tail cell)");
     if (!q || !out)
         return fail(QSA_ERR_ARG, "q / out is NULL");
     const WsLayout L = decode_layout(desc, cache->capacity);
@@ -923,6 +925,8 @@ qsa_status qsa_attend_masked(const qsa_layer_desc *desc, const qsa_layer_cache *
         return fail(QSA_ERR_ARG, "n_tokens %d outside [1, %d]", n_tokens, cache->capacity);
     if (n_sel_blocks < 0 || n_sel_blocks > nb || (n_sel_blocks > 0 && !sel))
         return fail(QSA_ERR_ARG, "n_sel_blocks %d outside [0, %d] or sel NULL", n_sel_blocks, nb);
+    if (n_sel_blocks == 0 && n_tokens % 4 == 0)
+        return fail(QSA_ERR_ARG, "no cell to attend (no block and no tail cell)");
     if (!q || !out || !aligned(q, 16) || !aligned(out, 16))
         return fail(QSA_ERR_ARG, "q / out NULL or not 16-byte aligned");
     const size_t need = qsa_ablation_workspace_bytes(desc, cache->capacity);
