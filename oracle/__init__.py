@@ -26,7 +26,12 @@ Pins (checked by the CPU tests, none of them a re-typing of this code):
   attention       -- torch scaled_dot_product_attention in float64 when every
                      block is kept, one-cell / equal-rows / zero-query cases;
   watermark       -- incremental == full rebuild after every append, and
-                     after invalidate / truncate.
+                     after invalidate / truncate;
+  q8_0 quantise   -- power-of-two scales (every step exact: codes are the
+                     rounded quotients), a hand-checked tie block, a zero
+                     block, the half-scale error bound and the 127 ceiling;
+  q8_0 attention  -- equals attend() when every value is a binary16, and
+                     torch attention in float64 over the decoded values.
 No function here is "parity unpinned".
 """
 import ctypes
@@ -58,6 +63,8 @@ def lib():
         L.qsa_oracle_summary_row.argtypes = [P, i, i, i, l, P, d, d, P]
         L.qsa_oracle_rope.argtypes = [P, i, d, d, P]
         L.qsa_oracle_cache_update.argtypes = [P, P, i, i, i, l, l, P, d, d]
+        L.qsa_oracle_q8_0_quantize.argtypes = [P, l, P, P]
+        L.qsa_oracle_attend_q8_0.argtypes = [P, P, P, P, P, P, l, i, i, i, d, P]
         L.qsa_oracle_scores.argtypes = [P, i, l, i, i, P, P, P, P]
         L.qsa_oracle_topk.restype = l
         L.qsa_oracle_topk.argtypes = [P, l, l, P]
@@ -169,6 +176,43 @@ def attend(q, K, V, cell_ids, scale=None):
     out = np.empty((Hq, Dh), np.float64)
     lib().qsa_oracle_attend(_p(q), _p(K.view(np.uint16)), _p(V.view(np.uint16)), _p(c),
                             c.shape[0], Hq, Hkv, Dh, float(scale), _p(out))
+    return out
+
+
+def q8_0_quantize(x):
+    """q8_0 of a float16 array whose last axis is a multiple of 32: returns
+    (codes int8, same shape; scales as binary16 bits, last axis / 32)."""
+    x = np.ascontiguousarray(x, dtype=np.float16)
+    assert x.shape[-1] % 32 == 0
+    nblk = x.size // 32
+    codes = np.empty(x.shape, np.int8)
+    d = np.empty(x.shape[:-1] + (x.shape[-1] // 32,), np.uint16)
+    lib().qsa_oracle_q8_0_quantize(_p(x.view(np.uint16)), nblk, _p(codes), _p(d))
+    return codes, d
+
+
+def q8_0_values(codes, d):
+    """code * scale in float64 (exact), same shape as codes."""
+    c = np.asarray(codes, np.float64)
+    s = np.asarray(d, np.uint16).view(np.float16).astype(np.float64)
+    return c * np.repeat(s, 32, axis=-1)
+
+
+def attend_q8_0(q, Kc, Kd, Vc, Vd, cell_ids, scale=None):
+    """attend() over a q8_0 cache: Kc, Vc [tokens, Hkv, Dh] int8 codes;
+    Kd, Vd [tokens, Hkv, Dh/32] binary16 scale bits.  Returns [Hq, Dh] float64."""
+    q = _c(q, np.float32)
+    Hq, Dh = q.shape
+    Kc, Vc = _c(Kc, np.int8), _c(Vc, np.int8)
+    Kd, Vd = _c(Kd, np.uint16), _c(Vd, np.uint16)
+    Hkv = Kc.shape[1]
+    assert Dh % 32 == 0 and Kd.shape[-1] == Dh // 32 and Vd.shape == Kd.shape
+    c = _c(cell_ids, np.int32)
+    if scale is None:
+        scale = 1.0 / np.sqrt(Dh)
+    out = np.empty((Hq, Dh), np.float64)
+    lib().qsa_oracle_attend_q8_0(_p(q), _p(Kc), _p(Kd), _p(Vc), _p(Vd), _p(c), c.shape[0],
+                                 Hq, Hkv, Dh, float(scale), _p(out))
     return out
 
 

@@ -307,6 +307,79 @@ void qsa_oracle_attend(const float *q, const uint16_t *K, const uint16_t *V,
     free(lg);
 }
 
+/* ---- q8_0 K/V: 8-bit codes, one binary16 scale per 32 values --------------
+ * The tuning post (the one on runtime parameters, section "KV cacheをQ8_0に
+ * してみる") runs llama.cpp with its q8_0 K/V cache type and gives no format;
+ * q8_0 is llama.cpp's published one: 32 consecutive values share a scale.
+ * Reading, in the format's own precision (binary32 decisions):
+ *   amax = max_j |x_j|;  s = amax / 127;  inv = (s != 0) ? 1 / s : 0;
+ *   code_j = round(x_j * inv), halves away from zero (|code_j| <= 127);
+ *   the scale is stored as s rounded to nearest-even binary16 (d16), and
+ *   value j is code_j * d16.
+ * x: n_blocks * 32 binary16 values; codes: as many int8; d: n_blocks scales.
+ */
+void qsa_oracle_q8_0_quantize(const uint16_t *x, long n_blocks, int8_t *codes, uint16_t *d)
+{
+    for (long b = 0; b < n_blocks; ++b) {
+        float v[32];
+        float amax = 0.0f;
+        for (int j = 0; j < 32; ++j) {
+            v[j] = (float)qsa_oracle_half_to_double(x[b * 32 + j]);
+            if (fabsf(v[j]) > amax)
+                amax = fabsf(v[j]);
+        }
+        const float s = amax / 127.0f;
+        const float inv = s != 0.0f ? 1.0f / s : 0.0f;
+        for (int j = 0; j < 32; ++j) {
+            const float t = v[j] * inv;
+            codes[b * 32 + j] = (int8_t)roundf(t);
+        }
+        d[b] = qsa_oracle_double_to_half((double)s);
+    }
+}
+
+/* Value i of a q8_0 tensor (blocks of 32 consecutive values). */
+static double q8_value(const int8_t *codes, const uint16_t *d, size_t i)
+{
+    return (double)codes[i] * qsa_oracle_half_to_double(d[i / 32]);
+}
+
+/* O8 over a q8_0 K/V cache: the same attention as qsa_oracle_attend, with
+ * every K and V element read as code * scale.  Kc/Vc: [tokens][Hkv][Dh]
+ * codes; Kd/Vd: [tokens][Hkv][Dh/32] scales (Dh a multiple of 32). */
+void qsa_oracle_attend_q8_0(const float *q, const int8_t *Kc, const uint16_t *Kd,
+                            const int8_t *Vc, const uint16_t *Vd, const int32_t *cells, long nc,
+                            int Hq, int Hkv, int Dh, double scale, double *out)
+{
+    double *lg = (double *)malloc(sizeof(double) * (size_t)(nc > 0 ? nc : 1));
+    const size_t row = (size_t)Hkv * Dh;
+    for (int h = 0; h < Hq; ++h) {
+        const int g = (int)(((long)h * Hkv) / Hq);
+        double mx = -INFINITY;
+        for (long c = 0; c < nc; ++c) {
+            const size_t base = (size_t)cells[c] * row + (size_t)g * Dh;
+            double dot = 0.0;
+            for (int e = 0; e < Dh; ++e)
+                dot += (double)q[(size_t)h * Dh + e] * q8_value(Kc, Kd, base + e);
+            lg[c] = scale * dot;
+            if (lg[c] > mx)
+                mx = lg[c];
+        }
+        double z = 0.0;
+        for (long c = 0; c < nc; ++c) {
+            lg[c] = exp(lg[c] - mx);
+            z += lg[c];
+        }
+        for (int e = 0; e < Dh; ++e) {
+            double acc = 0.0;
+            for (long c = 0; c < nc; ++c)
+                acc += lg[c] * q8_value(Vc, Vd, (size_t)cells[c] * row + (size_t)g * Dh + e);
+            out[(size_t)h * Dh + e] = acc / z;
+        }
+    }
+    free(lg);
+}
+
 /* ---- A whole decode step (O1..O9 in order) ----------------------------------
  * The caller has already written the new token's raw key and K/V rows at
  * position n-1.  Rows [valid, n/4) of the summary cache are rebuilt, then
