@@ -397,6 +397,75 @@ def bench_ablations(args, torch, qsa, w, desc, layers, ws, stream, dev, decode_u
     return res
 
 
+def bench_q8(args, torch, qsa, w, desc, layers, ws, stream, dev):
+    """q8_0 K/V (the 8-bit cache type of the runtime-tuning post) on the
+    headline caches: every layer's K and V quantised (qsa_q8_0_quantize over
+    the n0 rows), then the gathered attention over the q8_0 planes against the
+    f16 one with the same ids (12 layers round-robin, HIP events on the
+    library's stream)."""
+    n0 = w.n0
+    nb = n0 // 4
+    K = w.k_blocks
+    Hkv, Dh = w.kv_heads, w.head_dim
+    cap = layers[0]["buf"].capacity
+    scores = torch.empty(nb, dtype=torch.float32, device=dev)
+    sels = [torch.empty(K, dtype=torch.int32, device=dev) for _ in layers]
+    for L in layers:
+        qsa.qsa_state_truncate(L["state"], n0)
+    for i, L in enumerate(layers):
+        inp = L["inp"]
+        qsa.qsa_index_score(desc, L["buf"].cache, nb, inp.q_idx[0], inp.w[0], scores, stream)
+        qsa.qsa_topk_blocks(scores, nb, K, sels[i], ws, stream)
+    planes = [[(torch.empty((cap, Hkv, Dh), dtype=torch.int8, device=dev),
+                torch.empty((cap, Hkv, Dh // 32), dtype=torch.int16, device=dev)) for _ in range(2)]
+              for _ in layers]
+    out = torch.empty((w.q_heads, Dh), dtype=torch.float32, device=dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def quantize_all():
+        for L, pl in zip(layers, planes):
+            for X, (c, s) in zip((L["buf"].k, L["buf"].v), pl):
+                qsa.qsa_q8_0_quantize(X, c, s, n_values=n0 * Hkv * Dh, stream=stream)
+
+    quantize_all()
+    a.record(stream)
+    quantize_all()
+    b.record(stream)
+    torch.cuda.synchronize()
+    quant_us = 1e3 * a.elapsed_time(b) / len(layers)
+    kvs = [qsa.kv_q8_0(pl[0][0], pl[0][1], pl[1][0], pl[1][1]) for pl in planes]
+
+    def timed(fn, reps):
+        for i, L in enumerate(layers):
+            fn(i, L)
+        a.record(stream)
+        for _ in range(reps):
+            for i, L in enumerate(layers):
+                fn(i, L)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return 1e3 * a.elapsed_time(b) / (reps * len(layers))
+
+    def f16(i, L):
+        qsa.qsa_gather_attend(desc, L["buf"].cache, n0, sels[i], K, L["inp"].q[0], out, ws, stream)
+
+    def q8(i, L):
+        qsa.qsa_gather_attend_q8_0(desc, kvs[i], n0, sels[i], K, L["inp"].q[0], out, ws, stream)
+
+    r = args.ablation_reps
+    n_cells = 4 * K + n0 % 4
+    res = {"workload": f"{w.name} (n0={n0}, {len(layers)} layers round-robin, {n_cells} cells)",
+           "quantize_us_per_layer": round(quant_us, 2),
+           "gather_attend_f16_us": round(timed(f16, r), 2),
+           "gather_attend_q8_0_us": round(timed(q8, r), 2),
+           "gathered_bytes_f16": n_cells * Hkv * Dh * 2 * 2,
+           "gathered_bytes_q8_0": n_cells * Hkv * (Dh + Dh // 16) * 2}
+    q_bytes = 2 * n0 * Hkv * (2 * Dh + Dh + Dh // 16)      # K and V: f16 in, codes + scales out
+    res["quantize_gbs"] = round(q_bytes / (quant_us / 1e6) / 1e9, 1)
+    log(f"q8_0: {res}")
+    return res
+
+
 def bench_batch_and_chunk(args, torch, qsa, W, stream, dev):
     """Batched decode of 8 mixed-context sequences, and one 1024-token prefill
     chunk at 128k, on the headline layer shapes."""
@@ -599,6 +668,7 @@ def main():
     ap.add_argument("--sweep-steps", type=int, default=16, help="decode steps per context of the sweep")
     ap.add_argument("--no-sweep", action="store_true", help="skip the 64k / 128k context sweep")
     ap.add_argument("--no-ablations", action="store_true", help="skip the ablation leg")
+    ap.add_argument("--no-q8", action="store_true", help="skip the q8_0 K/V leg")
     ap.add_argument("--batch-only", action="store_true", help="only the batched-decode / chunk leg")
     ap.add_argument("--traffic-run", action="store_true",
                     help="only launch the score kernel and a plain copy (for rocprofv3 --pmc)")
@@ -746,6 +816,8 @@ def main():
     if not args.no_ablations:
         result["ablations"] = bench_ablations(args, torch, qsa, w, desc, layers, ws, stream, dev,
                                               result["layer_step_us"]["median"])
+    if not args.no_q8:
+        result["q8_0_kv"] = bench_q8(args, torch, qsa, w, desc, layers, ws, stream, dev)
     del layers, ws                      # the 256k caches: the legs below allocate their own
     torch.cuda.empty_cache()
     if not args.no_sweep:

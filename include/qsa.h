@@ -358,6 +358,55 @@ qsa_status qsa_attend_masked(const qsa_layer_desc *desc, const qsa_layer_cache *
                              const float *q, float *out, void *ws, size_t ws_bytes,
                              hipStream_t stream);
 
+/* ------------------------------------------------------------ q8_0 K/V
+ * The 8-bit K/V cache type the runtime-tuning post tried (section "KV
+ * cacheをQ8_0にしてみる": llama.cpp's q8_0; the post saw no speed gain on its
+ * APU and names no layout).  q8_0 is llama.cpp's published format: each 32
+ * consecutive values of a row share one binary16 scale d = amax / 127 and
+ * are stored as int8 codes round(x / d), halves away from zero; value =
+ * code * d.  Here the codes and the scales live in two planes (the values
+ * are those of the format; only the layout differs from llama.cpp's
+ * interleaved 34-byte blocks, so that code loads stay aligned):
+ *   codes  [capacity][Hkv][Dh] int8, row t = position t;
+ *   scales [capacity][Hkv][Dh/32] binary16 bits.
+ * The library quantises (qsa_q8_0_quantize) and attends
+ * (qsa_gather_attend_q8_0); the caller owns the planes.  Scoring, top-k and
+ * the pooled-key cache are unchanged (they never read K/V). */
+typedef struct {
+    const int8_t *k_codes;     /* DEVICE [capacity][Hkv][Dh], 16-byte aligned */
+    const uint16_t *k_scales;  /* DEVICE [capacity][Hkv][Dh/32] binary16, 16-byte aligned */
+    const int8_t *v_codes;
+    const uint16_t *v_scales;
+    int32_t capacity;          /* tokens; a positive multiple of 4, <= 2^21 */
+} qsa_kv_q8_0;
+
+/* q8_0 of n_values binary16 values (n_values a multiple of 32; blocks of 32
+ * consecutive values).  The decisions are taken in binary32 (correctly
+ * rounded amax / 127, its reciprocal and the product), the scale stored
+ * rounded to nearest-even binary16.  To quantise cache rows [t0, t1) pass
+ * x = the f16 rows, codes = k_codes + t0 * Hkv * Dh, scales = k_scales +
+ * t0 * Hkv * Dh / 32 and n_values = (t1 - t0) * Hkv * Dh.  x: DEVICE, 16-byte
+ * aligned; codes: DEVICE, 16-byte aligned; scales: DEVICE, 2-byte aligned.
+ * Inputs must be finite.  n_values = 0 enqueues nothing.
+ * Errors: ARG if n_values < 0 or not a multiple of 32, or a pointer is null
+ * or misaligned. */
+qsa_status qsa_q8_0_quantize(const uint16_t *x, int64_t n_values, int8_t *codes, uint16_t *scales,
+                             hipStream_t stream);
+
+/* Stage 4 over a q8_0 K/V cache: the attention of qsa_gather_attend
+ * [post 10, "selected QSA K/V gather（COMMON-005）"] with every K and V
+ * element read as code * scale: the same cells (sel blocks + tail), softmax
+ * over scale * <q_h, K_c>, weighted sum of V.  Reads n_sel * Hkv * (Dh + Dh/16)
+ * bytes per K and per V, about half of the f16 gather.  Arguments as in
+ * qsa_gather_attend, with kv in place of the cache; q and out 16-byte
+ * aligned; workspace >= qsa_workspace_bytes(desc, kv->capacity).
+ * Errors: ARG as in qsa_gather_attend (and a null or misaligned kv pointer,
+ * q or out); UNSUPPORTED / WORKSPACE as there. */
+qsa_status qsa_gather_attend_q8_0(const qsa_layer_desc *desc, const qsa_kv_q8_0 *kv,
+                                  int32_t n_tokens, const int32_t *sel, int32_t n_sel_blocks,
+                                  const float *q, float *out, void *ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
 /* Static text for a status code. */
 const char *qsa_status_string(qsa_status s);
 

@@ -24,10 +24,10 @@ namespace {
 using namespace att;
 
 // Split `split` of KV head g with the partial written to the workspace.
-template <int DH, int G>
-__device__ void attend_split(const AttendArgs &a, AttLds<DH, G> &L, int split, int g)
+template <int DH, int G, bool Q8 = false>
+__device__ void attend_split(const AttendArgs &a, AttLds<DH, G> &L, int split, int g, Q8Scales q8 = {})
 {
-    attend_tile<DH, G>(a, L, L.blk, split * kCells, g, [&](AttLds<DH, G> &T) {
+    attend_tile<DH, G, Q8>(a, L, L.blk, split * kCells, g, [&](AttLds<DH, G> &T) {
         float *part = a.part + ((size_t)g * a.n_split + split) * (size_t)part_stride(G, DH);
         for (int i = threadIdx.x; i < G * DH; i += kAT)
             part[2 * G + i] = tile_acc<DH, G>(T, i);
@@ -35,7 +35,7 @@ __device__ void attend_split(const AttendArgs &a, AttLds<DH, G> &L, int split, i
             part[threadIdx.x] = T.m[threadIdx.x];
             part[G + threadIdx.x] = T.l[threadIdx.x];
         }
-    });
+    }, q8);
 }
 
 template <int DH, int G>
@@ -50,6 +50,20 @@ __global__ __launch_bounds__(kAT) void k_attend(AttendArgs a)
     }
     __syncthreads();
     attend_split<DH, G>(a, L, split, blockIdx.y);
+}
+
+// The same splits over a q8_0 K/V cache (codes in a.k / a.v, scales in q8).
+template <int DH, int G>
+__global__ __launch_bounds__(kAT) void k_attend_q8(AttendArgs a, Q8Scales q8)
+{
+    __shared__ AttLds<DH, G> L;
+    const int split = blockIdx.x;
+    if (threadIdx.x < kCells / 4) {
+        const int i = split * (kCells / 4) + threadIdx.x;
+        L.blk[threadIdx.x] = !a.sel ? i : (i < a.n_sel_blocks ? a.sel[i] : -1);
+    }
+    __syncthreads();
+    attend_split<DH, G, true>(a, L, split, blockIdx.y, q8);
 }
 
 // Stages 3 and 4 in one kernel: every attention workgroup runs the top-k
@@ -388,6 +402,50 @@ hipError_t launch_merge_batch(const AttendBatchArgs &b, int Dh, int G, hipStream
     }
 #undef QSA_MERGE_G
     return hipGetLastError();
+}
+
+hipError_t launch_attend_q8(const AttendArgs &a, const uint16_t *k_scales, const uint16_t *v_scales,
+                            int Dh, int G, hipStream_t s)
+{
+    // the merge folds no tail of its own here: it would read the rows as f16
+    if (a.n_tail != 0 || a.n_split < 1 || a.n_split > kMaxSplits)
+        return hipErrorInvalidValue;
+    const Q8Scales q8{k_scales, v_scales};
+    const dim3 grid((unsigned)a.n_split, (unsigned)a.kv_heads);
+#define QSA_Q8_G(DHV)                                                                             \
+    switch (G) {                                                                                  \
+    case 1: hipLaunchKernelGGL((k_attend_q8<DHV, 1>), grid, dim3(kAT), 0, s, a, q8); break;       \
+    case 2: hipLaunchKernelGGL((k_attend_q8<DHV, 2>), grid, dim3(kAT), 0, s, a, q8); break;       \
+    case 4: hipLaunchKernelGGL((k_attend_q8<DHV, 4>), grid, dim3(kAT), 0, s, a, q8); break;       \
+    case 8: hipLaunchKernelGGL((k_attend_q8<DHV, 8>), grid, dim3(kAT), 0, s, a, q8); break;       \
+    default: return hipErrorInvalidValue;                                                         \
+    }                                                                                             \
+    break;
+    switch (Dh) {
+    case 64: QSA_Q8_G(64)
+    case 128: QSA_Q8_G(128)
+    case 256: QSA_Q8_G(256)
+    default: return hipErrorInvalidValue;
+    }
+#undef QSA_Q8_G
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    switch (Dh * 16 + G) {
+    case 64 * 16 + 1: return merge<64, 1>(a, s);
+    case 64 * 16 + 2: return merge<64, 2>(a, s);
+    case 64 * 16 + 4: return merge<64, 4>(a, s);
+    case 64 * 16 + 8: return merge<64, 8>(a, s);
+    case 128 * 16 + 1: return merge<128, 1>(a, s);
+    case 128 * 16 + 2: return merge<128, 2>(a, s);
+    case 128 * 16 + 4: return merge<128, 4>(a, s);
+    case 128 * 16 + 8: return merge<128, 8>(a, s);
+    case 256 * 16 + 1: return merge<256, 1>(a, s);
+    case 256 * 16 + 2: return merge<256, 2>(a, s);
+    case 256 * 16 + 4: return merge<256, 4>(a, s);
+    case 256 * 16 + 8: return merge<256, 8>(a, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_select_attend(const AttendArgs &a, const SelectArgs &sa, int Dh, int G,

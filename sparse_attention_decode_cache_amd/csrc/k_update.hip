@@ -49,7 +49,54 @@ __global__ void k_tail_cells(int32_t *cells, int32_t at, int32_t nb, int32_t tai
         cells[at + threadIdx.x] = 4 * nb + (int)threadIdx.x;
 }
 
+// q8_0 (the 8-bit K/V cache type of the runtime-tuning post, section "KV
+// cacheをQ8_0にしてみる"; llama.cpp's format): 32 values share the binary16
+// scale amax / 127 and are stored as round(x * 127 / amax) in int8, halves
+// away from zero.  The decisions are taken in binary32 with correctly
+// rounded division and product (the format's own precision).  One thread per
+// 32-value block: 64 B in, 32 B of codes and 2 B of scale out.
+__global__ __launch_bounds__(256) void k_q8_0_quantize(const uint16_t *x, int64_t n_blocks,
+                                                       int8_t *codes, uint16_t *scales)
+{
+    for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < n_blocks;
+         b += (int64_t)gridDim.x * 256) {
+        const uint4 *src = (const uint4 *)(x + b * 32);
+        uint4 w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = src[i];
+        _Float16 h[32];
+        __builtin_memcpy(h, w, 64);
+        float amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 32; ++j)
+            amax = fmaxf(amax, fabsf((float)h[j]));
+        const float sc = __fdiv_rn(amax, 127.0f);
+        const float inv = sc != 0.0f ? __fdiv_rn(1.0f, sc) : 0.0f;
+        int8_t c[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j)
+            c[j] = (int8_t)roundf(__fmul_rn((float)h[j], inv));
+        uint4 o[2];
+        __builtin_memcpy(o, c, 32);
+        uint4 *dst = (uint4 *)(codes + b * 32);
+        dst[0] = o[0];
+        dst[1] = o[1];
+        scales[b] = __builtin_bit_cast(uint16_t, (_Float16)sc);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_q8_0_quantize(const uint16_t *x, int64_t n_blocks, int8_t *codes, uint16_t *scales,
+                                hipStream_t s)
+{
+    int64_t grid = (n_blocks + 255) / 256;
+    grid = grid < 1 ? 1 : (grid > 16384 ? 16384 : grid);
+    hipLaunchKernelGGL(k_q8_0_quantize, dim3((unsigned)grid), dim3(256), 0, s, x, n_blocks, codes,
+                       scales);
+    return hipGetLastError();
+}
 
 hipError_t launch_expand_cells(const float *scores, int32_t nb, float *cells, hipStream_t s)
 {

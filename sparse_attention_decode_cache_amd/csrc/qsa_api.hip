@@ -948,6 +948,69 @@ qsa_status qsa_attend_masked(const qsa_layer_desc *desc, const qsa_layer_cache *
     return e == hipSuccess ? ok() : hip_fail(e, "attend_masked");
 }
 
+qsa_status qsa_q8_0_quantize(const uint16_t *x, int64_t n_values, int8_t *codes, uint16_t *scales,
+                             hipStream_t stream)
+{
+    if (n_values < 0 || n_values % 32 != 0)
+        return fail(QSA_ERR_ARG, "n_values %lld is not a non-negative multiple of 32",
+                    (long long)n_values);
+    if (n_values == 0)
+        return ok();
+    if (!x || !codes || !scales || !aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2))
+        return fail(QSA_ERR_ARG, "x / codes / scales NULL or misaligned");
+    hipError_t e = launch_q8_0_quantize(x, n_values / 32, codes, scales, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "q8_0 quantize");
+    return ok();
+}
+
+qsa_status qsa_gather_attend_q8_0(const qsa_layer_desc *desc, const qsa_kv_q8_0 *kv,
+                                  int32_t n_tokens, const int32_t *sel, int32_t n_sel_blocks,
+                                  const float *q, float *out, void *ws, size_t ws_bytes,
+                                  hipStream_t stream)
+{
+    qsa_status s;
+    if ((s = check_desc(desc)) != QSA_OK)
+        return s;
+    if (!kv)
+        return fail(QSA_ERR_ARG, "kv is NULL");
+    if (kv->capacity < 4 || kv->capacity % 4 != 0 || kv->capacity > (1 << 21))
+        return fail(QSA_ERR_ARG, "capacity must be a positive multiple of 4, <= 2^21 (got %d)",
+                    kv->capacity);
+    if (!kv->k_codes || !kv->v_codes || !kv->k_scales || !kv->v_scales ||
+        !aligned(kv->k_codes, 16) || !aligned(kv->v_codes, 16) || !aligned(kv->k_scales, 16) ||
+        !aligned(kv->v_scales, 16))
+        return fail(QSA_ERR_ARG, "kv pointer NULL or not 16-byte aligned");
+    const int32_t nb = n_tokens / 4;
+    const int32_t K = desc->top_k_tokens / 4;
+    if (n_tokens < 1 || n_tokens > kv->capacity)
+        return fail(QSA_ERR_ARG, "n_tokens %d outside [1, %d]", n_tokens, kv->capacity);
+    if (n_sel_blocks < 0 || n_sel_blocks > nb || n_sel_blocks > K)
+        return fail(QSA_ERR_ARG, "n_sel_blocks %d outside [0, min(%d, %d)]", n_sel_blocks, K, nb);
+    if (!sel && n_sel_blocks != nb)
+        return fail(QSA_ERR_ARG, "sel may be NULL only when every block is kept");
+    if (n_sel_blocks == 0 && n_tokens % 4 == 0)
+        return fail(QSA_ERR_ARG, "no cell to attend (no block and no tail cell)");
+    if (!q || !out || !aligned(q, 16) || !aligned(out, 16))
+        return fail(QSA_ERR_ARG, "q / out NULL or not 16-byte aligned");
+    const WsLayout L = decode_layout(desc, kv->capacity);
+    if ((s = check_ws(ws, ws_bytes, L.total)) != QSA_OK)
+        return s;
+    // the q8_0 planes stand in for the f16 rows; every other argument as in
+    // the f16 gather (the splits hold the tail cells, n_tail = 0)
+    qsa_layer_cache c{};
+    c.k = (uint16_t *)kv->k_codes;
+    c.v = (uint16_t *)kv->v_codes;
+    c.capacity = kv->capacity;
+    const AttendArgs a = attend_args(desc, &c, n_tokens, sel, n_sel_blocks, q, out,
+                                     (float *)((char *)ws + L.part));
+    hipError_t e = launch_attend_q8(a, kv->k_scales, kv->v_scales, desc->head_dim,
+                                    desc->q_heads / desc->kv_heads, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "q8_0 attend");
+    return ok();
+}
+
 const char *qsa_status_string(qsa_status s)
 {
     switch (s) {

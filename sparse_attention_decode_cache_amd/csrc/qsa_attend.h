@@ -51,14 +51,25 @@ struct AttLds {
     int32_t blk[kCells / 4];
 };
 
+// Scales of a q8_0 K/V cache ([rows][kv_heads][DH/32] binary16); a.k and a.v
+// then point at the int8 codes ([rows][kv_heads][DH]).
+struct Q8Scales {
+    const uint16_t *k = nullptr, *v = nullptr;
+};
+
 // Attention of the 16 cells e0 .. e0+15 of KV head g; blk[0..4) holds their
 // 4 block ids (read only for cells inside the chosen blocks) and is visible to
 // all threads.  The tile's (m[G], l[G], acc[G][DH]) end in L.m, L.l and the
 // L.acc groups; sink(L) consumes them after the last barrier (every thread
 // calls it).  Whole workgroup calls.
-template <int DH, int G, class Sink>
+//
+// Q8: K and V are q8_0 rows (code * scale, one scale per 32 values).  An MFMA
+// k-step spans 32 dims, one q8_0 block: the codes (exact in f16) meet q on
+// the matrix cores and each k-step's partial logit is multiplied by its
+// cell's scale in fp32; the PV lanes decode their 8 values in fp32.
+template <int DH, int G, bool Q8 = false, class Sink>
 __device__ void attend_tile(const AttendArgs &a, AttLds<DH, G> &L, const int32_t *blk, int e0, int g,
-                            Sink sink)
+                            Sink sink, Q8Scales q8 = {})
 {
     using S = AttShape<DH, G>;
     const int t = threadIdx.x;
@@ -83,6 +94,7 @@ __device__ void attend_tile(const AttendArgs &a, AttLds<DH, G> &L, const int32_t
     const int tv = t - kPV0;
     const int v_chunk = tv % S::CH, v_head = (tv / S::CH) % G, v_grp = tv / (S::CH * G);
     uint4 vr[S::CPG];
+    [[maybe_unused]] float vs[S::CPG];      // Q8: the V scales of the lane's cells
 
     if (wave == 0) {
         // ---- logits on the matrix cores: D[cell][head] = K[cell][:] . q[head][:]
@@ -93,11 +105,23 @@ __device__ void attend_tile(const AttendArgs &a, AttLds<DH, G> &L, const int32_t
         const int mc = lane & 15, kg = lane >> 4;
         bool valid;
         const size_t row = cell_row(mc, valid);
-        const uint4 *kp = (const uint4 *)(a.k + (row * a.kv_heads + g) * DH) + kg;
         uint4 kr[S::KS];
+        [[maybe_unused]] float ks[S::KS];   // Q8: row mc's scale of k-step i
+        if constexpr (Q8) {
+            const int8_t *kp = (const int8_t *)a.k + (row * a.kv_heads + g) * DH + 8 * kg;
+            const uint16_t *sp = q8.k + (row * a.kv_heads + g) * (DH / 32);
 #pragma unroll
-        for (int i = 0; i < S::KS; ++i)
-            kr[i] = kp[4 * i];
+            for (int i = 0; i < S::KS; ++i) {
+                const uint2 w = *(const uint2 *)(kp + 32 * i);
+                kr[i] = make_uint4(w.x, w.y, 0u, 0u);
+                ks[i] = (float)__builtin_bit_cast(_Float16, sp[i]);
+            }
+        } else {
+            const uint4 *kp = (const uint4 *)(a.k + (row * a.kv_heads + g) * DH) + kg;
+#pragma unroll
+            for (int i = 0; i < S::KS; ++i)
+                kr[i] = kp[4 * i];
+        }
         const bool hq = mc < G;
         const float4 *qp = (const float4 *)(a.q + ((size_t)g * G + (hq ? mc : 0)) * DH) + 2 * kg;
         float4v d = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -112,9 +136,24 @@ __device__ void attend_tile(const AttendArgs &a, AttLds<DH, G> &L, const int32_t
                 hi[j] = (_Float16)q;
                 lo[j] = (_Float16)(q - (float)hi[j]);
             }
-            __builtin_memcpy(&kh, &kr[i], 16);
-            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, hi, d, 0, 0, 0);
-            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, lo, d, 0, 0, 0);
+            if constexpr (Q8) {
+                // D[4kg + j][mc] += scale(cell 4kg + j, k-step i) * (codes . q)
+                int8_t c8[8];
+                __builtin_memcpy(c8, &kr[i], 8);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    kh[j] = (_Float16)c8[j];
+                float4v p = {0.0f, 0.0f, 0.0f, 0.0f};
+                p = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, hi, p, 0, 0, 0);
+                p = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, lo, p, 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    d[j] = fmaf(__shfl(ks[i], 4 * kg + j), p[j], d[j]);
+            } else {
+                __builtin_memcpy(&kh, &kr[i], 16);
+                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, hi, d, 0, 0, 0);
+                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, lo, d, 0, 0, 0);
+            }
         }
         if (hq) {
 #pragma unroll
@@ -130,7 +169,14 @@ __device__ void attend_tile(const AttendArgs &a, AttLds<DH, G> &L, const int32_t
         for (int i = 0; i < S::CPG; ++i) {
             bool valid;
             const size_t row = cell_row(v_grp + S::SV * i, valid);
-            vr[i] = *(const uint4 *)(a.v + (row * a.kv_heads + g) * DH + v_chunk * 8);
+            if constexpr (Q8) {
+                const size_t rb = row * a.kv_heads + g;
+                const uint2 w = *(const uint2 *)((const int8_t *)a.v + rb * DH + v_chunk * 8);
+                vr[i] = make_uint4(w.x, w.y, 0u, 0u);
+                vs[i] = (float)__builtin_bit_cast(_Float16, q8.v[rb * (DH / 32) + v_chunk / 4]);
+            } else {
+                vr[i] = *(const uint4 *)(a.v + (row * a.kv_heads + g) * DH + v_chunk * 8);
+            }
         }
     }
     __syncthreads();
@@ -159,11 +205,19 @@ __device__ void attend_tile(const AttendArgs &a, AttLds<DH, G> &L, const int32_t
 #pragma unroll
         for (int i = 0; i < S::CPG; ++i) {
             const float p = L.lg[v_grp + S::SV * i][v_head];
-            half8 vh;
-            __builtin_memcpy(&vh, &vr[i], 16);
+            if constexpr (Q8) {
+                int8_t c8[8];
+                __builtin_memcpy(c8, &vr[i], 8);
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                acc[j] = fmaf(p, (float)vh[j], acc[j]);
+                for (int j = 0; j < 8; ++j)
+                    acc[j] = fmaf(p, (float)c8[j] * vs[i], acc[j]);
+            } else {
+                half8 vh;
+                __builtin_memcpy(&vh, &vr[i], 16);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    acc[j] = fmaf(p, (float)vh[j], acc[j]);
+            }
         }
         float4 *dst = (float4 *)&L.acc[v_grp][v_head * DH + v_chunk * 8];
         dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);

@@ -24,7 +24,8 @@ EXPORTS = ("qsa_workspace_bytes", "qsa_state_invalidate", "qsa_state_truncate",
            "qsa_decode_step", "qsa_batch_workspace_bytes", "qsa_decode_step_batch",
            "qsa_chunk_workspace_bytes", "qsa_chunk_step", "qsa_multi_workspace_bytes",
            "qsa_decode_step_multi", "qsa_ablation_workspace_bytes", "qsa_topk_cells",
-           "qsa_attend_masked", "qsa_status_string", "qsa_last_error")
+           "qsa_attend_masked", "qsa_q8_0_quantize", "qsa_gather_attend_q8_0",
+           "qsa_status_string", "qsa_last_error")
 QSA_MAX_BATCH = 8
 QSA_MAX_CHUNK = 4096
 QSA_MAX_MULTI = 4
@@ -48,6 +49,12 @@ class qsa_layer_desc(ctypes.Structure):
 class qsa_layer_cache(ctypes.Structure):
     _fields_ = [("idx_k", ctypes.c_void_p), ("summary", ctypes.c_void_p),
                 ("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("capacity", ctypes.c_int32)]
+
+
+class qsa_kv_q8_0(ctypes.Structure):
+    _fields_ = [("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
+                ("v_codes", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
+                ("capacity", ctypes.c_int32)]
 
 
 class qsa_seq_state(ctypes.Structure):
@@ -96,9 +103,12 @@ def lib():
         L.qsa_ablation_workspace_bytes.argtypes = [D, i32]
         L.qsa_topk_cells.argtypes = [P, i32, i32, P, P, sz, P]
         L.qsa_attend_masked.argtypes = [D, C, i32, P, i32, P, P, P, sz, P]
+        L.qsa_q8_0_quantize.argtypes = [P, ctypes.c_int64, P, P, P]
+        L.qsa_gather_attend_q8_0.argtypes = [D, ctypes.POINTER(qsa_kv_q8_0), i32, P, i32, P, P, P, sz, P]
         for f in ("qsa_cache_update", "qsa_index_score", "qsa_topk_blocks", "qsa_gather_attend",
                   "qsa_decode_step", "qsa_decode_step_batch", "qsa_chunk_step",
-                  "qsa_decode_step_multi", "qsa_topk_cells", "qsa_attend_masked"):
+                  "qsa_decode_step_multi", "qsa_topk_cells", "qsa_attend_masked",
+                  "qsa_q8_0_quantize", "qsa_gather_attend_q8_0"):
             getattr(L, f).restype = ctypes.c_int
         L.qsa_status_string.restype = ctypes.c_char_p
         L.qsa_status_string.argtypes = [ctypes.c_int]
@@ -289,3 +299,22 @@ def qsa_attend_masked(desc, cache, n_tokens, sel, n_sel_blocks, q, out, ws, stre
     p, n = _ws(ws)
     _check(lib().qsa_attend_masked(ctypes.byref(desc), ctypes.byref(cache), int(n_tokens), _ptr(sel),
                                    int(n_sel_blocks), _ptr(q), _ptr(out), p, n, _stream(stream)))
+
+
+# ------------------------------------------------------------------ q8_0 K/V
+def kv_q8_0(k_codes, k_scales, v_codes, v_scales):
+    """qsa_kv_q8_0 over torch tensors: codes int8 [cap, Hkv, Dh], scales
+    (binary16 bits, any 2-byte dtype) [cap, Hkv, Dh/32]."""
+    return qsa_kv_q8_0(k_codes.data_ptr(), k_scales.data_ptr(), v_codes.data_ptr(),
+                       v_scales.data_ptr(), int(k_codes.shape[0]))
+
+
+def qsa_q8_0_quantize(x, codes, scales, n_values=None, stream=None):
+    n = x.numel() if n_values is None else n_values
+    _check(lib().qsa_q8_0_quantize(_ptr(x), int(n), _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def qsa_gather_attend_q8_0(desc, kv, n_tokens, sel, n_sel_blocks, q, out, ws, stream=None):
+    p, n = _ws(ws)
+    _check(lib().qsa_gather_attend_q8_0(ctypes.byref(desc), ctypes.byref(kv), int(n_tokens), _ptr(sel),
+                                        int(n_sel_blocks), _ptr(q), _ptr(out), p, n, _stream(stream)))

@@ -221,3 +221,37 @@ def test_ablation_argument_errors_before_launch():
     assert L.qsa_attend_masked(D, C, 4096, P(16), 5, P(8), P(16), P(256), need, None) == -1
     assert L.qsa_attend_masked(D, C, 4096, P(16), 5, P(16), P(16), P(256), need - 256, None) == -3
     assert L.qsa_attend_masked(D, C, 4096, None, 0, P(16), P(16), P(256), need, None) == -1   # no cell
+
+
+def test_q8_0_argument_errors_before_launch():
+    qsa, d, c = _objs()
+    L = qsa.lib()
+    P = ctypes.c_void_p
+    D = ctypes.byref(d)
+    # quantise: n a non-negative multiple of 32, aligned pointers; 0 values is a no-op
+    assert L.qsa_q8_0_quantize(P(16), 31, P(16), P(16), None) == -1
+    assert L.qsa_q8_0_quantize(P(16), -32, P(16), P(16), None) == -1
+    assert L.qsa_q8_0_quantize(None, 64, P(16), P(16), None) == -1
+    assert L.qsa_q8_0_quantize(P(8), 64, P(16), P(16), None) == -1
+    assert L.qsa_q8_0_quantize(P(16), 64, P(16), P(17), None) == -1
+    assert L.qsa_q8_0_quantize(None, 0, None, None, None) == 0
+    # attention over the q8_0 planes
+    kv = qsa.qsa_kv_q8_0(0x1000, 0x2000, 0x3000, 0x4000, 4096)
+    K = ctypes.byref(kv)
+    need = qsa.qsa_workspace_bytes(d, 4096)
+    assert L.qsa_gather_attend_q8_0(D, K, 4096, P(16), 5, P(16), P(16), P(256), need - 256, None) == -3
+    assert L.qsa_gather_attend_q8_0(D, K, 0, P(16), 0, P(16), P(16), P(256), need, None) == -1
+    assert L.qsa_gather_attend_q8_0(D, K, 4097, P(16), 1, P(16), P(16), P(256), need, None) == -1
+    assert L.qsa_gather_attend_q8_0(D, K, 4096, P(16), 513, P(16), P(16), P(256), need, None) == -1
+    assert L.qsa_gather_attend_q8_0(D, K, 4096, None, 5, P(16), P(16), P(256), need, None) == -1
+    assert L.qsa_gather_attend_q8_0(D, K, 4096, P(16), 0, P(16), P(16), P(256), need, None) == -1
+    assert L.qsa_gather_attend_q8_0(D, K, 4096, P(16), 5, P(8), P(16), P(256), need, None) == -1
+    assert L.qsa_gather_attend_q8_0(D, None, 4096, P(16), 5, P(16), P(16), P(256), need, None) == -1
+    for bad in (qsa.qsa_kv_q8_0(0x1000, 0x2000, 0x3000, 0x4008, 4096),
+                qsa.qsa_kv_q8_0(0, 0x2000, 0x3000, 0x4000, 4096),
+                qsa.qsa_kv_q8_0(0x1000, 0x2000, 0x3000, 0x4000, 4094)):
+        assert L.qsa_gather_attend_q8_0(D, ctypes.byref(bad), 4096, P(16), 5, P(16), P(16), P(256),
+                                        need, None) == -1
+    bad_desc = qsa.make_desc(4, 128, qsa.QSA_F16, 16, 2, 96, 2048)
+    assert L.qsa_gather_attend_q8_0(ctypes.byref(bad_desc), K, 4096, P(16), 5, P(16), P(16), P(256),
+                                    need, None) < 0
