@@ -6,13 +6,14 @@
 // materialised: the attention workgroups load the selected rows directly.
 //
 // Split-context flash decode.  Cells are enumerated e = 0..n_cells-1 (chosen
-// blocks ascending, 4 cells each, then the tail).  Workgroup (split, g) takes
-// 16 consecutive cells of KV head g for all G query heads of the group (GQA:
-// each K/V row is read once for G heads) -- 258 workgroups for 2051 cells and
-// 2 KV heads, one per CU -- with the tile routine of qsa_attend.h.
-// The split's partial (m, l, acc) goes to the workspace; a second kernel
-// merges the partials of a head (one global latency round, fixed order:
-// bitwise repeatable).
+// blocks ascending, 4 cells each, then the tail when the splits hold it).
+// Workgroup (split, g) takes 16 consecutive cells of KV head g for all G
+// query heads of the group (GQA: each K/V row is read once for G heads) with
+// the tile routine of qsa_attend.h: 2048 chosen cells and 2 KV heads make 256
+// workgroups, one per CU, and the merge folds in the <= 3 tail cells.  The
+// split's partial (m, l, acc) goes to the workspace; a second kernel merges
+// the partials of a head (one global latency round, fixed order: bitwise
+// repeatable).
 #include "qsa_attend.h"
 #include "qsa_internal.h"
 #include "qsa_select.h"

@@ -182,7 +182,15 @@ qsa_status do_attend(const qsa_layer_desc *d, const qsa_layer_cache *c, int32_t 
                      const int32_t *sel, int32_t n_sel_blocks, const float *q, float *out,
                      float *part, hipStream_t stream)
 {
-    const AttendArgs a = attend_args(d, c, n_tokens, sel, n_sel_blocks, q, out, part);
+    AttendArgs a = attend_args(d, c, n_tokens, sel, n_sel_blocks, q, out, part);
+    if (n_sel_blocks > 0 && n_tokens % 4 != 0) {
+        // the splits hold the chosen blocks' cells and the merge adds the
+        // tail: 4K cells fill 2 x 128 workgroups, one per CU, where 4K + tail
+        // would need two more and a second round for them
+        a.n_cells = 4 * n_sel_blocks;
+        a.n_tail = n_tokens % 4;
+        a.n_split = (int32_t)n_splits(a.n_cells);
+    }
     hipError_t e = launch_attend(a, d->head_dim, d->q_heads / d->kv_heads, stream);
     if (e != hipSuccess)
         return hip_fail(e, "attend");

@@ -124,10 +124,20 @@ __device__ void attend_tile(const AttendArgs &a, AttLds<DH, G> &L, const int32_t
         }
         const bool hq = mc < G;
         const float4 *qp = (const float4 *)(a.q + ((size_t)g * G + (hq ? mc : 0)) * DH) + 2 * kg;
+        float4 qx[S::KS], qy[S::KS];
+#pragma unroll
+        for (int i = 0; i < S::KS; ++i) {
+            qx[i] = qp[8 * i];
+            qy[i] = qp[8 * i + 1];
+        }
+        // every K / q load above is in flight before the first use: left to
+        // itself the scheduler sinks some of them into the MFMA chain, which
+        // then waits out one memory round trip after another
+        __builtin_amdgcn_sched_barrier(0);
         float4v d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int i = 0; i < S::KS; ++i) {
-            const float4 x = qp[8 * i], y = qp[8 * i + 1];
+            const float4 x = qx[i], y = qy[i];
             const float qf[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
             half8 hi, lo, kh;
 #pragma unroll
