@@ -121,9 +121,10 @@ struct MergeLds {
 };
 
 // Output unit (query head h, 64-dim slice ds) from the split partials and the
-// tail.  Whole workgroup (kMT threads) calls.
-template <int DH, int G>
-__device__ void merge_unit(const AttendArgs &a, MergeLds &ml, int h, int ds)
+// tail.  Whole workgroup (kMT threads) calls.  Q8: the tail rows are q8_0
+// (codes in a.k / a.v, scales in q8), read as code * scale.
+template <int DH, int G, bool Q8 = false>
+__device__ void merge_unit(const AttendArgs &a, MergeLds &ml, int h, int ds, Q8Scales q8 = {})
 {
     float *s_w = ml.w, *s_red = ml.red, *s_l = ml.l;
     auto &s_acc = ml.acc;
@@ -152,12 +153,24 @@ __device__ void merge_unit(const AttendArgs &a, MergeLds &ml, int h, int ds)
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
             const size_t cell = j < nt ? 4 * (size_t)a.nb + j : 0;   // row 0: always there
-            const _Float16 *kr = (const _Float16 *)a.k + (cell * a.kv_heads + g) * DH;
-            const _Float16 *vr = (const _Float16 *)a.v + (cell * a.kv_heads + g) * DH;
+            const size_t rb = cell * a.kv_heads + g;
+            if constexpr (Q8) {
+                const int8_t *kr = (const int8_t *)a.k + rb * DH;
+                const int8_t *vr = (const int8_t *)a.v + rb * DH;
+                const uint16_t *ks = q8.k + rb * (DH / 32), *vs = q8.v + rb * (DH / 32);
 #pragma unroll
-            for (int i = 0; i < QD; ++i)
-                kq[j][i] = (float)kr[lane + kWave * i];
-            vt[j] = (float)vr[d];
+                for (int i = 0; i < QD; ++i)
+                    kq[j][i] = (float)kr[lane + kWave * i] *
+                               (float)__builtin_bit_cast(_Float16, ks[(lane + kWave * i) / 32]);
+                vt[j] = (float)vr[d] * (float)__builtin_bit_cast(_Float16, vs[d / 32]);
+            } else {
+                const _Float16 *kr = (const _Float16 *)a.k + rb * DH;
+                const _Float16 *vr = (const _Float16 *)a.v + rb * DH;
+#pragma unroll
+                for (int i = 0; i < QD; ++i)
+                    kq[j][i] = (float)kr[lane + kWave * i];
+                vt[j] = (float)vr[d];
+            }
         }
 #pragma unroll
         for (int i = 0; i < QD; ++i)
@@ -253,6 +266,13 @@ __global__ __launch_bounds__(kMT) void k_merge(AttendArgs a)
     merge_unit<DH, G>(a, ml, blockIdx.x, blockIdx.y);
 }
 
+template <int DH, int G>
+__global__ __launch_bounds__(kMT) void k_merge_q8(AttendArgs a, Q8Scales q8)
+{
+    __shared__ MergeLds ml;
+    merge_unit<DH, G, true>(a, ml, blockIdx.x, blockIdx.y, q8);
+}
+
 // A batch: grid (sequence x query head, 64-dim slice), over each sequence's
 // split partials.
 template <int DH, int G>
@@ -291,6 +311,14 @@ template <int DH, int G>
 hipError_t merge(const AttendArgs &a, hipStream_t s)
 {
     hipLaunchKernelGGL((k_merge<DH, G>), dim3(a.kv_heads * G, DH / kWave), dim3(kMT), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int DH, int G>
+hipError_t merge_q8(const AttendArgs &a, const Q8Scales &q8, hipStream_t s)
+{
+    hipLaunchKernelGGL((k_merge_q8<DH, G>), dim3(a.kv_heads * G, DH / kWave), dim3(kMT), 0, s, a,
+                       q8);
     return hipGetLastError();
 }
 
@@ -408,8 +436,7 @@ hipError_t launch_merge_batch(const AttendBatchArgs &b, int Dh, int G, hipStream
 hipError_t launch_attend_q8(const AttendArgs &a, const uint16_t *k_scales, const uint16_t *v_scales,
                             int Dh, int G, hipStream_t s)
 {
-    // the merge folds no tail of its own here: it would read the rows as f16
-    if (a.n_tail != 0 || a.n_split < 1 || a.n_split > kMaxSplits)
+    if (a.n_tail < 0 || a.n_tail > 3 || a.n_split < 1 || a.n_split > kMaxSplits)
         return hipErrorInvalidValue;
     const Q8Scales q8{k_scales, v_scales};
     const dim3 grid((unsigned)a.n_split, (unsigned)a.kv_heads);
@@ -433,18 +460,18 @@ hipError_t launch_attend_q8(const AttendArgs &a, const uint16_t *k_scales, const
     if (e != hipSuccess)
         return e;
     switch (Dh * 16 + G) {
-    case 64 * 16 + 1: return merge<64, 1>(a, s);
-    case 64 * 16 + 2: return merge<64, 2>(a, s);
-    case 64 * 16 + 4: return merge<64, 4>(a, s);
-    case 64 * 16 + 8: return merge<64, 8>(a, s);
-    case 128 * 16 + 1: return merge<128, 1>(a, s);
-    case 128 * 16 + 2: return merge<128, 2>(a, s);
-    case 128 * 16 + 4: return merge<128, 4>(a, s);
-    case 128 * 16 + 8: return merge<128, 8>(a, s);
-    case 256 * 16 + 1: return merge<256, 1>(a, s);
-    case 256 * 16 + 2: return merge<256, 2>(a, s);
-    case 256 * 16 + 4: return merge<256, 4>(a, s);
-    case 256 * 16 + 8: return merge<256, 8>(a, s);
+    case 64 * 16 + 1: return merge_q8<64, 1>(a, q8, s);
+    case 64 * 16 + 2: return merge_q8<64, 2>(a, q8, s);
+    case 64 * 16 + 4: return merge_q8<64, 4>(a, q8, s);
+    case 64 * 16 + 8: return merge_q8<64, 8>(a, q8, s);
+    case 128 * 16 + 1: return merge_q8<128, 1>(a, q8, s);
+    case 128 * 16 + 2: return merge_q8<128, 2>(a, q8, s);
+    case 128 * 16 + 4: return merge_q8<128, 4>(a, q8, s);
+    case 128 * 16 + 8: return merge_q8<128, 8>(a, q8, s);
+    case 256 * 16 + 1: return merge_q8<256, 1>(a, q8, s);
+    case 256 * 16 + 2: return merge_q8<256, 2>(a, q8, s);
+    case 256 * 16 + 4: return merge_q8<256, 4>(a, q8, s);
+    case 256 * 16 + 8: return merge_q8<256, 8>(a, q8, s);
     }
     return hipErrorInvalidValue;
 }

@@ -1005,13 +1005,18 @@ qsa_status qsa_gather_attend_q8_0(const qsa_layer_desc *desc, const qsa_kv_q8_0 
     if ((s = check_ws(ws, ws_bytes, L.total)) != QSA_OK)
         return s;
     // the q8_0 planes stand in for the f16 rows; every other argument as in
-    // the f16 gather (the splits hold the tail cells, n_tail = 0)
+    // the f16 gather (the merge adds the tail when blocks are chosen)
     qsa_layer_cache c{};
     c.k = (uint16_t *)kv->k_codes;
     c.v = (uint16_t *)kv->v_codes;
     c.capacity = kv->capacity;
-    const AttendArgs a = attend_args(desc, &c, n_tokens, sel, n_sel_blocks, q, out,
-                                     (float *)((char *)ws + L.part));
+    AttendArgs a = attend_args(desc, &c, n_tokens, sel, n_sel_blocks, q, out,
+                               (float *)((char *)ws + L.part));
+    if (n_sel_blocks > 0 && n_tokens % 4 != 0) {
+        a.n_cells = 4 * n_sel_blocks;
+        a.n_tail = n_tokens % 4;
+        a.n_split = (int32_t)n_splits(a.n_cells);
+    }
     hipError_t e = launch_attend_q8(a, kv->k_scales, kv->v_scales, desc->head_dim,
                                     desc->q_heads / desc->kv_heads, stream);
     if (e != hipSuccess)

@@ -172,7 +172,7 @@ struct AttendArgs {
 hipError_t launch_attend(const AttendArgs &a, int Dh, int G, hipStream_t s);
 // The same over a q8_0 K/V cache: a.k / a.v hold the int8 codes
 // ([rows][kv_heads][Dh]), the scales are [rows][kv_heads][Dh/32] binary16;
-// a.n_tail must be 0 (the splits hold the tail cells).
+// the merge reads the a.n_tail tail rows (if any) in the same format.
 hipError_t launch_attend_q8(const AttendArgs &a, const uint16_t *k_scales, const uint16_t *v_scales,
                             int Dh, int G, hipStream_t s);
 // q8_0 quantisation of n_blocks blocks of 32 binary16 values.
