@@ -136,7 +136,10 @@ __device__ void merge_unit(const AttendArgs &a, MergeLds &ml, int h, int ds, Q8S
     const float *base = a.part + (size_t)g * ns * ps;
     const int d = ds * kWave + lane;
 
-    // first round of (l, acc) loads, issued before anything waits
+    // m_s first, without a branch (threads past the splits read split 0 and
+    // drop it), then the first round of (l, acc) loads: every load in flight
+    // before anything waits
+    float ms = base[(size_t)(t < ns ? t : 0) * ps + hh];
     float l[kMRound], x[kMRound];
 #pragma unroll
     for (int i = 0; i < kMRound; ++i) {
@@ -150,6 +153,10 @@ __device__ void merge_unit(const AttendArgs &a, MergeLds &ml, int h, int ds, Q8S
     const int nt = wave == 0 ? a.n_tail : 0;
     float kq[3][QD], vt[3], qv[QD];
     if (nt) {
+        // raw elements (f16, or q8_0 code and scale) loaded first, converted
+        // after the barrier: a conversion scheduled between the loads would
+        // wait for every load before it
+        uint16_t kh[3][QD], vh[3], ksc[3][QD], vsc[3];
 #pragma unroll
         for (int j = 0; j < 3; ++j) {
             const size_t cell = j < nt ? 4 * (size_t)a.nb + j : 0;   // row 0: always there
@@ -159,25 +166,44 @@ __device__ void merge_unit(const AttendArgs &a, MergeLds &ml, int h, int ds, Q8S
                 const int8_t *vr = (const int8_t *)a.v + rb * DH;
                 const uint16_t *ks = q8.k + rb * (DH / 32), *vs = q8.v + rb * (DH / 32);
 #pragma unroll
-                for (int i = 0; i < QD; ++i)
-                    kq[j][i] = (float)kr[lane + kWave * i] *
-                               (float)__builtin_bit_cast(_Float16, ks[(lane + kWave * i) / 32]);
-                vt[j] = (float)vr[d] * (float)__builtin_bit_cast(_Float16, vs[d / 32]);
+                for (int i = 0; i < QD; ++i) {
+                    kh[j][i] = (uint16_t)(uint8_t)kr[lane + kWave * i];
+                    ksc[j][i] = ks[(lane + kWave * i) / 32];
+                }
+                vh[j] = (uint16_t)(uint8_t)vr[d];
+                vsc[j] = vs[d / 32];
             } else {
-                const _Float16 *kr = (const _Float16 *)a.k + rb * DH;
-                const _Float16 *vr = (const _Float16 *)a.v + rb * DH;
+                const uint16_t *kr = a.k + rb * DH;
+                const uint16_t *vr = a.v + rb * DH;
 #pragma unroll
                 for (int i = 0; i < QD; ++i)
-                    kq[j][i] = (float)kr[lane + kWave * i];
-                vt[j] = (float)vr[d];
+                    kh[j][i] = kr[lane + kWave * i];
+                vh[j] = vr[d];
             }
         }
 #pragma unroll
         for (int i = 0; i < QD; ++i)
             qv[i] = a.q[(size_t)h * DH + lane + kWave * i];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            if constexpr (Q8) {
+#pragma unroll
+                for (int i = 0; i < QD; ++i)
+                    kq[j][i] = (float)(int8_t)(uint8_t)kh[j][i] *
+                               (float)__builtin_bit_cast(_Float16, ksc[j][i]);
+                vt[j] = (float)(int8_t)(uint8_t)vh[j] * (float)__builtin_bit_cast(_Float16, vsc[j]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < QD; ++i)
+                    kq[j][i] = (float)__builtin_bit_cast(_Float16, kh[j][i]);
+                vt[j] = (float)__builtin_bit_cast(_Float16, vh[j]);
+            }
+        }
     }
 
-    const float ms = t < ns ? base[(size_t)t * ps + hh] : -INFINITY;
+    if (t >= ns)
+        ms = -INFINITY;
     float wm = wave::reduce_max_f(ms);
     float mt = -INFINITY, lt = 0.0f, at = 0.0f;
     if (nt) {

@@ -521,9 +521,7 @@ template <class Emit>
 __device__ void run(const SelectArgs &a, char *lds, Emit emit)
 {
     Smem &sm = *reinterpret_cast<Smem *>(lds);
-    const uint32_t nb = (uint32_t)a.nb;
     const uint32_t k = (uint32_t)a.k;
-    const uint32_t nwords = (nb + 31) >> 5;
     uint32_t *bitmap = reinterpret_cast<uint32_t *>(lds + (sizeof(Smem) + 15) / 16 * 16);
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const uint32_t nchunks = (uint32_t)a.ntiles * (uint32_t)a.T / 2;
