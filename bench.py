@@ -149,7 +149,9 @@ def oracle_beside_legs(result, w256, cpu_step_ms):
     """The CPU oracle beside the other legs, on bounded samples: a verify call
     is n_q oracle decode steps; a batched step is one oracle step per
     sequence (one step each, timed on that sequence's own context); a chunk
-    is n_q oracle steps, estimated from 4 steps at the chunk's context."""
+    is n_q oracle steps, estimated from 4 steps at the chunk's context; the
+    q8_0 leg's quantisation is timed on 8,192 rows and scaled, its attention
+    timed once on the 256k selection's cells."""
     from qsagen import workloads as W
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     md = result.get("multi_decode")
@@ -169,6 +171,32 @@ def oracle_beside_legs(result, w256, cpu_step_ms):
         bc["chunk"]["cpu_oracle"] = {
             "ms_per_chunk": round(ms * c.steps, 1), "cores": threads,
             "sample": f"{c.steps} x the median of 4 oracle decode steps at n0={c.n0} ({ms:.1f} ms)"}
+    q8 = result.get("q8_0_kv")
+    if q8:
+        import numpy as np
+        import oracle
+        import qsagen
+        rows = 8192
+        k, v = W.host_kv_rows(w256, np.arange(rows), 0)
+        t0 = time.perf_counter()
+        oracle.q8_0_quantize(k)
+        oracle.q8_0_quantize(v)
+        quant_ms = (time.perf_counter() - t0) * 1e3 * w256.n0 / rows
+        rng = np.random.default_rng(0)
+        sel = np.sort(rng.choice(w256.n0 // 4, w256.k_blocks, replace=False)).astype(np.int32)
+        cells = oracle.cells(sel, w256.n0)
+        k, v = W.host_kv_rows(w256, cells, 0)
+        kc, kd = oracle.q8_0_quantize(k)
+        vc, vd = oracle.q8_0_quantize(v)
+        q = qsagen.host_normal((w256.q_heads, w256.head_dim), w256.seed, 7)
+        t0 = time.perf_counter()
+        oracle.attend_q8_0(q, kc, kd, vc, vd, np.arange(len(cells), dtype=np.int32))
+        att_ms = (time.perf_counter() - t0) * 1e3
+        q8["cpu_oracle"] = {
+            "quantize_ms_per_layer": round(quant_ms, 1), "gather_attend_q8_0_ms": round(att_ms, 2),
+            "cores": 1,
+            "sample": f"q8_0 of {rows} K and V rows scaled to {w256.n0}; one attention over "
+                      f"{len(cells)} cells (single-threaded C)"}
 
 
 TRAFFIC_COPY_MB = 256
