@@ -595,7 +595,10 @@ __device__ void run(const SelectArgs &a, char *lds, Emit emit)
 
     if (!general) {
         // 2. linear histogram; an empty slot (key 0) lands in bin 0, which the
-        //    fast path never resolves (it falls back below)
+        //    fast path never resolves (it falls back below), and is left out
+        //    of the counts: its atomic would only add to bin 0's, and the
+        //    empty slots of short lists (a few thousand at 64k contexts) all
+        //    hitting one LDS address serialise for microseconds
         uint32_t bins[kEntries];
 #pragma unroll
         for (int e = 0; e < kEntries; ++e) {
@@ -609,7 +612,8 @@ __device__ void run(const SelectArgs &a, char *lds, Emit emit)
                 b = b < (uint32_t)kBins - 1 ? b : (uint32_t)kBins - 1;
             }
             bins[e] = b;
-            atomicAdd(&sm.hist[b], 1u);
+            if (key != 0u)
+                atomicAdd(&sm.hist[b], 1u);
         }
         __syncthreads();                                                // barrier
         // the bin d holding the k-th largest: thread t takes bin 1023 - t, so a
