@@ -177,20 +177,26 @@ AttendArgs attend_args(const qsa_layer_desc *d, const qsa_layer_cache *c, int32_
     return a;
 }
 
+// The splits hold the chosen blocks' cells and the merge adds the <= 3 tail
+// cells: 4K cells fill whole workgroups (2 x 128 16-cell splits in the decode
+// attention, 2 x 32 64-cell iterations per sequence in the batch), where 4K +
+// tail needs one more per KV head and, on a full chip, a second round for it.
+void fold_tail(AttendArgs &a, int32_t n_tokens)
+{
+    if (a.n_sel_blocks > 0 && n_tokens % 4 != 0) {
+        a.n_cells = 4 * a.n_sel_blocks;
+        a.n_tail = n_tokens % 4;
+        a.n_split = (int32_t)n_splits(a.n_cells);
+    }
+}
+
 // Stage 4 launch shared by qsa_gather_attend and qsa_decode_step.
 qsa_status do_attend(const qsa_layer_desc *d, const qsa_layer_cache *c, int32_t n_tokens,
                      const int32_t *sel, int32_t n_sel_blocks, const float *q, float *out,
                      float *part, hipStream_t stream)
 {
     AttendArgs a = attend_args(d, c, n_tokens, sel, n_sel_blocks, q, out, part);
-    if (n_sel_blocks > 0 && n_tokens % 4 != 0) {
-        // the splits hold the chosen blocks' cells and the merge adds the
-        // tail: 4K cells fill 2 x 128 workgroups, one per CU, where 4K + tail
-        // would need two more and a second round for them
-        a.n_cells = 4 * n_sel_blocks;
-        a.n_tail = n_tokens % 4;
-        a.n_split = (int32_t)n_splits(a.n_cells);
-    }
+    fold_tail(a, n_tokens);
     hipError_t e = launch_attend(a, d->head_dim, d->q_heads / d->kv_heads, stream);
     if (e != hipSuccess)
         return hip_fail(e, "attend");
@@ -630,6 +636,7 @@ qsa_status qsa_decode_step_batch(const qsa_layer_desc *desc, int32_t n_seq,
         selb.seq[i] = select_args(wsp, L, nb, K, tile_rows, a.list_t, sel);
         ab.seq[i] = attend_args(desc, c, n, need_select ? sel : nullptr, need_select ? K : nb,
                                 x.q, x.out, (float *)(wsp + L.part));
+        fold_tail(ab.seq[i], n);
     }
     e = launch_score_batch(sb, f16, rowb, stream);
     if (e != hipSuccess)
@@ -738,6 +745,7 @@ qsa_status qsa_decode_step_multi(const qsa_layer_desc *desc, const qsa_layer_cac
         ab.seq[i] = attend_args(desc, cache, n, need_select ? sel : nullptr, need_select ? K : nb,
                                 q + (size_t)i * qa, out + (size_t)i * qa,
                                 (float *)(wsp + L.part));
+        fold_tail(ab.seq[i], n);
     }
     if (score) {
         e = launch_score_multi(sm, n_q, f16, rowb, stream);
@@ -1012,11 +1020,7 @@ qsa_status qsa_gather_attend_q8_0(const qsa_layer_desc *desc, const qsa_kv_q8_0 
     c.capacity = kv->capacity;
     AttendArgs a = attend_args(desc, &c, n_tokens, sel, n_sel_blocks, q, out,
                                (float *)((char *)ws + L.part));
-    if (n_sel_blocks > 0 && n_tokens % 4 != 0) {
-        a.n_cells = 4 * n_sel_blocks;
-        a.n_tail = n_tokens % 4;
-        a.n_split = (int32_t)n_splits(a.n_cells);
-    }
+    fold_tail(a, n_tokens);
     hipError_t e = launch_attend_q8(a, kv->k_scales, kv->v_scales, desc->head_dim,
                                     desc->q_heads / desc->kv_heads, stream);
     if (e != hipSuccess)
