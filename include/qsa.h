@@ -203,6 +203,8 @@ typedef struct qsa_seq_io {
     const float *q;             /* DEVICE fp32 [Hq][Dh], 16-byte aligned */
     float *out;                 /* DEVICE fp32 [Hq][Dh] */
     int32_t *sel_out;           /* optional DEVICE int32 [min(K, n/4)] (NULL to skip) */
+    float *scores_out;          /* optional DEVICE fp32 [n/4]: the fp32 score of every block,
+                                   the values the top-k ranks (NULL to skip) */
 } qsa_seq_io;
 
 /* Workspace bytes for qsa_decode_step_batch over sequences of the given

@@ -2,7 +2,7 @@
 
 Plain gcc, no fast-math and no FMA contraction, so every double operation in
 qsa_oracle.c is rounded exactly as written.  OpenMP only splits independent
-per-block loops; it changes no result.
+per-block and per-head loops; it changes no result.
 """
 import os
 import subprocess

@@ -278,9 +278,12 @@ void qsa_oracle_attend(const float *q, const uint16_t *K, const uint16_t *V,
                        const int32_t *cells, long nc, int Hq, int Hkv, int Dh,
                        double scale, double *out)
 {
-    double *lg = (double *)malloc(sizeof(double) * (size_t)(nc > 0 ? nc : 1));
     const size_t row = (size_t)Hkv * Dh;
-    for (int h = 0; h < Hq; ++h) {
+    int h;
+    /* heads are independent: each thread runs the same per-head arithmetic */
+#pragma omp parallel for schedule(static)
+    for (h = 0; h < Hq; ++h) {
+        double *lg = (double *)malloc(sizeof(double) * (size_t)(nc > 0 ? nc : 1));
         const int g = (int)(((long)h * Hkv) / Hq);
         double mx = -INFINITY;
         for (long c = 0; c < nc; ++c) {
@@ -303,8 +306,8 @@ void qsa_oracle_attend(const float *q, const uint16_t *K, const uint16_t *V,
                 acc += lg[c] * qsa_oracle_half_to_double(V[(size_t)cells[c] * row + (size_t)g * Dh + d]);
             out[(size_t)h * Dh + d] = acc / z;
         }
+        free(lg);
     }
-    free(lg);
 }
 
 /* ---- q8_0 K/V: 8-bit codes, one binary16 scale per 32 values --------------
@@ -378,35 +381,4 @@ void qsa_oracle_attend_q8_0(const float *q, const int8_t *Kc, const uint16_t *Kd
         }
     }
     free(lg);
-}
-
-/* ---- A whole decode step (O1..O9 in order) ----------------------------------
- * The caller has already written the new token's raw key and K/V rows at
- * position n-1.  Rows [valid, n/4) of the summary cache are rebuilt, then
- * every stored block is scored, the top-k blocks chosen, and attention runs
- * over their cells plus the tail.  Returns the new valid-block watermark
- * (= n/4).  sel must hold min(k, n/4) ids, cells 4*k + 3 entries,
- * scores n/4 entries.
- * [post 10, "incremental pooled-key cache（COMMON-004）", "QSA indexer",
- *  "selected QSA K/V gather（COMMON-005）"]
- */
-long qsa_oracle_decode_step(const void *raw, void *summary, int dtype, int H, int D,
-                            const float *gamma, double eps, double theta,
-                            const uint16_t *K, const uint16_t *V, int Hq, int Hkv, int Dh,
-                            double scale, long n, long valid, long k_blocks,
-                            const float *q_idx, const float *w, const float *q,
-                            double *scores, int32_t *sel, int32_t *cells,
-                            long *n_sel_blocks, long *n_cells, double *out)
-{
-    const long nb = n / 4;
-    if (valid > nb)
-        valid = nb;
-    qsa_oracle_cache_update(raw, summary, dtype, H, D, valid, nb, gamma, eps, theta);
-    qsa_oracle_scores(summary, dtype, nb, H, D, q_idx, w, scores, NULL);
-    const long kb = qsa_oracle_topk(scores, nb, k_blocks, sel);
-    const long nc = qsa_oracle_cells(sel, kb, n, cells);
-    qsa_oracle_attend(q, K, V, cells, nc, Hq, Hkv, Dh, scale, out);
-    *n_sel_blocks = kb;
-    *n_cells = nc;
-    return nb;
 }

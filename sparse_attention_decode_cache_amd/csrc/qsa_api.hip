@@ -624,10 +624,12 @@ qsa_status qsa_decode_step_batch(const qsa_layer_desc *desc, int32_t n_seq,
         a.summary = c->summary;
         a.q = x.q_idx;
         a.w = x.w;
+        a.scores = x.scores_out;
         a.keys = need_select ? (uint32_t *)(wsp + L.keys) : nullptr;
         a.lists = need_select ? (uint64_t *)(wsp + L.lists) : nullptr;
         a.list_t = list_len(tile_rows, nb, K);
-        a.nb = need_select ? nb : 0;     // kept-everything sequences only run the prologue
+        // kept-everything sequences only run the prologue (and their scores when asked)
+        a.nb = need_select || x.scores_out ? nb : 0;
         a.D = desc->idx_dim;
         a.fuse = fuse ? 1 : 0;
         a.upd = u;

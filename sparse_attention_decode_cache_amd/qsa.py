@@ -64,7 +64,8 @@ class qsa_seq_state(ctypes.Structure):
 class qsa_seq_io(ctypes.Structure):
     _fields_ = [("idx_k_row", ctypes.c_void_p), ("k_row", ctypes.c_void_p),
                 ("v_row", ctypes.c_void_p), ("q_idx", ctypes.c_void_p), ("w", ctypes.c_void_p),
-                ("q", ctypes.c_void_p), ("out", ctypes.c_void_p), ("sel_out", ctypes.c_void_p)]
+                ("q", ctypes.c_void_p), ("out", ctypes.c_void_p), ("sel_out", ctypes.c_void_p),
+                ("scores_out", ctypes.c_void_p)]
 
 
 _lib = None
@@ -230,7 +231,8 @@ def qsa_decode_step_batch(desc, caches, states, io, gamma, ws, stream=None):
     s_arr = (qsa_seq_state * n)(*[qsa_seq_state(s.n_tokens, s.n_valid_blocks) for s in states])
     io_arr = (qsa_seq_io * n)(*[qsa_seq_io(*[None if x.get(k) is None else x[k].data_ptr()
                                               for k in ("idx_k_row", "k_row", "v_row", "q_idx", "w",
-                                                        "q", "out", "sel_out")]) for x in io])
+                                                        "q", "out", "sel_out", "scores_out")])
+                                  for x in io])
     p, nbytes = _ws(ws)
     _check(lib().qsa_decode_step_batch(ctypes.byref(desc), n, c_arr, s_arr, io_arr, _ptr(gamma), p,
                                        nbytes, _stream(stream)))

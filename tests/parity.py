@@ -77,6 +77,20 @@ def check_topk(sel, ref_scores, scale, k):
     return "threshold"
 
 
+def check_topk_on_gpu_scores(sel, gpu_scores, k):
+    """The GPU's chosen ids against the oracle's top-k rule applied to the
+    GPU's own fp32 scores (the values its keys were made from): with equal
+    scores on both sides the selection has one correct answer, so the ids
+    must match bit for bit, whatever the gap at the k-th."""
+    import oracle
+    nb = int(np.asarray(gpu_scores).shape[0])
+    ref = oracle.topk(np.asarray(gpu_scores, dtype=np.float32).astype(np.float64), k)
+    sel = np.asarray(sel, dtype=np.int64)
+    assert sel.shape == (min(k, nb),), f"{sel.shape} ids, expected {min(k, nb)}"
+    bad = np.nonzero(sel != ref)[0]
+    assert bad.size == 0, f"top-k differs from the rule on the GPU's scores at slot {bad[0]}: {sel[bad[0]]} vs {ref[bad[0]]}"
+
+
 def check_attention(gpu, ref):
     """P4: <= 2e-3 absolute per element.  Returns the max error."""
     err = np.abs(gpu.astype(np.float64) - ref)

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 import oracle
-from parity import check_attention, check_summaries, check_topk
+from parity import check_attention, check_summaries, check_topk, check_topk_on_gpu_scores
 from gpu_layer import GpuLayer, OracleMirror, with_size
 from qsagen import workloads as W
 
@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 def _batch_io(g, s, sel):
     inp = g.inp
     return {"idx_k_row": inp.raw[s], "k_row": inp.k[s], "v_row": inp.v[s], "q_idx": inp.q_idx[s],
-            "w": inp.w[s], "q": inp.q[s], "out": g.out, "sel_out": sel}
+            "w": inp.w[s], "q": inp.q[s], "out": g.out, "sel_out": sel, "scores_out": g.scores}
 
 
 def _run_batch(base, contexts, steps, check_sel=True):
@@ -45,6 +45,8 @@ def _run_batch(base, contexts, steps, check_sel=True):
             out = g.out.cpu().numpy().astype(np.float64)
             branch = check_topk(sel, ro["scores"], ro["scale"], base.k_blocks)
             stats[branch] += 1
+            if nb > 0:
+                check_topk_on_gpu_scores(sel, g.scores[:nb].cpu().numpy(), base.k_blocks)
             cells = oracle.cells(sel, n)
             assert len(cells) == oracle.n_cells(n, base.k_blocks)
             ref = oracle.attend(ro["q"], o.L.K, o.L.V, cells)
@@ -123,6 +125,7 @@ def test_batch_winners_clustered_in_a_few_tiles():
         n = g.state.n_tokens
         sel = sels[i].cpu().numpy()
         branch = check_topk(sel, ro["scores"], ro["scale"], W.CTX64K.k_blocks)
+        check_topk_on_gpu_scores(sel, g.scores[:n // 4].cpu().numpy(), W.CTX64K.k_blocks)
         if cl:
             assert branch == "exact" and np.array_equal(sel, np.arange(cl[1] - 512, cl[1]))
         ref = oracle.attend(ro["q"], o.L.K, o.L.V, oracle.cells(sel, n))

@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 
 import oracle
-from parity import check_attention, check_scores, check_summaries, check_topk
+from parity import check_attention, check_scores, check_summaries, check_topk, check_topk_on_gpu_scores
 from gpu_layer import GpuLayer, OracleMirror, with_size
 from qsagen import workloads as W
 
@@ -21,6 +21,8 @@ def _compare_step(g, o, s, stats):
         check_scores(rg["scores"], ro["scores"], ro["scale"])
     branch = check_topk(rg["sel"], ro["scores"], ro["scale"], g.w.k_blocks)
     stats[branch] += 1
+    if nb > 0:
+        check_topk_on_gpu_scores(rg["sel"], rg["scores"], g.w.k_blocks)
     cells = oracle.cells(rg["sel"], n)
     assert len(cells) == oracle.n_cells(n, g.w.k_blocks) <= g.w.top_k_tokens + 3
     ref = oracle.attend(ro["q"], o.L.K, o.L.V, cells)
@@ -99,6 +101,7 @@ def test_invalidate_and_truncate_on_gpu():
         sc = oracle.scores(o.L.summary, nb, qi, wt, with_scale=True)[1]
         sel = g.sel[:min(w.k_blocks, nb)].cpu().numpy()
         check_topk(sel, r["scores"], sc, w.k_blocks)
+        check_topk_on_gpu_scores(sel, g.scores[:nb].cpu().numpy(), w.k_blocks)
         check_attention(g.out.cpu().numpy(), oracle.attend(q, o.L.K, o.L.V, oracle.cells(sel, n)))
 
 

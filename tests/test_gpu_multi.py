@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import oracle
-from parity import check_attention, check_scores, check_summaries, check_topk
+from parity import check_attention, check_scores, check_summaries, check_topk, check_topk_on_gpu_scores
 from gpu_layer import GpuLayer, OracleMirror, with_size
 from qsagen import workloads as W
 
@@ -72,6 +72,8 @@ def _check(i, L, toks, res, k_blocks, stats):
         assert np.all(scores[i, nb:nb_last] == -np.inf), f"query {i}: masked scores not -inf"
     branch = check_topk(sel[i, :kb], s_ref, scale, k_blocks)
     stats[branch] += 1
+    if nb > 0:
+        check_topk_on_gpu_scores(sel[i, :kb], scores[i, :nb], k_blocks)
     cells = oracle.cells(sel[i, :kb], n)
     assert len(cells) == oracle.n_cells(n, k_blocks)
     ref = oracle.attend(q[i], L.K, L.V, cells)
