@@ -44,8 +44,11 @@
  *     multiple of 4, at most 16380; capacity a positive multiple of 4, at
  *     most 2^21 tokens (n_blocks of qsa_topk_blocks at most 2^19).
  *   - A workspace (DEVICE, 256-byte aligned, >= qsa_workspace_bytes) holds
- *     scratch only.  Calls that share a workspace must be stream-ordered.
- *     Its contents need no initialisation and are meaningless between calls.
+ *     scratch.  Calls that share a workspace must be stream-ordered.  Its
+ *     contents need no initialisation.  The decode step keeps a small region
+ *     of it (a score histogram, qsa_decode_step below) cleared between calls
+ *     and checks a tag before trusting it: a fresh or reused workspace only
+ *     makes the first call take the slower exact path.
  */
 #ifndef QSA_H
 #define QSA_H
@@ -103,6 +106,16 @@ typedef struct {
  * qsa_topk_blocks for any token count up to `capacity`.  Returns 0 for an
  * invalid or unsupported descriptor. */
 size_t qsa_workspace_bytes(const qsa_layer_desc *desc, int32_t capacity);
+
+/* Diagnostics: a qsa_decode_step workspace holds, at this byte offset, a
+ * 64-bit word whose low byte tells how the last decode step on it that
+ * selected blocks chose them: QSA_PATH_HIST (the score histogram decided
+ * exactly) or QSA_PATH_FULL (it could not, and the full top-k over every
+ * block key ran).  The word is written by the device at the end of the step;
+ * it is undefined before the first such step. */
+#define QSA_DECODE_STATUS_OFFSET 8
+#define QSA_PATH_HIST 1
+#define QSA_PATH_FULL 2
 
 /* State load or distrust from position `pos` [post 10, COMMON-004 section:
  * the cache is invalidated and rebuilt when next needed]:

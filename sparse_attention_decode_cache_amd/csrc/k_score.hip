@@ -26,6 +26,7 @@
 // verify call's) and pools that block straight into LDS; the lanes that
 // loaded the row's stale chunks take the pooled ones from there.  The
 // pooling latency hides under the stream.
+#include "qsa_hist.h"
 #include "qsa_pool.h"
 #include "qsa_wave.h"
 
@@ -73,13 +74,6 @@ struct Butterfly {
     }
 };
 
-__device__ inline uint32_t score_key(float s)
-{
-    // -0 and +0 must compare equal: canonicalise before taking the bits.
-    const uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
 // Tile list: the T largest of the R composites in s_c (0 = no row), written
 // descending to lists[tile*T ...]; slots past the tile's rows get 0.  T <= R
 // is chosen per call (longer lists where a tile holds more winners).  Ranks
@@ -89,7 +83,7 @@ __device__ inline uint32_t score_key(float s)
 // workgroup calls (uniform control flow: DPP reads neighbouring lanes).
 template <int R>
 __device__ inline void write_tile_list(const uint64_t *s_c, uint64_t *lists, int tile, int valid_rows,
-                                       int T)
+                                       int T, const HistOut *h = nullptr, const hist::Map *map = nullptr)
 {
     static_assert(R == 64 || R == 128 || R == 256, "tile rows");
     constexpr int P = 256 / R;
@@ -104,8 +98,22 @@ __device__ inline void write_tile_list(const uint64_t *s_c, uint64_t *lists, int
         rank += wave::dpp<wave::kQuadXor1>(rank);
     if constexpr (P == 4)
         rank += wave::dpp<wave::kQuadXor2>(rank);
-    if (part == 0 && c != 0 && rank < (uint32_t)T)
+    if (part == 0 && c != 0 && rank < (uint32_t)T) {
         lists[(size_t)tile * T + rank] = c;
+        if (h && hist::in_window((uint32_t)(c >> 32), *map)) {
+            // an entry inside the window: its bin's count (its bucket slot)
+            // and, for the last entry of a list that may hide rows, the
+            // maximum of such entries
+            const uint32_t b = hist::bin_of((uint32_t)(c >> 32), *map);
+            const uint32_t slot =
+                __hip_atomic_fetch_add(h->hist + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (slot < (uint32_t)hist::kCap)
+                h->bucket[(size_t)b * hist::kCap + slot] = c;
+            if (rank == (uint32_t)T - 1 && valid_rows > T)
+                __hip_atomic_fetch_max(h->last + (tile & (hist::kLast - 1)), c, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
     // the nonzero composites take ranks [0, valid_rows): the rest are empty
     if ((int)threadIdx.x >= valid_rows && threadIdx.x < (unsigned)T)
         lists[(size_t)tile * T + threadIdx.x] = 0;
@@ -141,6 +149,7 @@ struct ScoreMultiLds {
     float qw[Q][LPR * EPL];
     uint64_t c[Q][ScoreShape<LPR>::R];
     u32x4 fresh[LPR];
+    float nrm2[4], g2;          // histogram window: ||w_h q_h||^2 per head, sum of gamma^2
 };
 
 template <bool F16, int LPR, int Q>
@@ -165,6 +174,13 @@ __device__ inline void score_tile(const ScoreMultiArgs &a, ScoreLdsOf<F16, LPR, 
     const int sub = lane / L;
     const int64_t base = (int64_t)tile * R + (int64_t)wave * S::RPW;
 
+    // the fed-back histogram window (read with the queries, used at the end)
+    float rho_lo = 0.0f, rho_hi = 0.0f;
+    if (Q == 1 && a.h.hist) {
+        const hist::Ctrl *ctrl = reinterpret_cast<const hist::Ctrl *>(a.h.ctrl);
+        rho_lo = ctrl->rho_lo;
+        rho_hi = ctrl->rho_hi;
+    }
     // the queries' float4 groups this thread folds into LDS, loaded ahead of the rows
     float4 qraw[QPT];
     float wraw[QPT];
@@ -218,7 +234,32 @@ __device__ inline void score_tile(const ScoreMultiArgs &a, ScoreLdsOf<F16, LPR, 
                 buf[i] = sl.fresh[col + L * (i % C)];
         }
     }
-
+    if (Q == 1 && a.h.hist) {
+        // the histogram window's scale (qsa_hist.h): wave h < H takes the
+        // squared norm of head h's folded query, wave 3 the sum of gamma^2;
+        // the same arithmetic in every workgroup, so every one maps alike
+        const int H = HD / a.D;
+        if (wave < H) {
+            float ss = 0.0f;
+            for (int e = lane; e < a.D; e += kWave) {
+                const float x = sl.qw[0][wave * a.D + e];
+                ss = fmaf(x, x, ss);
+            }
+            ss = wave::reduce_add_f(ss);
+            if (lane == 0)
+                sl.nrm2[wave] = ss;
+        }
+        if (wave == 3) {
+            float gg = 0.0f;
+            for (int e = lane; e < a.D; e += kWave) {
+                const float x = a.h.gamma[e];
+                gg = fmaf(x, x, gg);
+            }
+            gg = wave::reduce_add_f(gg);
+            if (lane == 0)
+                sl.g2 = gg;
+        }
+    }
     float v[Q][V];
 #pragma unroll
     for (int qi = 0; qi < Q; ++qi)
@@ -295,6 +336,33 @@ __device__ inline void score_tile(const ScoreMultiArgs &a, ScoreLdsOf<F16, LPR, 
         }
     }
     __syncthreads();
+    if (Q == 1 && a.h.hist) {
+        const int H = HD / a.D;
+        float n2 = 0.0f;
+        for (int h = 0; h < H; ++h)
+            n2 += sl.nrm2[h];
+        const float sigma = sqrtf(n2 * (sl.g2 / (float)a.D));
+        hist::Ctrl *ctrl = reinterpret_cast<hist::Ctrl *>(a.h.ctrl);
+        float lo, hi;
+        hist::window(sigma, rho_lo, rho_hi, a.h.def_lo, a.h.def_hi, lo, hi);
+        const hist::Map map = hist::make_map(lo, hi);
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            // stamp the region with this call (clean start or not) and leave the
+            // window and its bin map for the attention kernel
+            ctrl->tag = ctrl->tag == hist::kTagClean ? hist::tag_ok(a.h.epoch) : hist::tag_bad(a.h.epoch);
+            ctrl->sigma = sigma;
+            ctrl->lo = lo;
+            ctrl->hi = hi;
+            ctrl->inv = map.inv;
+            ctrl->klo = map.klo;
+            ctrl->khi = map.khi;
+            ctrl->map_ok = map.ok ? 1u : 0u;
+        }
+        const int64_t valid = a.nbq[0] - (int64_t)tile * R;
+        write_tile_list<R>(sl.c[0], a.lists[0], tile, (int)(valid < 0 ? 0 : (valid < R ? valid : R)),
+                           a.list_t, map.ok ? &a.h : nullptr, &map);
+        return;
+    }
 #pragma unroll
     for (int qi = 0; qi < Q; ++qi) {
         if (a.lists[qi]) {
@@ -331,6 +399,7 @@ __device__ inline ScoreMultiArgs single(const ScoreArgs &a)
     m.scores = a.scores;
     m.ld_scores = 0;
     m.list_t = a.list_t;
+    m.h = a.h;
     return m;
 }
 

@@ -4,6 +4,9 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+#include <chrono>
+
 #include "qsa_internal.h"
 #include "qsa_select.h"
 
@@ -92,12 +95,56 @@ int64_t decode_part_floats(const qsa_layer_desc *d)
 {
     const int G = d->q_heads / d->kv_heads;
     const int64_t max_cells = (int64_t)d->top_k_tokens + 3;
-    return (int64_t)d->kv_heads * n_splits(max_cells) * part_stride(G, d->head_dim);
+    const int64_t a = n_splits(max_cells) * part_stride(G, d->head_dim);
+    const int64_t b = (int64_t)kDecodeMaxSplits * dec_part_stride(G, d->head_dim);
+    return (int64_t)d->kv_heads * (a > b ? a : b);
 }
 
 WsLayout decode_layout(const qsa_layer_desc *d, int32_t capacity)
 {
-    return ws_layout(capacity / 4, d->top_k_tokens / 4, decode_part_floats(d));
+    return ws_layout(capacity / 4, d->top_k_tokens / 4, decode_part_floats(d), kDecodeMaxSplits,
+                     d->top_k_tokens / 4);
+}
+
+// The histogram window's lower end, in units of the score scale, when no
+// earlier call fed one back: half a unit below where the k-th largest of nb
+// normally distributed scores falls (the upper quantile k / nb, by bisection
+// on the normal tail).  Any value is exact; a window that misses only costs
+// that call the full top-k.
+float default_window_lo(int64_t nb, int64_t k)
+{
+    const double p = (double)k / (double)nb;        // < 1: there is a selection
+    double lo = -10.0, hi = 10.0;
+    for (int i = 0; i < 60; ++i) {
+        const double mid = 0.5 * (lo + hi);
+        if (0.5 * erfc(mid / sqrt(2.0)) > p)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    return (float)(0.5 * (lo + hi) - 0.5);
+}
+
+// A distinct 56-bit value per decode-step call in this process (never 0):
+// the score pass stamps the histogram region's tag with it and the attention
+// kernel trusts the region only under its own call's stamp, so a tag left in
+// a workspace by any earlier call never matches.
+uint64_t next_epoch()
+{
+    static std::atomic<uint64_t> ctr{0};
+    static const uint64_t base = [] {
+        uint64_t x = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+        x ^= (uint64_t)(uintptr_t)&ctr;
+        x ^= x >> 33;
+        x *= 0xff51afd7ed558ccdull;
+        x ^= x >> 33;
+        return x;
+    }();
+    uint64_t e;
+    do {
+        e = (base + ctr.fetch_add(1, std::memory_order_relaxed)) & ((1ull << 56) - 1);
+    } while (e == 0);
+    return e;
 }
 
 // Prefill-chunk workspace: folded queries, their scales, the keys of every
@@ -475,9 +522,24 @@ qsa_status qsa_decode_step(const qsa_layer_desc *desc, const qsa_layer_cache *ca
             return hip_fail(e, "decode_step/update");
     }
 
-    // 2. score every completed block (keys for the top-k)
+    // 2. score every completed block (keys for the top-k).  With a selection
+    //    the pass also fills the global histogram, from which one kernel
+    //    selects, attends and merges (k_decode.hip) when the shapes fit it.
     const int tile_rows = score_tile_rows(desc->idx_dtype == QSA_F16, rowb);
     const int32_t list_t = list_len(tile_rows, nb, K);
+    const int64_t ntiles = ((int64_t)nb + tile_rows - 1) / tile_rows;
+    const int G = desc->q_heads / desc->kv_heads;
+    int64_t ns = device_cus() / desc->kv_heads;
+    if (ns > kDecodeMaxSplits)
+        ns = kDecodeMaxSplits;
+    if (ns > ntiles)
+        ns = ntiles;
+    const bool hist_path = need_select && ns >= 1 &&
+                           ((ntiles + ns - 1) / ns) * list_t <= kDecodeThreads &&
+                           (int64_t)desc->kv_heads * ns <= kDecodeThreads &&
+                           sel::lds_bytes(nb) + decode_static_lds(desc->head_dim, G) <= sel::kMaxLds;
+    const uint64_t epoch = hist_path ? next_epoch() : 0;
+    const float def_lo = hist_path ? default_window_lo(nb, K) : 0.0f;
     if (score) {
         ScoreArgs a{};
         a.summary = cache->summary;
@@ -491,19 +553,49 @@ qsa_status qsa_decode_step(const qsa_layer_desc *desc, const qsa_layer_cache *ca
         a.D = desc->idx_dim;
         a.fuse = fuse ? 1 : 0;
         a.upd = u;
+        if (hist_path) {
+            a.h.hist = (uint32_t *)(wsp + L.hist);
+            a.h.bucket = (uint64_t *)(wsp + L.bucket);
+            a.h.last = (uint64_t *)(wsp + L.last);
+            a.h.ctrl = wsp + L.ctrl;
+            a.h.gamma = gamma;
+            a.h.epoch = epoch;
+            a.h.def_lo = def_lo;
+            a.h.def_hi = def_lo + 5.0f;
+        }
         e = launch_score(a, desc->idx_dtype == QSA_F16, rowb, stream);
         if (e != hipSuccess)
             return hip_fail(e, "decode_step/score");
     }
 
-    // 3 + 4. top-k (every block is kept when nb <= K), gather + attend.  When
-    //    the tile lists fit one workgroup and the attention grid fits one
-    //    workgroup per CU, every attention workgroup selects for itself (one
-    //    kernel; a second workgroup on a CU would halve the speed of both);
-    //    otherwise the select kernel runs first.
+    // 3 + 4. top-k (every block is kept when nb <= K), gather + attend.
     float *part = (float *)(wsp + L.part);
-    const int G = desc->q_heads / desc->kv_heads;
-    if (need_select) {
+    if (hist_path) {
+        DecodeArgs da{};
+        da.k = cache->k;
+        da.v = cache->v;
+        da.q = q;
+        da.out = out;
+        da.sel_out = sel_out;
+        da.nb = nb;
+        da.n_tail = n % 4;
+        da.kv_heads = desc->kv_heads;
+        da.k_blocks = K;
+        da.scale = attn_scale(desc);
+        da.sa = select_args(wsp, L, nb, K, tile_rows, list_t, nullptr);
+        da.hist = (const uint32_t *)(wsp + L.hist);
+        da.bucket = (const uint64_t *)(wsp + L.bucket);
+        da.last = (const uint64_t *)(wsp + L.last);
+        da.ctrl = wsp + L.ctrl;
+        da.ns = (int32_t)ns;
+        da.part = part;
+        da.stage = (int32_t *)(wsp + L.stage);
+        da.stage_n = (int32_t *)(wsp + L.stage_n);
+        da.epoch = epoch;
+        e = launch_decode_attend(da, desc->head_dim, G, stream);
+        if (e != hipSuccess)
+            return hip_fail(e, "decode_step/decode_attend");
+    } else if (need_select) {
         SelectArgs sa = select_args(wsp, L, nb, K, tile_rows, list_t, sel_out);
         // fused: the splits hold the 4K chosen cells, the merge adds the tail
         AttendArgs aa = attend_args(desc, cache, n, nullptr, K, q, out, part);

@@ -12,14 +12,20 @@ namespace qsa {
 constexpr int kWave = 64;           // CDNA wavefront width
 constexpr int kListDiv = 8;         // per-tile top-k lists keep R / 8 entries or more (up to R / 2)
 
-// Workspace carve-up.
+// Workspace carve-up.  The histogram region (decode step) is optional:
+// hist_splits > 0 sizes its per-split id staging.
 struct WsLayout {
-    size_t keys, lists, sel, part, total;
+    size_t keys, lists, sel, part;
+    size_t ctrl, hist, last, bucket, stage, stage_n;   // 0 without the histogram region
+    size_t total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-inline WsLayout ws_layout(int64_t max_blocks, int64_t sel_entries, int64_t part_floats)
+constexpr int kHistBins = 2048, kHistCap = 64, kHistLast = 64;   // qsa_hist.h
+
+inline WsLayout ws_layout(int64_t max_blocks, int64_t sel_entries, int64_t part_floats,
+                          int64_t hist_splits = 0, int64_t k_blocks = 0)
 {
     WsLayout L{};
     size_t off = 0;
@@ -28,16 +34,30 @@ inline WsLayout ws_layout(int64_t max_blocks, int64_t sel_entries, int64_t part_
         off = align256(off + bytes);
         return o;
     };
+    if (hist_splits > 0)
+        L.ctrl = take(256);     // first: the region's control words sit at a fixed offset
     L.keys = take(sizeof(uint32_t) * (size_t)max_blocks);
     L.lists = take(sizeof(uint64_t) * (size_t)((max_blocks + 1) / 2 + 64));
     L.sel = take(sizeof(int32_t) * (size_t)sel_entries);
     L.part = take(sizeof(float) * (size_t)part_floats);
+    if (hist_splits > 0) {
+        L.hist = take(sizeof(uint32_t) * kHistBins);
+        L.last = take(sizeof(uint64_t) * kHistLast);
+        L.bucket = take(sizeof(uint64_t) * (size_t)kHistBins * kHistCap);
+        L.stage = take(sizeof(int32_t) * (size_t)(hist_splits * k_blocks));
+        L.stage_n = take(sizeof(int32_t) * (size_t)hist_splits);
+    }
     L.total = off;
     return L;
 }
 
 // Floats of one attention partial: m[G], l[G], acc[G][Dh].
 __host__ __device__ inline int64_t part_stride(int G, int Dh) { return 2 * (int64_t)G + (int64_t)G * Dh; }
+// The decode-step kernel's partial: acc[G][Dh], m[G], l[G], padded to 16 bytes.
+__host__ __device__ inline int64_t dec_part_stride(int G, int Dh)
+{
+    return ((int64_t)G * Dh + 2 * (int64_t)G + 3) / 4 * 4;
+}
 
 // Cells handled by one attention workgroup.
 constexpr int kCellsPerSplit = 16;
@@ -69,6 +89,17 @@ struct UpdateArgs {
 };
 hipError_t launch_update(const UpdateArgs &a, bool f16, hipStream_t s);
 
+// Histogram insertion by the score pass (see qsa_hist.h); off when hist is null.
+struct HistOut {
+    uint32_t *hist;             // [hist::kBins] counts (cleared by the previous call)
+    uint64_t *bucket;           // [hist::kBins][hist::kCap] composites
+    uint64_t *last;             // [hist::kLast] maxima of the tiles' last list entries
+    void *ctrl;                 // hist::Ctrl: window feedback in, tag / sigma / window out
+    const float *gamma;         // [D] RMSNorm weights (for sigma)
+    uint64_t epoch;             // this call's epoch (the tag stamp)
+    float def_lo, def_hi;       // window in units of sigma when no feedback is usable
+};
+
 struct ScoreArgs {
     const void *summary;
     const float *q;
@@ -81,6 +112,7 @@ struct ScoreArgs {
     int32_t D;
     int32_t fuse;               // workgroup 0 first runs `upd` (append, pool <= 1 row)
     UpdateArgs upd;
+    HistOut h;                  // histogram insertion (lists required)
 };
 hipError_t launch_score(const ScoreArgs &a, bool f16, int row_bytes, hipStream_t s);
 
@@ -113,6 +145,7 @@ struct ScoreMultiArgs {
     float *scores;                  // optional [n_q][ld_scores]: -inf at b >= nbq[i]
     int64_t ld_scores;
     int32_t list_t;                 // T: entries per tile list (with lists)
+    HistOut h;                      // one query only: histogram insertion of its lists
 };
 hipError_t launch_score_multi(const ScoreMultiArgs &a, int n_q, bool f16, int row_bytes,
                               hipStream_t s);
@@ -148,6 +181,20 @@ struct SelectBatchArgs {
     SelectArgs seq[kMaxBatch];
 };
 hipError_t launch_select_batch(const SelectBatchArgs &b, hipStream_t s);
+
+// Order-preserving 32-bit key of an fp32 score: larger scores give larger
+// keys; -0 and +0 must compare equal, so -0 is folded into +0 first.
+__device__ inline uint32_t score_key(float s)
+{
+    const uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// The score an order-preserving key was made from (-0 was folded into +0).
+__device__ inline float key_score(uint32_t key)
+{
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
 
 __host__ __device__ inline uint64_t comp_key(uint32_t key, uint32_t id)
 {
@@ -195,6 +242,40 @@ hipError_t launch_merge_chunk(float *part, float *out, int n_q, int kv_heads, in
 // the chosen ids come from `sa`, sa.sel optionally receives them all).
 hipError_t launch_select_attend(const AttendArgs &a, const SelectArgs &sa, int Dh, int G,
                                 hipStream_t s);
+
+// Stages 3 + 4 of the decode step in one kernel after a score pass with
+// histogram insertion: grid (ns splits, kv_heads), 1024 threads.  Split s
+// owns the tiles [s ntiles / ns, (s + 1) ntiles / ns); it finds kappa from
+// the histogram, attends the cells of its own winners, publishes its partial
+// and a flag; the first workgroups of each KV head merge, one workgroup
+// clears the histogram for the next call.  Falls back to the full top-k of
+// qsa_select.h (every workgroup, slots dealt out evenly) when the histogram
+// cannot decide.
+constexpr int kDecodeThreads = 1024;
+constexpr int kDecodeMaxSplits = 128;
+struct DecodeArgs {
+    const uint16_t *k;
+    const uint16_t *v;
+    const float *q;
+    float *out;
+    int32_t *sel_out;           // optional: all chosen ids, ascending
+    int32_t nb, n_tail, kv_heads, k_blocks;
+    float scale;
+    SelectArgs sa;              // keys and tile lists of the score pass (sa.sel unused)
+    const uint32_t *hist;
+    const uint64_t *bucket;
+    const uint64_t *last;
+    void *ctrl;                 // hist::Ctrl
+    int32_t ns;                 // splits per KV head
+    float *part;                // [kv_heads][ns] partials
+    int32_t *stage;             // [ns][k_blocks] each split's winners, ascending (sel_out only)
+    int32_t *stage_n;           // [ns]
+    uint64_t epoch;             // unique per call
+};
+// The attention kernel (grid ns x kv_heads) and then the merge kernel.
+hipError_t launch_decode_attend(const DecodeArgs &a, int Dh, int G, hipStream_t s);
+// Static LDS bytes of that kernel (its dynamic LDS is the full top-k's, sel::lds_bytes(nb)).
+size_t decode_static_lds(int Dh, int G);
 
 // ------------------------------------------------------------ prefill chunk
 // n_q consecutive tokens of one sequence in one call: query i sits at position

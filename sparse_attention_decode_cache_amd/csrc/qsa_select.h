@@ -97,12 +97,6 @@ __host__ __device__ inline bool fits_fast(int32_t ntiles, int32_t T)
 __device__ inline uint64_t max64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ inline uint64_t min64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 
-// The score an order-preserving key was made from (-0 was folded into +0).
-__device__ inline float key_score(uint32_t key)
-{
-    return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
-}
-
 // Keys of finite scores: strictly between the keys of -inf and +inf.
 constexpr uint32_t kKeyFiniteLo = 0x00800000u;
 constexpr uint32_t kKeyFiniteHi = 0xFF7FFFFFu;

@@ -29,6 +29,8 @@ EXPORTS = ("qsa_workspace_bytes", "qsa_state_invalidate", "qsa_state_truncate",
 QSA_MAX_BATCH = 8
 QSA_MAX_CHUNK = 4096
 QSA_MAX_MULTI = 4
+QSA_DECODE_STATUS_OFFSET = 8        # byte offset of the decode step's status word in its workspace
+QSA_PATH_HIST, QSA_PATH_FULL = 1, 2
 
 
 class QSAError(RuntimeError):

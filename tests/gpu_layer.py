@@ -45,6 +45,12 @@ class GpuLayer:
         self.sel = torch.empty(w.k_blocks, dtype=torch.int32, device="cuda")
         self.scores = torch.empty(self.cap // 4, dtype=torch.float32, device="cuda")
 
+    def path(self):
+        """How the last selecting decode step chose its blocks (the low byte of
+        the workspace's status word): QSA_PATH_HIST or QSA_PATH_FULL."""
+        o = self.qsa.QSA_DECODE_STATUS_OFFSET
+        return int(self.ws[o:o + 8].cpu().numpy().view("<u8")[0] & 0xFF)
+
     def step(self, s):
         q = self.qsa
         q.qsa_decode_step(self.desc, self.buf.cache, self.state, self.inp.raw[s], self.inp.k[s],

@@ -20,6 +20,11 @@ def test_fullsize_decode_parity(w):
     g = GpuLayer(w)
     o = OracleMirror(w)
     stats = {"ulp_diffs": 0, "exact": 0, "threshold": 0, "attn_err": 0.0}
+    paths = []
     for s in range(w.steps):
         _compare_step(g, o, s, stats)
-    print(f"  {stats}")
+        paths.append(g.path())
+    print(f"  {stats} paths {paths}")
+    # the first step on a fresh workspace may not trust its histogram; after
+    # that, iid scores at these sizes are decided by the histogram path
+    assert all(p == g.qsa.QSA_PATH_HIST for p in paths[1:]), paths
