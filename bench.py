@@ -241,15 +241,18 @@ def multi_call_bytes(w, n0, n_q):
     return idx_row * nb_last + gathered + n_q * (idx_row + 2 * kv_row) + 5 * idx_row * new_blocks + queries
 
 
-def time_decode(torch, qsa, W, w, desc, stream, dev, steps, warmup, kernel_reps):
-    """12 layers of workload w (independent caches, round-robin): median
-    layer-step time over `steps` decode steps, and the score kernel's own time
-    (passes of back-to-back qsa_index_score launches over the same caches)."""
+def time_decode(torch, qsa, W, w, desc, stream, dev, steps, warmup, kernel_reps, n_layers=None):
+    """n_layers layers of workload w (independent caches, round-robin; default
+    w.layers): the mean layer-step time of `steps` decode steps captured in a
+    HIP graph (after `warmup` eager steps; one untimed replay, one timed), and
+    the score kernel's own time (passes of back-to-back qsa_index_score
+    launches over the same caches)."""
     import dataclasses
+    n_layers = n_layers or w.layers
     w = dataclasses.replace(w, steps=warmup + steps)
     cap = w.capacity()
     layers = []
-    for li in range(w.layers):
+    for li in range(n_layers):
         buf = qsa.LayerBuffers(desc, cap)
         W.dev_fill_layer_(w, buf, li, w.n0)
         gamma = W.dev_gamma(w, li)
@@ -258,21 +261,30 @@ def time_decode(torch, qsa, W, w, desc, stream, dev, steps, warmup, kernel_reps)
                        qsa.qsa_seq_state(w.n0, w.n0 // 4)))
     ws = qsa.workspace(desc, cap)
     out = torch.empty((w.q_heads, w.head_dim), dtype=torch.float32, device=dev)
+
+    def step(s, st):
+        for buf, gamma, inp, state in layers:
+            qsa.qsa_decode_step(desc, buf.cache, state, inp.raw[s], inp.k[s], inp.v[s], gamma,
+                                inp.q_idx[s], inp.w[s], inp.q[s], out, None, None, ws, st)
+
     for s in range(warmup):
-        for buf, gamma, inp, st in layers:
-            qsa.qsa_decode_step(desc, buf.cache, st, inp.raw[s], inp.k[s], inp.v[s], gamma,
-                                inp.q_idx[s], inp.w[s], inp.q[s], out, None, None, ws, stream)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        step(s, stream)
     torch.cuda.synchronize()
-    ev[0].record(stream)
-    for i in range(steps):
-        s = warmup + i
-        for buf, gamma, inp, st in layers:
-            qsa.qsa_decode_step(desc, buf.cache, st, inp.raw[s], inp.k[s], inp.v[s], gamma,
-                                inp.q_idx[s], inp.w[s], inp.q[s], out, None, None, ws, stream)
-        ev[i + 1].record(stream)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cs = torch.cuda.current_stream()
+        for i in range(steps):
+            step(warmup + i, cs)
     torch.cuda.synchronize()
-    step_us = statistics.median(1e3 * ev[i].elapsed_time(ev[i + 1]) / len(layers) for i in range(steps))
+    graph.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    graph.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    step_us = 1e3 * a.elapsed_time(b) / (steps * n_layers)
+    del graph
     nb = layers[0][3].n_tokens // 4
     scores = torch.empty(nb, dtype=torch.float32, device=dev)
     durs = []
@@ -287,27 +299,49 @@ def time_decode(torch, qsa, W, w, desc, stream, dev, steps, warmup, kernel_reps)
     score_us = statistics.mean(1e3 * a.elapsed_time(b) / len(layers) for a, b in durs[1:])
     del layers, ws
     torch.cuda.empty_cache()
-    return step_us, score_us
+    return step_us, score_us, nb
+
+
+# Context points of the sweep: (tokens in the cache, layers).  Below 256k more
+# layer replicas than the headline's 12, so that every point's pooled keys
+# (1 KB per block per layer) exceed twice the 256 MB last-level cache and each
+# step streams them from HBM.
+SWEEP_POINTS = ((61789, 36), (126253, 18), (300000, 12), (524000, 12))
 
 
 def bench_context_sweep(args, torch, qsa, W, w256, desc, stream, dev, head):
-    """The same 12-layer decode at 61,789 and 126,253 tokens beside the 256k
-    headline: the score pass grows with the context (one read of every
-    summary), the rest of the step (top-k over the tile lists, gather +
-    attention of at most 2,051 cells, merge) should not."""
+    """The decode step at 61,789 / 126,253 / 300,000 / 524,000 tokens beside
+    the 255,181-token headline, every point streaming its pooled keys from
+    HBM: the score pass grows with the context (one read of every summary),
+    the rest of the step (selection, gather + attention of at most 2,051
+    cells, merge) should not.  A least-squares line t = a + c N_b over the
+    points gives the per-block cost c and the context-independent part a."""
     import dataclasses
     res = {}
-    for n0 in (61789, 126253):
+    for n0, nl in SWEEP_POINTS:
         w = dataclasses.replace(w256, n0=n0)
-        step_us, score_us = time_decode(torch, qsa, W, w, desc, stream, dev, args.sweep_steps, 4,
-                                        args.kernel_reps)
-        res[str(n0)] = {"layer_step_us": round(step_us, 2), "score_us": round(score_us, 2),
-                        "rest_us": round(step_us - score_us, 2)}
-    res[str(w256.n0)] = {"layer_step_us": head["layer_step_us"]["median"],
+        step_us, score_us, nb = time_decode(torch, qsa, W, w, desc, stream, dev, args.sweep_steps, 4,
+                                            args.kernel_reps, n_layers=nl)
+        res[str(n0)] = {"layers": nl, "n_blocks": nb, "layer_step_us": round(step_us, 2),
+                        "score_us": round(score_us, 2), "rest_us": round(step_us - score_us, 2)}
+        log(f"context {n0} x {nl} layers: {res[str(n0)]}")
+    res[str(w256.n0)] = {"layers": w256.layers, "n_blocks": head["nb"],
+                         "layer_step_us": head["layer_step_us"]["mean"],
                          "score_us": head["roofline"]["avg_launch_us"],
-                         "rest_us": round(head["layer_step_us"]["median"] - head["roofline"]["avg_launch_us"], 2)}
-    log(f"context sweep: {res}")
-    return {"workload": "12 layers x {61789, 126253, 255181} tokens, headline layer shapes", "by_context": res,
+                         "rest_us": round(head["layer_step_us"]["mean"] - head["roofline"]["avg_launch_us"], 2)}
+    pts = sorted(res.values(), key=lambda r: r["n_blocks"])
+    xs = [float(r["n_blocks"]) for r in pts]
+    ys = [float(r["layer_step_us"]) for r in pts]
+    mx, my = sum(xs) / len(xs), sum(ys) / len(ys)
+    c = sum((x - mx) * (y - my) for x, y in zip(xs, ys)) / sum((x - mx) ** 2 for x in xs)
+    a = my - c * mx
+    fit = {"a_us": round(a, 3), "c_ns_per_block": round(1e3 * c, 4),
+           "implied_GBs_per_block_stream": round(1024 / (1e3 * c), 1) if c > 0 else None,
+           "max_residual_us": round(max(abs(y - (a + c * x)) for x, y in zip(xs, ys)), 3)}
+    log(f"context sweep fit: {fit}")
+    return {"workload": "decode step at 61,789 (36 layers) / 126,253 (18) / 255,181 (12) / "
+                        "300,000 (12) / 524,000 (12) tokens, headline layer shapes, HIP graph",
+            "by_context": res, "fit_t_eq_a_plus_c_Nb": fit,
             "note": "rest_us = layer step - score kernel (the score kernel's own time, scores only)"}
 
 
@@ -726,7 +760,9 @@ def main():
         return
 
     w0 = W.WORKLOADS[args.workload]
-    total = args.warmup + args.steps
+    # eager warmup, eager timed steps, then the same number of steps again
+    # captured in a HIP graph (replayed once untimed, once timed)
+    total = args.warmup + 2 * args.steps
     import dataclasses
     w = dataclasses.replace(w0, steps=total)
     cap = w.capacity()
@@ -750,11 +786,11 @@ def main():
     torch.cuda.synchronize()
     log(f"{w.name}: {w.layers} layers, capacity {cap}, set up in {time.time() - t0:.1f}s")
 
-    def layer_step(L, s):
+    def layer_step(L, s, st=stream):
         inp = L["inp"]
         qsa.qsa_decode_step(desc, L["buf"].cache, L["state"], inp.raw[s], inp.k[s], inp.v[s],
                             L["gamma"], inp.q_idx[s], inp.w[s], inp.q[s], L["out"], None, None, ws,
-                            stream)
+                            st)
 
     for s in range(args.warmup):
         for L in layers:
@@ -762,24 +798,47 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
+    # eager: every call launched from the host as it comes
     events = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    nbytes = 0
     torch.cuda.synchronize()
     events[0].record(stream)
     for i in range(args.steps):
         s = args.warmup + i
         for L in layers:
-            n = L["state"].n_tokens + 1
-            nbytes += layer_step_bytes(w, n)
             layer_step(L, s)
         events[i + 1].record(stream)
     torch.cuda.synchronize()
     step_ms = [events[i].elapsed_time(events[i + 1]) for i in range(args.steps)]
-    total_ms = events[0].elapsed_time(events[-1])
+    eager_ms = events[0].elapsed_time(events[-1])
     layer_steps = args.steps * w.layers
+    eager_value = layer_steps / (eager_ms / 1e3)
+    log(f"eager: {args.steps} steps in {eager_ms:.3f} ms, {eager_value:.0f} layer-steps/s")
+
+    # graph: the next `steps` steps of every layer captured once (each call's
+    # arguments fixed at capture, as the host computed them), replayed as one
+    # launch; a replay repeats exactly those steps (same rows, same queries)
+    nbytes = 0
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cs = torch.cuda.current_stream()
+        for i in range(args.steps):
+            s = args.warmup + args.steps + i
+            for L in layers:
+                nbytes += layer_step_bytes(w, L["state"].n_tokens + 1)
+                layer_step(L, s, cs)
+    torch.cuda.synchronize()
+    graph.replay()                      # untimed: first replay
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = g0.elapsed_time(g1)
     value = layer_steps / (total_ms / 1e3)
     step_gbs = nbytes / (total_ms / 1e3) / 1e9
-    log(f"timed {args.steps} steps: {total_ms:.3f} ms, {value:.0f} layer-steps/s, {step_gbs:.0f} GB/s")
+    log(f"graph: {args.steps} steps in {total_ms:.3f} ms, {value:.0f} layer-steps/s, {step_gbs:.0f} GB/s")
+    del graph
 
     # Dominant kernel: the block-score stream.  Same kernel and grid as inside the
     # decode step, launched through qsa_index_score on the same stream over the
@@ -823,9 +882,13 @@ def main():
                    "layer_steps_per_step": w.layers, "idx": f"{w.idx_heads}x{w.idx_dim} "
                    f"{'f16' if w.idx_f16 else 'f32'}", "attn": f"{w.q_heads}/{w.kv_heads}x{w.head_dim} f16",
                    "top_k_tokens": w.top_k_tokens, "storage": "f16", "accumulate": "f32"},
-        "layer_step_us": {"median": round(1e3 * statistics.median(step_ms) / w.layers, 3),
-                          "p10": round(1e3 * sorted(step_ms)[len(step_ms) // 10] / w.layers, 3),
-                          "p90": round(1e3 * sorted(step_ms)[(9 * len(step_ms)) // 10] / w.layers, 3)},
+        "launch": "hip graph (the timed steps captured once, replayed)",
+        "layer_step_us": {"mean": round(1e3 * total_ms / layer_steps, 3)},
+        "eager": {"value": round(eager_value, 1), "ms_per_step": round(eager_ms / args.steps, 4),
+                  "layer_step_us": {
+                      "median": round(1e3 * statistics.median(step_ms) / w.layers, 3),
+                      "p10": round(1e3 * sorted(step_ms)[len(step_ms) // 10] / w.layers, 3),
+                      "p90": round(1e3 * sorted(step_ms)[(9 * len(step_ms)) // 10] / w.layers, 3)}},
         "step_hbm": {"achieved": round(step_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(step_gbs / HBM_PEAK_GBS, 4),
                      "bytes_per_layer_step": round(nbytes / layer_steps)},
@@ -834,16 +897,17 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "bytes_per_launch": kbytes,
                      "avg_launch_us": round(1e6 * k_avg_s, 3)},
+        "nb": nb,
         "cpu_baseline": None,
         "batch_and_chunk": None,
         "context_sweep": None,
     }
     if not args.no_multi:
         result["multi_decode"] = bench_multi(args, torch, qsa, w, desc, layers, stream, dev,
-                                             result["layer_step_us"]["median"])
+                                             result["eager"]["layer_step_us"]["median"])
     if not args.no_ablations:
         result["ablations"] = bench_ablations(args, torch, qsa, w, desc, layers, ws, stream, dev,
-                                              result["layer_step_us"]["median"])
+                                              result["eager"]["layer_step_us"]["median"])
     if not args.no_q8:
         result["q8_0_kv"] = bench_q8(args, torch, qsa, w, desc, layers, ws, stream, dev)
     del layers, ws                      # the 256k caches: the legs below allocate their own

@@ -11,21 +11,19 @@
 // cells of the winners among its tiles' list entries.  The kernel is bound by
 // latency, and with 16 waves on a CU every instruction all of them execute
 // costs 16 cycles, so each phase runs on the waves that need it:
-//   1. one round of loads: waves 0-3 the 2048-bin histogram (8 bins a lane,
-//      top bins first), wave 4 the tiles' last-entry maxima, thread t the
-//      split's list entry t, waves 8-15 the q operand;
-//   2. waves 0-3 count the bins from the top: the bin d holding the k-th
-//      largest entry, how many of bin d win (`need`), the top nonempty bin;
-//   3. the split's entries in bins above d win, those in bin d are
-//      candidates: both go to its block list (ballot compaction) with their
-//      composites, and the last split adds its tail cells 4 nb + j
-//      (j < n mod 4) as a block of their own; wave 0 loads bin d's bucket;
+//   1. one round of loads: thread t two bins of the histogram (count and
+//      extremes, top bins first), wave 4 the tiles' last-entry maxima,
+//      thread t the split's list entry t, waves 8-15 the q operand;
+//   2. a prefix sum over the threads finds the bin d holding the k-th
+//      largest entry, how many of bin d win (`need`), kappa from the bin's
+//      extremes and the top nonempty bin;
+//   3. the split's entries >= kappa win: they go to its block list (ballot
+//      compaction), and the last split adds its tail cells 4 nb + j
+//      (j < n mod 4) as a block of their own;
 //   4. 16 threads per cell load its K and V rows (one address per thread);
-//      wave 0 ranks the bucket meanwhile (kappa = the need-th largest); K
-//      and V land in separate LDS tiles;
+//      K and V land in separate LDS tiles;
 //   5. a wave per 16 cells takes their G logits on the matrix cores (q as
-//      f16 hi + lo), a cell counting only if its block's composite is >=
-//      kappa; waves h < G run the online softmax of head h; every wave takes
+//      f16 hi + lo); waves h < G run the online softmax of head h; every wave takes
 //      P.V for its 16-dim output tiles on the matrix cores (passes of up to
 //      64 cells, k-steps only over the pass's cells);
 //   6. the partial (acc, m, l) and, when the ids are wanted, the split's
@@ -37,9 +35,9 @@
 // splits publish, was measured slower on gfx950: coherent stores, their
 // waits and the polling cost more than a kernel boundary.)
 // The histogram decides exactly when its region started this call cleared,
-// at least k entries reached the window, bin d's bucket holds all of its
-// entries and no tile list can hide a winner (the largest last entry of a
-// full list lies below the window or in a bin below d).  Otherwise every
+// at least k entries reached the window, bin d is split all-or-one (so that
+// its extremes give kappa) and no tile list can hide a winner (the largest
+// last entry of a full list is below kappa).  Otherwise every
 // workgroup runs the full top-k of qsa_select.h over the keys and takes an
 // even share of the chosen blocks.  No workgroup waits on another.
 #include "qsa_hist.h"
@@ -52,19 +50,16 @@ namespace {
 
 constexpr int kNT = kDecodeThreads;
 constexpr int kNW = kNT / kWave;
-constexpr int kPC = 64;                          // cells per pass
+constexpr int kNA = kNT / 2;                     // threads that attend (waves 0-7)
+constexpr int kNAW = kNA / kWave;
+constexpr int kPC = 64;                          // cells per pass (two per 16 threads)
 constexpr int kMaxOwn = kNT;                     // blocks a split attends at most
-static_assert(hist::kBins == 8 * 256, "waves 0-3 scan the histogram, 8 bins a lane");
 static_assert(kNT == sel::kT, "the full top-k runs in the same workgroup");
-static_assert(hist::kCap <= kWave, "wave 0 ranks a bucket");
+static_assert(hist::kBins == 4 * kNA, "thread t < 512 scans four bins");
+static_assert(kNW == 16 && kNAW == 8 && kPC == 2 * (kNA / 16), "wave counts the phases assume");
 static_assert(offsetof(hist::Ctrl, status) == QSA_DECODE_STATUS_OFFSET && hist::kPathFast == QSA_PATH_HIST &&
                   hist::kPathFull == QSA_PATH_FULL,
               "the status word as the header documents it");
-// Margins of the fed-back window, in units of sigma: below kappa (the next
-// query's kappa / sigma moves by a few hundredths for scores of independent
-// rows) and above the top entry.
-constexpr float kWindowBelow = 0.3f;
-constexpr float kWindowAbove = 0.5f;
 // The full top-k's LDS for up to 2^19 blocks (it overlays the K / V tiles).
 constexpr size_t kFullLds = (sizeof(sel::Smem) + 15) / 16 * 16 + 4 * ((size_t)1 << 19) / 32;
 
@@ -78,7 +73,7 @@ struct DecShape {
     static constexpr int CH = DH / 8;            // 16-byte chunks of a row
     static constexpr int CPT = (CH + 15) / 16;   // chunks per thread (16 threads per cell)
     static constexpr int NT = DH / 16;           // 16-dim output tiles of P.V
-    static constexpr int TPW = (NT + kNW - 1) / kNW;
+    static constexpr int TPW = (NT + kNAW - 1) / kNAW;
     static constexpr size_t TILE = (size_t)kPC * KROW;
 };
 
@@ -90,16 +85,16 @@ struct DecLds {
     alignas(16) uint4 qb[S::KS][2][kWave];
     float lg[kPC][G + 1];
     alignas(16) _Float16 pt[2][G][kPC];          // softmax weights, hi and lo halves, [head][cell]
-    float sc[G], mrow[G], lrow[G];
-    int32_t ids[kMaxOwn];                        // the split's blocks
-    uint64_t comp[kMaxOwn];                      // their composites (~0: kept outright)
-    uint32_t wcnt[kNW], wtot[kNW];
+    float sc[G];
+    int32_t ids[kMaxOwn + 1];                    // the split's blocks (and the tail)
+    alignas(16) uint32_t wcnt[2 * kNAW];         // winners per wave, entries t and 512 + t
+    alignas(16) uint32_t wtot[kNW];              // histogram counts per wave (waves 0-7)
     uint32_t d, need, in_d, found, nown, btop, kmin_w, kmax_w;
     uint64_t kappa, lastmax;
 };
 
-// The K and V chunks one thread loads in a pass: cell (lc) of pass p, its
-// 16-byte chunks sub + 16 j (returned by value, so they stay in registers).
+// The K and V chunks of one cell a thread loads: chunks sub + 16 j of the
+// cell's rows (returned by value, so they stay in registers).
 template <int N>
 struct RowChunks {
     uint4 k[N], v[N];
@@ -107,11 +102,10 @@ struct RowChunks {
 
 template <int DH>
 __device__ inline RowChunks<DecShape<DH>::CPT> load_rows(const DecodeArgs &a, const int32_t *ids, int ncell,
-                                                         int p, int lc, int sub, int g)
+                                                         int c, int sub, int g)
 {
     using S = DecShape<DH>;
     RowChunks<S::CPT> r;
-    const int c = kPC * p + lc;
     if (c < ncell) {
         const int32_t b = ids[c >> 2];
         const size_t row = ((size_t)(4 * (int64_t)b + (c & 3)) * a.kv_heads + (size_t)g) * DH;
@@ -127,15 +121,48 @@ __device__ inline RowChunks<DecShape<DH>::CPT> load_rows(const DecodeArgs &a, co
     return r;
 }
 
+// Cell `lc` of a pass into the LDS tiles.  V rows of cells that do not count
+// (past the pass's cells, up to the last k-step, and the tail block's cells
+// past the tail) are zeroed: their weight is 0, and 0 times whatever is there
+// could be NaN; their K rows are left alone (those logits become -inf).
+template <int DH, int CPT>
+__device__ inline void put_rows(unsigned char *ktile, unsigned char *vtile, const RowChunks<CPT> &kv, int lc,
+                                int sub, bool live)
+{
+    using S = DecShape<DH>;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j)
+        if (sub + 16 * j < S::CH) {
+            if (live)
+                *(uint4 *)(ktile + lc * S::KROW + 16 * (sub + 16 * j)) = kv.k[j];
+            *(uint4 *)(vtile + lc * S::KROW + 16 * (sub + 16 * j)) = live ? kv.v[j] : make_uint4(0u, 0u, 0u, 0u);
+        }
+}
+
+// Sum of v[i] over i < n (n <= 16, wave-uniform) of 16 words read as uint4.
+__device__ inline uint32_t sum_below(const uint32_t *v, int n)
+{
+    const uint4 *v4 = reinterpret_cast<const uint4 *>(v);
+    uint32_t s = 0;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+        const uint4 x = v4[q4];
+        s += (4 * q4 + 0 < n ? x.x : 0u) + (4 * q4 + 1 < n ? x.y : 0u) + (4 * q4 + 2 < n ? x.z : 0u) +
+             (4 * q4 + 3 < n ? x.w : 0u);
+    }
+    return s;
+}
+
 template <int DH, int G>
 __global__ __launch_bounds__(kNT) void k_decode_attend(DecodeArgs a)
 {
     using S = DecShape<DH>;
-    constexpr int KS = S::KS, KROW = S::KROW, CH = S::CH, CPT = S::CPT, NT = S::NT, TPW = S::TPW;
+    constexpr int KS = S::KS, KROW = S::KROW, CPT = S::CPT, NT = S::NT, TPW = S::TPW;
     extern __shared__ uint4 dec_lds[];
     DecLds<DH, G> &L = *reinterpret_cast<DecLds<DH, G> *>(dec_lds);
     unsigned char *ktile = L.tiles, *vtile = L.tiles + S::TILE;
-    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(t >> 6);
     const int s = blockIdx.x, g = blockIdx.y;
     const int ns = a.ns;
     const int T = a.sa.T;
@@ -148,20 +175,29 @@ __global__ __launch_bounds__(kNT) void k_decode_attend(DecodeArgs a)
     // ---- 1. first-round loads, by role
     const uint64_t tag = ctrl->tag;
     const hist::Map map = hist::stored_map(*ctrl);
-    uint32_t hv[8];                                 // waves 0-3: bins 8 (255 - t) + j
-    if (t < 256) {
-        const uint4 *h4 = reinterpret_cast<const uint4 *>(a.hist) + 2 * (255 - t);
-        const uint4 u = h4[0], v = h4[1];
-        hv[0] = u.x, hv[1] = u.y, hv[2] = u.z, hv[3] = u.w;
-        hv[4] = v.x, hv[5] = v.y, hv[6] = v.z, hv[7] = v.w;
+    // waves 0-7, thread t: bins b0 + 3 .. b0 (b0 = 2044 - 4t), so that
+    // counts summed over threads in order run from the top bin down
+    const int b0 = hist::kBins - 4 - 4 * t;
+    uint4 hc = make_uint4(0u, 0u, 0u, 0u);
+    ulonglong2 mx01{}, mx23{}, mn01{}, mn23{};
+    uint64_t ent0 = 0, ent1 = 0;                    // list entries t and 512 + t
+    if (t < kNA) {
+        hc = *reinterpret_cast<const uint4 *>(a.hist + b0);
+        mx01 = *reinterpret_cast<const ulonglong2 *>(a.bmax + b0);
+        mx23 = *reinterpret_cast<const ulonglong2 *>(a.bmax + b0 + 2);
+        mn01 = *reinterpret_cast<const ulonglong2 *>(a.bminc + b0);
+        mn23 = *reinterpret_cast<const ulonglong2 *>(a.bminc + b0 + 2);
+        if (t < nent)
+            ent0 = a.sa.lists[(size_t)tile0 * T + t];
+        if (kNA + t < nent)
+            ent1 = a.sa.lists[(size_t)tile0 * T + kNA + t];
     }
-    uint64_t lm = wv == 4 ? a.last[lane] : 0ull;
-    const uint64_t ent = t < nent ? a.sa.lists[(size_t)tile0 * T + t] : 0ull;
-    if (t >= kNT / 2) {
+    uint64_t lm = wv == 8 ? a.last[lane] : 0ull;
+    if (t >= kNA) {
         // q of the group's G heads as the logit MFMA's B operand: slot x =
         // (k-step, lane) holds q[head x % 16][32 ks + 8 (x % 64 / 16) .. +8],
         // zero past G, as f16 hi and lo halves
-        const int x = t - kNT / 2;
+        const int x = t - kNA;
         if (x < KS * kWave) {
             const int ks = x / kWave, l = x % kWave, hq = l % 16, d0 = 32 * ks + 8 * (l / 16);
             float4 u = make_float4(0.0f, 0.0f, 0.0f, 0.0f), v = u;
@@ -182,19 +218,17 @@ __global__ __launch_bounds__(kNT) void k_decode_attend(DecodeArgs a)
         }
     }
 
-    // ---- 2. waves 0-3: their bins' counts from the top (wave prefix sums);
-    //         wave 4: the largest last entry; the waves holding list entries:
-    //         which are inside the window (their blocks' rows are loaded at once,
-    //         before kappa is known: the winners are among them)
+    // ---- 2. waves 0-7: counts from the top (wave prefix sums, then the
+    //         waves before); the thread whose bins reach k finds bin d, how
+    //         many of it win (`need`) and kappa from the bin's extremes;
+    //         wave 8: the largest last entry
     uint32_t cnt = 0, incl = 0;
-    if (t < 256) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            cnt += hv[j];
+    if (t < kNA) {
+        cnt = hc.x + hc.y + hc.z + hc.w;
         incl = wave::incl_scan_add(cnt);
         if (lane == 63)
             L.wtot[wv] = incl;
-    } else if (wv == 4) {
+    } else if (wv == 8) {
         lm = wave::reduce_max_u64(lm);
         if (lane == 0)
             L.lastmax = lm;
@@ -202,33 +236,37 @@ __global__ __launch_bounds__(kNT) void k_decode_attend(DecodeArgs a)
     if (t == 0) {
         L.found = 0u;
         L.btop = 0u;
-        L.kappa = 0ull;
+        L.kappa = ~0ull;
         L.kmin_w = 0xFFFFFFFFu;
         L.kmax_w = 0u;
     }
     __syncthreads();                                                    // barrier
-    if (t < 256) {
-        uint32_t above = incl - cnt;
-        for (int w = 0; w < wv; ++w)
-            above += L.wtot[w];
-        const uint32_t b0 = 8u * (uint32_t)(255 - t);
+    if (t < kNA) {
+        const uint32_t above = incl - cnt + sum_below(L.wtot, wv);
+        const uint32_t hv[4] = {hc.x, hc.y, hc.z, hc.w};
+        const uint64_t mx[4] = {mx01.x, mx01.y, mx23.x, mx23.y};
+        const uint64_t mnc[4] = {mn01.x, mn01.y, mn23.x, mn23.y};
         if (above == 0 && cnt > 0) {
-            uint32_t bt = b0;
+            uint32_t bt = (uint32_t)b0;
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < 4; ++j)
                 if (hv[j] != 0u)
-                    bt = b0 + (uint32_t)j;
+                    bt = (uint32_t)(b0 + j);
             L.btop = bt;
         }
         if (above < k && above + cnt >= k) {
             uint32_t acc = above, dd = 0, nd = 0, id = 0;
+            uint64_t kx = 0;
             bool seek = true;
 #pragma unroll
-            for (int j = 7; j >= 0; --j) {
+            for (int j = 3; j >= 0; --j) {
                 if (seek && acc + hv[j] >= k) {
-                    dd = b0 + (uint32_t)j;
+                    dd = (uint32_t)(b0 + j);
                     nd = k - acc;
                     id = hv[j];
+                    // all of bin d win: kappa is its smallest; one wins: its
+                    // largest; any other split is left to the full top-k
+                    kx = nd == id ? ~mnc[j] : mx[j];
                     seek = false;
                 }
                 acc += hv[j];
@@ -236,54 +274,44 @@ __global__ __launch_bounds__(kNT) void k_decode_attend(DecodeArgs a)
             L.d = dd;
             L.need = nd;
             L.in_d = id;
-            L.found = 1u;
+            L.kappa = kx;
+            L.found = (nd == id || nd == 1u) ? 1u : 2u;
         }
     }
     __syncthreads();                                                    // barrier
-    const uint32_t d = L.d, need = L.need, in_d = L.in_d;
-    const uint32_t lastkey = (uint32_t)(L.lastmax >> 32);
-    const bool fast = tag == hist::tag_ok(a.epoch) && L.found != 0u && in_d <= (uint32_t)hist::kCap &&
-                      map.ok && (!hist::in_window(lastkey, map) || hist::bin_of(lastkey, map) < d);
+    const uint64_t kappa = L.kappa;
+    // a list of T entries hides no winner when its last entry is below kappa
+    const bool fast = tag == hist::tag_ok(a.epoch) && L.found == 1u && map.ok && L.lastmax < kappa;
     // the last split also takes the tail cells 4 nb + j (j < n_tail) as a
     // block of its own (id nb)
     const bool tail_here = s == ns - 1 && a.n_tail > 0;
 
-    // ---- 3. the split's blocks: its entries in bins from d up (those in bin d
-    //         are candidates until kappa is known), in list order (ballot
-    //         compaction); or the full top-k, split s taking the chosen slots
-    //         [s per, s per + per)
-    uint64_t bc = 0;                                // wave 0: an entry of bin d's bucket
+    // ---- 3. the split's blocks: its list entries >= kappa (the winners), in
+    //         list order (ballot compaction); or the full top-k, split s
+    //         taking the chosen slots [s per, s per + per).  From here on
+    //         waves 0-7 carry on alone (the rest end: barriers then count
+    //         only the waves still running).
     if (fast) {
-        bool mine = false;
-        if (t < nent && ent != 0ull) {
-            const uint32_t key = (uint32_t)(ent >> 32);
-            mine = hist::in_window(key, map) && hist::bin_of(key, map) >= d;
+        if (wv >= kNAW)
+            return;
+        const bool m0 = ent0 != 0ull && ent0 >= kappa, m1 = ent1 != 0ull && ent1 >= kappa;
+        const uint64_t bal0 = __ballot(m0), bal1 = __ballot(m1);
+        const uint32_t p0 = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal0 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal0, 0u));
+        const uint32_t p1 = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal1 >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal1, 0u));
+        if (lane == 0) {
+            L.wcnt[wv] = (uint32_t)__popcll(bal0);
+            L.wcnt[kNAW + wv] = (uint32_t)__popcll(bal1);
         }
-        const uint64_t bal = __ballot(mine);
-        const uint32_t wpos = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-        if (lane == 0)
-            L.wcnt[wv] = (uint32_t)__popcll(bal);
-        if (wv == 0 && (uint32_t)lane < in_d)
-            bc = a.bucket[(size_t)d * hist::kCap + lane];
         __syncthreads();                                                // barrier
-        if (mine) {
-            uint32_t off = 0;
-            for (int w = 0; w < wv; ++w)
-                off += L.wcnt[w];
-            L.ids[off + wpos] = (int32_t)(~(uint32_t)ent);
-            L.comp[off + wpos] = ent;
-        }
+        const uint32_t tot0 = sum_below(L.wcnt, kNAW);
+        if (m0)
+            L.ids[sum_below(L.wcnt, wv) + p0] = (int32_t)(~(uint32_t)ent0);
+        if (m1)
+            L.ids[tot0 + sum_below(L.wcnt + kNAW, wv) + p1] = (int32_t)(~(uint32_t)ent1);
         if (t == 0) {
-            uint32_t tot = 0;
-#pragma unroll
-            for (int w = 0; w < kNW; ++w)
-                tot += L.wcnt[w];
-            if (tail_here) {
-                L.ids[tot] = a.nb;
-                L.comp[tot] = ~0ull;
-                ++tot;
-            }
+            uint32_t tot = tot0 + sum_below(L.wcnt + kNAW, kNAW);
+            if (tail_here)
+                L.ids[tot++] = a.nb;
             L.nown = tot;
         }
         __syncthreads();                                                // barrier
@@ -292,14 +320,11 @@ __global__ __launch_bounds__(kNT) void k_decode_attend(DecodeArgs a)
         const uint32_t s0 = (uint32_t)s * per;
         int32_t *all = (s == 0 && g == 0) ? a.sel_out : nullptr;
         int32_t *ids = L.ids;
-        uint64_t *comp = L.comp;
         const uint32_t *keys = (s == ns - 1 && g == a.kv_heads - 1) ? a.sa.keys : nullptr;   // the window feedback
         uint32_t *kmin = &L.kmin_w, *kmax = &L.kmax_w;
         sel::run(a.sa, reinterpret_cast<char *>(L.tiles), [=](uint32_t slot, uint32_t id) {
-            if (slot - s0 < per) {
+            if (slot - s0 < per)
                 ids[slot - s0] = (int32_t)id;
-                comp[slot - s0] = ~0ull;
-            }
             if (all)
                 all[slot] = (int32_t)id;
             if (keys) {
@@ -310,31 +335,24 @@ __global__ __launch_bounds__(kNT) void k_decode_attend(DecodeArgs a)
         });
         if (t == 0) {
             uint32_t tot = s0 < k ? (k - s0 < per ? k - s0 : per) : 0u;
-            if (tail_here) {
-                L.ids[tot] = a.nb;
-                L.comp[tot] = ~0ull;
-                ++tot;
-            }
+            if (tail_here)
+                L.ids[tot++] = a.nb;
             L.nown = tot;
         }
         __syncthreads();                                                // barrier
+        if (wv >= kNAW)
+            return;
     }
     const uint32_t nown = L.nown;
     const int ncell = 4 * (int)nown;
     const int npass = (ncell + kPC - 1) / kPC;
 
-    // ---- 4. K / V rows of the split's cells: thread t takes cell (t / 16) of
-    //         the pass, 16-byte chunks (t % 16) + 16 j of its K and V rows
+    // ---- 4. K / V rows of the split's cells: thread t takes cells t / 16 and
+    //         t / 16 + 32 of the pass, 16-byte chunks (t % 16) + 16 j of each
+    //         one's K and V rows
     const int lc = t >> 4, sub = t & 15;
-    RowChunks<CPT> kv = load_rows<DH>(a, L.ids, ncell, 0, lc, sub, g);
-    if (fast && wv == 0) {
-        // rank bin d's entries by counting: kappa = the need-th largest
-        uint32_t r = 0;
-        for (uint32_t i = 0; i < in_d; ++i)
-            r += wave::readlane64(bc, (int)i) > bc ? 1u : 0u;
-        if ((uint32_t)lane < in_d && r == need - 1u)
-            L.kappa = bc;
-    }
+    RowChunks<CPT> kv0 = load_rows<DH>(a, L.ids, ncell, lc, sub, g);
+    RowChunks<CPT> kv1 = load_rows<DH>(a, L.ids, ncell, lc + kPC / 2, sub, g);
 
     // ---- 5. attention in passes of up to 64 cells
     const int hn = lane & 15, kq = lane >> 4;
@@ -344,26 +362,20 @@ __global__ __launch_bounds__(kNT) void k_decode_attend(DecodeArgs a)
         acc[i] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
     float m_run = -INFINITY, l_run = 0.0f;          // wave h < G: head h
     for (int p = 0; p < npass; ++p) {
-        if (p > 0)
-            kv = load_rows<DH>(a, L.ids, ncell, p, lc, sub, g);
+        if (p > 0) {
+            kv0 = load_rows<DH>(a, L.ids, ncell, kPC * p + lc, sub, g);
+            kv1 = load_rows<DH>(a, L.ids, ncell, kPC * p + lc + kPC / 2, sub, g);
+        }
         const int np = ncell - kPC * p < kPC ? ncell - kPC * p : kPC;   // cells of this pass
         const int nks = (np + 31) / 32;                                  // P.V k-steps
-        // V rows of cells that do not count (past the pass's cells, up to the
-        // last k-step, and the tail block's cells past the tail) are zeroed:
-        // their weight is 0, and 0 times whatever is there could be NaN; their
-        // K rows are left alone (those logits are replaced by -inf)
-        const bool live = lc < np && !(L.ids[(kPC * p + lc) >> 2] == a.nb && (lc & 3) >= a.n_tail);
-        if (lc < 32 * nks) {
-#pragma unroll
-            for (int j = 0; j < CPT; ++j)
-                if (sub + 16 * j < CH) {
-                    if (live)
-                        *(uint4 *)(ktile + lc * KROW + 16 * (sub + 16 * j)) = kv.k[j];
-                    *(uint4 *)(vtile + lc * KROW + 16 * (sub + 16 * j)) =
-                        live ? kv.v[j] : make_uint4(0u, 0u, 0u, 0u);
-                }
-        }
-        __syncthreads();                                                // barrier: tiles, kappa
+        const int c0 = kPC * p + lc, c1 = c0 + kPC / 2;
+        if (lc < 32 * nks)
+            put_rows<DH, CPT>(ktile, vtile, kv0, lc, sub,
+                              lc < np && !(L.ids[c0 >> 2] == a.nb && (lc & 3) >= a.n_tail));
+        if (lc + kPC / 2 < 32 * nks)
+            put_rows<DH, CPT>(ktile, vtile, kv1, lc + kPC / 2, sub,
+                              lc + kPC / 2 < np && !(L.ids[c1 >> 2] == a.nb && (lc & 3) >= a.n_tail));
+        __syncthreads();                                                // barrier: tiles
         if (wv < (np + 15) / 16) {
             // D[cell][head] = K[cell][:] . q[head][:], 16 cells per wave
             const int mc = lane & 15, kg = lane >> 4;
@@ -378,13 +390,11 @@ __global__ __launch_bounds__(kNT) void k_decode_attend(DecodeArgs a)
                 de = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bl, de, 0, 0, 0);
             }
             if (mc < G) {
-                const uint64_t kappa = L.kappa;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int cl = 16 * wv + 4 * kg + j;
                     const int b = (kPC * p + cl) >> 2;
-                    const bool valid = cl < np && L.comp[b] >= kappa &&
-                                       !(L.ids[b] == a.nb && (cl & 3) >= a.n_tail);
+                    const bool valid = cl < np && !(L.ids[b] == a.nb && (cl & 3) >= a.n_tail);
                     L.lg[cl][mc] = valid ? a.scale * (dd[j] + de[j]) : -INFINITY;
                 }
             }
@@ -424,8 +434,8 @@ __global__ __launch_bounds__(kNT) void k_decode_attend(DecodeArgs a)
             }
 #pragma unroll
             for (int i = 0; i < TPW; ++i) {
-                const int tile = wv + kNW * i;
-                if (NT % kNW == 0 || tile < NT) {
+                const int tile = wv + kNAW * i;
+                if (NT % kNAW == 0 || tile < NT) {
                     half8 av;
                     const unsigned char *col = vtile + (32 * ks + 8 * kq) * KROW + 2 * (16 * tile + hn);
 #pragma unroll
@@ -448,8 +458,8 @@ __global__ __launch_bounds__(kNT) void k_decode_attend(DecodeArgs a)
     if (hn < G) {
 #pragma unroll
         for (int i = 0; i < TPW; ++i) {
-            const int tile = wv + kNW * i;
-            if (NT % kNW != 0 && tile >= NT)
+            const int tile = wv + kNAW * i;
+            if (NT % kNAW != 0 && tile >= NT)
                 continue;
             *(float4v *)(part + hn * DH + 16 * tile + 4 * kq) = acc[i];
         }
@@ -459,22 +469,23 @@ __global__ __launch_bounds__(kNT) void k_decode_attend(DecodeArgs a)
         part[G * DH + G + wv] = l_run;
     }
     if (fast && a.sel_out && g == 0) {
-        const uint64_t kappa = L.kappa;
-        const bool win = (uint32_t)t < nown && L.comp[t] >= kappa && L.ids[t] != a.nb;
-        if (win) {
-            const int32_t id = L.ids[t];
+        // the split's winners ascending: each one's rank among them (every
+        // listed block but the tail wins)
+        for (uint32_t j = (uint32_t)t; j < nown; j += kNA) {
+            const int32_t id = L.ids[j];
+            if (id == a.nb)
+                continue;
             uint32_t r = 0;
             for (uint32_t i = 0; i < nown; ++i)
-                r += (L.comp[i] >= kappa && L.ids[i] < id) ? 1u : 0u;
+                r += (L.ids[i] != a.nb && L.ids[i] < id) ? 1u : 0u;
             a.stage[(size_t)s * k + r] = id;
         }
-        const int nw = __syncthreads_count(win ? 1 : 0);
         if (t == 0)
-            a.stage_n[s] = nw;
+            a.stage_n[s] = (int32_t)nown - (tail_here ? 1 : 0);
     }
     if (t == 0 && s == 0 && g == 0) {
         ctrl->path = fast ? hist::kPathFast : hist::kPathFull;
-        ctrl->kappa = L.kappa;
+        ctrl->kappa = kappa;
         ctrl->btop = L.btop;
     }
     if (!fast && t == 0 && s == ns - 1 && g == a.kv_heads - 1) {
@@ -567,29 +578,30 @@ __global__ __launch_bounds__(kNT) void k_decode_merge(DecodeArgs a)
     // the bookkeeping workgroup
     hist::Ctrl *ctrl = reinterpret_cast<hist::Ctrl *>(a.ctrl);
     const bool fast = ctrl->path == hist::kPathFast;
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
     if (t < hist::kBins / 4)
-        reinterpret_cast<uint4 *>(const_cast<uint32_t *>(a.hist))[t] = make_uint4(0u, 0u, 0u, 0u);
-    if (t < hist::kLast)
-        const_cast<uint64_t *>(a.last)[t] = 0ull;
+        reinterpret_cast<uint4 *>(const_cast<uint32_t *>(a.hist))[t] = z;
+    if (t < hist::kBins / 2) {
+        reinterpret_cast<uint4 *>(const_cast<uint64_t *>(a.bmax))[t] = z;
+        reinterpret_cast<uint4 *>(const_cast<uint64_t *>(a.bminc))[t] = z;
+    }
+    if (t < hist::kLast / 2)
+        reinterpret_cast<uint4 *>(const_cast<uint64_t *>(a.last))[t] = z;
     if (t == 0) {
-        // the next call's window: kappa / sigma less a margin below, the top
-        // entry / sigma plus a margin above (the top bin holds every score
-        // >= H: then the window widens)
-        const float sigma = ctrl->sigma, wlo = ctrl->lo, whi = ctrl->hi;
-        float klo, ktop;
+        // the next call's window: this call's kappa / sigma and top entry /
+        // sigma (the histogram path knows the top only to its bin)
+        const hist::Map map = hist::stored_map(*ctrl);
+        const float sigma = ctrl->sigma;
+        float kk, ktop;
         if (fast) {
-            klo = key_score((uint32_t)(ctrl->kappa >> 32));
-            ktop = ctrl->btop == (uint32_t)hist::kBins - 1u ? whi + (whi - wlo)
-                                                            : wlo + (float)(ctrl->btop + 1u) / ctrl->inv;
+            kk = key_score((uint32_t)(ctrl->kappa >> 32));
+            ktop = hist::bin_top(ctrl->btop, map, ctrl->hi);
         } else {
-            klo = key_score(ctrl->kmin);
+            kk = key_score(ctrl->kmin);
             ktop = key_score(ctrl->kmax);
         }
-        float rlo = klo / sigma - kWindowBelow, rhi = ktop / sigma + kWindowAbove;
-        if (!(rhi > rlo + 1.0f))
-            rhi = rlo + 1.0f;
-        ctrl->rho_lo = rlo;         // NaN when sigma is 0 or not finite: defaults next time
-        ctrl->rho_hi = rhi;
+        ctrl->rho_k = kk / sigma;       // NaN when sigma is 0 or not finite: defaults next time
+        ctrl->rho_top = (ktop > kk ? ktop : kk) / sigma;
         ctrl->tag = hist::kTagClean;
         ctrl->status = (a.epoch << 8) | (fast ? hist::kPathFast : hist::kPathFull);
     }
@@ -643,23 +655,34 @@ hipError_t go_g(const DecodeArgs &a, int G, hipStream_t s)
 
 }  // namespace
 
-size_t decode_static_lds(int Dh, int G)
+namespace {
+template <int DH, int G>
+bool fits(int64_t nb)
 {
-    switch (Dh * 16 + G) {
-    case 64 * 16 + 1: return sizeof(DecLds<64, 1>);
-    case 64 * 16 + 2: return sizeof(DecLds<64, 2>);
-    case 64 * 16 + 4: return sizeof(DecLds<64, 4>);
-    case 64 * 16 + 8: return sizeof(DecLds<64, 8>);
-    case 128 * 16 + 1: return sizeof(DecLds<128, 1>);
-    case 128 * 16 + 2: return sizeof(DecLds<128, 2>);
-    case 128 * 16 + 4: return sizeof(DecLds<128, 4>);
-    case 128 * 16 + 8: return sizeof(DecLds<128, 8>);
-    case 256 * 16 + 1: return sizeof(DecLds<256, 1>);
-    case 256 * 16 + 2: return sizeof(DecLds<256, 2>);
-    case 256 * 16 + 4: return sizeof(DecLds<256, 4>);
-    case 256 * 16 + 8: return sizeof(DecLds<256, 8>);
+    return sizeof(DecLds<DH, G>) <= sel::kMaxLds && nb <= ((int64_t)1 << 19) &&
+           sel::lds_bytes((int32_t)nb) <= DecLds<DH, G>::kTiles;
+}
+template <int DH>
+bool fits_g(int64_t nb, int G)
+{
+    switch (G) {
+    case 1: return fits<DH, 1>(nb);
+    case 2: return fits<DH, 2>(nb);
+    case 4: return fits<DH, 4>(nb);
+    case 8: return fits<DH, 8>(nb);
     }
-    return (size_t)1 << 30;
+    return false;
+}
+}  // namespace
+
+bool decode_fits(int64_t nb, int Dh, int G)
+{
+    switch (Dh) {
+    case 64: return fits_g<64>(nb, G);
+    case 128: return fits_g<128>(nb, G);
+    case 256: return fits_g<256>(nb, G);
+    }
+    return false;
 }
 
 hipError_t launch_decode_attend(const DecodeArgs &a, int Dh, int G, hipStream_t s)

@@ -101,14 +101,13 @@ __device__ inline void write_tile_list(const uint64_t *s_c, uint64_t *lists, int
     if (part == 0 && c != 0 && rank < (uint32_t)T) {
         lists[(size_t)tile * T + rank] = c;
         if (h && hist::in_window((uint32_t)(c >> 32), *map)) {
-            // an entry inside the window: its bin's count (its bucket slot)
-            // and, for the last entry of a list that may hide rows, the
-            // maximum of such entries
+            // an entry inside the window: its bin's count and extremes and,
+            // for the last entry of a list that may hide rows, the maximum of
+            // such entries (no result is waited for)
             const uint32_t b = hist::bin_of((uint32_t)(c >> 32), *map);
-            const uint32_t slot =
-                __hip_atomic_fetch_add(h->hist + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (slot < (uint32_t)hist::kCap)
-                h->bucket[(size_t)b * hist::kCap + slot] = c;
+            __hip_atomic_fetch_add(h->hist + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_max(h->bmax + b, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_max(h->bminc + b, ~c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (rank == (uint32_t)T - 1 && valid_rows > T)
                 __hip_atomic_fetch_max(h->last + (tile & (hist::kLast - 1)), c, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
@@ -149,7 +148,6 @@ struct ScoreMultiLds {
     float qw[Q][LPR * EPL];
     uint64_t c[Q][ScoreShape<LPR>::R];
     u32x4 fresh[LPR];
-    float nrm2[4], g2;          // histogram window: ||w_h q_h||^2 per head, sum of gamma^2
 };
 
 template <bool F16, int LPR, int Q>
@@ -174,12 +172,19 @@ __device__ inline void score_tile(const ScoreMultiArgs &a, ScoreLdsOf<F16, LPR, 
     const int sub = lane / L;
     const int64_t base = (int64_t)tile * R + (int64_t)wave * S::RPW;
 
-    // the fed-back histogram window (read with the queries, used at the end)
-    float rho_lo = 0.0f, rho_hi = 0.0f;
+    // the fed-back histogram window and gamma (for its scale), loaded with
+    // the queries ahead of the rows so that the window is set while the rows
+    // are in flight
+    float rho_k = 0.0f, rho_top = 0.0f;
+    constexpr int GPL = HD / kWave;            // >= the gamma entries a lane takes (D <= HD)
+    float gam[GPL];
     if (Q == 1 && a.h.hist) {
         const hist::Ctrl *ctrl = reinterpret_cast<const hist::Ctrl *>(a.h.ctrl);
-        rho_lo = ctrl->rho_lo;
-        rho_hi = ctrl->rho_hi;
+        rho_k = ctrl->rho_k;
+        rho_top = ctrl->rho_top;
+#pragma unroll
+        for (int j = 0; j < GPL; ++j)
+            gam[j] = lane + kWave * j < a.D ? a.h.gamma[lane + kWave * j] : 0.0f;
     }
     // the queries' float4 groups this thread folds into LDS, loaded ahead of the rows
     float4 qraw[QPT];
@@ -234,30 +239,40 @@ __device__ inline void score_tile(const ScoreMultiArgs &a, ScoreLdsOf<F16, LPR, 
                 buf[i] = sl.fresh[col + L * (i % C)];
         }
     }
+    hist::Map map{};
     if (Q == 1 && a.h.hist) {
-        // the histogram window's scale (qsa_hist.h): wave h < H takes the
-        // squared norm of head h's folded query, wave 3 the sum of gamma^2;
-        // the same arithmetic in every workgroup, so every one maps alike
-        const int H = HD / a.D;
-        if (wave < H) {
-            float ss = 0.0f;
-            for (int e = lane; e < a.D; e += kWave) {
-                const float x = sl.qw[0][wave * a.D + e];
-                ss = fmaf(x, x, ss);
-            }
-            ss = wave::reduce_add_f(ss);
-            if (lane == 0)
-                sl.nrm2[wave] = ss;
+        // the histogram window (qsa_hist.h), every wave alike: its scale from
+        // the folded query's squared norm and the mean of gamma^2
+        float ss = 0.0f, gg = 0.0f;
+#pragma unroll
+        for (int j = 0; j < HD / kWave; ++j) {
+            const float x = sl.qw[0][lane + kWave * j];
+            ss = fmaf(x, x, ss);
         }
-        if (wave == 3) {
-            float gg = 0.0f;
-            for (int e = lane; e < a.D; e += kWave) {
-                const float x = a.h.gamma[e];
-                gg = fmaf(x, x, gg);
-            }
-            gg = wave::reduce_add_f(gg);
-            if (lane == 0)
-                sl.g2 = gg;
+#pragma unroll
+        for (int j = 0; j < GPL; ++j)
+            gg = fmaf(gam[j], gam[j], gg);
+        ss = wave::reduce_add_f(ss);
+        gg = wave::reduce_add_f(gg);
+        const float sigma = sqrtf(ss * (gg / (float)a.D));
+        float lo, mid, hi;
+        hist::window(sigma, rho_k, rho_top, a.h.def_k, a.h.def_top, lo, mid, hi);
+        map = hist::make_map(lo, mid, hi);
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+            // stamp the region with this call (clean start or not) and leave the
+            // window and its bin map for the attention kernel
+            hist::Ctrl *ctrl = reinterpret_cast<hist::Ctrl *>(a.h.ctrl);
+            ctrl->tag = ctrl->tag == hist::kTagClean ? hist::tag_ok(a.h.epoch) : hist::tag_bad(a.h.epoch);
+            ctrl->sigma = sigma;
+            ctrl->lo = lo;
+            ctrl->mid = mid;
+            ctrl->hi = hi;
+            ctrl->inv1 = map.inv1;
+            ctrl->inv2 = map.inv2;
+            ctrl->klo = map.klo;
+            ctrl->kmid = map.kmid;
+            ctrl->khi = map.khi;
+            ctrl->map_ok = map.ok ? 1u : 0u;
         }
     }
     float v[Q][V];
@@ -337,27 +352,6 @@ __device__ inline void score_tile(const ScoreMultiArgs &a, ScoreLdsOf<F16, LPR, 
     }
     __syncthreads();
     if (Q == 1 && a.h.hist) {
-        const int H = HD / a.D;
-        float n2 = 0.0f;
-        for (int h = 0; h < H; ++h)
-            n2 += sl.nrm2[h];
-        const float sigma = sqrtf(n2 * (sl.g2 / (float)a.D));
-        hist::Ctrl *ctrl = reinterpret_cast<hist::Ctrl *>(a.h.ctrl);
-        float lo, hi;
-        hist::window(sigma, rho_lo, rho_hi, a.h.def_lo, a.h.def_hi, lo, hi);
-        const hist::Map map = hist::make_map(lo, hi);
-        if (blockIdx.x == 0 && threadIdx.x == 0) {
-            // stamp the region with this call (clean start or not) and leave the
-            // window and its bin map for the attention kernel
-            ctrl->tag = ctrl->tag == hist::kTagClean ? hist::tag_ok(a.h.epoch) : hist::tag_bad(a.h.epoch);
-            ctrl->sigma = sigma;
-            ctrl->lo = lo;
-            ctrl->hi = hi;
-            ctrl->inv = map.inv;
-            ctrl->klo = map.klo;
-            ctrl->khi = map.khi;
-            ctrl->map_ok = map.ok ? 1u : 0u;
-        }
         const int64_t valid = a.nbq[0] - (int64_t)tile * R;
         write_tile_list<R>(sl.c[0], a.lists[0], tile, (int)(valid < 0 ? 0 : (valid < R ? valid : R)),
                            a.list_t, map.ok ? &a.h : nullptr, &map);

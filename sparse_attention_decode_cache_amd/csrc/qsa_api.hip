@@ -106,12 +106,12 @@ WsLayout decode_layout(const qsa_layer_desc *d, int32_t capacity)
                      d->top_k_tokens / 4);
 }
 
-// The histogram window's lower end, in units of the score scale, when no
-// earlier call fed one back: half a unit below where the k-th largest of nb
-// normally distributed scores falls (the upper quantile k / nb, by bisection
-// on the normal tail).  Any value is exact; a window that misses only costs
-// that call the full top-k.
-float default_window_lo(int64_t nb, int64_t k)
+// Where the histogram window expects kappa, in units of the score scale, when
+// no earlier call fed one back: where the k-th largest of nb normally
+// distributed scores falls (the upper quantile k / nb, by bisection on the
+// normal tail).  Any value is exact; a window that misses only costs that
+// call the full top-k.
+float default_kappa(int64_t nb, int64_t k)
 {
     const double p = (double)k / (double)nb;        // < 1: there is a selection
     double lo = -10.0, hi = 10.0;
@@ -122,7 +122,7 @@ float default_window_lo(int64_t nb, int64_t k)
         else
             hi = mid;
     }
-    return (float)(0.5 * (lo + hi) - 0.5);
+    return (float)(0.5 * (lo + hi));
 }
 
 // A distinct 56-bit value per decode-step call in this process (never 0):
@@ -537,9 +537,9 @@ qsa_status qsa_decode_step(const qsa_layer_desc *desc, const qsa_layer_cache *ca
     const bool hist_path = need_select && ns >= 1 &&
                            ((ntiles + ns - 1) / ns) * list_t <= kDecodeThreads &&
                            (int64_t)desc->kv_heads * ns <= kDecodeThreads &&
-                           sel::lds_bytes(nb) + decode_static_lds(desc->head_dim, G) <= sel::kMaxLds;
+                           decode_fits(nb, desc->head_dim, G);
     const uint64_t epoch = hist_path ? next_epoch() : 0;
-    const float def_lo = hist_path ? default_window_lo(nb, K) : 0.0f;
+    const float def_k = hist_path ? default_kappa(nb, K) : 0.0f;
     if (score) {
         ScoreArgs a{};
         a.summary = cache->summary;
@@ -555,13 +555,14 @@ qsa_status qsa_decode_step(const qsa_layer_desc *desc, const qsa_layer_cache *ca
         a.upd = u;
         if (hist_path) {
             a.h.hist = (uint32_t *)(wsp + L.hist);
-            a.h.bucket = (uint64_t *)(wsp + L.bucket);
+            a.h.bmax = (uint64_t *)(wsp + L.bmax);
+            a.h.bminc = (uint64_t *)(wsp + L.bminc);
             a.h.last = (uint64_t *)(wsp + L.last);
             a.h.ctrl = wsp + L.ctrl;
             a.h.gamma = gamma;
             a.h.epoch = epoch;
-            a.h.def_lo = def_lo;
-            a.h.def_hi = def_lo + 5.0f;
+            a.h.def_k = def_k;
+            a.h.def_top = def_k + 2.5f;
         }
         e = launch_score(a, desc->idx_dtype == QSA_F16, rowb, stream);
         if (e != hipSuccess)
@@ -584,7 +585,8 @@ qsa_status qsa_decode_step(const qsa_layer_desc *desc, const qsa_layer_cache *ca
         da.scale = attn_scale(desc);
         da.sa = select_args(wsp, L, nb, K, tile_rows, list_t, nullptr);
         da.hist = (const uint32_t *)(wsp + L.hist);
-        da.bucket = (const uint64_t *)(wsp + L.bucket);
+        da.bmax = (const uint64_t *)(wsp + L.bmax);
+        da.bminc = (const uint64_t *)(wsp + L.bminc);
         da.last = (const uint64_t *)(wsp + L.last);
         da.ctrl = wsp + L.ctrl;
         da.ns = (int32_t)ns;

@@ -16,13 +16,13 @@ constexpr int kListDiv = 8;         // per-tile top-k lists keep R / 8 entries o
 // hist_splits > 0 sizes its per-split id staging.
 struct WsLayout {
     size_t keys, lists, sel, part;
-    size_t ctrl, hist, last, bucket, stage, stage_n;   // 0 without the histogram region
+    size_t ctrl, hist, bmax, bminc, last, stage, stage_n;   // 0 without the histogram region
     size_t total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-constexpr int kHistBins = 2048, kHistCap = 64, kHistLast = 64;   // qsa_hist.h
+constexpr int kHistBins = 2048, kHistLast = 64;   // qsa_hist.h
 
 inline WsLayout ws_layout(int64_t max_blocks, int64_t sel_entries, int64_t part_floats,
                           int64_t hist_splits = 0, int64_t k_blocks = 0)
@@ -42,8 +42,9 @@ inline WsLayout ws_layout(int64_t max_blocks, int64_t sel_entries, int64_t part_
     L.part = take(sizeof(float) * (size_t)part_floats);
     if (hist_splits > 0) {
         L.hist = take(sizeof(uint32_t) * kHistBins);
+        L.bmax = take(sizeof(uint64_t) * kHistBins);
+        L.bminc = take(sizeof(uint64_t) * kHistBins);
         L.last = take(sizeof(uint64_t) * kHistLast);
-        L.bucket = take(sizeof(uint64_t) * (size_t)kHistBins * kHistCap);
         L.stage = take(sizeof(int32_t) * (size_t)(hist_splits * k_blocks));
         L.stage_n = take(sizeof(int32_t) * (size_t)hist_splits);
     }
@@ -92,12 +93,13 @@ hipError_t launch_update(const UpdateArgs &a, bool f16, hipStream_t s);
 // Histogram insertion by the score pass (see qsa_hist.h); off when hist is null.
 struct HistOut {
     uint32_t *hist;             // [hist::kBins] counts (cleared by the previous call)
-    uint64_t *bucket;           // [hist::kBins][hist::kCap] composites
+    uint64_t *bmax;             // [hist::kBins] largest composite per bin
+    uint64_t *bminc;            // [hist::kBins] complement of the smallest composite per bin
     uint64_t *last;             // [hist::kLast] maxima of the tiles' last list entries
     void *ctrl;                 // hist::Ctrl: window feedback in, tag / sigma / window out
     const float *gamma;         // [D] RMSNorm weights (for sigma)
     uint64_t epoch;             // this call's epoch (the tag stamp)
-    float def_lo, def_hi;       // window in units of sigma when no feedback is usable
+    float def_k, def_top;       // kappa / sigma and top / sigma when no feedback is usable
 };
 
 struct ScoreArgs {
@@ -263,7 +265,8 @@ struct DecodeArgs {
     float scale;
     SelectArgs sa;              // keys and tile lists of the score pass (sa.sel unused)
     const uint32_t *hist;
-    const uint64_t *bucket;
+    const uint64_t *bmax;
+    const uint64_t *bminc;
     const uint64_t *last;
     void *ctrl;                 // hist::Ctrl
     int32_t ns;                 // splits per KV head
@@ -274,8 +277,9 @@ struct DecodeArgs {
 };
 // The attention kernel (grid ns x kv_heads) and then the merge kernel.
 hipError_t launch_decode_attend(const DecodeArgs &a, int Dh, int G, hipStream_t s);
-// Static LDS bytes of that kernel (its dynamic LDS is the full top-k's, sel::lds_bytes(nb)).
-size_t decode_static_lds(int Dh, int G);
+// Whether that kernel takes nb blocks at these shapes (its LDS, the full
+// top-k's overlay included, fits a workgroup).
+bool decode_fits(int64_t nb, int Dh, int G);
 
 // ------------------------------------------------------------ prefill chunk
 // n_q consecutive tokens of one sequence in one call: query i sits at position
