@@ -22,7 +22,7 @@ def with_size(w, n0=None, steps=None, **kw):
 
 
 class GpuLayer:
-    def __init__(self, w, layer=0, seq=0, prefill=True, gamma_seq=None):
+    def __init__(self, w, layer=0, seq=0, prefill=True, gamma_seq=None, planted=None):
         import torch
         import sparse_attention_decode_cache_amd as qsa
         self.qsa = qsa
@@ -34,6 +34,9 @@ class GpuLayer:
                                   w.rms_eps, w.rope_theta)
         self.buf = qsa.LayerBuffers(self.desc, self.cap)
         W.dev_fill_layer_(w, self.buf, layer, w.n0, seq)
+        if planted is not None:
+            import planted as PL
+            PL.apply_device(planted, self.buf.idx_k)
         self.gamma = W.dev_gamma(w, layer, seq if gamma_seq is None else gamma_seq)
         self.ws = qsa.workspace(self.desc, self.cap)
         self.state = qsa.qsa_seq_state(w.n0, 0)
@@ -41,6 +44,9 @@ class GpuLayer:
             qsa.qsa_cache_update(self.desc, self.buf.cache, self.gamma, 0, w.n0 // 4)
             self.state.n_valid_blocks = w.n0 // 4
         self.inp = W.dev_step_inputs(w, layer, 0, max(w.steps, 1), seq)
+        if planted is not None:
+            self.inp.q_idx[:] = torch.from_numpy(planted.q_idx).cuda()
+            self.inp.w[:] = torch.from_numpy(planted.w).cuda()
         self.out = torch.empty((w.q_heads, w.head_dim), dtype=torch.float32, device="cuda")
         self.sel = torch.empty(w.k_blocks, dtype=torch.int32, device="cuda")
         self.scores = torch.empty(self.cap // 4, dtype=torch.float32, device="cuda")
@@ -64,7 +70,7 @@ class GpuLayer:
 
 
 class OracleMirror:
-    def __init__(self, w, layer=0, seq=0, gamma_seq=None):
+    def __init__(self, w, layer=0, seq=0, gamma_seq=None, planted=None):
         self.w = w
         self.layer = layer
         cap = w.capacity()
@@ -74,6 +80,10 @@ class OracleMirror:
         V = np.zeros_like(K)
         rows = np.arange(w.n0)
         raw[:w.n0] = W.host_raw_rows(w, rows, layer, seq)
+        self.planted = planted
+        if planted is not None:
+            import planted as PL
+            PL.apply_host(planted, raw)
         K[:w.n0], V[:w.n0] = W.host_kv_rows(w, rows, layer, seq)
         self.gamma = W.host_gamma(w, layer, seq if gamma_seq is None else gamma_seq)
         self.L = oracle.OracleLayer(raw, K, V, self.gamma, w.rms_eps, w.rope_theta, w.n0, w.k_blocks)
@@ -87,6 +97,8 @@ class OracleMirror:
         raw_row = W.host_raw_rows(w, [pos], self.layer, self.seq)[0]
         k_row, v_row = (x[0] for x in W.host_kv_rows(w, [pos], self.layer, self.seq))
         q_idx, wt, q = W.host_step_inputs(w, self.layer, s, self.seq)
+        if self.planted is not None:
+            q_idx, wt = self.planted.q_idx, self.planted.w
         r = self.L.step(raw_row, k_row, v_row, q_idx, wt, q)
         nb = self.L.n // 4
         r["scale"] = oracle.scores(self.L.summary, nb, q_idx, wt, with_scale=True)[1]
