@@ -82,13 +82,26 @@ def traffic_record(w, nb):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, n_steps):
-    """The CPU oracle on one layer of the same workload, `n_steps` decode steps."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, n_steps, n_serial=3):
+    """The CPU oracle on one layer of the same workload: `n_steps` decode
+    steps with its OpenMP loops on every thread it is given, then `n_serial`
+    more on one thread."""
     import numpy as np
     import oracle
     from qsagen import workloads as W
     t0 = time.time()
-    cap = w.n0 + n_steps
+    cap = w.n0 + n_steps + n_serial
     dt = np.float16 if w.idx_f16 else np.float32
     raw = np.zeros((cap,) + w.idx_row, dt)
     K = np.zeros((cap,) + w.kv_row, np.float16)
@@ -99,20 +112,33 @@ def cpu_baseline(w, n_steps):
     L = oracle.OracleLayer(raw, K, V, W.host_gamma(w, 0), w.rms_eps, w.rope_theta, w.n0, w.k_blocks)
     L.rebuild()
     log(f"cpu baseline: oracle cache built in {time.time() - t0:.1f}s")
-    steps = []
-    for s in range(n_steps):
-        pos = w.n0 + s
-        rr = W.host_raw_rows(w, [pos], 0)[0]
-        kr, vr = (x[0] for x in W.host_kv_rows(w, [pos], 0))
-        qi, wt, q = W.host_step_inputs(w, 0, s)
-        t = time.perf_counter()
-        L.step(rr, kr, vr, qi, wt, q)
-        steps.append(time.perf_counter() - t)
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+    def run(s0, n):
+        out = []
+        for s in range(s0, s0 + n):
+            pos = w.n0 + s
+            rr = W.host_raw_rows(w, [pos], 0)[0]
+            kr, vr = (x[0] for x in W.host_kv_rows(w, [pos], 0))
+            qi, wt, q = W.host_step_inputs(w, 0, s)
+            t = time.perf_counter()
+            L.step(rr, kr, vr, qi, wt, q)
+            out.append(time.perf_counter() - t)
+        return out
+
+    threads = oracle.threads()
+    steps = run(0, n_steps)
+    oracle.set_threads(1)
+    serial = run(n_steps, n_serial)
+    oracle.set_threads(threads)
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None
     return {"value": round(len(steps) / sum(steps), 3), "unit": "QSA-layer decode steps/s",
             "cores": threads, "kind": "oracle",
+            "cpu": cpu_model(), "nproc": os.cpu_count(), "affinity_cpus": affinity,
+            "single_thread": {"value": round(len(serial) / sum(serial), 3),
+                              "median_step_ms": round(1e3 * statistics.median(serial), 1), "steps": n_serial},
             "sample": f"{n_steps} decode steps of layer 0 of {w.name} (n0={w.n0}), fp64 C oracle "
-                      f"with OpenMP over blocks; cache build excluded; median step "
+                      f"with OpenMP over blocks (pooling, scores) and heads (attention) on {threads} "
+                      f"threads, top-k serial; cache build excluded; median step "
                       f"{1e3 * statistics.median(steps):.1f} ms"}
 
 

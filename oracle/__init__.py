@@ -71,8 +71,20 @@ def lib():
         L.qsa_oracle_cells.restype = l
         L.qsa_oracle_cells.argtypes = [P, l, l, P]
         L.qsa_oracle_attend.argtypes = [P, P, P, P, l, i, i, i, d, P]
+        L.qsa_oracle_threads.restype = i
+        L.qsa_oracle_threads.argtypes = []
+        L.qsa_oracle_set_threads.argtypes = [i]
         _lib = L
     return _lib
+
+
+def threads():
+    """OpenMP threads of the oracle's parallel loops (blocks, heads)."""
+    return int(lib().qsa_oracle_threads())
+
+
+def set_threads(n):
+    lib().qsa_oracle_set_threads(int(n))
 
 
 def _p(a):

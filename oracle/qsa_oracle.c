@@ -46,6 +46,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORACLE_F32 0
 #define ORACLE_F16 1
@@ -381,4 +384,24 @@ void qsa_oracle_attend_q8_0(const float *q, const int8_t *Kc, const uint16_t *Kd
         }
     }
     free(lg);
+}
+
+/* Harness helpers (no arithmetic of the method): the OpenMP threads the
+ * parallel loops above use, and a way to set them (1 = the serial oracle). */
+int qsa_oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void qsa_oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    omp_set_num_threads(n > 0 ? n : 1);
+#else
+    (void)n;
+#endif
 }
