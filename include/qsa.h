@@ -35,7 +35,10 @@
  *   - Argument checks run before any launch.  On a failed check nothing is
  *     enqueued, no state is changed, and the status is QSA_ERR_ARG,
  *     QSA_ERR_UNSUPPORTED (shape outside the supported set) or
- *     QSA_ERR_WORKSPACE.  A launch failure returns QSA_ERR_HIP.
+ *     QSA_ERR_WORKSPACE.  A launch failure (the HIP runtime refusing a
+ *     launch, e.g. an invalid stream) returns QSA_ERR_HIP; kernels of the
+ *     same call enqueued before the failing launch stay enqueued, and the
+ *     sequence state is left unchanged.
  *     qsa_last_error() gives a thread-local description of the last failure.
  *   - Supported shapes: block = 4; idx_heads in {1, 4}; idx_dim in {64, 128};
  *     idx row (idx_heads * idx_dim * sizeof(dtype)) <= 1024 bytes;
@@ -265,8 +268,10 @@ qsa_status qsa_decode_step_batch(const qsa_layer_desc *desc, int32_t n_seq,
  * floor((pos_0 + n_q) / 4)): written only when some query has more than K
  * blocks; entry (i, b) is query i's score of block b for b < floor(n_i / 4),
  * -INFINITY past it.
- * On success st becomes {pos_0 + n_q, nb_last}; on any error nothing is
- * enqueued and st is unchanged.
+ * On success st becomes {pos_0 + n_q, nb_last}; on a failed argument check
+ * nothing is enqueued, and on any error st is unchanged (after QSA_ERR_HIP
+ * the kernels enqueued before the failing launch, the append of the chunk's
+ * rows first, stay enqueued).
  * Errors: ARG if n_q is outside [1, QSA_MAX_CHUNK], a pointer is null or
  * misaligned, or pos_0 + n_q > capacity; UNSUPPORTED / WORKSPACE as in
  * qsa_decode_step (workspace >= qsa_chunk_workspace_bytes). */
@@ -311,8 +316,10 @@ qsa_status qsa_chunk_step(const qsa_layer_desc *desc, const qsa_layer_cache *cac
  * fp32 [n_q][nb_last], nb_last = floor((pos_0 + n_q) / 4)): entry (i, b) is
  * query i's score of block b for b < floor(n_i / 4), -INFINITY past it
  * (written whenever nb_last > 0).  Workspace >= qsa_multi_workspace_bytes.
- * On success st becomes {pos_0 + n_q, nb_last}; on any error nothing is
- * enqueued and st is unchanged.
+ * On success st becomes {pos_0 + n_q, nb_last}; on a failed argument check
+ * nothing is enqueued, and on any error st is unchanged (after QSA_ERR_HIP
+ * the kernels enqueued before the failing launch, the append of the call's
+ * rows first, stay enqueued).
  * Errors: ARG if n_q is outside [1, QSA_MAX_MULTI], a pointer is null or
  * misaligned, or pos_0 + n_q > capacity; UNSUPPORTED / WORKSPACE as in
  * qsa_decode_step. */

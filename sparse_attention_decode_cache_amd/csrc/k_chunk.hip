@@ -17,10 +17,11 @@
 //           blocks;
 //   select  one workgroup per query: the exact top-k over its keys, held
 //           in LDS (a linear histogram, then the boundary bin ranked);
-//   attend  workgroup (query, split, KV head): the tile routine of the decode
-//           path over the split's 16-cell tiles, folded into a running
-//           (max, sum, acc) in registers; with one split the output is
-//           written directly, otherwise a small merge follows.
+//   attend  workgroup (query, split, KV head): the attention unit of
+//           qsa_unit.h over the split's share of the query's iterations of
+//           64 cells, folded into a running (max, sum, acc) in registers;
+//           with one split the output is written directly, otherwise a small
+//           merge follows.
 #include <type_traits>
 
 #include "qsa_attend.h"

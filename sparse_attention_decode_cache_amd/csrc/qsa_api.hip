@@ -467,6 +467,8 @@ qsa_status qsa_gather_attend(const qsa_layer_desc *desc, const qsa_layer_cache *
         return fail(QSA_ERR_ARG, "no cell to attend (no block and no tail cell)");
     if (!q || !out)
         return fail(QSA_ERR_ARG, "q / out is NULL");
+    if (!aligned(q, 16) || !aligned(out, 16))
+        return fail(QSA_ERR_ARG, "q / out must be 16-byte aligned");
     const WsLayout L = decode_layout(desc, cache->capacity);
     if ((s = check_ws(ws, ws_bytes, L.total)) != QSA_OK)
         return s;
@@ -946,12 +948,14 @@ qsa_status qsa_chunk_step(const qsa_layer_desc *desc, const qsa_layer_cache *cac
     c.D = desc->idx_dim;
     c.kv_heads = desc->kv_heads;
     c.scale = attn_scale(desc);
-    // few queries: split each query's tiles so that the chip is still filled
+    // few queries: split each query's iterations of 64 cells so that the
+    // chip is still filled, every split getting at least one
     const int64_t units = (int64_t)n_q * desc->kv_heads;
-    const int64_t max_tiles = n_splits(4 * (int64_t)K + 3);
+    const int64_t max_it = (4 * (int64_t)K + 3 + kUnitCells - 1) / kUnitCells;
     int64_t ns = units >= kChunkWgTarget ? 1 : (kChunkWgTarget + units - 1) / units;
-    ns = ns < max_tiles ? ns : max_tiles;
+    ns = ns < max_it ? ns : max_it;
     ns = ns < kChunkMaxSplits ? ns : kChunkMaxSplits;
+    ns = (max_it + (max_it + ns - 1) / ns - 1) / ((max_it + ns - 1) / ns);   // no split left empty
     c.n_split = (int32_t)ns;
 
     hipError_t e = launch_chunk_append(c, stream);

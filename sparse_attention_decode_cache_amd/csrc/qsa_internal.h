@@ -68,6 +68,10 @@ inline int64_t n_splits(int64_t n_cells)
     return (n_cells + kCellsPerSplit - 1) / kCellsPerSplit;
 }
 
+// Cells per iteration of the attention unit of the chunk / batch / masked
+// kernels (qsa_unit.h).
+constexpr int kUnitCells = 64;
+
 // ------------------------------------------------------------- launchers
 struct UpdateArgs {
     void *idx_k;

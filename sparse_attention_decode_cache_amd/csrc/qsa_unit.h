@@ -35,7 +35,7 @@
 namespace qsa {
 namespace unit {
 
-constexpr int kCI = 64;                      // cells per iteration
+constexpr int kCI = kUnitCells;              // cells per iteration
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));

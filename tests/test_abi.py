@@ -84,6 +84,9 @@ def test_argument_errors_before_launch():
     assert L.qsa_gather_attend(D, C, 4096, P(16), 5, P(16), P(16), P(256), 64, None) == -3
     assert L.qsa_gather_attend(D, C, 4096, P(16), 0, P(16), P(16), P(256), 1 << 30, None) == -1   # no cell
     assert b"no cell" in L.qsa_last_error()
+    assert L.qsa_gather_attend(D, C, 4096, P(16), 5, P(8), P(16), P(256), 1 << 30, None) == -1    # q misaligned
+    assert L.qsa_gather_attend(D, C, 4096, P(16), 5, P(16), P(8), P(256), 1 << 30, None) == -1    # out misaligned
+    assert b"aligned" in L.qsa_last_error()
     # decode step: position at capacity, null rows, small workspace
     st = qsa.qsa_seq_state(4096, 1024)
     args = [P(16)] * 8
