@@ -288,6 +288,27 @@ qsa_status qsa_chunk_step(const qsa_layer_desc *desc, const qsa_layer_cache *cac
                           int32_t *sel_out, float *scores_out, void *ws, size_t ws_bytes,
                           hipStream_t stream);
 
+/* Stage 2 of qsa_decode_step on its own [post 10, "QSA indexer": block scores
+ * s_b = sum_h w_h <q_idx_h, summary_b,h>], as the step launches it: the score
+ * pass over the floor(st->n_tokens / 4) completed blocks (no append, no
+ * pooling, st is not changed), writing into the workspace the selection keys,
+ * the per-tile candidate lists and the score histogram whenever there are
+ * more than K = top_k_tokens / 4 blocks -- the same kernel, grid and outputs
+ * as inside the step.  For timing or inspecting the step's dominant kernel.
+ * It leaves the workspace's histogram region filled: the next
+ * qsa_decode_step on that workspace finds it unclean and takes the full
+ * top-k once (same results).
+ * gamma: DEVICE fp32 [D_i]; q_idx: DEVICE fp32 [H_i][D_i] (16-byte aligned);
+ * w: DEVICE fp32 [H_i]; scores_out (optional): DEVICE fp32 [n_tokens / 4].
+ * Workspace >= qsa_workspace_bytes(desc, capacity).  With no block, or at
+ * most K blocks and no scores_out, nothing is enqueued.
+ * Errors: ARG if a pointer is null or misaligned or n_tokens is outside
+ * [0, capacity]; UNSUPPORTED / WORKSPACE as in qsa_decode_step. */
+qsa_status qsa_decode_score(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
+                            const qsa_seq_state *st, const float *gamma, const float *q_idx,
+                            const float *w, float *scores_out, void *ws, size_t ws_bytes,
+                            hipStream_t stream);
+
 /* ------------------------------------------------ multi-query decode
  * Speculative verification: the token at pos_0 = st->n_tokens and up to
  * QSA_MAX_MULTI - 1 drafted tokens after it, decoded in one call with the

@@ -148,6 +148,7 @@ struct ScoreMultiLds {
     float qw[Q][LPR * EPL];
     uint64_t c[Q][ScoreShape<LPR>::R];
     u32x4 fresh[LPR];
+    float gam[128];             // RMSNorm weights (histogram window)
 };
 
 template <bool F16, int LPR, int Q>
@@ -176,16 +177,17 @@ __device__ inline void score_tile(const ScoreMultiArgs &a, ScoreLdsOf<F16, LPR, 
     // the queries ahead of the rows so that the window is set while the rows
     // are in flight
     float rho_k = 0.0f, rho_top = 0.0f;
-    constexpr int GPL = HD / kWave;            // >= the gamma entries a lane takes (D <= HD)
-    float gam[GPL];
     if (Q == 1 && a.h.hist) {
         const hist::Ctrl *ctrl = reinterpret_cast<const hist::Ctrl *>(a.h.ctrl);
         rho_k = ctrl->rho_k;
         rho_top = ctrl->rho_top;
-#pragma unroll
-        for (int j = 0; j < GPL; ++j)
-            gam[j] = lane + kWave * j < a.D ? a.h.gamma[lane + kWave * j] : 0.0f;
     }
+    // gamma entry t (thread t < D), staged through LDS like the queries: the
+    // load is unconditional (any readable word without a window) so that
+    // nothing waits for it before the rows are issued
+    const bool want_g = Q == 1 && a.h.hist != nullptr;
+    const float *gsrc = want_g ? a.h.gamma : a.w[0];
+    const float graw = gsrc[want_g && (int)threadIdx.x < a.D ? (int)threadIdx.x : 0];
     // the queries' float4 groups this thread folds into LDS, loaded ahead of the rows
     float4 qraw[QPT];
     float wraw[QPT];
@@ -224,6 +226,9 @@ __device__ inline void score_tile(const ScoreMultiArgs &a, ScoreLdsOf<F16, LPR, 
         }
     }
 
+    if (want_g && (int)threadIdx.x < a.D)
+        sl.gam[threadIdx.x] = graw;
+
     if (pool_here) {
         if (a.upd.new_idx_row)
             append_rows(a.upd, threadIdx.x, 256);
@@ -249,9 +254,8 @@ __device__ inline void score_tile(const ScoreMultiArgs &a, ScoreLdsOf<F16, LPR, 
             const float x = sl.qw[0][lane + kWave * j];
             ss = fmaf(x, x, ss);
         }
-#pragma unroll
-        for (int j = 0; j < GPL; ++j)
-            gg = fmaf(gam[j], gam[j], gg);
+        for (int e = lane; e < a.D; e += kWave)
+            gg = fmaf(sl.gam[e], sl.gam[e], gg);
         ss = wave::reduce_add_f(ss);
         gg = wave::reduce_add_f(gg);
         const float sigma = sqrtf(ss * (gg / (float)a.D));

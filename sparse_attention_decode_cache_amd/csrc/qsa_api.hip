@@ -477,6 +477,70 @@ qsa_status qsa_gather_attend(const qsa_layer_desc *desc, const qsa_layer_cache *
     return s == QSA_OK ? ok() : s;
 }
 
+// How a decode step over nb completed blocks selects: the histogram path
+// (score pass + k_decode.hip) when the shapes fit it, with ns splits per KV
+// head, a fresh epoch and the default window.
+struct DecodePlan {
+    bool hist_path;
+    int64_t ns;
+    uint64_t epoch;
+    float def_k;
+};
+
+DecodePlan decode_plan(const qsa_layer_desc *desc, int32_t nb)
+{
+    const int32_t K = desc->top_k_tokens / 4;
+    const int rowb = desc->idx_heads * desc->idx_dim * elem_bytes(desc->idx_dtype);
+    const int tile_rows = score_tile_rows(desc->idx_dtype == QSA_F16, rowb);
+    const int32_t list_t = list_len(tile_rows, nb, K);
+    const int64_t ntiles = ((int64_t)nb + tile_rows - 1) / tile_rows;
+    const int G = desc->q_heads / desc->kv_heads;
+    DecodePlan P{};
+    P.ns = device_cus() / desc->kv_heads;
+    if (P.ns > kDecodeMaxSplits)
+        P.ns = kDecodeMaxSplits;
+    if (P.ns > ntiles)
+        P.ns = ntiles;
+    P.hist_path = nb > K && P.ns >= 1 && ((ntiles + P.ns - 1) / P.ns) * list_t <= kDecodeThreads &&
+                  (int64_t)desc->kv_heads * P.ns <= kDecodeThreads && decode_fits(nb, desc->head_dim, G);
+    P.epoch = P.hist_path ? next_epoch() : 0;
+    P.def_k = P.hist_path ? default_kappa(nb, K) : 0.0f;
+    return P;
+}
+
+// The decode step's score pass: scores (optional), keys and tile lists when
+// there is a selection, the histogram on the histogram path.
+ScoreArgs decode_score_args(const qsa_layer_desc *desc, const qsa_layer_cache *cache, const WsLayout &L,
+                            char *wsp, const DecodePlan &P, int32_t nb, bool need_select, const float *gamma,
+                            const float *q_idx, const float *w, float *scores_out)
+{
+    const int32_t K = desc->top_k_tokens / 4;
+    const int rowb = desc->idx_heads * desc->idx_dim * elem_bytes(desc->idx_dtype);
+    const int tile_rows = score_tile_rows(desc->idx_dtype == QSA_F16, rowb);
+    ScoreArgs a{};
+    a.summary = cache->summary;
+    a.q = q_idx;
+    a.w = w;
+    a.scores = scores_out;
+    a.keys = need_select ? (uint32_t *)(wsp + L.keys) : nullptr;
+    a.lists = need_select ? (uint64_t *)(wsp + L.lists) : nullptr;
+    a.list_t = list_len(tile_rows, nb, K);
+    a.nb = nb;
+    a.D = desc->idx_dim;
+    if (P.hist_path) {
+        a.h.hist = (uint32_t *)(wsp + L.hist);
+        a.h.bmax = (uint64_t *)(wsp + L.bmax);
+        a.h.bminc = (uint64_t *)(wsp + L.bminc);
+        a.h.last = (uint64_t *)(wsp + L.last);
+        a.h.ctrl = wsp + L.ctrl;
+        a.h.gamma = gamma;
+        a.h.epoch = P.epoch;
+        a.h.def_k = P.def_k;
+        a.h.def_top = P.def_k + 2.5f;
+    }
+    return a;
+}
+
 qsa_status qsa_decode_step(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
                            qsa_seq_state *st, const void *idx_k_row, const uint16_t *k_row,
                            const uint16_t *v_row, const float *gamma, const float *q_idx,
@@ -525,47 +589,19 @@ qsa_status qsa_decode_step(const qsa_layer_desc *desc, const qsa_layer_cache *ca
     }
 
     // 2. score every completed block (keys for the top-k).  With a selection
-    //    the pass also fills the global histogram, from which one kernel
-    //    selects, attends and merges (k_decode.hip) when the shapes fit it.
+    //    the pass also fills the global histogram, from which the attention
+    //    kernel selects (k_decode.hip) when the shapes fit it.
     const int tile_rows = score_tile_rows(desc->idx_dtype == QSA_F16, rowb);
     const int32_t list_t = list_len(tile_rows, nb, K);
-    const int64_t ntiles = ((int64_t)nb + tile_rows - 1) / tile_rows;
     const int G = desc->q_heads / desc->kv_heads;
-    int64_t ns = device_cus() / desc->kv_heads;
-    if (ns > kDecodeMaxSplits)
-        ns = kDecodeMaxSplits;
-    if (ns > ntiles)
-        ns = ntiles;
-    const bool hist_path = need_select && ns >= 1 &&
-                           ((ntiles + ns - 1) / ns) * list_t <= kDecodeThreads &&
-                           (int64_t)desc->kv_heads * ns <= kDecodeThreads &&
-                           decode_fits(nb, desc->head_dim, G);
-    const uint64_t epoch = hist_path ? next_epoch() : 0;
-    const float def_k = hist_path ? default_kappa(nb, K) : 0.0f;
+    const DecodePlan P = decode_plan(desc, nb);
+    const bool hist_path = P.hist_path;
+    const int64_t ns = P.ns;
+    const uint64_t epoch = P.epoch;
     if (score) {
-        ScoreArgs a{};
-        a.summary = cache->summary;
-        a.q = q_idx;
-        a.w = w;
-        a.scores = scores_out;
-        a.keys = need_select ? (uint32_t *)(wsp + L.keys) : nullptr;
-        a.lists = need_select ? (uint64_t *)(wsp + L.lists) : nullptr;
-        a.list_t = list_t;
-        a.nb = nb;
-        a.D = desc->idx_dim;
+        ScoreArgs a = decode_score_args(desc, cache, L, wsp, P, nb, need_select, gamma, q_idx, w, scores_out);
         a.fuse = fuse ? 1 : 0;
         a.upd = u;
-        if (hist_path) {
-            a.h.hist = (uint32_t *)(wsp + L.hist);
-            a.h.bmax = (uint64_t *)(wsp + L.bmax);
-            a.h.bminc = (uint64_t *)(wsp + L.bminc);
-            a.h.last = (uint64_t *)(wsp + L.last);
-            a.h.ctrl = wsp + L.ctrl;
-            a.h.gamma = gamma;
-            a.h.epoch = epoch;
-            a.h.def_k = def_k;
-            a.h.def_top = def_k + 2.5f;
-        }
         e = launch_score(a, desc->idx_dtype == QSA_F16, rowb, stream);
         if (e != hipSuccess)
             return hip_fail(e, "decode_step/score");
@@ -632,6 +668,39 @@ qsa_status qsa_decode_step(const qsa_layer_desc *desc, const qsa_layer_cache *ca
 
     st->n_tokens = n;
     st->n_valid_blocks = nb;
+    return ok();
+}
+
+qsa_status qsa_decode_score(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
+                            const qsa_seq_state *st, const float *gamma, const float *q_idx,
+                            const float *w, float *scores_out, void *ws, size_t ws_bytes,
+                            hipStream_t stream)
+{
+    qsa_status s;
+    if ((s = check_desc(desc)) != QSA_OK || (s = check_cache(cache, false, true, false)) != QSA_OK)
+        return s;
+    if (!st)
+        return fail(QSA_ERR_ARG, "state is NULL");
+    if (!gamma || !q_idx || !w)
+        return fail(QSA_ERR_ARG, "gamma / q_idx / w is NULL");
+    if (!aligned(q_idx, 16))
+        return fail(QSA_ERR_ARG, "q_idx must be 16-byte aligned");
+    const int32_t n = st->n_tokens;
+    if (n < 0 || n > cache->capacity)
+        return fail(QSA_ERR_ARG, "n_tokens %d outside [0, %d]", n, cache->capacity);
+    const WsLayout L = decode_layout(desc, cache->capacity);
+    if ((s = check_ws(ws, ws_bytes, L.total)) != QSA_OK)
+        return s;
+    const int32_t nb = n / 4;
+    const int32_t K = desc->top_k_tokens / 4;
+    if (nb == 0 || (nb <= K && !scores_out))
+        return ok();
+    const int rowb = desc->idx_heads * desc->idx_dim * elem_bytes(desc->idx_dtype);
+    const DecodePlan P = decode_plan(desc, nb);
+    const ScoreArgs a = decode_score_args(desc, cache, L, (char *)ws, P, nb, nb > K, gamma, q_idx, w, scores_out);
+    const hipError_t e = launch_score(a, desc->idx_dtype == QSA_F16, rowb, stream);
+    if (e != hipSuccess)
+        return hip_fail(e, "decode_score");
     return ok();
 }
 

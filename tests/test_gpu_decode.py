@@ -142,3 +142,37 @@ def test_decode_winners_clustered_in_a_few_tiles(n0, lo, hi):
     rg, ro = _compare_step(g, o, 0, stats)
     assert stats["exact"] == 1
     assert np.array_equal(rg["sel"], np.arange(hi - w.k_blocks, hi))
+
+
+def test_decode_score_stage_alone():
+    """qsa_decode_score runs the step's score pass alone: its scores equal
+    qsa_index_score's bit for bit (same kernel arithmetic) and the oracle's to
+    the score tolerance; the histogram it leaves makes the next step take the
+    full top-k once, with the same results."""
+    import numpy as np
+    import torch
+    import oracle
+    from parity import check_scores
+    w = with_size(W.CTX64K, steps=3)
+    print(f"decode score stage {w.name} n0={w.n0}", flush=True)
+    g = GpuLayer(w)
+    o = OracleMirror(w)
+    q = g.qsa
+    nb = w.n0 // 4
+    s1 = torch.empty(nb, dtype=torch.float32, device="cuda")
+    s2 = torch.empty_like(s1)
+    q.qsa_decode_score(g.desc, g.buf.cache, g.state, g.gamma, g.inp.q_idx[0], g.inp.w[0], s1, g.ws)
+    q.qsa_index_score(g.desc, g.buf.cache, nb, g.inp.q_idx[0], g.inp.w[0], s2)
+    assert g.state.n_tokens == w.n0
+    a, b = s1.cpu().numpy(), s2.cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    q_idx, wt, _ = W.host_step_inputs(w, 0, 0)
+    ref, scale = oracle.scores(o.L.summary, nb, q_idx, wt, with_scale=True)
+    check_scores(a, ref, scale)
+    stats = {"ulp_diffs": 0, "exact": 0, "threshold": 0, "attn_err": 0.0}
+    paths = []
+    for s in range(w.steps):
+        _compare_step(g, o, s, stats)
+        paths.append(g.path())
+    print(f"  {stats} paths {paths}")
+    assert paths[0] == q.QSA_PATH_FULL and all(p == q.QSA_PATH_HIST for p in paths[1:]), paths
