@@ -288,6 +288,30 @@ qsa_status qsa_chunk_step(const qsa_layer_desc *desc, const qsa_layer_cache *cac
                           int32_t *sel_out, float *scores_out, void *ws, size_t ws_bytes,
                           hipStream_t stream);
 
+/* qsa_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Its workspace is a static device array
+ * of QSA_STATIC_SCRATCH_BYTES per GPU, part of the library's image: every
+ * GPU the library runs on holds it until the process ends, and the call
+ * allocates nothing.  Arguments, results and errors are those of
+ * qsa_decode_step, plus QSA_ERR_WORKSPACE when the cache's workspace
+ * (qsa_workspace_bytes(desc, capacity)) exceeds the static one.  With the
+ * 4 x 128 f16 indexer, 16 / 2 x 256 attention and top 2048 tokens every
+ * capacity the library takes fits (6.3 MiB at 2^21 tokens); shapes with many
+ * KV heads or a much larger top-k can exceed it.
+ * Every call on one GPU shares that GPU's array and its contents carry from
+ * call to call: calls that may overlap on one GPU (different streams not
+ * ordered with each other) race and give wrong results.  Stream-ordered calls
+ * need nothing cleared: the decode step checks its histogram region's tag,
+ * so a region left by another layer or sequence only makes the next call
+ * take the full top-k (same results). */
+#define QSA_STATIC_SCRATCH_BYTES (16u << 20)
+qsa_status qsa_decode_step_static(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
+                                  qsa_seq_state *st, const void *idx_k_row, const uint16_t *k_row,
+                                  const uint16_t *v_row, const float *gamma, const float *q_idx,
+                                  const float *w, const float *q, float *out, int32_t *sel_out,
+                                  float *scores_out, hipStream_t stream);
+
 /* Stage 2 of qsa_decode_step on its own [post 10, "QSA indexer": block scores
  * s_b = sum_h w_h <q_idx_h, summary_b,h>], as the step launches it: the score
  * pass over the floor(st->n_tokens / 4) completed blocks (no append, no

@@ -6,6 +6,7 @@
 
 #include <atomic>
 #include <chrono>
+#include <mutex>
 
 #include "qsa_internal.h"
 #include "qsa_select.h"
@@ -669,6 +670,62 @@ qsa_status qsa_decode_step(const qsa_layer_desc *desc, const qsa_layer_cache *ca
     st->n_tokens = n;
     st->n_valid_blocks = nb;
     return ok();
+}
+
+// ----------------------------------------------- decode step without allocation
+// The workspace of qsa_decode_step_static: one array per device, held until
+// the process ends.  Host code never uses the array's name as an address:
+// the device address comes from hipGetSymbolAddress, once per device, with
+// that device current.
+static __device__ __align__(256) unsigned char scratch[QSA_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch` (its address looked up once).
+qsa_status static_scratch(void **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_fail(e, "decode_step_static/hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(QSA_ERR_UNSUPPORTED, "device %d beyond the %d the static workspace serves", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "decode_step_static/hipGetSymbolAddress");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return QSA_OK;
+}
+}  // namespace
+
+qsa_status qsa_decode_step_static(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
+                                  qsa_seq_state *st, const void *idx_k_row, const uint16_t *k_row,
+                                  const uint16_t *v_row, const float *gamma, const float *q_idx,
+                                  const float *w, const float *q, float *out, int32_t *sel_out,
+                                  float *scores_out, hipStream_t stream)
+{
+    qsa_status s;
+    if ((s = check_desc(desc)) != QSA_OK || (s = check_cache(cache, true, true, true)) != QSA_OK)
+        return s;
+    const size_t need = decode_layout(desc, cache->capacity).total;
+    if (need > (size_t)QSA_STATIC_SCRATCH_BYTES)
+        return fail(QSA_ERR_WORKSPACE,
+                    "this cache needs a %zu-byte workspace, above the static one's %zu bytes "
+                    "(use qsa_decode_step with a workspace)",
+                    need, (size_t)QSA_STATIC_SCRATCH_BYTES);
+    void *ws = nullptr;
+    if ((s = static_scratch(&ws)) != QSA_OK)
+        return s;
+    return qsa_decode_step(desc, cache, st, idx_k_row, k_row, v_row, gamma, q_idx, w, q, out, sel_out,
+                           scores_out, ws, (size_t)QSA_STATIC_SCRATCH_BYTES, stream);
 }
 
 qsa_status qsa_decode_score(const qsa_layer_desc *desc, const qsa_layer_cache *cache,

@@ -21,7 +21,7 @@ QSA_F32, QSA_F16 = 0, 1
 # Entry points declared in include/qsa.h (checked by the ABI test).
 EXPORTS = ("qsa_workspace_bytes", "qsa_state_invalidate", "qsa_state_truncate",
            "qsa_cache_update", "qsa_index_score", "qsa_topk_blocks", "qsa_gather_attend",
-           "qsa_decode_step", "qsa_decode_score", "qsa_batch_workspace_bytes", "qsa_decode_step_batch",
+           "qsa_decode_step", "qsa_decode_step_static", "qsa_decode_score", "qsa_batch_workspace_bytes", "qsa_decode_step_batch",
            "qsa_chunk_workspace_bytes", "qsa_chunk_step", "qsa_multi_workspace_bytes",
            "qsa_decode_step_multi", "qsa_ablation_workspace_bytes", "qsa_topk_cells",
            "qsa_attend_masked", "qsa_q8_0_quantize", "qsa_gather_attend_q8_0",
@@ -94,6 +94,7 @@ def lib():
         L.qsa_gather_attend.argtypes = [D, C, i32, P, i32, P, P, P, sz, P]
         L.qsa_decode_step.argtypes = [D, C, S, P, P, P, P, P, P, P, P, P, P, P, sz, P]
         L.qsa_decode_score.argtypes = [D, C, S, P, P, P, P, P, sz, P]
+        L.qsa_decode_step_static.argtypes = [D, C, S, P, P, P, P, P, P, P, P, P, P, P]
         L.qsa_batch_workspace_bytes.restype = sz
         L.qsa_batch_workspace_bytes.argtypes = [D, i32, ctypes.POINTER(i32)]
         L.qsa_decode_step_batch.argtypes = [D, i32, C, S, ctypes.POINTER(qsa_seq_io), P, P, sz, P]
@@ -110,7 +111,7 @@ def lib():
         L.qsa_q8_0_quantize.argtypes = [P, ctypes.c_int64, P, P, P]
         L.qsa_gather_attend_q8_0.argtypes = [D, ctypes.POINTER(qsa_kv_q8_0), i32, P, i32, P, P, P, sz, P]
         for f in ("qsa_cache_update", "qsa_index_score", "qsa_topk_blocks", "qsa_gather_attend",
-                  "qsa_decode_step", "qsa_decode_score", "qsa_decode_step_batch", "qsa_chunk_step",
+                  "qsa_decode_step", "qsa_decode_step_static", "qsa_decode_score", "qsa_decode_step_batch", "qsa_chunk_step",
                   "qsa_decode_step_multi", "qsa_topk_cells", "qsa_attend_masked",
                   "qsa_q8_0_quantize", "qsa_gather_attend_q8_0"):
             getattr(L, f).restype = ctypes.c_int
@@ -211,6 +212,14 @@ def qsa_decode_step(desc, cache, state, idx_k_row, k_row, v_row, gamma, q_idx, w
                                  _ptr(idx_k_row), _ptr(k_row), _ptr(v_row), _ptr(gamma), _ptr(q_idx),
                                  _ptr(w), _ptr(q), _ptr(out), _ptr(sel_out), _ptr(scores_out),
                                  p, n, _stream(stream)))
+
+
+def qsa_decode_step_static(desc, cache, state, idx_k_row, k_row, v_row, gamma, q_idx, w, q, out,
+                           sel_out=None, scores_out=None, stream=None):
+    _check(lib().qsa_decode_step_static(ctypes.byref(desc), ctypes.byref(cache), ctypes.byref(state),
+                                        _ptr(idx_k_row), _ptr(k_row), _ptr(v_row), _ptr(gamma),
+                                        _ptr(q_idx), _ptr(w), _ptr(q), _ptr(out), _ptr(sel_out),
+                                        _ptr(scores_out), _stream(stream)))
 
 
 def qsa_decode_score(desc, cache, state, gamma, q_idx, w, scores_out=None, ws=None, stream=None):

@@ -258,3 +258,22 @@ def test_q8_0_argument_errors_before_launch():
     bad_desc = qsa.make_desc(4, 128, qsa.QSA_F16, 16, 2, 96, 2048)
     assert L.qsa_gather_attend_q8_0(ctypes.byref(bad_desc), K, 4096, P(16), 5, P(16), P(16), P(256),
                                     need, None) < 0
+
+
+def test_static_workspace_too_small_is_an_error_before_launch():
+    """qsa_decode_step_static rejects, before touching the device, a cache
+    whose workspace exceeds its static one (many KV heads, large top-k)."""
+    import sparse_attention_decode_cache_amd as qsa
+    L = qsa.lib()
+    d = qsa.make_desc(4, 128, qsa.QSA_F16, 256, 32, 256, 16380)
+    c = qsa.qsa_layer_cache(0x1000, 0x2000, 0x3000, 0x4000, 1 << 20)
+    assert qsa.qsa_workspace_bytes(d, 1 << 20) > L_STATIC_BYTES
+    st = qsa.qsa_seq_state(10, 0)
+    rc = L.qsa_decode_step_static(ctypes.byref(d), ctypes.byref(c), ctypes.byref(st),
+                                  *[ctypes.c_void_p(16)] * 8, None, None, None)
+    assert rc == -3
+    assert b"static" in L.qsa_last_error()
+    assert (st.n_tokens, st.n_valid_blocks) == (10, 0)
+
+
+L_STATIC_BYTES = 16 << 20      # QSA_STATIC_SCRATCH_BYTES in include/qsa.h
