@@ -71,6 +71,9 @@ def lib():
         L.qsa_oracle_cells.restype = l
         L.qsa_oracle_cells.argtypes = [P, l, l, P]
         L.qsa_oracle_attend.argtypes = [P, P, P, P, l, i, i, i, d, P]
+        L.qsa_oracle_union_blocks.restype = l
+        L.qsa_oracle_union_blocks.argtypes = [P, P, i, i, P, l]
+        L.qsa_oracle_union_attend.argtypes = [P, P, P, P, P, P, i, i, i, i, i, d, P]
         L.qsa_oracle_threads.restype = i
         L.qsa_oracle_threads.argtypes = []
         L.qsa_oracle_set_threads.argtypes = [i]
@@ -188,6 +191,48 @@ def attend(q, K, V, cell_ids, scale=None):
     out = np.empty((Hq, Dh), np.float64)
     lib().qsa_oracle_attend(_p(q), _p(K.view(np.uint16)), _p(V.view(np.uint16)), _p(c),
                             c.shape[0], Hq, Hkv, Dh, float(scale), _p(out))
+    return out
+
+
+def _sel_matrix(sels):
+    nq = len(sels)
+    kb = max(1, max(len(x) for x in sels))
+    m = np.zeros((nq, kb), np.int32)
+    k = np.zeros(nq, np.int32)
+    for i, x in enumerate(sels):
+        m[i, :len(x)] = x
+        k[i] = len(x)
+    return m, k, kb
+
+
+def union_blocks(sels):
+    """Ascending union of the queries' ascending block-id lists."""
+    m, k, kb = _sel_matrix(sels)
+    cap = int(k.sum()) + 1
+    out = np.empty(cap, np.int32)
+    nu = lib().qsa_oracle_union_blocks(_p(m), _p(k), len(sels), kb, _p(out), cap)
+    assert nu >= 0
+    return out[:nu].copy()
+
+
+def union_attend(q, K, V, sels, n, scale=None):
+    """Grouped-union attention of a group of queries (a reading: each query
+    attends over the union of the group's cells with the others masked).
+    q: [nq, Hq, Dh] fp32; sels: list of ascending id arrays; n: tokens seen
+    per query.  Returns [nq, Hq, Dh] float64."""
+    q = _c(q, np.float32)
+    nq, Hq, Dh = q.shape
+    K = np.ascontiguousarray(K)
+    V = np.ascontiguousarray(V)
+    assert K.dtype == np.float16 and V.dtype == np.float16
+    Hkv = K.shape[1]
+    m, k, kb = _sel_matrix(sels)
+    nn = _c(n, np.int64)
+    if scale is None:
+        scale = 1.0 / np.sqrt(Dh)
+    out = np.empty((nq, Hq, Dh), np.float64)
+    lib().qsa_oracle_union_attend(_p(q), _p(K.view(np.uint16)), _p(V.view(np.uint16)), _p(m), _p(k), _p(nn),
+                                  nq, kb, Hq, Hkv, Dh, float(scale), _p(out))
     return out
 
 

@@ -313,6 +313,140 @@ void qsa_oracle_attend(const float *q, const uint16_t *K, const uint16_t *V,
     }
 }
 
+/* ---- grouped-union prefill attention (a reading) --------------------------
+ * Post 10 (opening paragraphs; "Vulkan版のプロファイリングでTGが遅くなった
+ * 原因を調べる"; "COMMON-004実装結果", the prefill paragraph) names a "QSA
+ * grouped-union" that sped up prefill in an earlier build and does not define
+ * it.  Reading: consecutive queries of a prefill chunk form a group; the
+ * group reads the K / V rows of the UNION of its queries' chosen blocks, and
+ * of the cells from the first query's completed blocks to the last query's
+ * token (the queries' tails), once, and each query attends over that union
+ * with every cell outside its own cells masked out -- so each query's result
+ * is its own QSA attention (chosen blocks' cells and its tail).
+ *
+ * qsa_oracle_union_blocks: the union of nq ascending id lists (query i's
+ * ids at sel[i * kb .. + ksel[i])), ascending, into uni (capacity cap);
+ * returns its size (or -1 past cap). */
+static int cmp_i32(const void *a, const void *b)
+{
+    const int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+    return (x > y) - (x < y);
+}
+
+long qsa_oracle_union_blocks(const int32_t *sel, const int32_t *ksel, int nq, int kb, int32_t *uni, long cap)
+{
+    long m = 0;
+    for (int i = 0; i < nq; ++i)
+        m += ksel[i];
+    int32_t *all = (int32_t *)malloc(sizeof(int32_t) * (size_t)(m > 0 ? m : 1));
+    long p = 0;
+    for (int i = 0; i < nq; ++i)
+        for (int j = 0; j < ksel[i]; ++j)
+            all[p++] = sel[(size_t)i * kb + j];
+    qsort(all, (size_t)m, sizeof(int32_t), cmp_i32);
+    long u = 0;
+    for (long j = 0; j < m; ++j) {
+        if (j > 0 && all[j] == all[j - 1])
+            continue;
+        if (u >= cap) {
+            free(all);
+            return -1;
+        }
+        uni[u++] = all[j];
+    }
+    free(all);
+    return u;
+}
+
+/* Whether id is in the ascending list l[0 .. len). */
+static int in_sorted(const int32_t *l, int len, int32_t id)
+{
+    int lo = 0, hi = len;
+    while (lo < hi) {
+        const int mid = (lo + hi) / 2;
+        if (l[mid] < id)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    return lo < len && l[lo] == id;
+}
+
+/* qsa_oracle_union_attend: q [nq][Hq][Dh] fp32; n[i] tokens seen by query i;
+ * sel / ksel / kb as above (each query's ids below n[i] / 4); K, V
+ * [tokens][Hkv][Dh] binary16; out [nq][Hq][Dh].  Steps: the union of the
+ * ids; its cells (4 per block, ascending) followed by the group's tail range
+ * [4 floor(n_first / 4), n_last); for each query and head a softmax over
+ * those cells with a cell counting only when it is one of the query's own
+ * (in one of its chosen blocks, or in [4 floor(n_i / 4), n_i)). */
+void qsa_oracle_union_attend(const float *q, const uint16_t *K, const uint16_t *V, const int32_t *sel,
+                             const int32_t *ksel, const int64_t *n, int nq, int kb, int Hq, int Hkv, int Dh,
+                             double scale, double *out)
+{
+    long cap = (long)nq * kb + 1;
+    int32_t *uni = (int32_t *)malloc(sizeof(int32_t) * (size_t)cap);
+    const long nu = qsa_oracle_union_blocks(sel, ksel, nq, kb, uni, cap);
+    int64_t t0 = n[0] / 4 * 4, t1 = n[0];
+    for (int i = 1; i < nq; ++i) {
+        if (n[i] / 4 * 4 < t0)
+            t0 = n[i] / 4 * 4;
+        if (n[i] > t1)
+            t1 = n[i];
+    }
+    const long ncell = 4 * nu + (long)(t1 - t0);
+    int64_t *cell = (int64_t *)malloc(sizeof(int64_t) * (size_t)(ncell > 0 ? ncell : 1));
+    for (long u = 0; u < nu; ++u)
+        for (int r = 0; r < 4; ++r)
+            cell[4 * u + r] = 4 * (int64_t)uni[u] + r;
+    for (int64_t c = t0; c < t1; ++c)
+        cell[4 * nu + (c - t0)] = c;
+    const size_t row = (size_t)Hkv * Dh;
+    double *lg = (double *)malloc(sizeof(double) * (size_t)(ncell > 0 ? ncell : 1));
+    char *own = (char *)malloc((size_t)(ncell > 0 ? ncell : 1));
+    for (int i = 0; i < nq; ++i) {
+        const int32_t *si = sel + (size_t)i * kb;
+        const int64_t tail0 = n[i] / 4 * 4;
+        for (long c = 0; c < ncell; ++c) {
+            if (c < 4 * nu)
+                own[c] = (char)in_sorted(si, ksel[i], uni[c / 4]);
+            else
+                own[c] = (char)(cell[c] >= tail0 && cell[c] < n[i]);
+        }
+        for (int h = 0; h < Hq; ++h) {
+            const int g = (int)(((long)h * Hkv) / Hq);
+            const float *qh = q + ((size_t)i * Hq + h) * Dh;
+            double mx = -INFINITY;
+            for (long c = 0; c < ncell; ++c) {
+                if (!own[c])
+                    continue;
+                const size_t base = (size_t)cell[c] * row + (size_t)g * Dh;
+                double dot = 0.0;
+                for (int d = 0; d < Dh; ++d)
+                    dot += (double)qh[d] * qsa_oracle_half_to_double(K[base + d]);
+                lg[c] = scale * dot;
+                if (lg[c] > mx)
+                    mx = lg[c];
+            }
+            double z = 0.0;
+            for (long c = 0; c < ncell; ++c) {
+                lg[c] = own[c] ? exp(lg[c] - mx) : 0.0;
+                z += lg[c];
+            }
+            for (int d = 0; d < Dh; ++d) {
+                double acc = 0.0;
+                for (long c = 0; c < ncell; ++c)
+                    if (own[c])
+                        acc += lg[c] * qsa_oracle_half_to_double(V[(size_t)cell[c] * row + (size_t)g * Dh + d]);
+                out[((size_t)i * Hq + h) * Dh + d] = acc / z;
+            }
+        }
+    }
+    free(own);
+    free(lg);
+    free(cell);
+    free(uni);
+}
+
 /* ---- q8_0 K/V: 8-bit codes, one binary16 scale per 32 values --------------
  * The tuning post (the one on runtime parameters, section "KV cacheをQ8_0に
  * してみる") runs llama.cpp with its q8_0 K/V cache type and gives no format;
