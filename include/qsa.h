@@ -333,6 +333,26 @@ qsa_status qsa_decode_score(const qsa_layer_desc *desc, const qsa_layer_cache *c
                             const float *w, float *scores_out, void *ws, size_t ws_bytes,
                             hipStream_t stream);
 
+/* qsa_chunk_step with grouped-union attention [post 10 names a "QSA
+ * grouped-union" that sped up prefill (opening paragraphs; "Vulkan版の
+ * プロファイリングでTGが遅くなった原因を調べる"; "COMMON-004実装結果", the
+ * prefill paragraph) and does not define it; this is a reading].
+ * Consecutive queries of the chunk form groups of 16 / G (G = q_heads /
+ * kv_heads; fewer when 16 / G times K ids exceed 4,096 or their bitmaps
+ * exceed 128 KB); a group reads the K / V rows of the union of its queries'
+ * chosen blocks and of its queries' tail cells once, and each query attends
+ * over that union with the cells that are not its own masked out.  Results,
+ * arguments, workspace (qsa_chunk_workspace_bytes covers both) and errors
+ * are qsa_chunk_step's, plus UNSUPPORTED when no group fits; outputs equal
+ * qsa_chunk_step's up to the order of the softmax sums.  A chunk of at most
+ * QSA_MAX_MULTI tokens runs as qsa_decode_step_multi, as there. */
+qsa_status qsa_chunk_step_grouped(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
+                                  qsa_seq_state *st, int32_t n_q, const void *idx_k_rows,
+                                  const uint16_t *k_rows, const uint16_t *v_rows, const float *gamma,
+                                  const float *q_idx, const float *w, const float *q, float *out,
+                                  int32_t *sel_out, float *scores_out, void *ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
 /* ------------------------------------------------ multi-query decode
  * Speculative verification: the token at pos_0 = st->n_tokens and up to
  * QSA_MAX_MULTI - 1 drafted tokens after it, decoded in one call with the

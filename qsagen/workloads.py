@@ -100,6 +100,25 @@ def host_step_inputs(w: Workload, layer, step, seq=0):
     return q_idx, wt, q
 
 
+# Correlated queries: consecutive tokens of one passage tend to choose
+# overlapping blocks (the case a grouped-union prefill serves); here the
+# indexer query of step s is sqrt(rho) B + sqrt(1 - rho) N_s, B one seeded
+# N(0,1) tensor per layer and N_s step s's own q_idx (computed in double,
+# rounded once to fp32).
+CORR_BASE_STEP = (1 << 24) - 1          # step slot of the shared tensor B
+
+
+def host_correlated_q_idx(w: Workload, layer, first_step, steps, rho, seq=0):
+    """[steps, H_i, D_i] fp32 correlated indexer queries (see above)."""
+    base = host_normal(w.idx_row, w.seed, tensor_id(KIND_QIDX, layer=layer, step=CORR_BASE_STEP, seq=seq))
+    out = np.empty((steps,) + w.idx_row, np.float32)
+    for s in range(steps):
+        noise = host_step_inputs(w, layer, first_step + s, seq)[0]
+        out[s] = (np.sqrt(rho) * base.astype(np.float64) +
+                  np.sqrt(1.0 - rho) * noise.astype(np.float64)).astype(np.float32)
+    return out
+
+
 # ---------------------------------------------------------------- device side
 def poison_(t):
     """Fill with NaN so that a row read before it is written shows up."""

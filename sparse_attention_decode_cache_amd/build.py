@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libqsa.so")
 SOURCES = ["qsa_api.hip", "k_update.hip", "k_score.hip", "k_select.hip", "k_attend.hip", "k_chunk.hip",
-           "k_decode.hip"]
+           "k_decode.hip", "k_union.hip"]
 FLAGS = ["-O3", "--offload-arch=gfx950", "-fPIC", "-shared", "-std=c++17", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

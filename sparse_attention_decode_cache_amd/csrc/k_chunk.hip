@@ -654,6 +654,8 @@ hipError_t launch_chunk_rest(ChunkArgs c, bool f16, int Dh, int G, hipStream_t s
         if ((e = hipGetLastError()) != hipSuccess)
             return e;
     }
+    if (c.union_q > 0)
+        return launch_union(c, Dh, G, s);
     switch (Dh) {
     case 64: return attend_g<64>(c, G, s);
     case 128: return attend_g<128>(c, G, s);

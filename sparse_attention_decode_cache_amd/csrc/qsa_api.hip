@@ -151,7 +151,7 @@ uint64_t next_epoch()
 // Prefill-chunk workspace: folded queries, their scales, the keys of every
 // (query, block), the chosen ids and the attention partials.
 struct ChunkLayout {
-    size_t qhl, qscale, keys, sel, part, total;
+    size_t qhl, qscale, keys, sel, part, uni, umask, ucount, total;
 };
 
 ChunkLayout chunk_layout(const qsa_layer_desc *d, int32_t capacity, int32_t n_q)
@@ -172,8 +172,26 @@ ChunkLayout chunk_layout(const qsa_layer_desc *d, int32_t capacity, int32_t n_q)
     L.keys = take(sizeof(uint32_t) * (size_t)n_q * ldk);
     L.sel = take(sizeof(int32_t) * (size_t)n_q * (d->top_k_tokens / 4));
     L.part = take(sizeof(float) * 2 * (size_t)kChunkWgTarget * part_stride(G, d->head_dim));
+    // the grouped-union lists: at most n_q groups of up to 16 queries' ids
+    const size_t uents = ((size_t)n_q + 16) * (size_t)(d->top_k_tokens / 4);
+    L.uni = take(sizeof(int32_t) * uents);
+    L.umask = take(sizeof(uint32_t) * uents);
+    L.ucount = take(sizeof(int32_t) * (size_t)n_q);
     L.total = off;
     return L;
+}
+
+// Queries per group of the grouped-union attention: as many as fill the 16
+// rows of a matrix-core tile, fewer when their ids would not fit the
+// kernel's LDS lists or their bitmaps the union build's LDS.
+int union_group(const qsa_layer_desc *d, int32_t nb_last)
+{
+    const int G = d->q_heads / d->kv_heads;
+    const int32_t K = d->top_k_tokens / 4;
+    int qg = 16 / G;
+    while (qg > 1 && ((int64_t)qg * K > kChunkMaxIds || union_build_lds(qg, nb_last) > kUnionBuildLds))
+        --qg;
+    return (int64_t)qg * K <= kChunkMaxIds && union_build_lds(qg, nb_last) <= kUnionBuildLds ? qg : 0;
 }
 
 qsa_status check_ws(void *ws, size_t ws_bytes, size_t need)
@@ -1003,12 +1021,12 @@ size_t qsa_chunk_workspace_bytes(const qsa_layer_desc *desc, int32_t capacity, i
     return multi > chunk ? multi : chunk;
 }
 
-qsa_status qsa_chunk_step(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
-                          qsa_seq_state *st, int32_t n_q, const void *idx_k_rows,
-                          const uint16_t *k_rows, const uint16_t *v_rows, const float *gamma,
-                          const float *q_idx, const float *w, const float *q, float *out,
-                          int32_t *sel_out, float *scores_out, void *ws, size_t ws_bytes,
-                          hipStream_t stream)
+namespace {
+qsa_status chunk_step(const qsa_layer_desc *desc, const qsa_layer_cache *cache, qsa_seq_state *st,
+                      int32_t n_q, const void *idx_k_rows, const uint16_t *k_rows, const uint16_t *v_rows,
+                      const float *gamma, const float *q_idx, const float *w, const float *q, float *out,
+                      int32_t *sel_out, float *scores_out, void *ws, size_t ws_bytes, hipStream_t stream,
+                      bool grouped)
 {
     qsa_status s;
     if ((s = check_desc(desc)) != QSA_OK || (s = check_cache(cache, true, true, true)) != QSA_OK)
@@ -1083,6 +1101,16 @@ qsa_status qsa_chunk_step(const qsa_layer_desc *desc, const qsa_layer_cache *cac
     ns = ns < kChunkMaxSplits ? ns : kChunkMaxSplits;
     ns = (max_it + (max_it + ns - 1) / ns - 1) / ((max_it + ns - 1) / ns);   // no split left empty
     c.n_split = (int32_t)ns;
+    if (grouped) {
+        const int qg = union_group(desc, nb_last);
+        if (qg < 1)
+            return fail(QSA_ERR_UNSUPPORTED, "no grouped-union group fits these shapes");
+        c.union_q = qg;
+        c.ucap = qg * K;
+        c.uni = (int32_t *)(wsp + L.uni);
+        c.umask = (uint32_t *)(wsp + L.umask);
+        c.ucount = (int32_t *)(wsp + L.ucount);
+    }
 
     hipError_t e = launch_chunk_append(c, stream);
     if (e != hipSuccess)
@@ -1101,6 +1129,29 @@ qsa_status qsa_chunk_step(const qsa_layer_desc *desc, const qsa_layer_cache *cac
     st->n_tokens = n_end;
     st->n_valid_blocks = nb_last;
     return ok();
+}
+}  // namespace
+
+qsa_status qsa_chunk_step(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
+                          qsa_seq_state *st, int32_t n_q, const void *idx_k_rows,
+                          const uint16_t *k_rows, const uint16_t *v_rows, const float *gamma,
+                          const float *q_idx, const float *w, const float *q, float *out,
+                          int32_t *sel_out, float *scores_out, void *ws, size_t ws_bytes,
+                          hipStream_t stream)
+{
+    return chunk_step(desc, cache, st, n_q, idx_k_rows, k_rows, v_rows, gamma, q_idx, w, q, out, sel_out,
+                      scores_out, ws, ws_bytes, stream, false);
+}
+
+qsa_status qsa_chunk_step_grouped(const qsa_layer_desc *desc, const qsa_layer_cache *cache,
+                                  qsa_seq_state *st, int32_t n_q, const void *idx_k_rows,
+                                  const uint16_t *k_rows, const uint16_t *v_rows, const float *gamma,
+                                  const float *q_idx, const float *w, const float *q, float *out,
+                                  int32_t *sel_out, float *scores_out, void *ws, size_t ws_bytes,
+                                  hipStream_t stream)
+{
+    return chunk_step(desc, cache, st, n_q, idx_k_rows, k_rows, v_rows, gamma, q_idx, w, q, out, sel_out,
+                      scores_out, ws, ws_bytes, stream, true);
 }
 
 size_t qsa_ablation_workspace_bytes(const qsa_layer_desc *desc, int32_t capacity)

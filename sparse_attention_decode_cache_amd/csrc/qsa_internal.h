@@ -320,7 +320,18 @@ struct ChunkArgs {
     int32_t kv_heads, n_split;
     int32_t sel_cache_keys;     // the select keeps each query's keys in LDS (set by the launcher)
     float scale;
+    // grouped-union attention (k_union.hip) instead of the per-query one when
+    // union_q > 0: groups of union_q consecutive queries
+    int32_t union_q;
+    int32_t ucap;               // union entries per group (>= union_q * kb)
+    int32_t *uni;               // workspace: [groups][ucap] union block ids, ascending
+    uint32_t *umask;            // workspace: [groups][ucap] queries (bits) that chose each
+    int32_t *ucount;            // workspace: [groups] union sizes
 };
+// Grouped-union attention of a chunk: the union build, then the attention.
+constexpr size_t kUnionBuildLds = 128 * 1024;
+size_t union_build_lds(int qg, int32_t nb_last);
+hipError_t launch_union(const ChunkArgs &c, int Dh, int G, hipStream_t s);
 // The gather switched off (an ablation of the selected K/V gather): flash-
 // decode over every cached K / V row, the blocks outside `sel` masked out of
 // the softmax.  Same cells as the gathered attention.

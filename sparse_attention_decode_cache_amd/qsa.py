@@ -22,7 +22,8 @@ QSA_F32, QSA_F16 = 0, 1
 EXPORTS = ("qsa_workspace_bytes", "qsa_state_invalidate", "qsa_state_truncate",
            "qsa_cache_update", "qsa_index_score", "qsa_topk_blocks", "qsa_gather_attend",
            "qsa_decode_step", "qsa_decode_step_static", "qsa_decode_score", "qsa_batch_workspace_bytes", "qsa_decode_step_batch",
-           "qsa_chunk_workspace_bytes", "qsa_chunk_step", "qsa_multi_workspace_bytes",
+           "qsa_chunk_workspace_bytes", "qsa_chunk_step", "qsa_chunk_step_grouped",
+           "qsa_multi_workspace_bytes",
            "qsa_decode_step_multi", "qsa_ablation_workspace_bytes", "qsa_topk_cells",
            "qsa_attend_masked", "qsa_q8_0_quantize", "qsa_gather_attend_q8_0",
            "qsa_status_string", "qsa_last_error")
@@ -101,6 +102,7 @@ def lib():
         L.qsa_chunk_workspace_bytes.restype = sz
         L.qsa_chunk_workspace_bytes.argtypes = [D, i32, i32]
         L.qsa_chunk_step.argtypes = [D, C, S, i32, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+        L.qsa_chunk_step_grouped.argtypes = [D, C, S, i32, P, P, P, P, P, P, P, P, P, P, P, sz, P]
         L.qsa_multi_workspace_bytes.restype = sz
         L.qsa_multi_workspace_bytes.argtypes = [D, i32, i32]
         L.qsa_decode_step_multi.argtypes = [D, C, S, i32, P, P, P, P, P, P, P, P, P, P, P, sz, P]
@@ -111,7 +113,7 @@ def lib():
         L.qsa_q8_0_quantize.argtypes = [P, ctypes.c_int64, P, P, P]
         L.qsa_gather_attend_q8_0.argtypes = [D, ctypes.POINTER(qsa_kv_q8_0), i32, P, i32, P, P, P, sz, P]
         for f in ("qsa_cache_update", "qsa_index_score", "qsa_topk_blocks", "qsa_gather_attend",
-                  "qsa_decode_step", "qsa_decode_step_static", "qsa_decode_score", "qsa_decode_step_batch", "qsa_chunk_step",
+                  "qsa_decode_step", "qsa_decode_step_static", "qsa_decode_score", "qsa_decode_step_batch", "qsa_chunk_step", "qsa_chunk_step_grouped",
                   "qsa_decode_step_multi", "qsa_topk_cells", "qsa_attend_masked",
                   "qsa_q8_0_quantize", "qsa_gather_attend_q8_0"):
             getattr(L, f).restype = ctypes.c_int
@@ -277,6 +279,15 @@ def qsa_chunk_step(desc, cache, state, n_q, idx_k_rows, k_rows, v_rows, gamma, q
                                 _ptr(idx_k_rows), _ptr(k_rows), _ptr(v_rows), _ptr(gamma), _ptr(q_idx),
                                 _ptr(w), _ptr(q), _ptr(out), _ptr(sel_out), _ptr(scores_out),
                                 p, n, _stream(stream)))
+
+
+def qsa_chunk_step_grouped(desc, cache, state, n_q, idx_k_rows, k_rows, v_rows, gamma, q_idx, w, q, out,
+                           sel_out=None, scores_out=None, ws=None, stream=None):
+    p, n = _ws(ws)
+    _check(lib().qsa_chunk_step_grouped(ctypes.byref(desc), ctypes.byref(cache), ctypes.byref(state),
+                                        int(n_q), _ptr(idx_k_rows), _ptr(k_rows), _ptr(v_rows), _ptr(gamma),
+                                        _ptr(q_idx), _ptr(w), _ptr(q), _ptr(out), _ptr(sel_out),
+                                        _ptr(scores_out), p, n, _stream(stream)))
 
 
 def qsa_multi_workspace_bytes(desc, capacity, n_q):
