@@ -40,6 +40,8 @@ METRIC = "QSA-layer decode steps/s at 256k ctx + achieved HBM GB/s (% of peak)"
 # The whole decode step's share of HBM peak that the method's context-
 # independent design aims at (the pooled-key stream dominating the step).
 STEP_TARGET_FRAC = 0.60
+# Correlation of consecutive chunk queries in the grouped-union comparison.
+CHUNK_RHO = 0.95
 HBM_PEAK_GBS = 8000.0
 
 
@@ -256,11 +258,11 @@ def chunk_bytes(w, n_q):
 
 
 def chunk_flops(w, n_q):
-    """Matrix-core flops of the chunk's score GEMM as run: every query against
-    every block (the causal mask is applied in the epilogue), both f16 halves
-    of the query."""
+    """The method's flops of the chunk's score GEMM: every query against every
+    block (the causal mask is applied in the epilogue), one multiply-add per
+    element (the kernel issues it twice, the query as two f16 halves)."""
     nb_last = (w.n0 + n_q) // 4
-    return 2 * 2 * n_q * nb_last * w.idx_heads * w.idx_dim
+    return 2 * n_q * nb_last * w.idx_heads * w.idx_dim
 
 
 def multi_call_bytes(w, n0, n_q):
@@ -662,25 +664,48 @@ def bench_batch_and_chunk(args, torch, qsa, W, stream, dev):
     out = torch.empty((n_q, w.q_heads, w.head_dim), dtype=torch.float32, device=dev)
     cws = qsa.chunk_workspace(cdesc, w.capacity(), n_q)
     state = qsa.qsa_seq_state(w.n0, w.n0 // 4)
-    times = []
-    for rep in range(args.chunk_reps + 1):
-        qsa.qsa_state_truncate(state, w.n0)      # the same chunk again: re-append, re-pool
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        qsa.qsa_chunk_step(cdesc, buf.cache, state, n_q, inp.raw, inp.k, inp.v, cg, inp.q_idx, inp.w,
-                           inp.q, out, None, None, cws, stream)
-        b.record(stream)
-        times.append((a, b))
-    torch.cuda.synchronize()
-    cms = [a.elapsed_time(b) for a, b in times[1:]]
-    c_ms = statistics.median(cms)
+    q_iid = inp.q_idx.clone()
+    q_corr = torch.from_numpy(W.host_correlated_q_idx(w, 0, 0, n_q, CHUNK_RHO)).to(dev)
+
+    def chunk_ms(fn, q_idx):
+        times = []
+        for rep in range(args.chunk_reps + 1):
+            qsa.qsa_state_truncate(state, w.n0)      # the same chunk again: re-append, re-pool
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn(cdesc, buf.cache, state, n_q, inp.raw, inp.k, inp.v, cg, q_idx, inp.w, inp.q, out, None, None,
+               cws, stream)
+            b.record(stream)
+            times.append((a, b))
+        torch.cuda.synchronize()
+        return statistics.median([a.elapsed_time(b) for a, b in times[1:]])
+
+    def abba(q_idx):
+        a1 = chunk_ms(qsa.qsa_chunk_step, q_idx)
+        b1 = chunk_ms(qsa.qsa_chunk_step_grouped, q_idx)
+        b2 = chunk_ms(qsa.qsa_chunk_step_grouped, q_idx)
+        a2 = chunk_ms(qsa.qsa_chunk_step, q_idx)
+        return (a1 + a2) / 2, (b1 + b2) / 2, [round(x, 4) for x in (a1, b1, b2, a2)]
+
+    c_ms, g_ms, passes = abba(q_iid)
+    cc_ms, gc_ms, passes_c = abba(q_corr)
     cb = chunk_bytes(w, n_q)
-    log(f"prefill chunk: {c_ms:.3f} ms for {n_q} tokens at n0={w.n0}")
+    flops = chunk_flops(w, n_q)
+    log(f"prefill chunk: {c_ms:.3f} ms for {n_q} tokens at n0={w.n0} (grouped-union {g_ms:.3f} ms); "
+        f"correlated queries: {cc_ms:.3f} ms (grouped-union {gc_ms:.3f} ms)")
     res["chunk"] = {
         "workload": w.name, "n0": w.n0, "n_q": n_q, "reps": args.chunk_reps,
         "ms": round(c_ms, 4), "tokens_per_s": round(n_q / (c_ms / 1e3), 1),
         "algorithmic_gbs": round(cb / (c_ms / 1e3) / 1e9, 1), "bytes": cb,
-        "score_gemm_flops": chunk_flops(w, n_q), "mfma_f16_peak_tflops": MFMA_F16_PEAK_TFLOPS}
+        "score_gemm_flops": flops, "score_gemm_flops_issued": 2 * flops,
+        "score_gemm_note": "flops are the method's (2 n_q nb H D); the kernel issues twice that "
+                           "(the query as two f16 halves); the GEMM kernel's own time is in profiles/",
+        "whole_call_tflops": round(flops / (c_ms / 1e3) / 1e12, 2),
+        "mfma_f16_peak_tflops": MFMA_F16_PEAK_TFLOPS,
+        "grouped_union": {"order": "ABBA (per-query, grouped, grouped, per-query)",
+                          "iid_ms": round(g_ms, 4), "iid_per_query_ms": round(c_ms, 4), "iid_passes": passes,
+                          "correlated_rho": CHUNK_RHO, "correlated_ms": round(gc_ms, 4),
+                          "correlated_per_query_ms": round(cc_ms, 4), "correlated_passes": passes_c}}
     return res
 
 
