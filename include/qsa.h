@@ -337,8 +337,9 @@ qsa_status qsa_decode_score(const qsa_layer_desc *desc, const qsa_layer_cache *c
  * grouped-union" that sped up prefill (opening paragraphs; "Vulkan版の
  * プロファイリングでTGが遅くなった原因を調べる"; "COMMON-004実装結果", the
  * prefill paragraph) and does not define it; this is a reading].
- * Consecutive queries of the chunk form groups of 16 / G (G = q_heads /
- * kv_heads; fewer when 16 / G times K ids exceed 4,096 or their bitmaps
+ * Consecutive queries of the chunk form groups of min(64 / G, 32) (G =
+ * q_heads / kv_heads: 64 query x head rows, four matrix-core tiles; fewer
+ * when the group's bitmaps of ceil(n_blocks / 32) words per query would
  * exceed 128 KB); a group reads the K / V rows of the union of its queries'
  * chosen blocks and of its queries' tail cells once, and each query attends
  * over that union with the cells that are not its own masked out.  Results,

@@ -172,8 +172,9 @@ ChunkLayout chunk_layout(const qsa_layer_desc *d, int32_t capacity, int32_t n_q)
     L.keys = take(sizeof(uint32_t) * (size_t)n_q * ldk);
     L.sel = take(sizeof(int32_t) * (size_t)n_q * (d->top_k_tokens / 4));
     L.part = take(sizeof(float) * 2 * (size_t)kChunkWgTarget * part_stride(G, d->head_dim));
-    // the grouped-union lists: at most n_q groups of up to 16 queries' ids
-    const size_t uents = ((size_t)n_q + 16) * (size_t)(d->top_k_tokens / 4);
+    // the grouped-union lists: ceil(n_q / qg) groups of qg <= kUnionMaxQ
+    // queries' ids each
+    const size_t uents = ((size_t)n_q + kUnionMaxQ) * (size_t)(d->top_k_tokens / 4);
     L.uni = take(sizeof(int32_t) * uents);
     L.umask = take(sizeof(uint32_t) * uents);
     L.ucount = take(sizeof(int32_t) * (size_t)n_q);
@@ -181,17 +182,17 @@ ChunkLayout chunk_layout(const qsa_layer_desc *d, int32_t capacity, int32_t n_q)
     return L;
 }
 
-// Queries per group of the grouped-union attention: as many as fill the 16
-// rows of a matrix-core tile, fewer when their ids would not fit the
-// kernel's LDS lists or their bitmaps the union build's LDS.
+// Queries per group of the grouped-union attention: as many as fill 64
+// query x head rows (four matrix-core tiles), at most 32 (the bits of a
+// union block's mask), fewer when their bitmaps would not fit the union
+// build's LDS.
 int union_group(const qsa_layer_desc *d, int32_t nb_last)
 {
     const int G = d->q_heads / d->kv_heads;
-    const int32_t K = d->top_k_tokens / 4;
-    int qg = 16 / G;
-    while (qg > 1 && ((int64_t)qg * K > kChunkMaxIds || union_build_lds(qg, nb_last) > kUnionBuildLds))
+    int qg = kUnionMaxRows / G < kUnionMaxQ ? kUnionMaxRows / G : kUnionMaxQ;
+    while (qg > 1 && union_build_lds(qg, nb_last) > kUnionBuildLds)
         --qg;
-    return (int64_t)qg * K <= kChunkMaxIds && union_build_lds(qg, nb_last) <= kUnionBuildLds ? qg : 0;
+    return qg >= 1 && union_build_lds(qg, nb_last) <= kUnionBuildLds ? qg : 0;
 }
 
 qsa_status check_ws(void *ws, size_t ws_bytes, size_t need)

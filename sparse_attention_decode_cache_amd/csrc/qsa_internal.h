@@ -330,6 +330,8 @@ struct ChunkArgs {
 };
 // Grouped-union attention of a chunk: the union build, then the attention.
 constexpr size_t kUnionBuildLds = 128 * 1024;
+constexpr int kUnionMaxQ = 32;          // queries of a group (bits of a union block's mask)
+constexpr int kUnionMaxRows = 64;       // query x head rows of a group (four matrix-core tiles)
 size_t union_build_lds(int qg, int32_t nb_last);
 hipError_t launch_union(const ChunkArgs &c, int Dh, int G, hipStream_t s);
 // The gather switched off (an ablation of the selected K/V gather): flash-
