@@ -29,6 +29,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 import time
@@ -68,11 +69,20 @@ def score_kernel_bytes(w, nb):
     return idx_row * nb + 4 * (w.idx_heads * w.idx_dim + w.idx_heads) + 4 * nb
 
 
+def source_code(text):
+    """C / HIP source with its comments dropped and its whitespace collapsed:
+    what a change to the kernel has to touch."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash(*paths):
+    """Hash of the code of the given sources (comments and layout aside)."""
     h = hashlib.sha256()
     for path in paths:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update(source_code(f.read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -279,12 +289,37 @@ def multi_call_bytes(w, n0, n_q):
     return idx_row * nb_last + gathered + n_q * (idx_row + 2 * kv_row) + 5 * idx_row * new_blocks + queries
 
 
+def graph_kernel_us(torch, stream, launch_pass, per_pass, reps):
+    """Mean duration of one launch of a kernel: `reps` passes of `per_pass`
+    back-to-back launches (launch_pass(st) enqueues one pass on st) captured
+    in one HIP graph, replayed once untimed and once between HIP events on
+    the stream.  A graph keeps the host's per-call cost (the Python binding,
+    several microseconds a call) out of the figure, so short launches are not
+    timed at the host's rate."""
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cs = torch.cuda.current_stream()
+        for _ in range(reps):
+            launch_pass(cs)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return 1e3 * e0.elapsed_time(e1) / (reps * per_pass)
+
+
 def time_decode(torch, qsa, W, w, desc, stream, dev, steps, warmup, kernel_reps, n_layers=None):
     """n_layers layers of workload w (independent caches, round-robin; default
     w.layers): the mean layer-step time of `steps` decode steps captured in a
     HIP graph (after `warmup` eager steps; one untimed replay, one timed), and
     the score kernel's own time (passes of back-to-back qsa_index_score
-    launches over the same caches)."""
+    launches over the same caches, graph-replayed)."""
     import dataclasses
     n_layers = n_layers or w.layers
     w = dataclasses.replace(w, steps=warmup + steps)
@@ -325,16 +360,12 @@ def time_decode(torch, qsa, W, w, desc, stream, dev, steps, warmup, kernel_reps,
     del graph
     nb = layers[0][3].n_tokens // 4
     scores = torch.empty(nb, dtype=torch.float32, device=dev)
-    durs = []
-    for rep in range(kernel_reps):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for buf, gamma, inp, st in layers:
-            qsa.qsa_index_score(desc, buf.cache, nb, inp.q_idx[0], inp.w[0], scores, stream)
-        b.record(stream)
-        durs.append((a, b))
-    torch.cuda.synchronize()
-    score_us = statistics.mean(1e3 * a.elapsed_time(b) / len(layers) for a, b in durs[1:])
+
+    def score_pass(st):
+        for buf, gamma, inp, state in layers:
+            qsa.qsa_index_score(desc, buf.cache, nb, inp.q_idx[0], inp.w[0], scores, st)
+
+    score_us = graph_kernel_us(torch, stream, score_pass, len(layers), kernel_reps)
     del layers, ws
     torch.cuda.empty_cache()
     return step_us, score_us, nb
@@ -365,8 +396,8 @@ def bench_context_sweep(args, torch, qsa, W, w256, desc, stream, dev, head):
         log(f"context {n0} x {nl} layers: {res[str(n0)]}")
     res[str(w256.n0)] = {"layers": w256.layers, "n_blocks": head["nb"],
                          "layer_step_us": head["layer_step_us"]["mean"],
-                         "score_us": head["roofline"]["avg_launch_us"],
-                         "rest_us": round(head["layer_step_us"]["mean"] - head["roofline"]["avg_launch_us"], 2)}
+                         "score_us": head["roofline"]["scores_only_us"],
+                         "rest_us": round(head["layer_step_us"]["mean"] - head["roofline"]["scores_only_us"], 2)}
     pts = sorted(res.values(), key=lambda r: r["n_blocks"])
     xs = [float(r["n_blocks"]) for r in pts]
     ys = [float(r["layer_step_us"]) for r in pts]
@@ -924,35 +955,28 @@ def main():
     # Dominant kernel: the block-score stream, as the decode step runs it
     # (keys, tile lists and the score histogram besides the scores),
     # launched alone through qsa_decode_score on the same stream over the same
-    # 12 caches (round-robin, so HBM-resident); each pass of 12 back-to-back
-    # launches is bracketed by HIP events, so the average is the kernel's own
-    # duration (back-to-back dispatch leaves no gaps), as rocprofv3 reports
+    # 12 caches (round-robin, so HBM-resident); `kernel_reps` passes of 12
+    # back-to-back launches are captured in a HIP graph and one replay is
+    # bracketed by HIP events on the stream, so the average is the kernel's
+    # own duration plus the graph's short dispatch gap, as rocprofv3 reports
     # it.  The scores-only variant (qsa_index_score) is timed beside it.
     nb = layers[0]["state"].n_tokens // 4
     scores = torch.empty(nb, dtype=torch.float32, device=dev)
 
-    def kernel_passes(fn):
-        durs = []
-        for rep in range(args.kernel_reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
+    def kernel_us(fn):
+        def one_pass(st):
             for L in layers:
-                fn(L)
-            e1.record(stream)
-            durs.append((e0, e1))
-        torch.cuda.synchronize()
-        return [a.elapsed_time(b) / len(layers) for a, b in durs[1:]]   # drop the first pass
+                fn(L, st)
+        return graph_kernel_us(torch, stream, one_pass, len(layers), args.kernel_reps)
 
-    kms = kernel_passes(lambda L: qsa.qsa_decode_score(desc, L["buf"].cache, L["state"], L["gamma"],
-                                                       L["inp"].q_idx[0], L["inp"].w[0], None, ws, stream))
-    oms = kernel_passes(lambda L: qsa.qsa_index_score(desc, L["buf"].cache, nb, L["inp"].q_idx[0],
-                                                      L["inp"].w[0], scores, stream))
-    k_avg_s = statistics.mean(kms) / 1e3
-    scores_only_us = 1e3 * statistics.mean(oms)
+    k_avg_s = 1e-6 * kernel_us(lambda L, st: qsa.qsa_decode_score(
+        desc, L["buf"].cache, L["state"], L["gamma"], L["inp"].q_idx[0], L["inp"].w[0], None, ws, st))
+    scores_only_us = kernel_us(lambda L, st: qsa.qsa_index_score(
+        desc, L["buf"].cache, nb, L["inp"].q_idx[0], L["inp"].w[0], scores, st))
     kbytes = score_kernel_bytes(w, nb)
     achieved = kbytes / k_avg_s / 1e9
     traffic = traffic_record(w, nb)
-    log(f"score kernel (in-step variant): {1e6 * k_avg_s:.2f} us avg over {len(kms) * len(layers)} launches, "
+    log(f"score kernel (in-step variant): {1e6 * k_avg_s:.2f} us avg over {args.kernel_reps * len(layers)} launches, "
         f"{achieved:.0f} GB/s; scores only {scores_only_us:.2f} us")
 
     result = {

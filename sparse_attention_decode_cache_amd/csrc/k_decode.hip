@@ -11,9 +11,10 @@
 // cells of the winners among its tiles' list entries.  The kernel is bound by
 // latency, and with 16 waves on a CU every instruction all of them execute
 // costs 16 cycles, so each phase runs on the waves that need it:
-//   1. one round of loads: thread t two bins of the histogram (count and
-//      extremes, top bins first), wave 4 the tiles' last-entry maxima,
-//      thread t the split's list entry t, waves 8-15 the q operand;
+//   1. one round of loads: thread t < 512 four bins of the histogram
+//      (count and extremes, top bins first) and the split's list entries t
+//      and 512 + t; wave 8 the tiles' last-entry maxima; waves 8-15 the q
+//      operand;
 //   2. a prefix sum over the threads finds the bin d holding the k-th
 //      largest entry, how many of bin d win (`need`), kappa from the bin's
 //      extremes and the top nonempty bin;

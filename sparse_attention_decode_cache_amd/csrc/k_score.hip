@@ -13,10 +13,15 @@
 // finishes V rows in log2(L) rounds.  w[h] is folded into q_idx once per
 // workgroup, into LDS.
 //
-// Outputs (all optional, plain stores, no atomics): fp32 scores; the
-// order-preserving 32-bit key of every score; and, for the top-k, each tile's
-// T largest composite keys (key << 32 | ~block), sorted descending (T is
-// chosen per call, R/8 .. R/2).  Up to 4 queries of one sequence (the tokens
+// Outputs (all optional, plain stores): fp32 scores; the order-preserving
+// 32-bit key of every score; and, for the top-k, each tile's T largest
+// composite keys (key << 32 | ~block), sorted descending (T is chosen per
+// call, R/8 .. R/2).  In the decode step the list entries inside the score
+// window also go into the global score histogram of qsa_hist.h, by relaxed
+// device-scope atomics whose results no lane waits for (count, largest and
+// smallest composite of the bin, and the largest last entry of the tiles'
+// lists); the window is set from the fed-back ratios before the rows arrive.
+// Up to 4 queries of one sequence (the tokens
 // of a speculative-verify call) share one pass: every chunk is loaded once
 // and dotted with each query, each query with its own causal block limit.
 //
