@@ -976,6 +976,24 @@ def main():
     kbytes = score_kernel_bytes(w, nb)
     achieved = kbytes / k_avg_s / 1e9
     traffic = traffic_record(w, nb)
+
+    # Which selection path the decode steps take (untimed): two more rounds of
+    # the 12 layers, each step read back and then dropped again
+    # (qsa_state_truncate), so the caches end as they were.  The status word
+    # in the workspace names the path: the score histogram + tile lists, or
+    # the full top-k over every key.  The first step follows the score-only
+    # passes above (their histogram is not this step's) and is not counted.
+    paths = {"hist": 0, "full": 0}
+    status = ws[qsa.QSA_DECODE_STATUS_OFFSET:qsa.QSA_DECODE_STATUS_OFFSET + 8]
+    for rnd in range(2):
+        for li, L in enumerate(layers):
+            n_before = L["state"].n_tokens
+            layer_step(L, 0)
+            p = int(status.cpu().view(torch.int64).item()) & 0xFF
+            qsa.qsa_state_truncate(L["state"], n_before)
+            if rnd or li:
+                paths["hist" if p == qsa.QSA_PATH_HIST else "full"] += 1
+    log(f"selection paths over {sum(paths.values())} decode steps: {paths}")
     log(f"score kernel (in-step variant): {1e6 * k_avg_s:.2f} us avg over {args.kernel_reps * len(layers)} launches, "
         f"{achieved:.0f} GB/s; scores only {scores_only_us:.2f} us")
 
@@ -1015,6 +1033,8 @@ def main():
                      "avg_launch_us": round(1e6 * k_avg_s, 3),
                      "scores_only_us": round(scores_only_us, 3)},
         "nb": nb,
+        "selection_paths": {**paths, "note": "untimed decode steps after the timed ones, one per layer twice "
+                                             "around, read back one by one"},
         "cpu_baseline": None,
         "batch_and_chunk": None,
         "context_sweep": None,

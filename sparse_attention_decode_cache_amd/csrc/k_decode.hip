@@ -363,10 +363,6 @@ __global__ __launch_bounds__(kNT) void k_decode_attend(DecodeArgs a)
         acc[i] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
     float m_run = -INFINITY, l_run = 0.0f;          // wave h < G: head h
     for (int p = 0; p < npass; ++p) {
-        if (p > 0) {
-            kv0 = load_rows<DH>(a, L.ids, ncell, kPC * p + lc, sub, g);
-            kv1 = load_rows<DH>(a, L.ids, ncell, kPC * p + lc + kPC / 2, sub, g);
-        }
         const int np = ncell - kPC * p < kPC ? ncell - kPC * p : kPC;   // cells of this pass
         const int nks = (np + 31) / 32;                                  // P.V k-steps
         const int c0 = kPC * p + lc, c1 = c0 + kPC / 2;
@@ -376,6 +372,12 @@ __global__ __launch_bounds__(kNT) void k_decode_attend(DecodeArgs a)
         if (lc + kPC / 2 < 32 * nks)
             put_rows<DH, CPT>(ktile, vtile, kv1, lc + kPC / 2, sub,
                               lc + kPC / 2 < np && !(L.ids[c1 >> 2] == a.nb && (lc & 3) >= a.n_tail));
+        // the next pass's rows load while this one computes (the registers
+        // are free once the rows are in the tiles)
+        if (p + 1 < npass) {
+            kv0 = load_rows<DH>(a, L.ids, ncell, kPC * (p + 1) + lc, sub, g);
+            kv1 = load_rows<DH>(a, L.ids, ncell, kPC * (p + 1) + lc + kPC / 2, sub, g);
+        }
         __syncthreads();                                                // barrier: tiles
         if (wv < (np + 15) / 16) {
             // D[cell][head] = K[cell][:] . q[head][:], 16 cells per wave
