@@ -130,7 +130,7 @@ constexpr int kSBlocks = 4 * kSRT * 16;      // blocks per workgroup (4 waves)
 
 template <bool F16, int KS>
 struct ScShape {
-    static constexpr int KC = (F16 ? 4 : 2) < KS ? (F16 ? 4 : 2) : KS;   // k-steps per LDS stage
+    static constexpr int KC = 2 < KS ? 2 : KS;                            // k-steps per LDS stage
     static constexpr int NST = KS / KC;                                   // stages per query group
     static constexpr int ES = F16 ? 2 : 4;                                // summary element bytes
 };
@@ -141,14 +141,18 @@ struct ScShape {
 // The queries stream through LDS, 128 queries x KC k-steps per stage, the
 // next stage loaded straight into the other LDS buffer while the current one
 // runs on the matrix cores; each B fragment read from LDS feeds both row tiles.  After the last
-// stage of a query group, the epilogue writes its keys.
-template <bool F16, int KS>
+// stage of a query group, the epilogue writes its keys (and, with SCORES,
+// the fp32 scores).  The two buffers are two LDS arrays of their own: with
+// one array indexed by the buffer, the compiler cannot tell a stage's reads
+// from the next stage's direct-to-LDS loads and waits for those loads right
+// after issuing them.
+template <bool F16, int KS, bool SCORES>
 __global__ __launch_bounds__(256) void k_chunk_score(ChunkArgs c)
 {
     using S = ScShape<F16, KS>;
     constexpr int KC = S::KC, NST = S::NST, ES = S::ES;
-    extern __shared__ uint4 sc_lds[];
-    uint4 (*sb)[kSQT][KC][2][64] = reinterpret_cast<uint4 (*)[kSQT][KC][2][64]>(sc_lds);   // [2][kSQT][KC][2][64]
+    __shared__ uint4 sb0[kSQT][KC][2][64];
+    __shared__ uint4 sb1[kSQT][KC][2][64];
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     constexpr int QK = 32 * KS;
     const int QT = (c.n_q + 15) / 16;
@@ -197,9 +201,9 @@ __global__ __launch_bounds__(256) void k_chunk_score(ChunkArgs c)
             const int hl = seg & 1, kk = (seg >> 1) % KC, ct = (seg >> 1) / KC;
             const int qt = qg * kSQT + ct;
             const uint4 *src = qsrc + (((size_t)qt * KS + kc * KC + kk) * 2 + hl) * 64 + lane;
+            uint4 *dst = buf ? &sb1[ct][kk][hl][0] : &sb0[ct][kk][hl][0];
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                             (__attribute__((address_space(3))) void *)&sb[buf][ct][kk][hl][0],
-                                             16, 0, 0);
+                                             (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
         }
     };
 
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(256) void k_chunk_score(ChunkArgs c)
             auto frag = [&](int f) __attribute__((always_inline)) -> half8 {
                 const int ct = f % kSQT, hl = (f / kSQT) & 1, kk = f / (2 * kSQT);
                 half8 x;
-                __builtin_memcpy(&x, &sb[buf][ct][kk][hl][lane], 16);
+                __builtin_memcpy(&x, buf ? &sb1[ct][kk][hl][lane] : &sb0[ct][kk][hl][lane], 16);
                 return x;
             };
             half8 fr[FD];
@@ -276,7 +280,7 @@ __global__ __launch_bounds__(256) void k_chunk_score(ChunkArgs c)
                 if (b < c.ldk)
                     *(u32x4 *)(c.keys + (size_t)qi * c.ldk + b) = key;
             }
-            if (c.scores_out) {
+            if constexpr (SCORES) {
                 const float f = c.qscale[qi];
 #pragma unroll
                 for (int rt = 0; rt < kSRT; ++rt) {
@@ -295,15 +299,10 @@ __global__ __launch_bounds__(256) void k_chunk_score(ChunkArgs c)
 template <bool F16, int KS>
 hipError_t score_go(const ChunkArgs &c, dim3 grid, hipStream_t s)
 {
-    using S = ScShape<F16, KS>;
-    const size_t lds = 2 * sizeof(uint4) * kSQT * S::KC * 2 * 64;
-    if (lds > 64 * 1024) {
-        static hipError_t attr = hipFuncSetAttribute((const void *)k_chunk_score<F16, KS>,
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (attr != hipSuccess)
-            return attr;
-    }
-    hipLaunchKernelGGL((k_chunk_score<F16, KS>), grid, dim3(256), lds, s, c);
+    if (c.scores_out)
+        hipLaunchKernelGGL((k_chunk_score<F16, KS, true>), grid, dim3(256), 0, s, c);
+    else
+        hipLaunchKernelGGL((k_chunk_score<F16, KS, false>), grid, dim3(256), 0, s, c);
     return hipGetLastError();
 }
 
