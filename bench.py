@@ -200,11 +200,13 @@ def oracle_beside_legs(result, w256, cpu_step_ms):
     is n_q oracle steps, estimated from 4 steps at the chunk's context; the
     q8_0 leg's quantisation is timed on 8,192 rows and scaled, its attention
     timed once on the 256k selection's cells."""
+    import oracle
     from qsagen import workloads as W
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = oracle.threads()          # the OpenMP threads the oracle runs on
+    cpu = cpu_model()
     md = result.get("multi_decode")
     if md:
-        md["cpu_oracle"] = {"ms_per_call": round(md["n_q"] * cpu_step_ms, 1), "cores": threads,
+        md["cpu_oracle"] = {"ms_per_call": round(md["n_q"] * cpu_step_ms, 1), "cores": threads, "cpu": cpu,
                             "sample": f"{md['n_q']} x the median oracle decode step at n0={w256.n0} "
                                       f"({cpu_step_ms:.1f} ms, cpu_baseline's sample)"}
     bc = result.get("batch_and_chunk")
@@ -212,12 +214,12 @@ def oracle_beside_legs(result, w256, cpu_step_ms):
         b = W.BATCH
         per = [oracle_step_ms(b, n0, 1, seq=i) for i, n0 in enumerate(W.BATCH_CONTEXTS)]
         bc["batch_decode"]["cpu_oracle"] = {
-            "ms_per_batched_step": round(sum(per), 1), "cores": threads,
+            "ms_per_batched_step": round(sum(per), 1), "cores": threads, "cpu": cpu,
             "sample": "one oracle decode step per sequence, each at its own context"}
         c = W.CHUNK128K
         ms = oracle_step_ms(c, c.n0, 4)
         bc["chunk"]["cpu_oracle"] = {
-            "ms_per_chunk": round(ms * c.steps, 1), "cores": threads,
+            "ms_per_chunk": round(ms * c.steps, 1), "cores": threads, "cpu": cpu,
             "sample": f"{c.steps} x the median of 4 oracle decode steps at n0={c.n0} ({ms:.1f} ms)"}
     q8 = result.get("q8_0_kv")
     if q8:
@@ -242,7 +244,7 @@ def oracle_beside_legs(result, w256, cpu_step_ms):
         att_ms = (time.perf_counter() - t0) * 1e3
         q8["cpu_oracle"] = {
             "quantize_ms_per_layer": round(quant_ms, 1), "gather_attend_q8_0_ms": round(att_ms, 2),
-            "cores": 1,
+            "cores": 1, "cpu": cpu,
             "sample": f"q8_0 of {rows} K and V rows scaled to {w256.n0}; one attention over "
                       f"{len(cells)} cells (single-threaded C)"}
 
