@@ -605,6 +605,7 @@ __global__ __launch_bounds__(kNT) void k_decode_merge(DecodeArgs a)
         }
         ctrl->rho_k = kk / sigma;       // NaN when sigma is 0 or not finite: defaults next time
         ctrl->rho_top = (ktop > kk ? ktop : kk) / sigma;
+        ctrl->fb = hist::kFeedback;
         ctrl->tag = hist::kTagClean;
         ctrl->status = (a.epoch << 8) | (fast ? hist::kPathFast : hist::kPathFull);
     }

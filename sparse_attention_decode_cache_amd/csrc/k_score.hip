@@ -16,11 +16,13 @@
 // Outputs (all optional, plain stores): fp32 scores; the order-preserving
 // 32-bit key of every score; and, for the top-k, each tile's T largest
 // composite keys (key << 32 | ~block), sorted descending (T is chosen per
-// call, R/8 .. R/2).  In the decode step the list entries inside the score
-// window also go into the global score histogram of qsa_hist.h, by relaxed
-// device-scope atomics whose results no lane waits for (count, largest and
-// smallest composite of the bin, and the largest last entry of the tiles'
-// lists); the window is set from the fed-back ratios before the rows arrive.
+// call, R/8 .. R/2).  In the decode step every row inside the score window
+// also goes into the global score histogram of qsa_hist.h as soon as its
+// score is known (before the tile's ranking), by relaxed device-scope
+// atomics whose results no lane waits for (count, largest and smallest
+// composite of the bin), and the largest last entry of the tiles' lists
+// after it; the window is set from the fed-back ratios before the rows
+// arrive.
 // Up to 4 queries of one sequence (the tokens
 // of a speculative-verify call) share one pass: every chunk is loaded once
 // and dotted with each query, each query with its own causal block limit.
@@ -105,18 +107,11 @@ __device__ inline void write_tile_list(const uint64_t *s_c, uint64_t *lists, int
         rank += wave::dpp<wave::kQuadXor2>(rank);
     if (part == 0 && c != 0 && rank < (uint32_t)T) {
         lists[(size_t)tile * T + rank] = c;
-        if (h && hist::in_window((uint32_t)(c >> 32), *map)) {
-            // an entry inside the window: its bin's count and extremes and,
-            // for the last entry of a list that may hide rows, the maximum of
-            // such entries (no result is waited for)
-            const uint32_t b = hist::bin_of((uint32_t)(c >> 32), *map);
-            __hip_atomic_fetch_add(h->hist + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_fetch_max(h->bmax + b, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_fetch_max(h->bminc + b, ~c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (rank == (uint32_t)T - 1 && valid_rows > T)
-                __hip_atomic_fetch_max(h->last + (tile & (hist::kLast - 1)), c, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-        }
+        if (h && rank == (uint32_t)T - 1 && valid_rows > T && hist::in_window((uint32_t)(c >> 32), *map))
+            // the last entry of a list that may hide rows, inside the window:
+            // the maximum of such entries (no result is waited for)
+            __hip_atomic_fetch_max(h->last + (tile & (hist::kLast - 1)), c, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
     }
     // the nonzero composites take ranks [0, valid_rows): the rest are empty
     if ((int)threadIdx.x >= valid_rows && threadIdx.x < (unsigned)T)
@@ -184,7 +179,8 @@ __device__ inline void score_tile(const ScoreMultiArgs &a, ScoreLdsOf<F16, LPR, 
     float rho_k = 0.0f, rho_top = 0.0f;
     if (Q == 1 && a.h.hist) {
         const hist::Ctrl *ctrl = reinterpret_cast<const hist::Ctrl *>(a.h.ctrl);
-        rho_k = ctrl->rho_k;
+        const bool fed = ctrl->fb == hist::kFeedback;
+        rho_k = fed ? ctrl->rho_k : __builtin_nanf("");   // NaN: the default window
         rho_top = ctrl->rho_top;
     }
     // gamma entry t (thread t < D), staged through LDS like the queries: the
@@ -352,6 +348,15 @@ __device__ inline void score_tile(const ScoreMultiArgs &a, ScoreLdsOf<F16, LPR, 
                     const uint32_t key = score_key(sc);
                     a.keys[qi][r] = key;
                     c = comp_key(key, (uint32_t)r);
+                    if (Q == 1 && a.h.hist && map.ok && hist::in_window(key, map)) {
+                        // every row inside the window goes into its bin now,
+                        // before the tile's ranking (the counts are then of
+                        // all rows >= L, not only listed ones: exact)
+                        const uint32_t b = hist::bin_of(key, map);
+                        __hip_atomic_fetch_add(a.h.hist + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_fetch_max(a.h.bmax + b, c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        __hip_atomic_fetch_max(a.h.bminc + b, ~c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    }
                 }
             } else if (r < a.nb && a.scores) {
                 a.scores[qi * a.ld_scores + r] = -__builtin_inff();

@@ -3,13 +3,13 @@
 // candidate list [post 10, "QSA indexer" and "block-domain top-k（COMMON-006）
 // 実装は見送り": top-k over block scores].
 //
-// The score pass inserts the entries of each tile's list (its T largest
-// composite keys) whose score is >= L into kBins bins over the window [L, H]
-// (scores >= H share the top bin): per bin the count, the largest composite
-// and the smallest (kept as the largest complement), all by atomics whose
-// result nobody waits for.  If at least k entries are >= L, the k-th largest
+// The score pass inserts every block whose score is >= L into kBins bins
+// over the window [L, H] (scores >= H share the top bin) as soon as the
+// block's score is known: per bin the count, the largest composite and the
+// smallest (kept as the largest complement), all by atomics whose result
+// nobody waits for.  If at least k blocks are >= L, the k-th largest
 // composite kappa lies in the bin d where the count from the top reaches k;
-// the counts of the bins at and above d are exact because every entry >= L
+// the counts of the bins at and above d are exact because every block >= L
 // was inserted.  With `need` = how many of bin d win, kappa is bin d's
 // smallest composite when all of them win and its largest when one does; any
 // other split of a bin (rare: the bins are fine where kappa falls) and
@@ -29,6 +29,11 @@
 // H = (rho_top + kAbove) sigma.  A window that misses kappa only costs the
 // full top-k for that call (and moves the next window).
 //
+// A window is taken from the fed-back ratios only when the feedback word says
+// a merge wrote them (a fresh workspace holds whatever the memory held: its
+// ratios could put L anywhere, and every block >= L is inserted); otherwise
+// from defaults.  No kernel of the score pass writes that word or the ratios.
+//
 // Consistency: the histogram region is trusted only when its tag says the
 // previous call cleared it.  The score pass's workgroup 0 reads the tag and
 // stamps it with this call's epoch, marked clean-start or not; the attention
@@ -44,6 +49,7 @@ constexpr int kBins = kHistBins;
 constexpr int kFine = kBins * 3 / 4;     // bins over [L, M)
 constexpr int kLast = kHistLast;         // words holding the maximum of the tiles' last entries
 constexpr uint64_t kTagClean = 0x5153412d48495354ull;   // low byte 0x54: never an epoch stamp
+constexpr uint64_t kFeedback = 0x5153412d46454544ull;   // rho_k / rho_top were written by a merge
 // Window margins in units of sigma.  kappa / sigma of independent queries
 // over the same keys moves by about 0.02 from one call to the next.
 constexpr float kBelow = 0.12f;
@@ -67,7 +73,8 @@ struct Ctrl {
     uint32_t btop;      // the top nonempty bin (histogram path)
     uint32_t path;      // kPathFast or kPathFull
     uint32_t kmin, kmax;    // the smallest and largest chosen keys (full top-k)
-    uint32_t pad[42];
+    uint64_t fb;            // kFeedback once a merge has written rho_k / rho_top (else: defaults)
+    uint32_t pad[40];
 };
 static_assert(sizeof(Ctrl) == 256, "one 256-byte line");
 
