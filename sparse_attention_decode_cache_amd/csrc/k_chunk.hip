@@ -299,64 +299,30 @@ __global__ __launch_bounds__(256) void k_chunk_score(ChunkArgs c)
 // The f16 summaries' GEMM with the roles turned round: each wave keeps ONE
 // tile of 16 queries (f16 hi and lo, every k-step) in registers for the whole
 // kernel, and the blocks stream past it.  Workgroup = 8 waves = 128 queries x
-// one range of row tiles.  The range's rows go through LDS in stages of 16 KB
-// (RT = 16 / KS tiles of 16 rows), a ring of kBsBuf stages filled straight
-// from memory (global_load_lds), so that kBsBuf - 1 stages are in flight
-// while one runs on the matrix cores; every summary fragment read from LDS
-// feeds two products (the query's hi and lo).  Chunk c of row r of a stage
-// sits at slot c ^ (r % 16) of the row: the 16 rows that one fragment read
-// takes at one chunk position then fall in distinct banks, and each load
-// still covers whole rows.  The workgroups of one row range (its query
-// groups) are numbered so that they run on one XCD (dispatch deals
+// one range of row tiles.  The range's rows go through LDS in stages of 32 KB
+// (RT = 32 / KS tiles of 16 rows): each stage is loaded into registers
+// kBsAhead steps before it is due, written to one of two LDS buffers in the
+// step before, and read there by every wave; every summary fragment read
+// from LDS feeds two products (the query's hi and lo).  Chunk c of row r of
+// a stage sits at slot c ^ (r % 16) of the row: the 16 rows that one
+// fragment read takes at one chunk position then fall in distinct banks, and
+// each load still covers whole rows.  The workgroups of one row range (its
+// query groups) are numbered so that they run on one XCD (dispatch deals
 // workgroups to the XCDs in turn) and read the range once into its L2.
-//
-// The ring's loads are issued in inline assembly, out of the compiler's
-// sight (tracking them itself, it waits for every load in flight before
-// each stage), and each stage waits for exactly its own, by count: every
-// step -- the kBsBuf - 1 before the first stage included -- issues SEG load
-// slots, then ST stores, always (a slot with no stage to load stores to a
-// scratch area instead, as does a lane with nothing to write), and vmcnt
-// retires in issue order, so that when stage st is due the ops issued after
-// its loads are exactly the stores of its own step and the kBsBuf - 2 steps
-// after it.
 constexpr int kBsWaves = 8;                  // query tiles per workgroup
-constexpr int kBsBuf = 4;                    // stages in the LDS ring
-constexpr int kBsStage = 16 * 1024;          // bytes per stage
-constexpr size_t kBsLds = (size_t)kBsBuf * kBsStage;
+constexpr int kBsAhead = 4;                  // steps between a stage's loads and its use
+constexpr int kBsStage = 32 * 1024;          // bytes per stage
+constexpr size_t kBsLds = 2 * (size_t)kBsStage;
 constexpr int kXcds = 8;
 
 template <int KS>
 struct BsShape {
     static constexpr int RB = 64 * KS;                       // row bytes (f16)
     static constexpr int CPR = 4 * KS;                       // 16-byte chunks per row
-    static constexpr int RT = 16 / KS;                       // row tiles per stage
-    static constexpr int SEG = kBsStage / 1024 / kBsWaves;   // 1 KB loads per wave per stage
+    static constexpr int RT = kBsStage / (16 * RB);          // row tiles per stage
+    static constexpr int SEG = kBsStage / 1024 / kBsWaves;   // 16-byte pieces per lane per stage
     static_assert(RT >= 1 && RT * 16 * RB == kBsStage, "a stage is whole row tiles");
 };
-
-// lane's 16 bytes at src land at LDS byte lds + 16 * lane (m0 is set here
-// for this load alone, so clobbering it is what is meant)
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ inline void lds_load16(const void *src, uint32_t lds)
-{
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(lds)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-// a store the compiler neither merges nor drops nor waits for (it fills a
-// load slot that has no stage to load)
-__device__ inline void fill_store(uint32_t *dst)
-{
-    asm volatile("global_store_dwordx4 %0, %1, off" ::"v"(dst), "v"(u32x4{0u, 0u, 0u, 0u}) : "memory");
-}
-
-template <int N>
-__device__ inline void wait_vm()
-{
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 
 template <int KS, bool SCORES>
 __global__ __launch_bounds__(64 * kBsWaves) void k_chunk_score_bs(ChunkArgs c, int32_t n_qg, int32_t tiles_per)
@@ -364,11 +330,7 @@ __global__ __launch_bounds__(64 * kBsWaves) void k_chunk_score_bs(ChunkArgs c, i
     using S = BsShape<KS>;
     constexpr int RT = S::RT, CPR = S::CPR, SEG = S::SEG;
     constexpr int NV = kBsStage / 16;
-    constexpr int ST = RT * (SCORES ? 5 : 1);              // stores per step and wave
-    // ops issued after a stage's loads when it is due; past vmcnt's range
-    // (fp32 scores of short rows) every stage waits for all
-    constexpr int NW0 = (kBsBuf - 2) * SEG + (kBsBuf - 1) * ST;
-    constexpr int NW = NW0 <= 63 ? NW0 : 0;
+    static_assert(kBsAhead == 4, "the step loop below is unrolled by four");
     extern __shared__ uint4 ring[];
     const int t = threadIdx.x, lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -381,6 +343,11 @@ __global__ __launch_bounds__(64 * kBsWaves) void k_chunk_score_bs(ChunkArgs c, i
     if (tile0 >= tile1)
         return;
     const int nst = (tile1 - tile0 + RT - 1) / RT;
+    // whole groups of kBsAhead steps, so that no load or LDS write in the
+    // loop is conditional and the compiler's count of loads in flight stays
+    // exact around it; the steps past nst load the last row again and store
+    // nothing
+    const int nstp = (nst + kBsAhead - 1) / kBsAhead * kBsAhead;
     const int qt = qg * kBsWaves + wave;
     const int qi = qt * 16 + (lane & 15);
     const int kg = lane >> 4;
@@ -399,30 +366,27 @@ __global__ __launch_bounds__(64 * kBsWaves) void k_chunk_score_bs(ChunkArgs c, i
     const bool live = qi < c.n_q;
     const int64_t nbq = ((int64_t)c.n0 + qi + 1) >> 2;
     const float qs = SCORES && live ? c.qscale[qi] : 1.0f;
-    uint32_t *const trash = c.trash + 4 * lane;
-    const uint32_t ring_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)ring;
 
     const char *rows = (const char *)c.summary;
     const int64_t last = c.nb_last - 1;
-    // the SEG load slots of one step: stage st into its ring buffer, or
-    // (no such stage) as many stores to the scratch area
-    auto issue = [&](int st) __attribute__((always_inline)) {
-        const int64_t r0 = (int64_t)(tile0 + st * RT) * 16;
-        const uint32_t base = ring_lds + (uint32_t)((st % kBsBuf) * kBsStage);
+    // this lane's SEG pieces of stage j (slot f = 64 seg + lane of the stage)
+    auto load = [&](int j, u32x4 *dst) __attribute__((always_inline)) {
+        const int64_t r0 = (int64_t)(tile0 + j * RT) * 16;
 #pragma unroll
         for (int u = 0; u < SEG; ++u) {
-            const int seg = wave + kBsWaves * u;
-            if (st < nst) {
-                const int f = seg * 64 + lane;
-                const int rr = f / CPR, slot = f % CPR;
-                const int chunk = slot ^ (rr & 15 & (CPR - 1));
-                int64_t r = r0 + rr;
-                r = r < last ? r : last;
-                lds_load16((const uint4 *)(rows + r * S::RB) + chunk, base + (uint32_t)(seg * 1024));
-            } else {
-                fill_store(trash);
-            }
+            const int f = (wave + kBsWaves * u) * 64 + lane;
+            const int rr = f / CPR, slot = f % CPR;
+            const int chunk = slot ^ (rr & 15 & (CPR - 1));
+            int64_t r = r0 + rr;
+            r = r < last ? r : last;
+            dst[u] = *((const u32x4 *)(rows + r * S::RB) + chunk);
         }
+    };
+    auto put = [&](int j, const u32x4 *src) __attribute__((always_inline)) {
+        u32x4 *buf = (u32x4 *)(ring + (j & 1) * NV);
+#pragma unroll
+        for (int u = 0; u < SEG; ++u)
+            buf[(wave + kBsWaves * u) * 64 + lane] = src[u];
     };
     // fragment (rt, ks = 4 m + n) of this lane: row r = lane % 16, chunk
     // 4 ks + kg, stored at slot 16 m + ((4 n + kg) ^ r) of the row: four
@@ -435,7 +399,7 @@ __global__ __launch_bounds__(64 * kBsWaves) void k_chunk_score_bs(ChunkArgs c, i
             sidx[n] = r * CPR + ((4 * n + kg) ^ rx);
     }
     auto run = [&](int st) __attribute__((always_inline)) {
-        const uint4 *buf = ring + (st % kBsBuf) * NV;
+        const uint4 *buf = ring + (st & 1) * NV;
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             half8 a[KS];
@@ -452,44 +416,46 @@ __global__ __launch_bounds__(64 * kBsWaves) void k_chunk_score_bs(ChunkArgs c, i
             // scaled sums (a query's power of two changes no order or tie)
             const int tile = tile0 + st * RT + rt;
             const int64_t b = (int64_t)tile * 16 + 4 * kg;
-            const bool ok = tile < tile1 && live && b < c.ldk;
-            u32x4 key;
+            if (tile < tile1 && live) {
+                u32x4 key;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                key[j] = b + j < nbq ? chunk_key(ach[j] + acl[j]) : 0u;
-            *(u32x4 *)(ok ? c.keys + (size_t)qi * c.ldk + b : trash) = key;
-            if constexpr (SCORES) {
+                for (int j = 0; j < 4; ++j)
+                    key[j] = b + j < nbq ? chunk_key(ach[j] + acl[j]) : 0u;
+                if (b < c.ldk)
+                    *(u32x4 *)(c.keys + (size_t)qi * c.ldk + b) = key;
+                if constexpr (SCORES) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const bool in = ok && b + j < c.nb_last;
-                    float *d = in ? c.scores_out + (size_t)qi * c.nb_last + b + j : (float *)trash + j;
-                    *d = b + j < nbq ? (ach[j] + acl[j]) * qs : -INFINITY;
+                    for (int j = 0; j < 4; ++j)
+                        if (b + j < c.nb_last)
+                            c.scores_out[(size_t)qi * c.nb_last + b + j] =
+                                b + j < nbq ? (ach[j] + acl[j]) * qs : -INFINITY;
                 }
             }
         }
     };
-    // the steps before the first stage: its load slots, and ST stores each
-    for (int p = 0; p < kBsBuf - 1; ++p) {
-        issue(p);
-#pragma unroll
-        for (int u = 0; u < ST; ++u)
-            fill_store(trash);
-    }
-    for (int st = 0; st < nst; ++st) {
-        // this wave's loads of stage st are in; after the barrier (fenced
-        // for LDS only) every wave's are, and every wave is done with stage
-        // st - 1, whose buffer the loads of st + kBsBuf - 1 refill
-        if constexpr (NW0 <= 63)
-            wait_vm<NW>();
-        else
-            wait_vm<0>();
+    // step st: after the barrier (fenced for LDS only) stage st is in its
+    // buffer and every wave is done with stage st - 1, whose buffer stage
+    // st + 1 then takes; the registers that held stage st load st + 4
+    auto step = [&](int st, u32x4 *mine, const u32x4 *next) __attribute__((always_inline)) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-        issue(st + kBsBuf - 1);
+        load(st + kBsAhead, mine);
+        put(st + 1, next);
         run(st);
+    };
+    u32x4 r0[SEG], r1[SEG], r2[SEG], r3[SEG];
+    load(0, r0);
+    load(1, r1);
+    load(2, r2);
+    load(3, r3);
+    put(0, r0);
+    for (int s0 = 0; s0 < nstp; s0 += kBsAhead) {
+        step(s0, r0, r1);
+        step(s0 + 1, r1, r2);
+        step(s0 + 2, r2, r3);
+        step(s0 + 3, r3, r0);
     }
-    wait_vm<0>();
 }
 
 template <bool F16, int KS>
@@ -513,15 +479,11 @@ hipError_t score_bs_go(const ChunkArgs &c, hipStream_t s)
     const int mt = (int)((c.nb_last + 15) / 16);
     int n_ms = (256 + n_qg - 1) / n_qg;
     n_ms = n_ms < mt ? n_ms : mt;
-    const int tiles_per = (mt + n_ms - 1) / n_ms;
+    // ranges of whole groups of kBsAhead stages (the kernel pads to them)
+    constexpr int q = kBsAhead * BsShape<KS>::RT;
+    const int tiles_per = ((mt + n_ms - 1) / n_ms + q - 1) / q * q;
     n_ms = (mt + tiles_per - 1) / tiles_per;
     const int nwg = (n_qg * n_ms + kXcds - 1) / kXcds * kXcds;
-    static const hipError_t a0 = hipFuncSetAttribute((const void *)k_chunk_score_bs<KS, false>,
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBsLds);
-    static const hipError_t a1 = hipFuncSetAttribute((const void *)k_chunk_score_bs<KS, true>,
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBsLds);
-    if (a0 != hipSuccess || a1 != hipSuccess)
-        return a0 != hipSuccess ? a0 : a1;
     if (c.scores_out)
         hipLaunchKernelGGL((k_chunk_score_bs<KS, true>), dim3(nwg), dim3(64 * kBsWaves), kBsLds, s, c, n_qg, tiles_per);
     else

@@ -151,7 +151,7 @@ uint64_t next_epoch()
 // Prefill-chunk workspace: folded queries, their scales, the keys of every
 // (query, block), the chosen ids and the attention partials.
 struct ChunkLayout {
-    size_t qhl, qscale, keys, trash, sel, part, uni, umask, ucount, total;
+    size_t qhl, qscale, keys, sel, part, uni, umask, ucount, total;
 };
 
 ChunkLayout chunk_layout(const qsa_layer_desc *d, int32_t capacity, int32_t n_q)
@@ -170,7 +170,6 @@ ChunkLayout chunk_layout(const qsa_layer_desc *d, int32_t capacity, int32_t n_q)
     L.qhl = take(qpad * qk * 2 * sizeof(uint16_t));
     L.qscale = take(sizeof(float) * (size_t)n_q);
     L.keys = take(sizeof(uint32_t) * (size_t)n_q * ldk);
-    L.trash = take(1024);
     L.sel = take(sizeof(int32_t) * (size_t)n_q * (d->top_k_tokens / 4));
     L.part = take(sizeof(float) * 2 * (size_t)kChunkWgTarget * part_stride(G, d->head_dim));
     // the grouped-union lists: ceil(n_q / qg) groups of qg <= kUnionMaxQ
@@ -1083,7 +1082,6 @@ qsa_status chunk_step(const qsa_layer_desc *desc, const qsa_layer_cache *cache, 
     c.qhl = (_Float16 *)(wsp + L.qhl);
     c.qscale = (float *)(wsp + L.qscale);
     c.keys = (uint32_t *)(wsp + L.keys);
-    c.trash = (uint32_t *)(wsp + L.trash);
     c.sel = (int32_t *)(wsp + L.sel);
     c.part = (float *)(wsp + L.part);
     c.ldk = ((int64_t)nb_last + 3) / 4 * 4;

@@ -312,7 +312,6 @@ struct ChunkArgs {
                                 // zeros to whole groups of 128 queries
     float *qscale;              // workspace: [n_q] power-of-two factors
     uint32_t *keys;             // workspace: [n_q][ldk]
-    uint32_t *trash;            // workspace: 1 KB that stores with nothing to write go to
     int32_t *sel;               // workspace: [n_q][kb]
     float *part;                // workspace: attention partials (n_split > 1)
     int64_t ldk;
