@@ -16,7 +16,7 @@ from qsagen import workloads as W
 pytestmark = pytest.mark.gpu
 
 
-def _chunk(g, n_q):
+def _chunk(g, n_q, with_scores=True):
     """Run tokens 0 .. n_q-1 of g's step inputs as one chunk."""
     import torch
     qsa = g.qsa
@@ -26,13 +26,15 @@ def _chunk(g, n_q):
     ws = qsa.chunk_workspace(g.desc, g.cap, n_q)
     out = torch.full((n_q, w.q_heads, w.head_dim), float("nan"), dtype=torch.float32, device="cuda")
     sel = torch.full((n_q, w.k_blocks), -7, dtype=torch.int32, device="cuda")
-    scores = torch.full((n_q, max(nb_last, 1)), float("nan"), dtype=torch.float32, device="cuda")
+    scores = (torch.full((n_q, max(nb_last, 1)), float("nan"), dtype=torch.float32, device="cuda")
+              if with_scores else None)
     inp = g.inp
     qsa.qsa_chunk_step(g.desc, g.buf.cache, g.state, n_q, inp.raw[:n_q], inp.k[:n_q], inp.v[:n_q],
                        g.gamma, inp.q_idx[:n_q], inp.w[:n_q], inp.q[:n_q], out, sel, scores, ws)
     torch.cuda.synchronize()
     assert (g.state.n_tokens, g.state.n_valid_blocks) == (n0 + n_q, nb_last)
-    return out.cpu().numpy().astype(np.float64), sel.cpu().numpy(), scores.cpu().numpy()
+    return (out.cpu().numpy().astype(np.float64), sel.cpu().numpy(),
+            scores.cpu().numpy() if with_scores else None)
 
 
 def _check_query(i, o, out, sel, scores, k_blocks, scored, stats):
@@ -187,9 +189,34 @@ def test_chunk_attention_shapes(q_heads, kv_heads, head_dim, n_q):
 
 
 @pytest.mark.parametrize("idx_heads,idx_dim,idx_f16", [
-    (1, 128, True), (4, 64, False), (1, 64, True), (1, 128, False)])
+    (1, 128, True), (4, 64, False), (1, 64, True), (1, 128, False), (4, 64, True)])
 def test_chunk_indexer_shapes(idx_heads, idx_dim, idx_f16):
     """Indexer contractions of 64 .. 512 elements, f16 and fp32 summaries."""
     base = with_size(W.CTX64K, idx_heads=idx_heads, idx_dim=idx_dim, idx_f16=idx_f16)
     st = _run_full(base, 4001, 33)
     assert st["exact"] + st["threshold"] == 33
+
+
+@pytest.mark.parametrize("idx_heads,idx_dim,n0,n_q", [
+    (4, 128, 9001, 130), (1, 64, 4001, 33), (4, 64, 20003, 200)])
+def test_chunk_without_scores_output_is_identical(idx_heads, idx_dim, n0, n_q):
+    """Without the optional fp32 scores the score GEMM runs its keys-only
+    instance (the one a caller that wants only the attention gets): the ids
+    and outputs must be bit-identical to those of the run that writes scores
+    (the keys are formed the same way in both), and that run is checked
+    against the oracle."""
+    base = with_size(W.CTX64K, idx_heads=idx_heads, idx_dim=idx_dim, idx_f16=True)
+    w = with_size(base, n0=n0, steps=n_q)
+    print(f"chunk {w.name}: n0={n0} n_q={n_q} with and without scores", flush=True)
+    a = GpuLayer(w)
+    out_a, sel_a, scores = _chunk(a, n_q, with_scores=True)
+    b = GpuLayer(w)
+    out_b, sel_b, _ = _chunk(b, n_q, with_scores=False)
+    assert np.array_equal(sel_a, sel_b)
+    assert np.array_equal(out_a, out_b)
+    o = _Mirror(w)
+    stats = {"exact": 0, "threshold": 0, "attn_err": 0.0}
+    for i in range(n_q):
+        o.step(i)
+        if i % 7 == 0 or i == n_q - 1:
+            _check_query(i, o, out_a, sel_a, scores, w.k_blocks, True, stats)
