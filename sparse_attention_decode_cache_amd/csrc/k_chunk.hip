@@ -345,8 +345,8 @@ __global__ __launch_bounds__(64 * kBsWaves) void k_chunk_score_bs(ChunkArgs c, i
     const int nst = (tile1 - tile0 + RT - 1) / RT;
     // whole groups of kBsAhead steps, so that no load or LDS write in the
     // loop is conditional and the compiler's count of loads in flight stays
-    // exact around it; the steps past nst load the last row again and store
-    // nothing
+    // exact around it; the stages past nst load rows past the range (held to
+    // the last row at the end of the summaries) and store nothing
     const int nstp = (nst + kBsAhead - 1) / kBsAhead * kBsAhead;
     const int qt = qg * kBsWaves + wave;
     const int qi = qt * 16 + (lane & 15);
