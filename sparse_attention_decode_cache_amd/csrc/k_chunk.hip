@@ -128,16 +128,19 @@ constexpr int kSQT = 8;                      // query tiles (16 queries) per LDS
 constexpr int kSRT = 2;                      // block row tiles (16 blocks) per wave
 constexpr int kSBlocks = 4 * kSRT * 16;      // blocks per workgroup (4 waves)
 
-template <bool F16, int KS>
+template <int KS>
 struct ScShape {
     static constexpr int KC = 2 < KS ? 2 : KS;                            // k-steps per LDS stage
     static constexpr int NST = KS / KC;                                   // stages per query group
-    static constexpr int ES = F16 ? 2 : 4;                                // summary element bytes
+    static constexpr int ES = 4;                                          // summary element bytes
 };
 
+// The GEMM over fp32 summaries (f16 summaries take k_chunk_score_bs below).
 // Workgroup = 128 blocks x every query, 4 waves.  Wave w keeps the A operand
-// of its 32 blocks (two 16-row tiles, every k-step, f16 hi -- and lo for fp32
-// summaries) in registers for the whole kernel: the summaries are read once.
+// of its 32 blocks (two 16-row tiles, every k-step, as f16 hi and lo) in
+// registers for the whole kernel: the summaries are read once; a query's hi
+// and lo halves meet the rows' hi half, its hi half their lo half (the lo x
+// lo product is below 2^-22 of the term).
 // The queries stream through LDS, 128 queries x KC k-steps per stage, the
 // next stage loaded straight into the other LDS buffer while the current one
 // runs on the matrix cores; each B fragment read from LDS feeds both row tiles.  After the last
@@ -146,10 +149,10 @@ struct ScShape {
 // one array indexed by the buffer, the compiler cannot tell a stage's reads
 // from the next stage's direct-to-LDS loads and waits for those loads right
 // after issuing them.
-template <bool F16, int KS, bool SCORES>
+template <int KS, bool SCORES>
 __global__ __launch_bounds__(256) void k_chunk_score(ChunkArgs c)
 {
-    using S = ScShape<F16, KS>;
+    using S = ScShape<KS>;
     constexpr int KC = S::KC, NST = S::NST, ES = S::ES;
     __shared__ uint4 sb0[kSQT][KC][2][64];
     __shared__ uint4 sb1[kSQT][KC][2][64];
@@ -161,7 +164,7 @@ __global__ __launch_bounds__(256) void k_chunk_score(ChunkArgs c)
     const int mr = lane & 15, kg = lane >> 4;
 
     // A: lane l holds row l % 16 of each row tile, elements 32 ks + 8 (l / 16) .. +8
-    half8 ah[kSRT][KS], al[kSRT][F16 ? 1 : KS];
+    half8 ah[kSRT][KS], al[kSRT][KS];
 #pragma unroll
     for (int rt = 0; rt < kSRT; ++rt) {
         int64_t r = bw + 16 * rt + mr;
@@ -169,20 +172,15 @@ __global__ __launch_bounds__(256) void k_chunk_score(ChunkArgs c)
         const char *row = (const char *)c.summary + ((size_t)r * QK + 8 * kg) * ES;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            if constexpr (F16) {
-                const uint4 v = *(const uint4 *)(row + (size_t)(32 * ks) * ES);
-                __builtin_memcpy(&ah[rt][ks], &v, 16);
-            } else {
-                float f[8];
-                const uint4 v0 = *(const uint4 *)(row + (size_t)(32 * ks) * ES);
-                const uint4 v1 = *(const uint4 *)(row + (size_t)(32 * ks) * ES + 16);
-                __builtin_memcpy(f, &v0, 16);
-                __builtin_memcpy(f + 4, &v1, 16);
+            float f[8];
+            const uint4 v0 = *(const uint4 *)(row + (size_t)(32 * ks) * ES);
+            const uint4 v1 = *(const uint4 *)(row + (size_t)(32 * ks) * ES + 16);
+            __builtin_memcpy(f, &v0, 16);
+            __builtin_memcpy(f + 4, &v1, 16);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    ah[rt][ks][j] = (_Float16)f[j];
-                    al[rt][ks][j] = (_Float16)(f[j] - (float)ah[rt][ks][j]);
-                }
+            for (int j = 0; j < 8; ++j) {
+                ah[rt][ks][j] = (_Float16)f[j];
+                al[rt][ks][j] = (_Float16)(f[j] - (float)ah[rt][ks][j]);
             }
         }
     }
@@ -246,12 +244,10 @@ __global__ __launch_bounds__(256) void k_chunk_score(ChunkArgs c)
 #pragma unroll
                 for (int rt = 0; rt < kSRT; ++rt)
                     acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[rt][ks], fr[f % FD], acc[rt][ct], 0, 0, 0);
-                if constexpr (!F16) {
-                    if (hl == 0) {
+                if (hl == 0) {
 #pragma unroll
-                        for (int rt = 0; rt < kSRT; ++rt)
-                            acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[rt][ks], fr[f % FD], acc[rt][ct], 0, 0, 0);
-                    }
+                    for (int rt = 0; rt < kSRT; ++rt)
+                        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al[rt][ks], fr[f % FD], acc[rt][ct], 0, 0, 0);
                 }
                 if (f + FD < NF)
                     fr[f % FD] = frag(f + FD);
@@ -458,13 +454,13 @@ __global__ __launch_bounds__(64 * kBsWaves) void k_chunk_score_bs(ChunkArgs c, i
     }
 }
 
-template <bool F16, int KS>
+template <int KS>
 hipError_t score_go(const ChunkArgs &c, dim3 grid, hipStream_t s)
 {
     if (c.scores_out)
-        hipLaunchKernelGGL((k_chunk_score<F16, KS, true>), grid, dim3(256), 0, s, c);
+        hipLaunchKernelGGL((k_chunk_score<KS, true>), grid, dim3(256), 0, s, c);
     else
-        hipLaunchKernelGGL((k_chunk_score<F16, KS, false>), grid, dim3(256), 0, s, c);
+        hipLaunchKernelGGL((k_chunk_score<KS, false>), grid, dim3(256), 0, s, c);
     return hipGetLastError();
 }
 
@@ -503,9 +499,9 @@ hipError_t score_ks(const ChunkArgs &c, dim3 grid, hipStream_t s)
         }
     } else {
         switch (c.H * c.D / 32) {   // fp32 rows are at most 1 KB: 256 elements
-        case 2: return score_go<false, 2>(c, grid, s);
-        case 4: return score_go<false, 4>(c, grid, s);
-        case 8: return score_go<false, 8>(c, grid, s);
+        case 2: return score_go<2>(c, grid, s);
+        case 4: return score_go<4>(c, grid, s);
+        case 8: return score_go<8>(c, grid, s);
         }
     }
     return hipErrorInvalidValue;
