@@ -170,7 +170,7 @@ hipError_t launch_iota(int32_t *p, int32_t n, hipStream_t s);
 // largest composite keys, sorted descending, zero-filled past the tile's
 // blocks (a composite is never 0).  R depends on the producer.
 struct SelectArgs {
-    const uint32_t *keys;       // [nb] order-preserving score keys
+    const uint32_t *keys;       // [nb] order-preserving score keys (16-byte aligned)
     const uint64_t *lists;      // [ntiles * T] composites, descending per tile
     int32_t *sel;
     int32_t nb;

@@ -72,12 +72,13 @@ struct Smem {
 // when the total stays within `cap` (else without one).  Sets a.lkeys_off.
 inline size_t lds_with_cache(SelectArgs &a, int32_t nb_max, size_t cap);
 
-// Dynamic LDS of run(): Smem and the id bitmap.
+// Dynamic LDS of run(): Smem and the id bitmap (whole 16-byte words, so
+// that a key cache placed after it is 16-byte aligned).
 __host__ __device__ inline size_t lds_bytes(int32_t nb)
 {
     const size_t nwords = (size_t)(nb + 31) / 32;
     const size_t bm = nwords > (size_t)kFastWords ? nwords : (size_t)kFastWords;
-    return (sizeof(Smem) + 15) / 16 * 16 + 4 * bm;
+    return (sizeof(Smem) + 15) / 16 * 16 + 4 * ((bm + 3) / 4 * 4);
 }
 
 inline size_t lds_with_cache(SelectArgs &a, int32_t nb_max, size_t cap)
@@ -349,28 +350,46 @@ __device__ void keys_path(const SelectArgs &a, Smem &sm, uint32_t *bitmap, uint3
         sm.d = 0xFFFFFFFFu;
     }
     // 1. keys (to LDS when asked), their range, and this thread's largest;
-    //    16 loads in flight per thread (each round waits one memory latency)
-    constexpr int kRound = 16;
+    //    in 16-byte chunks of 4 keys (the keys are 16-byte aligned), 8 per
+    //    thread in flight (32,768 keys a memory latency), the last nb % 4
+    //    keys one by one (nothing past nb is read)
+    const uint32_t nch = nb >> 2, ntail = nb & 3u;
+    const uint4 *keys4 = reinterpret_cast<const uint4 *>(a.keys);
+    constexpr int kRound = 8;
     uint32_t kmin1 = 0xFFFFFFFFu, kmax = 0u;
-    for (uint32_t base = 0; base < nb; base += kT * kRound) {
-        uint32_t kk[kRound];
+    auto see = [&](uint32_t key) __attribute__((always_inline)) {
+        kmin1 = min(kmin1, key - 1u);
+        kmax = max(kmax, key);
+    };
+    for (uint32_t base = 0; base < nch; base += kT * kRound) {
+        uint4 kk[kRound];
 #pragma unroll
         for (int q = 0; q < kRound; ++q) {
-            const uint32_t e = base + q * kT + t;
-            kk[q] = a.keys[e < nb ? e : nb - 1];
+            const uint32_t c = base + q * kT + t;
+            kk[q] = keys4[c < nch ? c : nch - 1];
         }
 #pragma unroll
         for (int q = 0; q < kRound; ++q) {
-            const uint32_t e = base + q * kT + t;
-            if (e < nb) {
+            const uint32_t c = base + q * kT + t;
+            if (c < nch) {
                 if (lkeys)
-                    lkeys[e] = kk[q];
-                kmin1 = min(kmin1, kk[q] - 1u);
-                kmax = max(kmax, kk[q]);
+                    *reinterpret_cast<uint4 *>(lkeys + 4 * c) = kk[q];
+                see(kk[q].x);
+                see(kk[q].y);
+                see(kk[q].z);
+                see(kk[q].w);
             }
         }
     }
-    const uint32_t tmax = kmax;                 // this thread's largest key (it holds one iff t < nb)
+    if ((uint32_t)t < ntail) {
+        const uint32_t e = 4 * nch + t, key = a.keys[e];
+        if (lkeys)
+            lkeys[e] = key;
+        see(key);
+    }
+    // this thread's largest key (it holds one iff it took a chunk or a tail key)
+    const uint32_t tmax = kmax;
+    const bool holds = (uint32_t)t < nch || (uint32_t)t < ntail;
     kmin1 = wave::reduce_min_u32(kmin1);
     kmax = wave::reduce_max_u32(kmax);
     if (lane == 0) {
@@ -394,7 +413,20 @@ __device__ void keys_path(const SelectArgs &a, Smem &sm, uint32_t *bitmap, uint3
     const bool by_key = kmin >= 0x80000000u;
     const int kshift = 32 - __clz((int)(kmax - kmin)) - 10;
     const uint32_t ksh = kshift > 0 ? (uint32_t)kshift : 0u;
-    auto key_at = [&](uint32_t e) -> uint32_t { return lkeys ? lkeys[e] : a.keys[e]; };
+    // f(key, id) for every key, a 16-byte chunk at a time
+    auto each_key = [&](auto f) __attribute__((always_inline)) {
+        for (uint32_t c = t; c < nch; c += kT) {
+            const uint4 v = lkeys ? *reinterpret_cast<const uint4 *>(lkeys + 4 * c) : keys4[c];
+            f(v.x, 4 * c);
+            f(v.y, 4 * c + 1);
+            f(v.z, 4 * c + 2);
+            f(v.w, 4 * c + 3);
+        }
+        if ((uint32_t)t < ntail) {
+            const uint32_t e = 4 * nch + t;
+            f(lkeys ? lkeys[e] : a.keys[e], e);
+        }
+    };
     auto bin_of = [&](uint32_t key) -> uint32_t {
         if (by_key)
             return (key > kmin ? key - kmin : 0u) >> ksh;
@@ -443,13 +475,13 @@ __device__ void keys_path(const SelectArgs &a, Smem &sm, uint32_t *bitmap, uint3
     uint32_t tau = 0u;                          // keys below it cannot be among the k largest
     if (!general && k <= (uint32_t)kT) {
         // 2a. the k-th largest of the threads' maxima (composites: unique)
-        if ((uint32_t)t < nb)
+        if (holds)
             atomicAdd(&sm.hist[bin_of(tmax)], 1u);
         __syncthreads();
         kth_bin(k);
         const uint32_t dt = sm.d, mt = sm.in_d, need_t = sm.need;
         if (dt != 0xFFFFFFFFu && mt <= (uint32_t)kCap) {
-            if ((uint32_t)t < nb && bin_of(tmax) == dt)
+            if (holds && bin_of(tmax) == dt)
                 sm.cand[atomicAdd(&sm.ncand, 1u)] = comp_key(tmax, (uint32_t)t);
             __syncthreads();
             rank_cand(mt, need_t);
@@ -464,19 +496,17 @@ __device__ void keys_path(const SelectArgs &a, Smem &sm, uint32_t *bitmap, uint3
     }
     if (!general) {
         // 2. histogram of the keys >= tau
-        for (uint32_t e = t; e < nb; e += kT) {
-            const uint32_t key = key_at(e);
+        each_key([&](uint32_t key, uint32_t) __attribute__((always_inline)) {
             if (key >= tau)
                 atomicAdd(&sm.hist[bin_of(key)], 1u);
-        }
+        });
         __syncthreads();
         kth_bin(k);
         const uint32_t d = sm.d, m = sm.in_d;
         general = d == 0xFFFFFFFFu || m > (uint32_t)kCap;
         if (!general) {
             // 3. keys above bin d are winners; bin d's entries are ranked
-            for (uint32_t e = t; e < nb; e += kT) {
-                const uint32_t key = key_at(e);
+            each_key([&](uint32_t key, uint32_t e) __attribute__((always_inline)) {
                 if (key >= tau) {
                     const uint32_t b = bin_of(key);
                     if (b > d)
@@ -484,7 +514,7 @@ __device__ void keys_path(const SelectArgs &a, Smem &sm, uint32_t *bitmap, uint3
                     else if (b == d)
                         sm.cand[atomicAdd(&sm.ncand, 1u)] = comp_key(key, e);
                 }
-            }
+            });
             __syncthreads();
             rank_cand(m, sm.need);
             // 4. bin d's winners: its composites >= kappa
