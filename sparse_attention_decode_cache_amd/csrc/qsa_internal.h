@@ -318,7 +318,6 @@ struct ChunkArgs {
     int32_t n0, n_q, nb_last, kb;   // kb: blocks kept per query
     int32_t H, D;
     int32_t kv_heads, n_split;
-    int32_t sel_cache_keys;     // the select keeps each query's keys in LDS (set by the launcher)
     float scale;
     // grouped-union attention (k_union.hip) instead of the per-query one when
     // union_q > 0: groups of union_q consecutive queries
