@@ -220,3 +220,33 @@ def test_chunk_without_scores_output_is_identical(idx_heads, idx_dim, n0, n_q):
         o.step(i)
         if i % 7 == 0 or i == n_q - 1:
             _check_query(i, o, out_a, sel_a, scores, w.k_blocks, True, stats)
+
+
+def test_chunk_max_queries_sampled():
+    """The largest chunk the call takes (QSA_MAX_CHUNK = 4096 tokens) at 20k
+    context: 32 query groups of the score GEMM over its row ranges; every
+    query's ids checked for validity, sampled queries against the oracle at
+    their own position."""
+    from sparse_attention_decode_cache_amd import qsa as Q
+    n_q = Q.QSA_MAX_CHUNK
+    w = with_size(W.CTX64K, n0=20003, steps=n_q)
+    print(f"chunk {w.name}: n0={w.n0} n_q={n_q}", flush=True)
+    g = GpuLayer(w)
+    out, sel, scores = _chunk(g, n_q)
+    assert np.isfinite(out).all()
+    for i in range(n_q):
+        nb = (w.n0 + i + 1) // 4
+        row = sel[i]
+        assert np.all(np.diff(row) > 0) and row[0] >= 0 and row[-1] < nb, f"query {i} ids"
+    o = _Mirror(w)
+    stats = {"exact": 0, "threshold": 0, "attn_err": 0.0}
+    for i in [0, 1, 127, 128, 1023, 2048, 3001, 4094, 4095]:
+        pos = w.n0 + i
+        if o.L.n < pos:
+            rows = np.arange(o.L.n, pos)
+            o.L.raw[rows] = W.host_raw_rows(w, rows, 0)
+            o.L.K[rows], o.L.V[rows] = W.host_kv_rows(w, rows, 0)
+            o.L.n = pos
+        o.step(i)
+        _check_query(i, o, out, sel, scores, w.k_blocks, True, stats)
+    print(f"  {stats}")
