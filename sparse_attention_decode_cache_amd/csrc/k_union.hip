@@ -302,7 +302,7 @@ __global__ __launch_bounds__(kUT) void k_union_attend(ChunkArgs c)
         unit::static_for<PR>([&](auto rc) __attribute__((always_inline)) {
             constexpr int r = decltype(rc)::value;
             const int pr = t + kUT * r;
-            *(u32x4 *)(L.ktile + (pr / CH) * KROW + 16 * (pr % CH)) = kc.template at<r>();
+            *(u32x4 *)(L.ktile + (pr / CH) * KROW + 16 * ((pr % CH) ^ unit::swz(pr / CH))) = kc.template at<r>();
         });
         load_ids(it + 2, ib);
         load_rows(kp, it + 1, ia, kc);
@@ -319,7 +319,7 @@ __global__ __launch_bounds__(kUT) void k_union_attend(ChunkArgs c)
             // matrix cores (two register sets, by k-step parity)
             half8 a[2], bh[2][LRT], bl[2][LRT];
             auto fetch = [&](int ks, int b) __attribute__((always_inline)) {
-                __builtin_memcpy(&a[b], L.ktile + (16 * ct + mc) * KROW + 2 * (32 * ks + 8 * kg), 16);
+                __builtin_memcpy(&a[b], L.ktile + (16 * ct + mc) * KROW + 16 * ((4 * ks + kg) ^ unit::swz(16 * ct + mc)), 16);
 #pragma unroll
                 for (int i = 0; i < LRT; ++i) {
                     __builtin_memcpy(&bh[b][i], &L.qb[rt0 + i][ks][0][lane], 16);
@@ -397,7 +397,7 @@ __global__ __launch_bounds__(kUT) void k_union_attend(ChunkArgs c)
         unit::static_for<PR>([&](auto rc) __attribute__((always_inline)) {
             constexpr int r = decltype(rc)::value;
             const int pr = t + kUT * r;
-            *(u32x4 *)(L.ktile + (pr / CH) * KROW + 16 * (pr % CH)) =
+            *(u32x4 *)(L.ktile + (pr / CH) * KROW + 16 * ((pr % CH) ^ unit::swz(pr / CH))) =
                 kUC * it + pr / CH < ncells ? vc.template at<r>() : u32x4{0u, 0u, 0u, 0u};
         });
         load_rows(vp, it + 1, ia, vc);
@@ -422,7 +422,9 @@ __global__ __launch_bounds__(kUT) void k_union_attend(ChunkArgs c)
                 const int tile = wave + kUW * i;
                 a[i] = half8{};
                 if (NT % kUW == 0 || tile < NT) {
-                    const unsigned char *col = L.ktile + (32 * ks + 8 * kq) * KROW + 2 * (16 * tile + hn);
+                    // rows 32 ks + 8 kq + e: unit::swz = 2 kq for every e
+                    const unsigned char *col = L.ktile + (32 * ks + 8 * kq) * KROW +
+                                               16 * ((2 * tile + (hn >> 3)) ^ (2 * kq)) + 2 * (hn & 7);
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
                         a[i][e] = *(const _Float16 *)(col + e * KROW);

@@ -72,6 +72,13 @@ __device__ __forceinline__ void static_for(F &&f)
     }
 }
 
+// The LDS tile's 16-byte chunk c of row r sits at chunk c ^ swz(r): a P.V
+// operand read takes one 2-byte column of rows 8 kq + e (kq < 4, e < 8), and
+// with rows 2 DH + 16 bytes apart those four row groups would share banks;
+// the swizzle puts them 32 bytes apart.  Every access to the tile (K and V
+// writes, logit and P.V reads) goes through it.
+__device__ __forceinline__ int swz(int r) { return 2 * ((r >> 3) & 3); }
+
 // K moves in 16-byte chunks, V in 8-byte chunks, both through the LDS tile.
 template <int DH, int G, int NTH>
 struct CAShape {
@@ -269,7 +276,7 @@ __device__ void attend_unit(const QueryUnit &c, CALds<DH, G> &L, int s, int g, H
             constexpr int r = decltype(rc)::value;
             const int pr = t + NTH * r;
             if (pr < S::KPAIRS)
-                *(u32x4 *)(L.ktile + (pr / KCH) * KROW + 16 * (pr % KCH)) = kr.template at<r>();
+                *(u32x4 *)(L.ktile + (pr / KCH) * KROW + 16 * ((pr % KCH) ^ swz(pr / KCH))) = kr.template at<r>();
         });
         if (it + 1 < it1)
             load_k(it + 1, kr);
@@ -281,7 +288,7 @@ __device__ void attend_unit(const QueryUnit &c, CALds<DH, G> &L, int s, int g, H
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 half8 a, bh, bl;
-                __builtin_memcpy(&a, L.ktile + (16 * wave + mc) * KROW + 2 * (32 * ks + 8 * kg), 16);
+                __builtin_memcpy(&a, L.ktile + (16 * wave + mc) * KROW + 16 * ((4 * ks + kg) ^ swz(16 * wave + mc)), 16);
                 __builtin_memcpy(&bh, &L.qb[ks][0][lane], 16);
                 __builtin_memcpy(&bl, &L.qb[ks][1][lane], 16);
                 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bh, d, 0, 0, 0);
@@ -320,7 +327,8 @@ __device__ void attend_unit(const QueryUnit &c, CALds<DH, G> &L, int s, int g, H
             constexpr int r = decltype(rc)::value;
             const int pr = t + NTH * r;
             if (pr < S::VPAIRS)
-                *(u32x2 *)(L.ktile + (pr / VCH) * KROW + 8 * (pr % VCH)) = vr.template at<r>();
+                *(u32x2 *)(L.ktile + (pr / VCH) * KROW + 16 * (((pr % VCH) >> 1) ^ swz(pr / VCH)) +
+                           8 * ((pr % VCH) & 1)) = vr.template at<r>();
         });
         if (it + 1 < it1)
             load_v(it + 1, vr);
@@ -345,7 +353,9 @@ __device__ void attend_unit(const QueryUnit &c, CALds<DH, G> &L, int s, int g, H
                 const int tile = wave + NW * i;
                 if (NT % NW == 0 || tile < NT) {
                     half8 a;
-                    const unsigned char *col = L.ktile + (32 * ks + 8 * kq) * KROW + 2 * (16 * tile + hn);
+                    // rows 32 ks + 8 kq + e: swz = 2 kq for every e
+                    const unsigned char *col = L.ktile + (32 * ks + 8 * kq) * KROW +
+                                               16 * ((2 * tile + (hn >> 3)) ^ (2 * kq)) + 2 * (hn & 7);
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
                         a[e] = *(const _Float16 *)(col + e * KROW);
