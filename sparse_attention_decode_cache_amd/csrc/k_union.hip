@@ -169,7 +169,7 @@ struct ULds {
     alignas(16) unsigned char ktile[kUC * S::KROW];   // K, then V, of the iteration
     alignas(16) uint4 qb[RT][S::KS][2][kWave];
     alignas(16) float lg[S::RW][S::LGS];
-    alignas(16) _Float16 pt[2][S::RW][kUC];
+    alignas(16) _Float16 pt[2][S::RW][kUC + 8];     // rows padded: a P.V read's rows 4 banks apart
     float sc[S::RW], lrow[S::RW];
 };
 

@@ -106,7 +106,9 @@ struct CALds {
     alignas(16) unsigned char ktile[KT];
     alignas(16) uint4 qb[KS][2][kWave];
     float lg[kCI][G + 1];
-    alignas(16) _Float16 pt[2][G][kCI];        // softmax weights, hi and lo halves, [head][cell]
+    // softmax weights, hi and lo halves, [head][cell]: rows padded by 16
+    // bytes, so that the heads of one P.V operand read fall 4 banks apart
+    alignas(16) _Float16 pt[2][G][kCI + 8];
     float sc[G], mrow[G], lrow[G];
     int32_t ids[kChunkMaxIds];
 };
