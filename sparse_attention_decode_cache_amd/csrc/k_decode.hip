@@ -85,7 +85,9 @@ struct DecLds {
     alignas(16) unsigned char tiles[kTiles];     // K tile, V tile (or the full top-k's scratch)
     alignas(16) uint4 qb[S::KS][2][kWave];
     float lg[kPC][G + 1];
-    alignas(16) _Float16 pt[2][G][kPC];          // softmax weights, hi and lo halves, [head][cell]
+    // softmax weights, hi and lo halves, [head][cell]: rows padded by 16
+    // bytes, so that the heads of one P.V operand read fall 4 banks apart
+    alignas(16) _Float16 pt[2][G][kPC + 8];
     float sc[G];
     int32_t ids[kMaxOwn + 1];                    // the split's blocks (and the tail)
     alignas(16) uint32_t wcnt[2 * kNAW];         // winners per wave, entries t and 512 + t
@@ -126,6 +128,13 @@ __device__ inline RowChunks<DecShape<DH>::CPT> load_rows(const DecodeArgs &a, co
 // (past the pass's cells, up to the last k-step, and the tail block's cells
 // past the tail) are zeroed: their weight is 0, and 0 times whatever is there
 // could be NaN; their K rows are left alone (those logits become -inf).
+// The tiles' 16-byte chunk c of row r sits at chunk c ^ tswz(r): a P.V
+// operand read takes one 2-byte column of rows 8 kq + e (kq < 4, e < 8), and
+// with rows 2 DH + 16 bytes apart those four row groups would share banks;
+// the swizzle puts them 32 bytes apart.  Every access to the K and V tiles
+// goes through it.
+__device__ __forceinline__ int tswz(int r) { return 2 * ((r >> 3) & 3); }
+
 template <int DH, int CPT>
 __device__ inline void put_rows(unsigned char *ktile, unsigned char *vtile, const RowChunks<CPT> &kv, int lc,
                                 int sub, bool live)
@@ -134,9 +143,10 @@ __device__ inline void put_rows(unsigned char *ktile, unsigned char *vtile, cons
 #pragma unroll
     for (int j = 0; j < CPT; ++j)
         if (sub + 16 * j < S::CH) {
+            const int off = lc * S::KROW + 16 * ((sub + 16 * j) ^ tswz(lc));
             if (live)
-                *(uint4 *)(ktile + lc * S::KROW + 16 * (sub + 16 * j)) = kv.k[j];
-            *(uint4 *)(vtile + lc * S::KROW + 16 * (sub + 16 * j)) = live ? kv.v[j] : make_uint4(0u, 0u, 0u, 0u);
+                *(uint4 *)(ktile + off) = kv.k[j];
+            *(uint4 *)(vtile + off) = live ? kv.v[j] : make_uint4(0u, 0u, 0u, 0u);
         }
 }
 
@@ -386,7 +396,7 @@ __global__ __launch_bounds__(kNT) void k_decode_attend(DecodeArgs a)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 half8 av, bh, bl;
-                __builtin_memcpy(&av, ktile + (16 * wv + mc) * KROW + 2 * (32 * ks + 8 * kg), 16);
+                __builtin_memcpy(&av, ktile + (16 * wv + mc) * KROW + 16 * ((4 * ks + kg) ^ tswz(16 * wv + mc)), 16);
                 __builtin_memcpy(&bh, &L.qb[ks][0][lane], 16);
                 __builtin_memcpy(&bl, &L.qb[ks][1][lane], 16);
                 dd = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bh, dd, 0, 0, 0);
@@ -440,7 +450,9 @@ __global__ __launch_bounds__(kNT) void k_decode_attend(DecodeArgs a)
                 const int tile = wv + kNAW * i;
                 if (NT % kNAW == 0 || tile < NT) {
                     half8 av;
-                    const unsigned char *col = vtile + (32 * ks + 8 * kq) * KROW + 2 * (16 * tile + hn);
+                    // rows 32 ks + 8 kq + e: tswz = 2 kq for every e
+                    const unsigned char *col = vtile + (32 * ks + 8 * kq) * KROW +
+                                               16 * ((2 * tile + (hn >> 3)) ^ (2 * kq)) + 2 * (hn & 7);
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
                         av[e] = *(const _Float16 *)(col + e * KROW);
