@@ -81,6 +81,20 @@ struct Butterfly {
     }
 };
 
+// Slot of tile row r in the composites array: with P = 256/R threads
+// sharing an entry, each part's span of R/P rows starts 16 bytes further
+// along the banks than a plain array would put it, so that the P parts'
+// reads in one ranking step fall in distinct banks (unpadded, parts 0 and
+// 2 of a 64-row tile read 256 bytes apart: the same banks).
+template <int R>
+__device__ __forceinline__ int tl_slot(int r)
+{
+    constexpr int P = 256 / R;
+    return P > 1 ? r + 2 * (r / (R / P)) : r;
+}
+template <int R>
+constexpr int tl_size() { return R + 2 * (256 / R); }
+
 // Tile list: the T largest of the R composites in s_c (0 = no row), written
 // descending to lists[tile*T ...]; slots past the tile's rows get 0.  T <= R
 // is chosen per call (longer lists where a tile holds more winners).  Ranks
@@ -96,11 +110,12 @@ __device__ inline void write_tile_list(const uint64_t *s_c, uint64_t *lists, int
     constexpr int P = 256 / R;
     constexpr int SPAN = R / P;
     const int i = threadIdx.x / P, part = threadIdx.x % P;
-    const uint64_t c = s_c[i];
+    const uint64_t c = s_c[tl_slot<R>(i)];
+    const uint64_t *span = s_c + tl_slot<R>(part * SPAN);
     uint32_t rank = 0;
 #pragma unroll 8
     for (int u = 0; u < SPAN; ++u)
-        rank += s_c[part * SPAN + u] > c ? 1u : 0u;
+        rank += span[u] > c ? 1u : 0u;
     if constexpr (P >= 2)
         rank += wave::dpp<wave::kQuadXor1>(rank);
     if constexpr (P == 4)
@@ -143,10 +158,22 @@ struct ScoreShape {
 // once).  Query i sees the rows below a.nbq[i]; the rest get no key, no
 // list entry and a score of -inf.  The butterfly, keys and lists run once
 // per query.
+// Slot (in float4s) of quarter k4 of row chunk ch in the folded queries:
+// the H = EPL/4 float4s of a chunk are stored apart, L chunks to a run, so
+// that the L lanes of a row reading quarter k4 of chunks ch0 .. ch0+L-1 read
+// L consecutive float4s (no two in the same banks).  The squared-norm sum
+// of the histogram window reads every element and does not depend on the
+// order.
+template <int L, int H>
+__device__ __forceinline__ int q_slot(int ch, int k4)
+{
+    return (ch / L) * (H * L) + k4 * L + ch % L;
+}
+
 template <int LPR, int Q, int EPL>
 struct ScoreMultiLds {
     float qw[Q][LPR * EPL];
-    uint64_t c[Q][ScoreShape<LPR>::R];
+    uint64_t c[Q][tl_size<ScoreShape<LPR>::R>()];
     u32x4 fresh[LPR];
     float gam[128];             // RMSNorm weights (histogram window)
 };
@@ -223,7 +250,7 @@ __device__ inline void score_tile(const ScoreMultiArgs &a, ScoreLdsOf<F16, LPR, 
             f.y *= wraw[j];
             f.z *= wraw[j];
             f.w *= wraw[j];
-            *(float4 *)&sl.qw[qi][e0] = f;
+            *(float4 *)&sl.qw[qi][4 * q_slot<L, EPL / 4>(e0 / EPL, (e0 % EPL) / 4)] = f;
         }
     }
 
@@ -288,13 +315,12 @@ __device__ inline void score_tile(const ScoreMultiArgs &a, ScoreLdsOf<F16, LPR, 
             v[qi][g] = 0.0f;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
-        const int e0 = (col + L * c) * EPL;
         float qw[Q][EPL];
 #pragma unroll
         for (int qi = 0; qi < Q; ++qi)
 #pragma unroll
             for (int k4 = 0; k4 < EPL / 4; ++k4) {
-                const float4 f = *(const float4 *)&sl.qw[qi][e0 + 4 * k4];
+                const float4 f = *(const float4 *)&sl.qw[qi][4 * q_slot<L, EPL / 4>(col + L * c, k4)];
                 qw[qi][4 * k4] = f.x;
                 qw[qi][4 * k4 + 1] = f.y;
                 qw[qi][4 * k4 + 2] = f.z;
@@ -361,7 +387,7 @@ __device__ inline void score_tile(const ScoreMultiArgs &a, ScoreLdsOf<F16, LPR, 
             } else if (r < a.nb && a.scores) {
                 a.scores[qi * a.ld_scores + r] = -__builtin_inff();
             }
-            sl.c[qi][local] = c;
+            sl.c[qi][tl_slot<R>(local)] = c;
         }
     }
     __syncthreads();
