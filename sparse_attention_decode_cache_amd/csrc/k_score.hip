@@ -228,6 +228,13 @@ __device__ inline void score_tile(const ScoreMultiArgs &a, ScoreLdsOf<F16, LPR, 
             wraw[j] = a.w[qi][e0 / a.D];
         }
     }
+    // The pool of a completed block runs before this tile's rows are
+    // requested: loads are counted in issue order, so pool loads issued after
+    // the rows would wait for the whole tile, and the pool's double-precision
+    // chain would then start only when the tile is in, which can be the end
+    // of the pass.  The pooled row reaches this tile through LDS.
+    if (pool_here && a.upd.nblk > 0)
+        pool_row<F16>(a.upd, a.upd.b0, threadIdx.x, sl.fresh);
     __builtin_amdgcn_sched_barrier(0);
 
     const char *rows = (const char *)a.summary;
@@ -257,12 +264,8 @@ __device__ inline void score_tile(const ScoreMultiArgs &a, ScoreLdsOf<F16, LPR, 
     if (want_g && (int)threadIdx.x < a.D)
         sl.gam[threadIdx.x] = graw;
 
-    if (pool_here) {
-        if (a.upd.new_idx_row)
-            append_rows(a.upd, threadIdx.x, 256);
-        if (a.upd.nblk > 0)
-            pool_row<F16>(a.upd, a.upd.b0, threadIdx.x, sl.fresh);
-    }
+    if (pool_here && a.upd.new_idx_row)
+        append_rows(a.upd, threadIdx.x, 256);
     __syncthreads();
     if (pool_here && a.upd.nblk > 0) {
 #pragma unroll
