@@ -233,6 +233,12 @@ __device__ inline void score_tile(const ScoreMultiArgs &a, ScoreLdsOf<F16, LPR, 
     // the rows would wait for the whole tile, and the pool's double-precision
     // chain would then start only when the tile is in, which can be the end
     // of the pass.  The pooled row reaches this tile through LDS.
+    // The appended token's rows are fetched ahead of the tile for the same
+    // reason, and stored once the tile's loads are out.
+    const bool app = pool_here && a.upd.new_idx_row;
+    AppendWords aw;
+    if (app)
+        append_fetch(a.upd, threadIdx.x, 256, aw);
     if (pool_here && a.upd.nblk > 0)
         pool_row<F16>(a.upd, a.upd.b0, threadIdx.x, sl.fresh);
     __builtin_amdgcn_sched_barrier(0);
@@ -264,8 +270,8 @@ __device__ inline void score_tile(const ScoreMultiArgs &a, ScoreLdsOf<F16, LPR, 
     if (want_g && (int)threadIdx.x < a.D)
         sl.gam[threadIdx.x] = graw;
 
-    if (pool_here && a.upd.new_idx_row)
-        append_rows(a.upd, threadIdx.x, 256);
+    if (app)
+        append_put(a.upd, threadIdx.x, 256, aw);
     __syncthreads();
     if (pool_here && a.upd.nblk > 0) {
 #pragma unroll

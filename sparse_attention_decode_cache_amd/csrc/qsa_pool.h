@@ -67,6 +67,60 @@ __device__ inline void append_rows(const UpdateArgs &a, int t, int nthreads)
     }
 }
 
+// The append split in two for a caller that streams other rows meanwhile:
+// append_fetch loads the first kAppendPre words per thread of each appended
+// row into registers, append_put stores them and copies whatever lies past
+// them word by word.  Together they do what append_rows does.
+constexpr int kAppendPre = 2;
+
+struct AppendWords {
+    uint32_t idx[kAppendPre], k[kAppendPre], v[kAppendPre];
+};
+
+__device__ inline void append_fetch(const UpdateArgs &a, int t, int nthreads, AppendWords &w)
+{
+    const uint32_t *src = (const uint32_t *)a.new_idx_row;
+    const uint32_t *sk = (const uint32_t *)a.new_k_row;
+    const uint32_t *sv = (const uint32_t *)a.new_v_row;
+    const int iw = a.n_new * a.idx_row_words;
+    const int kw = a.n_new * a.kv_row_words;
+#pragma unroll
+    for (int m = 0; m < kAppendPre; ++m) {
+        const int i = t + nthreads * m;
+        w.idx[m] = i < iw ? src[i] : 0u;
+        w.k[m] = i < kw ? sk[i] : 0u;
+        w.v[m] = i < kw ? sv[i] : 0u;
+    }
+}
+
+__device__ inline void append_put(const UpdateArgs &a, int t, int nthreads, const AppendWords &w)
+{
+    const uint32_t *src = (const uint32_t *)a.new_idx_row;
+    uint32_t *dst = (uint32_t *)a.idx_k + (size_t)a.pos * a.idx_row_words;
+    const uint32_t *sk = (const uint32_t *)a.new_k_row;
+    const uint32_t *sv = (const uint32_t *)a.new_v_row;
+    uint32_t *dk = (uint32_t *)a.k + (size_t)a.pos * a.kv_row_words;
+    uint32_t *dv = (uint32_t *)a.v + (size_t)a.pos * a.kv_row_words;
+    const int iw = a.n_new * a.idx_row_words;
+    const int kw = a.n_new * a.kv_row_words;
+#pragma unroll
+    for (int m = 0; m < kAppendPre; ++m) {
+        const int i = t + nthreads * m;
+        if (i < iw)
+            dst[i] = w.idx[m];
+        if (i < kw) {
+            dk[i] = w.k[m];
+            dv[i] = w.v[m];
+        }
+    }
+    for (int i = t + nthreads * kAppendPre; i < iw; i += nthreads)
+        dst[i] = src[i];
+    for (int i = t + nthreads * kAppendPre; i < kw; i += nthreads) {
+        dk[i] = sk[i];
+        dv[i] = sv[i];
+    }
+}
+
 // Pool summary row b with a 256-thread workgroup (thread t).  Every thread of
 // a wave must call it (wave reduction); waves h >= H do nothing.  When
 // lds_row is given, the stored row is also written there (same bits).
