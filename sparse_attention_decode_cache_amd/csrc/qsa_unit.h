@@ -79,16 +79,16 @@ __device__ __forceinline__ void static_for(F &&f)
 // writes, logit and P.V reads) goes through it.
 __device__ __forceinline__ int swz(int r) { return 2 * ((r >> 3) & 3); }
 
-// K moves in 16-byte chunks, V in 8-byte chunks, both through the LDS tile.
+// K and V move in 16-byte chunks, both through the LDS tile.
 template <int DH, int G, int NTH>
 struct CAShape {
     static constexpr int NW = NTH / kWave;                // waves
     static constexpr int KCH = DH / 8;                    // 16-byte chunks of a K row
     static constexpr int KPAIRS = kCI * KCH;
     static constexpr int KR = (KPAIRS + NTH - 1) / NTH;   // K chunks per thread
-    static constexpr int VCH = DH / 4;                    // 8-byte chunks of a V row
+    static constexpr int VCH = DH / 8;                    // 16-byte chunks of a V row
     static constexpr int VPAIRS = kCI * VCH;
-    static constexpr int VR = (VPAIRS + NTH - 1) / NTH;   // V chunks (cells) per thread
+    static constexpr int VR = (VPAIRS + NTH - 1) / NTH;   // V chunks per thread
     static constexpr int KS = DH / 32;                    // MFMA k-steps of a row
     static constexpr int KROW = 2 * DH + 16;              // padded LDS bytes of a K (or V) row
     static constexpr int NT = DH / 16;                    // 16-dim output tiles of P.V
@@ -246,12 +246,12 @@ __device__ void attend_unit(const QueryUnit &c, CALds<DH, G> &L, int s, int g, H
                 kr.template at<r>() = *(const u32x4 *)(c.k + row_base(it, pr / KCH) + 8 * (pr % KCH));
         });
     };
-    auto load_v = [&](int it, Regs8<u32x2> &vr) __attribute__((always_inline)) {
+    auto load_v = [&](int it, Regs8<u32x4> &vr) __attribute__((always_inline)) {
         static_for<VR>([&](auto rc) __attribute__((always_inline)) {
             constexpr int r = decltype(rc)::value;
             const int pr = t + NTH * r;
             if (pr < S::VPAIRS)
-                vr.template at<r>() = *(const u32x2 *)(c.v + row_base(it, pr / VCH) + 4 * (pr % VCH));
+                vr.template at<r>() = *(const u32x4 *)(c.v + row_base(it, pr / VCH) + 8 * (pr % VCH));
         });
     };
 
@@ -266,7 +266,7 @@ __device__ void attend_unit(const QueryUnit &c, CALds<DH, G> &L, int s, int g, H
     // K and V one iteration ahead: K leaves the registers for the LDS tile
     // first thing, V when the tile is free again (after the logits)
     Regs8<u32x4> kr;
-    Regs8<u32x2> vr;
+    Regs8<u32x4> vr;
     if (it0 < it1) {
         load_k(it0, kr);
         load_v(it0, vr);
@@ -329,8 +329,8 @@ __device__ void attend_unit(const QueryUnit &c, CALds<DH, G> &L, int s, int g, H
             constexpr int r = decltype(rc)::value;
             const int pr = t + NTH * r;
             if (pr < S::VPAIRS)
-                *(u32x2 *)(L.ktile + (pr / VCH) * KROW + 16 * (((pr % VCH) >> 1) ^ swz(pr / VCH)) +
-                           8 * ((pr % VCH) & 1)) = vr.template at<r>();
+                *(u32x4 *)(L.ktile + (pr / VCH) * KROW + 16 * ((pr % VCH) ^ swz(pr / VCH))) =
+                    vr.template at<r>();
         });
         if (it + 1 < it1)
             load_v(it + 1, vr);
