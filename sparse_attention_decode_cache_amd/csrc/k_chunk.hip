@@ -509,11 +509,19 @@ hipError_t score_ks(const ChunkArgs &c, dim3 grid, hipStream_t s)
 
 // ----------------------------------------------------------------- select
 
-// The chunk select's LDS is Smem and the id bitmap only: its passes read a
-// query's keys from memory (L2) each time rather than holding them in LDS,
-// so that two of its workgroups share a CU and hide each other's latency
-// (with the keys held, one per CU: 66 against 59 us at 1024 queries x 31,819
-// blocks).
+// The chunk select's LDS is Smem, the id bitmap and a list of up to
+// kChunkKeep composites: its passes read a query's keys from memory (L2)
+// rather than holding them all in LDS, so that two of its workgroups share a
+// CU and hide each other's latency (with the keys held, one per CU: 66
+// against 59 us at 1024 queries x 31,819 blocks); the keys above the pruning
+// bound (a few per cent) are listed by the histogram pass, so the marking
+// pass reads the list instead of memory.
+constexpr uint32_t kChunkKeep = 4096;
+
+__host__ __device__ inline size_t chunk_sel_lds(int32_t nb)
+{
+    return sel::lds_bytes(nb) + sizeof(uint64_t) * kChunkKeep;
+}
 
 __global__ __launch_bounds__(sel::kT) void k_chunk_select(ChunkArgs c)
 {
@@ -541,11 +549,12 @@ __global__ __launch_bounds__(sel::kT) void k_chunk_select(ChunkArgs c)
     sel::Smem &sm = *reinterpret_cast<sel::Smem *>(lds);
     uint32_t *bitmap = reinterpret_cast<uint32_t *>(lds + (sizeof(sel::Smem) + 15) / 16 * 16);
     uint32_t *lkeys = nullptr;
+    uint64_t *klist = reinterpret_cast<uint64_t *>(lds + sel::lds_bytes(nbq));
     sel::keys_path(a, sm, bitmap, lkeys, [=](uint32_t slot, uint32_t id) {
         row[slot] = (int32_t)id;
         if (row_out)
             row_out[slot] = (int32_t)id;
-    });
+    }, klist, kChunkKeep);
 }
 
 // ----------------------------------------------------------------- attend
@@ -821,7 +830,7 @@ hipError_t launch_chunk_rest(ChunkArgs c, bool f16, int Dh, int G, hipStream_t s
             return e;
     }
     if (c.nb_last > c.kb || c.sel_out) {
-        const size_t lds = sel::lds_bytes(c.nb_last);
+        const size_t lds = chunk_sel_lds(c.nb_last);
         if (lds > sel::kMaxLds)
             return hipErrorInvalidValue;
         if (lds > 64 * 1024) {

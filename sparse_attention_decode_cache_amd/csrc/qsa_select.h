@@ -60,7 +60,7 @@ struct Smem {
     alignas(16) uint32_t rmax[kWaves];
     alignas(16) uint32_t wtot[kWaves];
     uint64_t kappa;
-    uint32_t d, need, in_d, ncand, bad;
+    uint32_t d, need, in_d, ncand, bad, nkeep;
     // general path
     uint32_t wsum[kWaves], woff[kWaves];
     uint64_t wmin[kWaves], wmax[kWaves];
@@ -333,10 +333,14 @@ __device__ void general_path(const SelectArgs &a, Smem &sm, uint32_t *bitmap, ui
 // on the 1024 maxima), and only keys >= tau -- a few per cent -- enter the
 // histogram, the boundary bin and the marks.  Non-finite scores or a
 // crowded bin fall back to the radix refinement.  lkeys (LDS, nb words, or
-// null): the keys are read from memory once and kept there.  Requires
+// null): the keys are read from memory once and kept there.  keep (LDS,
+// keep_cap composites, or null): the histogram pass also lists the keys >=
+// tau there, and the marking pass walks that list instead of every key
+// when it held them all (the same keys, so the same marks).  Requires
 // nb > k.  Whole workgroup calls; emit as in run().
 template <class Emit>
-__device__ void keys_path(const SelectArgs &a, Smem &sm, uint32_t *bitmap, uint32_t *lkeys, Emit emit)
+__device__ void keys_path(const SelectArgs &a, Smem &sm, uint32_t *bitmap, uint32_t *lkeys, Emit emit,
+                          uint64_t *keep = nullptr, uint32_t keep_cap = 0u)
 {
     const uint32_t nb = (uint32_t)a.nb;
     const uint32_t k = (uint32_t)a.k;
@@ -347,6 +351,7 @@ __device__ void keys_path(const SelectArgs &a, Smem &sm, uint32_t *bitmap, uint3
     sm.hist[t] = 0u;
     if (t == 0) {
         sm.ncand = 0u;
+        sm.nkeep = 0u;
         sm.d = 0xFFFFFFFFu;
     }
     // 1. keys (to LDS when asked), their range, and this thread's largest;
@@ -495,10 +500,17 @@ __device__ void keys_path(const SelectArgs &a, Smem &sm, uint32_t *bitmap, uint3
         __syncthreads();
     }
     if (!general) {
-        // 2. histogram of the keys >= tau
-        each_key([&](uint32_t key, uint32_t) __attribute__((always_inline)) {
-            if (key >= tau)
+        // 2. histogram of the keys >= tau (and their list, when kept)
+        const bool keeping = keep != nullptr && tau != 0u;
+        each_key([&](uint32_t key, uint32_t e) __attribute__((always_inline)) {
+            if (key >= tau) {
                 atomicAdd(&sm.hist[bin_of(key)], 1u);
+                if (keeping) {
+                    const uint32_t j = atomicAdd(&sm.nkeep, 1u);
+                    if (j < keep_cap)
+                        keep[j] = comp_key(key, e);
+                }
+            }
         });
         __syncthreads();
         kth_bin(k);
@@ -506,7 +518,7 @@ __device__ void keys_path(const SelectArgs &a, Smem &sm, uint32_t *bitmap, uint3
         general = d == 0xFFFFFFFFu || m > (uint32_t)kCap;
         if (!general) {
             // 3. keys above bin d are winners; bin d's entries are ranked
-            each_key([&](uint32_t key, uint32_t e) __attribute__((always_inline)) {
+            auto mark = [&](uint32_t key, uint32_t e) __attribute__((always_inline)) {
                 if (key >= tau) {
                     const uint32_t b = bin_of(key);
                     if (b > d)
@@ -514,7 +526,16 @@ __device__ void keys_path(const SelectArgs &a, Smem &sm, uint32_t *bitmap, uint3
                     else if (b == d)
                         sm.cand[atomicAdd(&sm.ncand, 1u)] = comp_key(key, e);
                 }
-            });
+            };
+            const uint32_t nkeep = sm.nkeep;
+            if (keeping && nkeep <= keep_cap) {
+                for (uint32_t j = t; j < nkeep; j += kT) {
+                    const uint64_t c = keep[j];
+                    mark((uint32_t)(c >> 32), ~(uint32_t)c);
+                }
+            } else {
+                each_key(mark);
+            }
             __syncthreads();
             rank_cand(m, sm.need);
             // 4. bin d's winners: its composites >= kappa
