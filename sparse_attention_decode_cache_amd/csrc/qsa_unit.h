@@ -79,6 +79,22 @@ __device__ __forceinline__ void static_for(F &&f)
 // writes, logit and P.V reads) goes through it.
 __device__ __forceinline__ int swz(int r) { return 2 * ((r >> 3) & 3); }
 
+// LDS transpose read of 16-bit values (gfx950): within each group of 16
+// lanes, lane r names 4 consecutive values M[r][0..3] at p (8-byte aligned),
+// and lane j receives M[4 i + j / 4][j % 4] for i = 0..3.
+typedef __attribute__((__vector_size__(4 * sizeof(__fp16)))) __fp16 tr16x4;
+
+__device__ __forceinline__ void lds_tr4(const unsigned char *p, half8 &a, int at)
+{
+    typedef __attribute__((address_space(3))) tr16x4 *lds_tr_ptr;
+    const tr16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_tr_ptr)(p));
+    _Float16 h[4];
+    __builtin_memcpy(h, &v, 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        a[at + e] = h[e];
+}
+
 // K and V move in 16-byte chunks, both through the LDS tile.
 template <int DH, int G, int NTH>
 struct CAShape {
@@ -354,13 +370,15 @@ __device__ void attend_unit(const QueryUnit &c, CALds<DH, G> &L, int s, int g, H
             for (int i = 0; i < TPW; ++i) {
                 const int tile = wave + NW * i;
                 if (NT % NW == 0 || tile < NT) {
+                    // a[e] = V[32 ks + 8 kq + e][16 tile + hn]: two transpose
+                    // reads, lane hn of the group naming row 8 kq + 4 h + hn / 4,
+                    // dims 16 tile + 4 (hn % 4) .. +4 (rows 32 ks + 8 kq + e: swz =
+                    // 2 kq for every e)
                     half8 a;
-                    // rows 32 ks + 8 kq + e: swz = 2 kq for every e
-                    const unsigned char *col = L.ktile + (32 * ks + 8 * kq) * KROW +
-                                               16 * ((2 * tile + (hn >> 3)) ^ (2 * kq)) + 2 * (hn & 7);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        a[e] = *(const _Float16 *)(col + e * KROW);
+                    const unsigned char *p0 = L.ktile + (32 * ks + 8 * kq + (hn >> 2)) * KROW +
+                                              16 * ((2 * tile + ((hn & 3) >> 1)) ^ (2 * kq)) + 8 * (hn & 1);
+                    lds_tr4(p0, a, 0);
+                    lds_tr4(p0 + 4 * KROW, a, 4);
                     acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bh, acc[i], 0, 0, 0);
                     acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bl, acc[i], 0, 0, 0);
                 }
