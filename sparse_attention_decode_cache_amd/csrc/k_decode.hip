@@ -44,6 +44,7 @@
 #include "qsa_hist.h"
 #include "qsa_internal.h"
 #include "qsa_select.h"
+#include "qsa_unit.h"
 #include "qsa_wave.h"
 
 namespace qsa {
@@ -449,13 +450,13 @@ __global__ __launch_bounds__(kNT) void k_decode_attend(DecodeArgs a)
             for (int i = 0; i < TPW; ++i) {
                 const int tile = wv + kNAW * i;
                 if (NT % kNAW == 0 || tile < NT) {
+                    // av[e] = V[32 ks + 8 kq + e][16 tile + hn] by two transpose
+                    // reads (rows 32 ks + 8 kq + e: tswz = 2 kq for every e)
                     half8 av;
-                    // rows 32 ks + 8 kq + e: tswz = 2 kq for every e
-                    const unsigned char *col = vtile + (32 * ks + 8 * kq) * KROW +
-                                               16 * ((2 * tile + (hn >> 3)) ^ (2 * kq)) + 2 * (hn & 7);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        av[e] = *(const _Float16 *)(col + e * KROW);
+                    const unsigned char *p0 = vtile + (32 * ks + 8 * kq + (hn >> 2)) * KROW +
+                                              16 * ((2 * tile + ((hn & 3) >> 1)) ^ (2 * kq)) + 8 * (hn & 1);
+                    unit::lds_tr4(p0, av, 0);
+                    unit::lds_tr4(p0 + 4 * KROW, av, 4);
                     acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bh, acc[i], 0, 0, 0);
                     acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bl, acc[i], 0, 0, 0);
                 }

@@ -422,12 +422,12 @@ __global__ __launch_bounds__(kUT) void k_union_attend(ChunkArgs c)
                 const int tile = wave + kUW * i;
                 a[i] = half8{};
                 if (NT % kUW == 0 || tile < NT) {
-                    // rows 32 ks + 8 kq + e: unit::swz = 2 kq for every e
-                    const unsigned char *col = L.ktile + (32 * ks + 8 * kq) * KROW +
-                                               16 * ((2 * tile + (hn >> 3)) ^ (2 * kq)) + 2 * (hn & 7);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        a[i][e] = *(const _Float16 *)(col + e * KROW);
+                    // a[i][e] = V[32 ks + 8 kq + e][16 tile + hn] by two transpose
+                    // reads (rows 32 ks + 8 kq + e: unit::swz = 2 kq for every e)
+                    const unsigned char *p0 = L.ktile + (32 * ks + 8 * kq + (hn >> 2)) * KROW +
+                                              16 * ((2 * tile + ((hn & 3) >> 1)) ^ (2 * kq)) + 8 * (hn & 1);
+                    unit::lds_tr4(p0, a[i], 0);
+                    unit::lds_tr4(p0 + 4 * KROW, a[i], 4);
                 }
             }
             // (rows past the group's take whatever their weight rows hold:
