@@ -95,6 +95,22 @@ __device__ __forceinline__ void lds_tr4(const unsigned char *p, half8 &a, int at
         a[at + e] = h[e];
 }
 
+// The V tile's layout (head dims >= 128): rows 2 DH + 32 bytes apart, so that
+// consecutive rows sit 32 bytes apart in the banks, and chunk c of row r at
+// c ^ vswz(r), the two 8-chunk halves of a 16-chunk group swapped for rows
+// with odd r / 8.  A P.V transpose read takes 32 bytes from each of 4
+// consecutive rows per 16-lane group, and a half-wave's two groups take rows
+// 8 apart: their 8 windows then fill the 64 banks once.  Head dim 64 (8
+// chunks a row) keeps the K layout.
+template <int DH>
+__device__ __forceinline__ int vswz(int r)
+{
+    if constexpr (DH >= 128)
+        return 8 * ((r >> 3) & 1);
+    else
+        return swz(r);
+}
+
 // K and V move in 16-byte chunks, both through the LDS tile.
 template <int DH, int G, int NTH>
 struct CAShape {
@@ -106,7 +122,8 @@ struct CAShape {
     static constexpr int VPAIRS = kCI * VCH;
     static constexpr int VR = (VPAIRS + NTH - 1) / NTH;   // V chunks per thread
     static constexpr int KS = DH / 32;                    // MFMA k-steps of a row
-    static constexpr int KROW = 2 * DH + 16;              // padded LDS bytes of a K (or V) row
+    static constexpr int KROW = 2 * DH + 16;              // padded LDS bytes of a K row
+    static constexpr int VROW = DH >= 128 ? 2 * DH + 32 : KROW;   // and of a V row
     static constexpr int NT = DH / 16;                    // 16-dim output tiles of P.V
     static constexpr int TPW = (NT + NW - 1) / NW;        // tiles per wave
     static_assert(NTH % KCH == 0 && NTH % VCH == 0 && KPAIRS % kWave == 0 && VPAIRS % kWave == 0 &&
@@ -117,8 +134,9 @@ template <int DH, int G>
 struct CALds {
     static constexpr int KS = DH / 32;
     static constexpr int KROW = 2 * DH + 16;
+    static constexpr int VROW = DH >= 128 ? 2 * DH + 32 : KROW;
     // the K tile, then (after the logits) the V tile of the iteration
-    static constexpr int KT = kCI * KROW;
+    static constexpr int KT = kCI * (VROW > KROW ? VROW : KROW);
     alignas(16) unsigned char ktile[KT];
     alignas(16) uint4 qb[KS][2][kWave];
     float lg[kCI][G + 1];
@@ -193,7 +211,7 @@ template <int DH, int G, int NTH, int MODE, bool COHERENT = false, class Hook = 
 __device__ void attend_unit(const QueryUnit &c, CALds<DH, G> &L, int s, int g, Hook hook = Hook())
 {
     using S = CAShape<DH, G, NTH>;
-    constexpr int KCH = S::KCH, VCH = S::VCH, KR = S::KR, VR = S::VR, KS = S::KS, KROW = S::KROW,
+    constexpr int KCH = S::KCH, VCH = S::VCH, KR = S::KR, VR = S::VR, KS = S::KS, KROW = S::KROW, VROW = S::VROW,
                   NT = S::NT, TPW = S::TPW, NW = S::NW;
     constexpr bool SIGNED = MODE != kSplits;        // ids carry a masked-out sign bit
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -345,7 +363,7 @@ __device__ void attend_unit(const QueryUnit &c, CALds<DH, G> &L, int s, int g, H
             constexpr int r = decltype(rc)::value;
             const int pr = t + NTH * r;
             if (pr < S::VPAIRS)
-                *(u32x4 *)(L.ktile + (pr / VCH) * KROW + 16 * ((pr % VCH) ^ swz(pr / VCH))) =
+                *(u32x4 *)(L.ktile + (pr / VCH) * VROW + 16 * ((pr % VCH) ^ vswz<DH>(pr / VCH))) =
                     vr.template at<r>();
         });
         if (it + 1 < it1)
@@ -372,13 +390,14 @@ __device__ void attend_unit(const QueryUnit &c, CALds<DH, G> &L, int s, int g, H
                 if (NT % NW == 0 || tile < NT) {
                     // a[e] = V[32 ks + 8 kq + e][16 tile + hn]: two transpose
                     // reads, lane hn of the group naming row 8 kq + 4 h + hn / 4,
-                    // dims 16 tile + 4 (hn % 4) .. +4 (rows 32 ks + 8 kq + e: swz =
-                    // 2 kq for every e)
+                    // dims 16 tile + 4 (hn % 4) .. +4 (rows 32 ks + 8 kq + e share
+                    // one vswz)
                     half8 a;
-                    const unsigned char *p0 = L.ktile + (32 * ks + 8 * kq + (hn >> 2)) * KROW +
-                                              16 * ((2 * tile + ((hn & 3) >> 1)) ^ (2 * kq)) + 8 * (hn & 1);
+                    const int r0 = 32 * ks + 8 * kq + (hn >> 2);
+                    const unsigned char *p0 = L.ktile + r0 * VROW +
+                                              16 * ((2 * tile + ((hn & 3) >> 1)) ^ vswz<DH>(r0)) + 8 * (hn & 1);
                     lds_tr4(p0, a, 0);
-                    lds_tr4(p0 + 4 * KROW, a, 4);
+                    lds_tr4(p0 + 4 * VROW, a, 4);
                     acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bh, acc[i], 0, 0, 0);
                     acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bl, acc[i], 0, 0, 0);
                 }
