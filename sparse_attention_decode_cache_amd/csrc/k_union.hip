@@ -147,7 +147,8 @@ __device__ inline float group_sum(float v)
 template <int DH, int RT>
 struct UShape {
     static constexpr int KS = DH / 32;              // MFMA k-steps of a row
-    static constexpr int KROW = 2 * DH + 16;        // padded LDS bytes of a K / V row
+    static constexpr int KROW = 2 * DH + 16;        // padded LDS bytes of a K row
+    static constexpr int VROW = DH >= 128 ? 2 * DH + 32 : KROW;   // and of a V row (unit::vswz)
     static constexpr int CH = DH / 8;               // 16-byte chunks of a row
     static constexpr int PAIRS = kUC * CH;          // (cell, chunk) pairs of an iteration
     static constexpr int PR = PAIRS / kUT;
@@ -166,7 +167,7 @@ struct UShape {
 template <int DH, int RT>
 struct ULds {
     using S = UShape<DH, RT>;
-    alignas(16) unsigned char ktile[kUC * S::KROW];   // K, then V, of the iteration
+    alignas(16) unsigned char ktile[kUC * (S::VROW > S::KROW ? S::VROW : S::KROW)];   // K, then V, of the iteration
     alignas(16) uint4 qb[RT][S::KS][2][kWave];
     alignas(16) float lg[S::RW][S::LGS];
     alignas(16) _Float16 pt[2][S::RW][kUC + 8];     // rows padded: a P.V read's rows 4 banks apart
@@ -177,7 +178,7 @@ template <int DH, int G, int RT>
 __global__ __launch_bounds__(kUT) void k_union_attend(ChunkArgs c)
 {
     using S = UShape<DH, RT>;
-    constexpr int KS = S::KS, KROW = S::KROW, CH = S::CH, PR = S::PR, TPR = S::TPR, CPS = S::CPS,
+    constexpr int KS = S::KS, KROW = S::KROW, VROW = S::VROW, CH = S::CH, PR = S::PR, TPR = S::TPR, CPS = S::CPS,
                   LW = S::LW, LRT = S::LRT, NT = S::NT, TPW = S::TPW;
     extern __shared__ uint4 ua_lds[];
     ULds<DH, RT> &L = *reinterpret_cast<ULds<DH, RT> *>(ua_lds);
@@ -397,7 +398,7 @@ __global__ __launch_bounds__(kUT) void k_union_attend(ChunkArgs c)
         unit::static_for<PR>([&](auto rc) __attribute__((always_inline)) {
             constexpr int r = decltype(rc)::value;
             const int pr = t + kUT * r;
-            *(u32x4 *)(L.ktile + (pr / CH) * KROW + 16 * ((pr % CH) ^ unit::swz(pr / CH))) =
+            *(u32x4 *)(L.ktile + (pr / CH) * VROW + 16 * ((pr % CH) ^ unit::vswz<DH>(pr / CH))) =
                 kUC * it + pr / CH < ncells ? vc.template at<r>() : u32x4{0u, 0u, 0u, 0u};
         });
         load_rows(vp, it + 1, ia, vc);
@@ -423,11 +424,12 @@ __global__ __launch_bounds__(kUT) void k_union_attend(ChunkArgs c)
                 a[i] = half8{};
                 if (NT % kUW == 0 || tile < NT) {
                     // a[i][e] = V[32 ks + 8 kq + e][16 tile + hn] by two transpose
-                    // reads (rows 32 ks + 8 kq + e: unit::swz = 2 kq for every e)
-                    const unsigned char *p0 = L.ktile + (32 * ks + 8 * kq + (hn >> 2)) * KROW +
-                                              16 * ((2 * tile + ((hn & 3) >> 1)) ^ (2 * kq)) + 8 * (hn & 1);
+                    // reads (rows 32 ks + 8 kq + e share one unit::vswz)
+                    const int r0 = 32 * ks + 8 * kq + (hn >> 2);
+                    const unsigned char *p0 = L.ktile + r0 * VROW +
+                                              16 * ((2 * tile + ((hn & 3) >> 1)) ^ unit::vswz<DH>(r0)) + 8 * (hn & 1);
                     unit::lds_tr4(p0, a[i], 0);
-                    unit::lds_tr4(p0 + 4 * KROW, a[i], 4);
+                    unit::lds_tr4(p0 + 4 * VROW, a[i], 4);
                 }
             }
             // (rows past the group's take whatever their weight rows hold:
